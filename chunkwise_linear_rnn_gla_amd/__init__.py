@@ -1,0 +1,112 @@
+"""MI355X-native Gated Linear Attention (chunkwise forward and backward).
+
+The computation runs in ``libgla.so`` (HIP kernels for gfx950, C ABI in
+``include/gla.h``).  This package only marshals arguments: PyTorch supplies
+device memory and the current HIP stream.
+
+``fwd`` / ``bwd`` allocate outputs and workspace with torch and call the
+library; ``_abi`` exposes the raw C entry points under their C names.
+"""
+from __future__ import annotations
+
+from . import _abi
+from ._abi import (GLA_BF16, GLA_FP32, GlaDims, GlaError, gla_abi_version, gla_bwd,  # noqa: F401
+                   gla_bwd_workspace_size, gla_fwd, gla_fwd_workspace_size, gla_status_string)
+
+__all__ = ["fwd", "bwd", "dims_for", "gla_fwd", "gla_bwd", "gla_fwd_workspace_size",
+           "gla_bwd_workspace_size", "gla_abi_version", "gla_status_string", "GlaDims",
+           "GlaError", "GLA_FP32", "GLA_BF16"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GLA_BF16
+    if t.dtype == torch.float32:
+        return GLA_FP32
+    raise TypeError(f"unsupported I/O dtype {t.dtype}")
+
+
+def dims_for(q, v, chunk=64, subchunk=16) -> GlaDims:
+    B, H, L, dk = q.shape
+    return GlaDims(B, H, L, dk, v.shape[-1], chunk, subchunk)
+
+
+def _check(t, name, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(device):
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def fwd(q, k, v, log_alpha, h0=None, chunk=64, subchunk=16, final_state=True, workspace=None,
+        out=None):
+    """GLA forward.  q, k [B,H,L,dk], v [B,H,L,dv] (fp32 or bf16), log_alpha
+    [B,H,L,dk] fp32, h0 [B,H,dk,dv] fp32 or None.  Returns (o, hT or None)."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    _check(q, "q", io)
+    _check(k, "k", io, q.shape)
+    _check(v, "v", io, (B, H, L, dv))
+    _check(log_alpha, "log_alpha", torch.float32, q.shape)
+    _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    dims = GlaDims(B, H, L, dk, dv, chunk, subchunk)
+    code = _dtype_code(q)
+    o = out if out is not None else torch.empty(B, H, L, dv, dtype=io, device=q.device)
+    hT = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if final_state else None
+    n = gla_fwd_workspace_size(dims, code)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = gla_fwd(dims, code, q, k, v, log_alpha, h0, o, hT, workspace, workspace.numel(),
+                 _stream(q.device))
+    if st != 0:
+        raise GlaError(st, "gla_fwd")
+    return o, hT
+
+
+def bwd(q, k, v, log_alpha, h0, dout, dhT=None, chunk=64, subchunk=16, want_dh0=True,
+        workspace=None):
+    """GLA backward.  Returns (dq, dk, dv, dlog_alpha, dh0 or None)."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    _check(q, "q", io)
+    _check(k, "k", io, q.shape)
+    _check(v, "v", io, (B, H, L, dv))
+    _check(log_alpha, "log_alpha", torch.float32, q.shape)
+    _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    _check(dout, "dout", io, (B, H, L, dv))
+    _check(dhT, "dhT", torch.float32, (B, H, dk, dv))
+    dims = GlaDims(B, H, L, dk, dv, chunk, subchunk)
+    code = _dtype_code(q)
+    dq = torch.empty_like(q)
+    dkk = torch.empty_like(k)
+    dvv = torch.empty_like(v)
+    dla = torch.empty_like(log_alpha)
+    dh0 = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if want_dh0 else None
+    n = gla_bwd_workspace_size(dims, code)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = gla_bwd(dims, code, q, k, v, log_alpha, h0, dout, dhT, dq, dkk, dvv, dla, dh0,
+                 workspace, workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise GlaError(st, "gla_bwd")
+    return dq, dkk, dvv, dla, dh0

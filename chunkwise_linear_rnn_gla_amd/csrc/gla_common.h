@@ -1,0 +1,90 @@
+// gla_common.h -- device helpers shared by the GLA kernels (gfx950 only).
+//
+// MFMA conventions used everywhere (16x16 output tiles, wave64):
+//   A (16 x K)  : lane l supplies A[l % 16][(l / 16) * KPL + e], e < KPL
+//   B (K x 16)  : lane l supplies B[(l / 16) * KPL + e][l % 16]
+//   D (16 x 16) : lane l holds    D[(l / 16) * 4 + r][l % 16],  r < 4
+// bf16 operands use v_mfma_f32_16x16x32_bf16 (K = 32, KPL = 8); fp32 operands
+// use v_mfma_f32_16x16x4_f32 (K = 4, KPL = 1).  Accumulation is always fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // every kernel here runs 4 waves per workgroup
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int K = 32;
+  static constexpr int KPL = 8;
+  typedef bf16x8 frag;
+  __device__ static inline floatx4 run(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int K = 4;
+  static constexpr int KPL = 1;
+  typedef float frag;
+  __device__ static inline floatx4 run(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Load a fragment of KPL contiguous elements (16-byte aligned for bf16).
+template <typename T>
+__device__ inline typename Mma<T>::frag load_frag(const T* p);
+template <> __device__ inline bf16x8 load_frag<bf16>(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+template <> __device__ inline float load_frag<float>(const float* p) { return *p; }
+
+// Fragment of KPL contiguous elements computed as x[e] * scale[e] in fp32 and
+// rounded once to T.  x is T, scale is fp32 (both contiguous).
+template <typename T>
+__device__ inline typename Mma<T>::frag scaled_frag(const T* x, const float* s);
+template <> __device__ inline bf16x8 scaled_frag<bf16>(const bf16* x, const float* s) {
+  bf16x8 xv = *reinterpret_cast<const bf16x8*>(x);
+  f32x4 s0 = *reinterpret_cast<const f32x4*>(s);
+  f32x4 s1 = *reinterpret_cast<const f32x4*>(s + 4);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = static_cast<bf16>(static_cast<float>(xv[e]) * s0[e]);
+    r[e + 4] = static_cast<bf16>(static_cast<float>(xv[e + 4]) * s1[e]);
+  }
+  return r;
+}
+template <> __device__ inline float scaled_frag<float>(const float* x, const float* s) {
+  return x[0] * s[0];
+}
+
+__device__ inline floatx4 zero4() {
+  floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+__device__ inline float fast_exp(float x) { return __expf(x); }
+
+__device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ inline int wave_id() { return threadIdx.x / kWave; }
+
+}  // namespace gla

@@ -1,0 +1,65 @@
+// gla_internal.h -- launch plan and kernel launchers shared by the GLA
+// translation units.  Not part of the public ABI (include/gla.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gla {
+
+// Everything a launch sequence needs, derived once from the problem sizes.
+struct Plan {
+  int B, H, L, dk, dv, C, c;
+  int bf16;          // 1: q, k, v, ... are bf16; 0: fp32
+  int BH;            // B * H
+  int NC;            // number of chunks, ceil(L / C)
+  int TS;            // square state-tile edge for the chunk-state kernel
+  int NSEG;          // sequence segments for the chunk-state recurrence
+  int seg_chunks;    // chunks per segment
+  int TVO;           // output column tile of the output kernels
+  size_t esize;      // bytes per I/O element
+  // workspace layout (byte offsets); 0-sized regions have offset 0
+  size_t off_cum, off_st, off_st2, off_seg_u, off_seg_in, off_end, off_dlt, off_rs;
+  size_t ws_fwd, ws_bwd;
+};
+
+// Fills everything but the status; returns false if the sizes are unsupported.
+bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan* p);
+
+// ---- forward kernels (gla_fwd.hip) ----
+hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t s);
+
+// Chunk-state recurrence.  Forward (rev = 0): S_n = diag(g_n) S_{n-1} +
+// (X ⊙ e^{b_n - B})^T Y with X = k, Y = v; writes S_{n-1} per chunk.
+// Reverse (rev = 1): dS_{n-1} = diag(g_n) dS_n + (X ⊙ e^{B})^T Y with X = q,
+// Y = dO; writes dS_n per chunk.  st_t: per-chunk states laid out [dv][dk];
+// st_n: laid out [dk][dv]; either may be null.
+//   mode SEG_LOCAL : zero start per segment, end state -> seg_u[seg]
+//   mode SEG_FILL  : start from seg_in[seg] (or init / zeros if NSEG == 1),
+//                    writes per-chunk states, end state -> end_out (last seg)
+enum StateMode { SEG_LOCAL = 0, SEG_FILL = 1 };
+hipError_t launch_chunk_state(const Plan& p, int rev, int mode, const void* X, const void* Y,
+                              const float* cum, const float* init, const float* seg_u_in,
+                              void* st_t, void* st_n, float* end_out, float* seg_u_out,
+                              hipStream_t s);
+// Combine per-segment local states: seg_in[seg] = state entering segment seg
+// (forward order, or reverse order when rev), end_out = final state.
+hipError_t launch_segment_scan(const Plan& p, int rev, const float* cum, const float* init,
+                               const float* seg_u, float* seg_in, float* end_out,
+                               hipStream_t s);
+hipError_t launch_chunk_output(const Plan& p, const void* q, const void* k, const void* v,
+                               const float* cum, const void* st_t, void* o, hipStream_t s);
+hipError_t launch_copy_state(const Plan& p, const float* src, float* dst, hipStream_t s);
+
+// ---- backward kernels (gla_bwd.hip) ----
+hipError_t launch_chunk_grad(const Plan& p, const void* q, const void* k, const void* v,
+                             const void* dout, const float* cum, const void* st_n,
+                             const void* dst_n, const void* dst_t, void* dq, void* dk,
+                             void* dv, float* dla_local, float* dlt, hipStream_t s);
+hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT, float* rs,
+                               hipStream_t s);
+hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,
+                            hipStream_t s);
+
+}  // namespace gla

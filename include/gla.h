@@ -1,0 +1,124 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) Gated Linear Attention library.
+ *
+ * The library computes the chunkwise-parallel forward and backward of the
+ * GLA layer, per (batch, head):
+ *
+ *     S_t = diag(alpha_t) S_{t-1} + k_t^T v_t,      o_t = q_t S_t,
+ *
+ * with the row gate G_t = alpha_t^T 1 given as a = log alpha_t in R^{d_k}
+ * ("Gated Linear Attention Transformers with Hardware-Efficient Training",
+ * papercache.org notes §4.1 recurrent form; chunkwise form §4.2; secondary
+ * chunking §4.3 / Figure 3; zako-mio deep-reading report ch. 2.3 and 3.4).
+ * The output includes the current token, S_0 = h0 may come from a previous
+ * segment (notes §2.2) and hT = S_L.  There is no normaliser and no scaling
+ * of q inside the library (notes §2.1, unnormalised linear attention).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * Pointers    : device pointers (HIP) to contiguous row-major arrays, each
+ *               16-byte aligned.  Outputs must not alias inputs or each other.
+ * Layouts     : q, k, dq, dk, log_alpha, dlog_alpha : [B][H][L][dk]
+ *               v, o, dout, dv                      : [B][H][L][dv]
+ *               h0, hT, dhT, dh0                    : [B][H][dk][dv]
+ * Dtypes      : q, k, v, o, dout, dq, dk, dv use the I/O dtype (GLA_FP32 or
+ *               GLA_BF16, bf16 = IEEE binary32 upper half, rounded to nearest
+ *               even).  log_alpha, dlog_alpha, h0, hT, dhT, dh0 are always
+ *               fp32.  Accumulation is fp32 throughout.
+ * Ownership   : the caller owns every buffer, including the workspace; the
+ *               library never allocates, frees or synchronises.
+ * Streams     : `stream` is a hipStream_t (NULL = the null stream).  All work
+ *               is enqueued on it in order; calls return without waiting.
+ * Errors      : validation happens before anything is enqueued, so any status
+ *               other than GLA_OK or GLA_ERR_HIP means nothing was launched.
+ *               GLA_ERR_HIP means a launch was rejected (hipGetLastError);
+ *               faults during execution surface at the caller's next sync.
+ *               NaN/Inf inputs are not checked; they propagate.
+ * Determinism : no atomics; repeated calls give bitwise-identical results.
+ * Shapes      : B, H, L >= 0 (L need not be a multiple of the chunk: the last
+ *               chunk is padded with log alpha = 0, k = v = 0 rows that never
+ *               reach memory).  chunk in {16, 32, 64} for GLA_FP32 and
+ *               {32, 64} for GLA_BF16; subchunk == 16.  dk and dv multiples
+ *               of 16 (GLA_FP32) or 32 (GLA_BF16), 16 <= dk <= 256,
+ *               16 <= dv <= 512.  Otherwise GLA_ERR_SHAPE.
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLA_ABI_VERSION 1
+
+typedef enum { GLA_FP32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_NULL = 1,      /* a required pointer (or dims) is NULL            */
+  GLA_ERR_SHAPE = 2,     /* sizes outside the supported set                 */
+  GLA_ERR_DTYPE = 3,     /* dtype is not a gla_dtype value                  */
+  GLA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                */
+  GLA_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required         */
+  GLA_ERR_HIP = 6        /* the HIP runtime rejected a launch               */
+} gla_status;
+
+/* Problem sizes.  chunk = C (tokens per chunk), subchunk = c (tokens per
+ * secondary chunk; papercache.org notes §4.3). */
+typedef struct {
+  int32_t B, H, L, dk, dv, chunk, subchunk;
+} gla_dims;
+
+/* ABI version of the loaded library (GLA_ABI_VERSION at build time). */
+int gla_abi_version(void);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char *gla_status_string(int status);
+
+/* Bytes of device workspace gla_fwd / gla_bwd need for `dims` and `dtype`.
+ * Writes *bytes and returns GLA_OK, or returns the validation error that the
+ * matching call would return (then *bytes is left unchanged).  bytes != NULL. */
+gla_status gla_fwd_workspace_size(const gla_dims *dims, int dtype, size_t *bytes);
+gla_status gla_bwd_workspace_size(const gla_dims *dims, int dtype, size_t *bytes);
+
+/* Forward (papercache.org notes §4.2-4.3; App. B forward listing).
+ *   in : q, k [B,H,L,dk] and v [B,H,L,dv] in `dtype`; log_alpha [B,H,L,dk]
+ *        fp32 (entries <= 0 expected; not checked); h0 [B,H,dk,dv] fp32 or
+ *        NULL for zeros.
+ *   out: o [B,H,L,dv] in `dtype`; hT [B,H,dk,dv] fp32, or NULL to skip.
+ *   Steps on `stream`: chunk-local cumsum of log_alpha; inter-chunk state
+ *   recurrence materialising the state entering every chunk; intra-chunk
+ *   output (MFMA between sub-chunks, fp32 on diagonal sub-blocks).
+ *   workspace: device memory of at least gla_fwd_workspace_size bytes,
+ *   16-byte aligned, contents on entry irrelevant, clobbered on exit. */
+gla_status gla_fwd(const gla_dims *dims, int dtype,
+                   const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *h0,
+                   void *o, float *hT,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward of gla_fwd for the loss gradients dout = dL/do and dhT = dL/dhT
+ * (NULL for zeros).  States are recomputed, not read from a forward call
+ * (zako-mio report ch. 2.2: materialise in the forward, recompute in the
+ * backward).  The gate gradient uses the closed form
+ *     dlog_alpha_t = sum_{i >= t} (q_i ⊙ dq_i - k_i ⊙ dk_i) + rowsum(hT ⊙ dhT)
+ * (zako-mio report ch. 3.4; papercache.org notes §4.3, App. B; the last term
+ * is the final-state path, zero when dhT is NULL).
+ *   out: dq, dk [B,H,L,dk], dv [B,H,L,dv] in `dtype`; dlog_alpha [B,H,L,dk]
+ *        fp32; dh0 [B,H,dk,dv] fp32, or NULL to skip.
+ *   workspace: at least gla_bwd_workspace_size bytes, as for gla_fwd. */
+gla_status gla_bwd(const gla_dims *dims, int dtype,
+                   const void *q, const void *k, const void *v,
+                   const float *log_alpha, const float *h0,
+                   const void *dout, const float *dhT,
+                   void *dq, void *dk, void *dv, float *dlog_alpha, float *dh0,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */
