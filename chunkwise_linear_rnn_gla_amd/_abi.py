@@ -19,7 +19,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_NULL", 2: "GLA_ERR_SHAPE", 3: "GLA_ERR_DTYPE"
 
 # Every symbol include/gla.h declares.
 EXPORTS = ("gla_abi_version", "gla_status_string", "gla_fwd_workspace_size",
-           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd")
+           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_profile_begin", "gla_profile_end",
+           "gla_profile_count", "gla_profile_get")
 
 
 class GlaDims(ctypes.Structure):
@@ -59,6 +60,14 @@ def load():
     lib.gla_fwd.restype = i32
     lib.gla_bwd.argtypes = [dims_p, i32] + [vp] * 12 + [vp, sz, vp]
     lib.gla_bwd.restype = i32
+    lib.gla_profile_begin.argtypes = [i32]
+    lib.gla_profile_begin.restype = i32
+    lib.gla_profile_end.argtypes = []
+    lib.gla_profile_end.restype = None
+    lib.gla_profile_count.argtypes = []
+    lib.gla_profile_count.restype = i32
+    lib.gla_profile_get.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+    lib.gla_profile_get.restype = i32
     _lib = lib
     return lib
 
@@ -111,3 +120,27 @@ def gla_bwd(dims, dtype, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv, dlog_alp
     return load().gla_bwd(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                           _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
                           _ptr(dlog_alpha), _ptr(dh0), _ptr(workspace), workspace_bytes, stream)
+
+
+def gla_profile_begin(capacity: int) -> None:
+    st = load().gla_profile_begin(int(capacity))
+    if st != 0:
+        raise GlaError(st, "gla_profile_begin")
+
+
+def gla_profile_end() -> None:
+    load().gla_profile_end()
+
+
+def gla_profile_count() -> int:
+    return load().gla_profile_count()
+
+
+def gla_profile_get(index: int):
+    """(kernel name, duration in ms) of the index-th launch record."""
+    name = ctypes.c_char_p()
+    ms = ctypes.c_float(0.0)
+    st = load().gla_profile_get(int(index), ctypes.byref(name), ctypes.byref(ms))
+    if st != 0:
+        raise GlaError(st, "gla_profile_get")
+    return name.value.decode(), ms.value

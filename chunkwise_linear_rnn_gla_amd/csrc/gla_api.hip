@@ -56,6 +56,11 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   P.off_end = off; off = align_up(off + BH * S * 4);
   P.off_dlt = off; off = align_up(off + BH * P.NC * dk * 4);
   P.off_rs = off; off = align_up(off + BH * dk * 4);
+  P.off_A = off; off = align_up(off + BH * P.NC * C * C * 4);
+  P.off_dA = off; off = align_up(off + BH * P.NC * C * C * 4);
+  // low halves of the recomputed states and state gradients (bf16 split)
+  P.off_stlo = off; off = align_up(off + (bf16 ? BH * P.NC * S * 2 : 0));
+  P.off_dstlo = off; off = align_up(off + (bf16 ? BH * P.NC * S * 2 : 0));
   P.ws_bwd = off;
   return true;
 }
@@ -85,9 +90,35 @@ static gla_status check_ptrs(std::initializer_list<const void*> required,
   return GLA_OK;
 }
 
-#define GLA_TRY(expr)                              \
-  do {                                             \
-    if ((expr) != hipSuccess) return GLA_ERR_HIP;  \
+// ---- launch profiling: HIP events around each launch on its stream
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+ProfRec* g_recs = nullptr;
+int g_cap = 0, g_n = 0, g_on = 0, g_pending = -1;
+
+void prof_before(const char* name, hipStream_t s) {
+  g_pending = -1;
+  if (!g_on || g_n >= g_cap) return;
+  if (hipEventRecord(g_recs[g_n].a, s) != hipSuccess) return;
+  g_recs[g_n].name = name;
+  g_pending = g_n;
+}
+void prof_after(hipStream_t s) {
+  if (g_pending < 0) return;
+  if (hipEventRecord(g_recs[g_pending].b, s) == hipSuccess) g_n = g_pending + 1;
+  g_pending = -1;
+}
+}  // namespace
+
+// Launch `expr` (a hipError_t-returning launcher) under the name `nm`.
+#define GLA_LAUNCH(nm, expr)                         \
+  do {                                               \
+    prof_before(nm, s);                              \
+    if ((expr) != hipSuccess) return GLA_ERR_HIP;    \
+    prof_after(s);                                   \
   } while (0)
 
 extern "C" {
@@ -135,7 +166,7 @@ gla_status gla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k
   hipStream_t s = (hipStream_t)stream;
   if (p.L == 0) {
     if ((st = check_ptrs({}, {h0, hT})) != GLA_OK) return st;
-    if (hT) GLA_TRY(launch_copy_state(p, h0, hT, s));
+    if (hT) GLA_LAUNCH("copy_state", launch_copy_state(p, h0, hT, s));
     return GLA_OK;
   }
   if ((st = check_ptrs({q, k, v, log_alpha, o}, {h0, hT})) != GLA_OK) return st;
@@ -148,18 +179,15 @@ gla_status gla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k
   float* seg_u = (float*)(ws + p.off_seg_u);
   float* seg_in = (float*)(ws + p.off_seg_in);
 
-  GLA_TRY(launch_cumsum(p, log_alpha, cum, s));
+  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
   if (p.NSEG > 1) {
-    GLA_TRY(launch_chunk_state(p, 0, SEG_LOCAL, k, v, cum, nullptr, nullptr, nullptr, nullptr,
-                               nullptr, seg_u, s));
-    GLA_TRY(launch_segment_scan(p, 0, cum, h0, seg_u, seg_in, hT, s));
-    GLA_TRY(launch_chunk_state(p, 0, SEG_FILL, k, v, cum, h0, seg_in, states, nullptr, nullptr,
-                               nullptr, s));
+    GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, 0, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, s));
+    GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, cum, h0, seg_u, seg_in, hT, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, 0, k, v, cum, h0, seg_in, states, nullptr, nullptr, nullptr, nullptr, s));
   } else {
-    GLA_TRY(launch_chunk_state(p, 0, SEG_FILL, k, v, cum, h0, nullptr, states, nullptr, hT,
-                               nullptr, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, 0, k, v, cum, h0, nullptr, states, nullptr, nullptr, hT, nullptr, s));
   }
-  GLA_TRY(launch_chunk_output(p, q, k, v, cum, states, o, s));
+  GLA_LAUNCH("chunk_output", launch_chunk_output(p, q, k, v, cum, states, o, s));
   return GLA_OK;
 }
 
@@ -174,7 +202,7 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
   hipStream_t s = (hipStream_t)stream;
   if (p.L == 0) {
     if ((st = check_ptrs({}, {dhT, dh0})) != GLA_OK) return st;
-    if (dh0) GLA_TRY(launch_copy_state(p, dhT, dh0, s));
+    if (dh0) GLA_LAUNCH("copy_state", launch_copy_state(p, dhT, dh0, s));
     return GLA_OK;
   }
   if ((st = check_ptrs({q, k, v, log_alpha, dout, dq, dk, dv, dlog_alpha}, {h0, dhT, dh0})) !=
@@ -193,34 +221,71 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
   float* hT = (float*)(ws + p.off_end);
   float* dlt = (float*)(ws + p.off_dlt);
   float* rs = (float*)(ws + p.off_rs);
+  float* Aw = (float*)(ws + p.off_A);
+  float* dAw = (float*)(ws + p.off_dA);
+  void* st_lo = p.bf16 ? (void*)(ws + p.off_stlo) : nullptr;
+  void* dst_lo = p.bf16 ? (void*)(ws + p.off_dstlo) : nullptr;
 
   // recompute the chunk states (not stored by the forward)
-  GLA_TRY(launch_cumsum(p, log_alpha, cum, s));
+  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
   if (p.NSEG > 1) {
-    GLA_TRY(launch_chunk_state(p, 0, SEG_LOCAL, k, v, cum, nullptr, nullptr, nullptr, nullptr,
-                               nullptr, seg_u, s));
-    GLA_TRY(launch_segment_scan(p, 0, cum, h0, seg_u, seg_in, hT, s));
-    GLA_TRY(launch_chunk_state(p, 0, SEG_FILL, k, v, cum, h0, seg_in, nullptr, st_n, nullptr,
-                               nullptr, s));
+    GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, p.bf16, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, s));
+    GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, cum, h0, seg_u, seg_in, hT, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, seg_in, nullptr, st_n, st_lo, nullptr, nullptr, s));
   } else {
-    GLA_TRY(launch_chunk_state(p, 0, SEG_FILL, k, v, cum, h0, nullptr, nullptr, st_n, hT,
-                               nullptr, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, nullptr, nullptr, st_n, st_lo, hT, nullptr, s));
   }
   // reverse recurrence of the state gradient
   if (p.NSEG > 1) {
-    GLA_TRY(launch_chunk_state(p, 1, SEG_LOCAL, q, dout, cum, nullptr, nullptr, nullptr, nullptr,
-                               nullptr, seg_u, s));
-    GLA_TRY(launch_segment_scan(p, 1, cum, dhT, seg_u, seg_in, dh0, s));
-    GLA_TRY(launch_chunk_state(p, 1, SEG_FILL, q, dout, cum, dhT, seg_in, dst_t, dst_n, nullptr,
-                               nullptr, s));
+    GLA_LAUNCH("chunk_state_rev_local", launch_chunk_state(p, 1, SEG_LOCAL, p.bf16, q, dout, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, s));
+    GLA_LAUNCH("segment_scan_rev", launch_segment_scan(p, 1, cum, dhT, seg_u, seg_in, dh0, s));
+    GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, seg_in, dst_t, dst_n, dst_lo, nullptr, nullptr, s));
   } else {
-    GLA_TRY(launch_chunk_state(p, 1, SEG_FILL, q, dout, cum, dhT, nullptr, dst_t, dst_n, dh0,
-                               nullptr, s));
+    GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, nullptr, dst_t, dst_n, dst_lo, dh0, nullptr, s));
   }
-  GLA_TRY(launch_chunk_grad(p, q, k, v, dout, cum, st_n, dst_n, dst_t, dq, dk, dv, dlog_alpha,
-                            dlt, s));
-  GLA_TRY(launch_rowsum_state(p, dhT ? hT : nullptr, dhT, rs, s));
-  GLA_TRY(launch_dla_carry(p, dlt, rs, dlog_alpha, s));
+  GLA_LAUNCH("chunk_attn", launch_chunk_attn(p, q, k, v, dout, cum, Aw, dAw, s));
+  GLA_LAUNCH("chunk_dqdk", launch_chunk_dqdk(p, q, k, v, dout, cum, st_n, st_lo, dst_n,
+                                             dst_lo, dAw, dq, dk, dlog_alpha, dlt, s));
+  GLA_LAUNCH("chunk_dv", launch_chunk_dv(p, k, dout, cum, dst_t, Aw, dv, s));
+  GLA_LAUNCH("rowsum_state", launch_rowsum_state(p, dhT ? hT : nullptr, dhT, rs, s));
+  GLA_LAUNCH("dla_carry", launch_dla_carry(p, dlt, rs, dlog_alpha, s));
+  return GLA_OK;
+}
+
+gla_status gla_profile_begin(int capacity) {
+  if (capacity < 1) return GLA_ERR_SHAPE;
+  if (capacity != g_cap) {
+    for (int i = 0; i < g_cap; ++i) {
+      (void)hipEventDestroy(g_recs[i].a);
+      (void)hipEventDestroy(g_recs[i].b);
+    }
+    free(g_recs);
+    g_cap = 0;
+    g_recs = (ProfRec*)calloc((size_t)capacity, sizeof(ProfRec));
+    if (!g_recs) return GLA_ERR_HIP;
+    for (int i = 0; i < capacity; ++i) {
+      if (hipEventCreate(&g_recs[i].a) != hipSuccess || hipEventCreate(&g_recs[i].b) != hipSuccess) {
+        g_cap = i;
+        return GLA_ERR_HIP;
+      }
+      g_cap = i + 1;
+    }
+  }
+  g_n = 0;
+  g_pending = -1;
+  g_on = 1;
+  return GLA_OK;
+}
+
+void gla_profile_end(void) { g_on = 0; }
+
+int gla_profile_count(void) { return g_n; }
+
+gla_status gla_profile_get(int index, const char** kernel, float* ms) {
+  if (!kernel || !ms) return GLA_ERR_NULL;
+  if (index < 0 || index >= g_n) return GLA_ERR_SHAPE;
+  if (hipEventElapsedTime(ms, g_recs[index].a, g_recs[index].b) != hipSuccess) return GLA_ERR_HIP;
+  *kernel = g_recs[index].name;
   return GLA_OK;
 }
 

@@ -1,19 +1,610 @@
 // gla_bwd.hip -- backward kernels of the GLA chunkwise layer for gfx950.
+//
+// The states S_{n-1} are recomputed (not kept from the forward; zako-mio report
+// ch. 2.2, materialise in the forward and recompute in the backward) and the
+// state gradient dS_n runs backwards over chunks:
+//   dS_{L/C} = dhT,  dS_{n-1} = diag(e^{b_n}) dS_n + (Q ⊙ Lambda)^T dO[n].
+// Per chunk, with A the chunk's causal gated score matrix (A[m][r] =
+// sum_k q_mk k_rk e^{B_mk - B_rk}, r <= m) and dA = (dO V^T) ⊙ M:
+//   dQ = (dO S_{n-1}^T) ⊙ Lambda + sum_r dA[m][r] k_r ⊙ e^{B_m - B_r}
+//   dK = (V dS_n^T) ⊙ Gamma     + sum_m dA[m][r] q_m ⊙ e^{B_m - B_r}
+//   dV = (K ⊙ Gamma) dS_n       + A^T dO
+// (the chain rule through the chunkwise form; the oracle checks these against
+// back-propagation through the token recurrence).  The gate gradient uses the
+// closed form of the pages (zako-mio report ch. 3.4; papercache.org notes §4.3
+// and App. B): dlog b = q ⊙ dq - k ⊙ dk from the fp32 dq, dk, then dlog alpha
+// = reverse cumsum of dlog b over the whole sequence, plus rowsum(hT ⊙ dhT)
+// when the final state has a gradient.
 #include "gla_common.h"
 #include "gla_internal.h"
+#include "gla_pblock.h"
 
 namespace gla {
 
-hipError_t launch_chunk_grad(const Plan&, const void*, const void*, const void*, const void*,
-                             const float*, const void*, const void*, const void*, void*, void*,
-                             void*, float*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+// ------------------------------------------------------------------ B3a: A and dA per chunk
+// A (the forward's score matrix, fp32) and dA = (dO V^T) ⊙ M, written to the
+// workspace as C x C fp32 blocks (zeros above the diagonal).
+template <typename T, int C>
+__global__ __launch_bounds__(kThreads) void k_chunk_attn(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ cum, float* __restrict__ Aw,
+    float* __restrict__ dAw, int L, int dk, int dv, int NC) {
+  using M = Mma<T>;
+  using PB = PBuilder<T, C>;
+  constexpr int LDT = PB::LDT, LDF = PB::LDF, KS = PB::KS;
+  constexpr int NRT = C / 16, NTRI = NRT * (NRT + 1) / 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[PB::SLICE_BYTES];
+  __shared__ float pd[4][16][17];
+  T* qs = reinterpret_cast<T*>(smem);
+  T* ks = qs + C * LDT;
+  float* bs = reinterpret_cast<float*>(ks + C * LDT);
+  float* als = bs + C * LDF;
+
+  const int n = blockIdx.x, bh = blockIdx.y;
+  const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int r0 = n * C, rv = min(C, L - r0);
+  const size_t qo = (size_t)bh * L * dk, vo = (size_t)bh * L * dv;
+  float* Ab = Aw + ((size_t)bh * NC + n) * C * C;
+  float* dAb = dAw + ((size_t)bh * NC + n) * C * C;
+
+  // dA on MFMA over d_v: lower block triangle tiles (ti >= tj)
+  for (int t = w; t < NTRI; t += 4) {
+    int ti = 0, rem = t;
+    while (rem > ti) { rem -= ti + 1; ++ti; }
+    const int tj = rem;
+    const int ra = ti * 16 + (l & 15), rb = tj * 16 + (l & 15);
+    floatx4 acc = zero4();
+    for (int kk = 0; kk < dv; kk += M::K) {
+      const int c = kk + (l >> 4) * M::KPL;
+      typename M::frag a, b;
+      if (ra < rv) a = load_frag<T>(dout + vo + (size_t)(r0 + ra) * dv + c);
+      else a = typename M::frag{};
+      if (rb < rv) b = load_frag<T>(v + vo + (size_t)(r0 + rb) * dv + c);
+      else b = typename M::frag{};
+      acc = M::run(a, b, acc);
+    }
+    const int col = tj * 16 + (l & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = ti * 16 + (l >> 4) * 4 + r;
+      dAb[row * C + col] = (col <= row) ? acc[r] : 0.f;
+    }
+  }
+  // zeros above the block diagonal
+  for (int it = tid; it < C * C; it += kThreads) {
+    const int row = it / C, col = it % C;
+    if ((col >> 4) > (row >> 4)) { dAb[it] = 0.f; Ab[it] = 0.f; }
+    else if (col > row) Ab[it] = 0.f;
+  }
+
+  PB pb;
+  pb.init();
+  for (int s0 = 0; s0 < dk; s0 += KS) {
+    __syncthreads();
+    PB::stage(q, k, cum, qo, r0, rv, dk, s0, qs, ks, bs, nullptr);
+    __syncthreads();
+    PB::gates(bs, als);
+    pb.offdiag(qs, ks, bs);
+    __syncthreads();
+    pb.diag(qs, ks, als);
+  }
+  __syncthreads();
+  pb.finish(pd, [&](int m, int r, float val) { Ab[m * C + r] = val; });
 }
-hipError_t launch_rowsum_state(const Plan&, const float*, const float*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+
+// ------------------------------------------------------------------ B3b: dq, dk, dlog b
+// One workgroup per (batch-head, chunk, d_k tile of TK channels).
+template <typename T, int C, int TK>
+__global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ cum, const T* __restrict__ st_n,
+    const T* __restrict__ st_lo, const T* __restrict__ dst_n, const T* __restrict__ dst_lo,
+    const float* __restrict__ dAw, T* __restrict__ dq, T* __restrict__ dkk,
+    float* __restrict__ dla, float* __restrict__ dlt, int L, int dk, int dv, int NC) {
+  using M = Mma<T>;
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int PT = 16 / (int)sizeof(T);
+  constexpr int LDA = C + PT;            // T rows of length C
+  constexpr int LDK = TK + 4;            // fp32 rows of length TK
+  constexpr int NRT = C / 16, NCT = TK / 16;
+  constexpr int WC = NCT < 4 ? NCT : 4, WR = 4 / WC;
+  constexpr int NCW = NCT / WC, NRW = (NRT + WR - 1) / WR;
+  __shared__ __attribute__((aligned(16))) T dah[C][LDA];    // dA, diagonal blocks zeroed
+  __shared__ __attribute__((aligned(16))) T dal[BF ? C : 1][BF ? LDA : 8];
+  __shared__ __attribute__((aligned(16))) T dath[C][LDA];   // transposed: [r][m]
+  __shared__ __attribute__((aligned(16))) T datl[BF ? C : 1][BF ? LDA : 8];
+  __shared__ float dad[C][17];                              // diagonal blocks, fp32
+  __shared__ float qf[C][LDK], kf[C][LDK], bt[C][LDK], al[C][LDK];
+  __shared__ __attribute__((aligned(16))) T opT[TK][LDA];   // scaled operand, [ch][row]
+  __shared__ __attribute__((aligned(16))) T opL[BF ? TK : 1][BF ? LDA : 8];  // its low part
+
+  const int n = blockIdx.x, c0 = blockIdx.y * TK, bh = blockIdx.z;
+  const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int r0 = n * C, rv = min(C, L - r0);
+  const size_t qo = (size_t)bh * L * dk, vo = (size_t)bh * L * dv;
+  const float* dAb = dAw + ((size_t)bh * NC + n) * C * C;
+
+  for (int it = tid; it < C * C; it += kThreads) {
+    const int m = it / C, r = it % C;
+    const float x = dAb[it];
+    const bool dgb = (m >> 4) == (r >> 4);
+    const float xo = dgb ? 0.f : x;
+    const T hi = from_f32<T>(xo);
+    dah[m][r] = hi;
+    dath[r][m] = hi;
+    if constexpr (BF) {
+      const T lo = from_f32<T>(xo - to_f32(hi));
+      dal[m][r] = lo;
+      datl[r][m] = lo;
+    }
+    if (dgb) dad[m][r & 15] = x;
+  }
+  for (int it = tid; it < C * TK; it += kThreads) {
+    const int row = it / TK, c = it % TK;
+    const bool valid = row < rv;
+    const int crow = valid ? r0 + row : r0 + rv - 1;
+    const size_t gi = qo + (size_t)crow * dk + c0 + c;
+    qf[row][c] = valid ? to_f32(q[gi]) : 0.f;
+    kf[row][c] = valid ? to_f32(k[gi]) : 0.f;
+    bt[row][c] = cum[gi];
+  }
+  __syncthreads();
+  for (int it = tid; it < C * TK; it += kThreads) {
+    const int row = it / TK, c = it % TK;
+    al[row][c] = (row & 15) ? gexp<T>(bt[row][c] - bt[row - 1][c]) : 1.f;
+  }
+
+  const int wc = w % WC, wr = w / WC;
+  floatx4 aq[NRW][NCW], ak[NRW][NCW];
+#pragma unroll
+  for (int a = 0; a < NRW; ++a)
+#pragma unroll
+    for (int b = 0; b < NCW; ++b) aq[a][b] = ak[a][b] = zero4();
+
+  // inter-chunk terms: dO S_{n-1}^T and V dS_n^T, reduction over d_v
+  const size_t so = ((size_t)bh * NC + n) * dk * dv;
+  const T* sp = st_n + so;
+  const T* dsp = dst_n + so;
+  const bool lo_s = st_lo != nullptr, lo_d = dst_lo != nullptr;
+  for (int kk = 0; kk < dv; kk += M::K) {
+    const int cc = kk + (l >> 4) * M::KPL;
+    typename M::frag bs_[NCW], bd_[NCW], bsl[NCW], bdl[NCW];
+#pragma unroll
+    for (int ct = 0; ct < NCW; ++ct) {
+      const int ch = c0 + (wc + WC * ct) * 16 + (l & 15);
+      bs_[ct] = load_frag<T>(sp + (size_t)ch * dv + cc);
+      bd_[ct] = load_frag<T>(dsp + (size_t)ch * dv + cc);
+      if (lo_s) bsl[ct] = load_frag<T>(st_lo + so + (size_t)ch * dv + cc);
+      if (lo_d) bdl[ct] = load_frag<T>(dst_lo + so + (size_t)ch * dv + cc);
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt) {
+      const int rti = wr + WR * rt;
+      if (rti >= NRT) continue;
+      const int row = rti * 16 + (l & 15);
+      typename M::frag ao, av;
+      if (row < rv) {
+        ao = load_frag<T>(dout + vo + (size_t)(r0 + row) * dv + cc);
+        av = load_frag<T>(v + vo + (size_t)(r0 + row) * dv + cc);
+      } else {
+        ao = typename M::frag{};
+        av = typename M::frag{};
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        aq[rt][ct] = M::run(ao, bs_[ct], aq[rt][ct]);
+        ak[rt][ct] = M::run(av, bd_[ct], ak[rt][ct]);
+        if (lo_s) aq[rt][ct] = M::run(ao, bsl[ct], aq[rt][ct]);
+        if (lo_d) ak[rt][ct] = M::run(av, bdl[ct], ak[rt][ct]);
+      }
+    }
+  }
+  __syncthreads();  // al ready
+#pragma unroll
+  for (int rt = 0; rt < NRW; ++rt) {
+    const int rti = wr + WR * rt;
+    if (rti >= NRT) continue;
+#pragma unroll
+    for (int ct = 0; ct < NCW; ++ct) {
+      const int c = (wc + WC * ct) * 16 + (l & 15);
+      const float blast = bt[C - 1][c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rti * 16 + (l >> 4) * 4 + r;
+        aq[rt][ct][r] *= gexp<T>(bt[row][c]);
+        ak[rt][ct][r] *= gexp<T>(blast - bt[row][c]);
+      }
+    }
+  }
+
+  // intra dq, off-diagonal sub-chunks: rows of sub-chunk j, keys r < 16 j,
+  // reference z_j = B at the first row of j:
+  //   e^{B_m - z_j} ⊙ [dA_off (K ⊙ e^{z_j - B})]
+  for (int j = 1; j < NRT; ++j) {
+    __syncthreads();
+    for (int it = tid; it < C * TK; it += kThreads) {
+      const int r = it / TK, c = it % TK;
+      const float x = r < 16 * j ? kf[r][c] * gexp<T>(bt[16 * j][c] - bt[r][c]) : 0.f;
+      const T hi = from_f32<T>(x);
+      opT[c][r] = hi;
+      if constexpr (BF) opL[c][r] = from_f32<T>(x - to_f32(hi));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt) {
+      if (wr + WR * rt != j) continue;
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int c = (wc + WC * ct) * 16 + (l & 15);
+        floatx4 t4 = zero4();
+        for (int kk = 0; kk < 16 * j; kk += M::K) {
+          const int kc = kk + (l >> 4) * M::KPL;
+          auto b = load_frag<T>(&opT[c][kc]);
+          auto ah = load_frag<T>(&dah[j * 16 + (l & 15)][kc]);
+          t4 = M::run(ah, b, t4);
+          if constexpr (BF) {
+            t4 = M::run(load_frag<T>(&dal[j * 16 + (l & 15)][kc]), b, t4);
+            t4 = M::run(ah, load_frag<T>(&opL[c][kc]), t4);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = j * 16 + (l >> 4) * 4 + r;
+          aq[rt][ct][r] += gexp<T>(bt[row][c] - bt[16 * j][c]) * t4[r];
+        }
+      }
+    }
+  }
+  // intra dk, off-diagonal sub-chunks: key rows of sub-chunk u, queries
+  // m > last(u), reference z = B at the last row of u:
+  //   e^{z - B_r} ⊙ [dA_off^T (Q ⊙ e^{B - z})]
+  for (int u = 0; u + 1 < NRT; ++u) {
+    __syncthreads();
+    for (int it = tid; it < C * TK; it += kThreads) {
+      const int m = it / TK, c = it % TK;
+      const float x = m >= 16 * (u + 1) ? qf[m][c] * gexp<T>(bt[m][c] - bt[16 * u + 15][c]) : 0.f;
+      const T hi = from_f32<T>(x);
+      opT[c][m] = hi;
+      if constexpr (BF) opL[c][m] = from_f32<T>(x - to_f32(hi));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt) {
+      if (wr + WR * rt != u) continue;
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int c = (wc + WC * ct) * 16 + (l & 15);
+        floatx4 t4 = zero4();
+        for (int kk = ((16 * (u + 1)) / M::K) * M::K; kk < C; kk += M::K) {
+          const int kc = kk + (l >> 4) * M::KPL;
+          auto b = load_frag<T>(&opT[c][kc]);
+          auto ah = load_frag<T>(&dath[u * 16 + (l & 15)][kc]);
+          t4 = M::run(ah, b, t4);
+          if constexpr (BF) {
+            t4 = M::run(load_frag<T>(&datl[u * 16 + (l & 15)][kc]), b, t4);
+            t4 = M::run(ah, load_frag<T>(&opL[c][kc]), t4);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = u * 16 + (l >> 4) * 4 + r;
+          ak[rt][ct][r] += gexp<T>(bt[16 * u + 15][c] - bt[row][c]) * t4[r];
+        }
+      }
+    }
+  }
+  // diagonal sub-chunk blocks, fp32 VALU with running gate products
+#pragma unroll
+  for (int rt = 0; rt < NRW; ++rt) {
+    const int rti = wr + WR * rt;
+    if (rti >= NRT) continue;
+#pragma unroll
+    for (int ct = 0; ct < NCW; ++ct) {
+      const int c = (wc + WC * ct) * 16 + (l & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mi = (l >> 4) * 4 + r;           // row within the block
+        const int row = rti * 16 + mi;
+        // dq: sum over keys s <= mi of dA[row][s] k_s E(row, s), E built downwards
+        float E = 1.f, sq = 0.f;
+#pragma unroll
+        for (int s = 15; s >= 0; --s) {
+          if (s < mi) E *= al[rti * 16 + s + 1][c];
+          if (s <= mi) sq += dad[row][s] * kf[rti * 16 + s][c] * E;
+        }
+        aq[rt][ct][r] += sq;
+        // dk: sum over queries s >= mi of dA[s][row] q_s E(s, row), E built upwards
+        float F = 1.f, sk = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          if (s > mi) F *= al[rti * 16 + s][c];
+          if (s >= mi) sk += dad[rti * 16 + s][mi] * qf[rti * 16 + s][c] * F;
+        }
+        ak[rt][ct][r] += sk;
+      }
+    }
+  }
+  __syncthreads();  // everyone is done with bt / al / opT
+  float* dlb = &al[0][0];  // reuse: dlog b of the tile, [C][LDK]
+#pragma unroll
+  for (int rt = 0; rt < NRW; ++rt) {
+    const int rti = wr + WR * rt;
+    if (rti >= NRT) continue;
+#pragma unroll
+    for (int ct = 0; ct < NCW; ++ct) {
+      const int c = (wc + WC * ct) * 16 + (l & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rti * 16 + (l >> 4) * 4 + r;
+        dlb[row * LDK + c] = qf[row][c] * aq[rt][ct][r] - kf[row][c] * ak[rt][ct][r];
+        if (row < rv) {
+          const size_t gi = qo + (size_t)(r0 + row) * dk + c0 + c;
+          dq[gi] = from_f32<T>(aq[rt][ct][r]);
+          dkk[gi] = from_f32<T>(ak[rt][ct][r]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // chunk-local reverse cumsum of dlog b, and the chunk total
+  for (int c = tid; c < TK; c += kThreads) {
+    float s = 0.f;
+    for (int row = rv - 1; row >= 0; --row) {
+      s += dlb[row * LDK + c];
+      dla[qo + (size_t)(r0 + row) * dk + c0 + c] = s;
+    }
+    dlt[((size_t)bh * NC + n) * dk + c0 + c] = s;
+  }
 }
-hipError_t launch_dla_carry(const Plan&, const float*, const float*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+
+// ------------------------------------------------------------------ B3c: dv
+// One workgroup per (batch-head, chunk, d_v tile): dV = (K ⊙ Gamma) dS_n + A^T dO.
+template <typename T, int C, int TVD>
+__global__ __launch_bounds__(kThreads) void k_chunk_dv(
+    const T* __restrict__ k, const T* __restrict__ dout, const float* __restrict__ cum,
+    const T* __restrict__ dst_t, const float* __restrict__ Aw, T* __restrict__ dvv, int L,
+    int dk, int dv, int NC) {
+  using M = Mma<T>;
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int PT = 16 / (int)sizeof(T);
+  constexpr int LDA = C + PT;
+  constexpr int KSL = 64;                 // d_k slice of the staged K ⊙ Gamma
+  constexpr int LDKT = KSL + PT;
+  constexpr int NRT = C / 16, NCT = TVD / 16;
+  constexpr int WC = NCT < 4 ? NCT : 4, WR = 4 / WC;
+  constexpr int NCW = NCT / WC, NRW = (NRT + WR - 1) / WR;
+  __shared__ __attribute__((aligned(16))) T ath[C][LDA];   // A^T, [r][m]
+  __shared__ __attribute__((aligned(16))) T atl[BF ? C : 1][BF ? LDA : 8];
+  __shared__ __attribute__((aligned(16))) T dot[TVD][LDA];  // dO^T, [col][m]
+  __shared__ __attribute__((aligned(16))) T kt[C][LDKT];    // K ⊙ Gamma slice, [m][ch]
+
+  const int n = blockIdx.x, j0 = blockIdx.y * TVD, bh = blockIdx.z;
+  const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int r0 = n * C, rv = min(C, L - r0);
+  const size_t qo = (size_t)bh * L * dk, vo = (size_t)bh * L * dv;
+  const float* Ab = Aw + ((size_t)bh * NC + n) * C * C;
+
+  for (int it = tid; it < C * C; it += kThreads) {
+    const int m = it / C, r = it % C;
+    const float x = Ab[it];
+    const T hi = from_f32<T>(x);
+    ath[r][m] = hi;
+    if constexpr (BF) atl[r][m] = from_f32<T>(x - to_f32(hi));
+  }
+  for (int it = tid; it < C * TVD; it += kThreads) {
+    const int m = it / TVD, c = it % TVD;
+    dot[c][m] = m < rv ? dout[vo + (size_t)(r0 + m) * dv + j0 + c] : from_f32<T>(0.f);
+  }
+
+  const int wc = w % WC, wr = w / WC;
+  floatx4 acc[NRW][NCW];
+#pragma unroll
+  for (int a = 0; a < NRW; ++a)
+#pragma unroll
+    for (int b = 0; b < NCW; ++b) acc[a][b] = zero4();
+
+  const T* dsp = dst_t + ((size_t)bh * NC + n) * dv * dk;
+  const float* blast = cum + qo + (size_t)(r0 + rv - 1) * dk;
+  for (int s0 = 0; s0 < dk; s0 += KSL) {
+    const int ks = min(KSL, dk - s0);
+    __syncthreads();
+    for (int it = tid; it < C * ks; it += kThreads) {
+      const int m = it / ks, c = it % ks;
+      float x = 0.f;
+      if (m < rv) {
+        const size_t gi = qo + (size_t)(r0 + m) * dk + s0 + c;
+        x = to_f32(k[gi]) * gexp<T>(blast[s0 + c] - cum[gi]);
+      }
+      kt[m][c] = from_f32<T>(x);
+    }
+    __syncthreads();
+    for (int kk = 0; kk < ks; kk += M::K) {
+      const int kc = kk + (l >> 4) * M::KPL;
+      typename M::frag b[NCW];
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int col = j0 + (wc + WC * ct) * 16 + (l & 15);
+        b[ct] = load_frag<T>(dsp + (size_t)col * dk + s0 + kc);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRW; ++rt) {
+        const int rti = wr + WR * rt;
+        if (rti >= NRT) continue;
+        auto a = load_frag<T>(&kt[rti * 16 + (l & 15)][kc]);
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) acc[rt][ct] = M::run(a, b[ct], acc[rt][ct]);
+      }
+    }
+  }
+  // A^T dO: rows are keys r, reduction over queries m >= r
+#pragma unroll
+  for (int rt = 0; rt < NRW; ++rt) {
+    const int rti = wr + WR * rt;
+    if (rti >= NRT) continue;
+    for (int kk = ((rti * 16) / M::K) * M::K; kk < C; kk += M::K) {
+      const int kc = kk + (l >> 4) * M::KPL;
+      auto ah = load_frag<T>(&ath[rti * 16 + (l & 15)][kc]);
+      typename M::frag alo{};
+      if constexpr (BF) alo = load_frag<T>(&atl[rti * 16 + (l & 15)][kc]);
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        auto b = load_frag<T>(&dot[(wc + WC * ct) * 16 + (l & 15)][kc]);
+        acc[rt][ct] = M::run(ah, b, acc[rt][ct]);
+        if constexpr (BF) acc[rt][ct] = M::run(alo, b, acc[rt][ct]);
+      }
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < NRW; ++rt) {
+    const int rti = wr + WR * rt;
+    if (rti >= NRT) continue;
+#pragma unroll
+    for (int ct = 0; ct < NCW; ++ct) {
+      const int col = j0 + (wc + WC * ct) * 16 + (l & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rti * 16 + (l >> 4) * 4 + r;
+        if (row < rv) dvv[vo + (size_t)(r0 + row) * dv + col] = from_f32<T>(acc[rt][ct][r]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ B4: final-state term and carry
+__global__ __launch_bounds__(kWave) void k_rowsum_state(const float* __restrict__ hT,
+                                                        const float* __restrict__ dhT,
+                                                        float* __restrict__ rs, int dk, int dv) {
+  const int i = blockIdx.x, bh = blockIdx.y;
+  float s = 0.f;
+  if (hT && dhT) {
+    const size_t base = ((size_t)bh * dk + i) * dv;
+    for (int j = threadIdx.x; j < dv; j += kWave) s += hT[base + j] * dhT[base + j];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (threadIdx.x == 0) rs[(size_t)bh * dk + i] = s;
+}
+
+// dlog alpha_t = (chunk-local reverse cumsum of dlog b)_t
+//              + sum of the totals of all later chunks + rowsum(hT ⊙ dhT).
+__global__ __launch_bounds__(kThreads) void k_dla_carry(const float* __restrict__ dlt,
+                                                        const float* __restrict__ rs,
+                                                        float* __restrict__ dla, int L, int dk,
+                                                        int C, int NC) {
+  const int n = blockIdx.x, bh = blockIdx.y;
+  const int r0 = n * C, r1 = min(L, r0 + C);
+  for (int c = threadIdx.x; c < dk; c += blockDim.x) {
+    float off = rs[(size_t)bh * dk + c];
+    for (int m = n + 1; m < NC; ++m) off += dlt[((size_t)bh * NC + m) * dk + c];
+    for (int r = r0; r < r1; ++r) dla[((size_t)bh * L + r) * dk + c] += off;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+template <typename T, int C>
+static hipError_t launch_attn_t(const Plan& p, const void* q, const void* k, const void* v,
+                                const void* dout, const float* cum, float* Aw, float* dAw,
+                                hipStream_t s) {
+  hipLaunchKernelGGL((k_chunk_attn<T, C>), dim3(p.NC, p.BH), dim3(kThreads), 0, s, (const T*)q,
+                     (const T*)k, (const T*)v, (const T*)dout, cum, Aw, dAw, p.L, p.dk, p.dv,
+                     p.NC);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_attn(const Plan& p, const void* q, const void* k, const void* v,
+                             const void* dout, const float* cum, float* Aw, float* dAw,
+                             hipStream_t s) {
+  if (p.bf16) {
+    if (p.C == 64) return launch_attn_t<bf16, 64>(p, q, k, v, dout, cum, Aw, dAw, s);
+    return launch_attn_t<bf16, 32>(p, q, k, v, dout, cum, Aw, dAw, s);
+  }
+  if (p.C == 64) return launch_attn_t<float, 64>(p, q, k, v, dout, cum, Aw, dAw, s);
+  if (p.C == 32) return launch_attn_t<float, 32>(p, q, k, v, dout, cum, Aw, dAw, s);
+  return launch_attn_t<float, 16>(p, q, k, v, dout, cum, Aw, dAw, s);
+}
+
+template <typename T, int C, int TK>
+static hipError_t launch_dqdk_t(const Plan& p, const void* q, const void* k, const void* v,
+                                const void* dout, const float* cum, const void* st_n,
+                                const void* st_lo, const void* dst_n, const void* dst_lo,
+                                const float* dAw, void* dq, void* dk, float* dla, float* dlt,
+                                hipStream_t s) {
+  hipLaunchKernelGGL((k_chunk_dqdk<T, C, TK>), dim3(p.NC, p.dk / TK, p.BH), dim3(kThreads), 0, s,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)dout, cum, (const T*)st_n,
+                     (const T*)st_lo, (const T*)dst_n, (const T*)dst_lo, dAw, (T*)dq, (T*)dk, dla,
+                     dlt, p.L, p.dk, p.dv, p.NC);
+  return hipGetLastError();
+}
+
+template <typename T, int C>
+static hipError_t launch_dqdk_c(const Plan& p, const void* q, const void* k, const void* v,
+                                const void* dout, const float* cum, const void* st_n,
+                                const void* st_lo, const void* dst_n, const void* dst_lo,
+                                const float* dAw, void* dq, void* dk, float* dla, float* dlt,
+                                hipStream_t s) {
+  if (p.dk % 32 == 0)
+    return launch_dqdk_t<T, C, 32>(p, q, k, v, dout, cum, st_n, st_lo, dst_n, dst_lo, dAw, dq, dk, dla, dlt, s);
+  return launch_dqdk_t<T, C, 16>(p, q, k, v, dout, cum, st_n, st_lo, dst_n, dst_lo, dAw, dq, dk, dla, dlt, s);
+}
+
+hipError_t launch_chunk_dqdk(const Plan& p, const void* q, const void* k, const void* v,
+                             const void* dout, const float* cum, const void* st_n,
+                             const void* st_lo, const void* dst_n, const void* dst_lo,
+                             const float* dAw, void* dq, void* dk, float* dla, float* dlt,
+                             hipStream_t s) {
+  if (p.bf16) {
+    if (p.C == 64)
+      return launch_dqdk_c<bf16, 64>(p, q, k, v, dout, cum, st_n, st_lo, dst_n, dst_lo, dAw, dq, dk, dla, dlt, s);
+    return launch_dqdk_c<bf16, 32>(p, q, k, v, dout, cum, st_n, st_lo, dst_n, dst_lo, dAw, dq, dk, dla, dlt, s);
+  }
+  if (p.C == 64)
+    return launch_dqdk_c<float, 64>(p, q, k, v, dout, cum, st_n, st_lo, dst_n, dst_lo, dAw, dq, dk, dla, dlt, s);
+  if (p.C == 32)
+    return launch_dqdk_c<float, 32>(p, q, k, v, dout, cum, st_n, st_lo, dst_n, dst_lo, dAw, dq, dk, dla, dlt, s);
+  return launch_dqdk_c<float, 16>(p, q, k, v, dout, cum, st_n, st_lo, dst_n, dst_lo, dAw, dq, dk, dla, dlt, s);
+}
+
+template <typename T, int C, int TVD>
+static hipError_t launch_dv_t(const Plan& p, const void* k, const void* dout, const float* cum,
+                              const void* dst_t, const float* Aw, void* dv, hipStream_t s) {
+  hipLaunchKernelGGL((k_chunk_dv<T, C, TVD>), dim3(p.NC, p.dv / TVD, p.BH), dim3(kThreads), 0, s,
+                     (const T*)k, (const T*)dout, cum, (const T*)dst_t, Aw, (T*)dv, p.L, p.dk,
+                     p.dv, p.NC);
+  return hipGetLastError();
+}
+
+template <typename T, int C>
+static hipError_t launch_dv_c(const Plan& p, const void* k, const void* dout, const float* cum,
+                              const void* dst_t, const float* Aw, void* dv, hipStream_t s) {
+  if (p.dv % 128 == 0) return launch_dv_t<T, C, 128>(p, k, dout, cum, dst_t, Aw, dv, s);
+  if (p.dv % 64 == 0) return launch_dv_t<T, C, 64>(p, k, dout, cum, dst_t, Aw, dv, s);
+  if (p.dv % 32 == 0) return launch_dv_t<T, C, 32>(p, k, dout, cum, dst_t, Aw, dv, s);
+  return launch_dv_t<T, C, 16>(p, k, dout, cum, dst_t, Aw, dv, s);
+}
+
+hipError_t launch_chunk_dv(const Plan& p, const void* k, const void* dout, const float* cum,
+                           const void* dst_t, const float* Aw, void* dv, hipStream_t s) {
+  if (p.bf16) {
+    if (p.C == 64) return launch_dv_c<bf16, 64>(p, k, dout, cum, dst_t, Aw, dv, s);
+    return launch_dv_c<bf16, 32>(p, k, dout, cum, dst_t, Aw, dv, s);
+  }
+  if (p.C == 64) return launch_dv_c<float, 64>(p, k, dout, cum, dst_t, Aw, dv, s);
+  if (p.C == 32) return launch_dv_c<float, 32>(p, k, dout, cum, dst_t, Aw, dv, s);
+  return launch_dv_c<float, 16>(p, k, dout, cum, dst_t, Aw, dv, s);
+}
+
+hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT, float* rs,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_rowsum_state, dim3(p.dk, p.BH), dim3(kWave), 0, s, hT, dhT, rs, p.dk, p.dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,
+                            hipStream_t s) {
+  const int threads = p.dk < kThreads ? p.dk : kThreads;
+  hipLaunchKernelGGL(k_dla_carry, dim3(p.NC, p.BH), dim3(threads), 0, s, dlt, rs, dla, p.L, p.dk,
+                     p.C, p.NC);
+  return hipGetLastError();
 }
 
 }  // namespace gla

@@ -84,6 +84,13 @@ __device__ inline floatx4 zero4() {
 
 __device__ inline float fast_exp(float x) { return __expf(x); }
 
+// exp for factors of a given I/O type: the fp32 path keeps full accuracy
+// (expf); the bf16 path uses the hardware exp2 based __expf, whose relative
+// error is far below bf16 rounding for the arguments that occur.
+template <typename T> __device__ inline float gexp(float x);
+template <> __device__ inline float gexp<float>(float x) { return expf(x); }
+template <> __device__ inline float gexp<bf16>(float x) { return __expf(x); }
+
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ inline int wave_id() { return threadIdx.x / kWave; }
 

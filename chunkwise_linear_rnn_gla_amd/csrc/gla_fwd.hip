@@ -12,51 +12,9 @@
 // <= 1, diagonal blocks in fp32 on the vector ALUs.
 #include "gla_common.h"
 #include "gla_internal.h"
+#include "gla_pblock.h"
 
 namespace gla {
-
-// ------------------------------------------------------------------ helpers
-
-// Load 8 consecutive elements (32-byte or 16-byte aligned) as fp32.
-__device__ inline void load8(const float* p, float* o) {
-  f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[e + 4] = b[e]; }
-}
-__device__ inline void load8(const bf16* p, float* o) {
-  bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = static_cast<float>(a[e]);
-}
-__device__ inline void store8(float* p, const float* x) {
-  f32x4 a, b;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[e + 4]; }
-  *reinterpret_cast<f32x4*>(p) = a;
-  *reinterpret_cast<f32x4*>(p + 4) = b;
-}
-__device__ inline void store8(bf16* p, const float* x) {
-  bf16x8 a;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] = static_cast<bf16>(x[e]);
-  *reinterpret_cast<bf16x8*>(p) = a;
-}
-// Store 4 consecutive elements from an accumulator column.
-__device__ inline void store4(float* p, floatx4 x) { *reinterpret_cast<f32x4*>(p) = x; }
-__device__ inline void store4(bf16* p, floatx4 x) {
-  bf16x4 a;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) a[e] = static_cast<bf16>(x[e]);
-  *reinterpret_cast<bf16x4*>(p) = a;
-}
-
-// Off-diagonal sub-chunk pair number pi -> (query sub-chunk j, key sub-chunk u < j).
-__device__ inline void pair_of(int pi, int& j, int& u) {
-  j = 1;
-  while (pi >= j) { pi -= j; ++j; }
-  u = pi;
-}
 
 // ------------------------------------------------------------------ K1: chunk cumsum
 // Chunk-local inclusive cumsum of log alpha (the App. B listing's "cumsum of
@@ -90,17 +48,23 @@ hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t 
 // backward's dS recurrence).  The tile lives in MFMA accumulators (fp32); each
 // chunk's operands are staged transposed through LDS so that both MFMA
 // operands read contiguous token runs.
-template <typename T, int TS, int REV>
+//
+// SPLIT (bf16 only): the scaled operand X ⊙ e^{...} is held as a high and a
+// low bf16 part (two MFMAs), and st_n_lo receives the low part of every
+// written state, so that the backward's gradients see ~16-bit operands.
+template <typename T, int TS, int REV, int SPLIT>
 __global__ __launch_bounds__(kThreads) void k_chunk_state(
     const T* __restrict__ X, const T* __restrict__ Y, const float* __restrict__ cum,
     const float* __restrict__ init, const float* __restrict__ seg_in, T* __restrict__ st_t,
-    T* __restrict__ st_n, float* __restrict__ end_out, float* __restrict__ seg_out, int L,
-    int dk, int dv, int C, int NC, int NSEG, int seg_chunks, int mode) {
+    T* __restrict__ st_n, T* __restrict__ st_n_lo, float* __restrict__ end_out,
+    float* __restrict__ seg_out, int L, int dk, int dv, int C, int NC, int NSEG, int seg_chunks,
+    int mode) {
   using M = Mma<T>;
   constexpr int NT1 = TS / 16, NTT = NT1 * NT1, NW = (NTT + 3) / 4;
   constexpr int LDC = 64 + 16 / (int)sizeof(T);  // chunk <= 64 tokens, padded rows
   constexpr int CG = TS / 8;
   __shared__ __attribute__((aligned(16))) T xs[TS][LDC];
+  __shared__ __attribute__((aligned(16))) T xl[SPLIT ? TS : 1][SPLIT ? LDC : 8];
   __shared__ __attribute__((aligned(16))) T ys[TS][LDC];
   __shared__ float gam[TS];
 
@@ -145,18 +109,20 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
         load8(cum + xo + (size_t)(r0 + row) * dk + i0 + c0, bv);
         load8(glast + c0, gv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] *= fast_exp(REV ? bv[e] : gv[e] - bv[e]);
+        for (int e = 0; e < 8; ++e) xv[e] *= gexp<T>(REV ? bv[e] : gv[e] - bv[e]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) xv[e] = yv[e] = 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        xs[c0 + e][row] = from_f32<T>(xv[e]);
+        const T hi = from_f32<T>(xv[e]);
+        xs[c0 + e][row] = hi;
+        if constexpr (SPLIT) xl[c0 + e][row] = from_f32<T>(xv[e] - to_f32(hi));
         ys[c0 + e][row] = from_f32<T>(yv[e]);
       }
     }
-    if (threadIdx.x < TS) gam[threadIdx.x] = fast_exp(glast[threadIdx.x]);
+    if (threadIdx.x < TS) gam[threadIdx.x] = gexp<T>(glast[threadIdx.x]);
     __syncthreads();
 
     // The state entering this chunk's update: S_{n-1} (forward) or dS_n (reverse).
@@ -171,8 +137,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
         if (st_t) store4(st_t + (((size_t)bh * NC + n) * dv + j) * dk + ib, acc[t]);
         if (st_n) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            st_n[(((size_t)bh * NC + n) * dk + ib + r) * dv + j] = from_f32<T>(acc[t][r]);
+          for (int r = 0; r < 4; ++r) {
+            const size_t idx = (((size_t)bh * NC + n) * dk + ib + r) * dv + j;
+            const T hi = from_f32<T>(acc[t][r]);
+            st_n[idx] = hi;
+            if (SPLIT && st_n_lo) st_n_lo[idx] = from_f32<T>(acc[t][r] - to_f32(hi));
+          }
         }
       }
     }
@@ -187,6 +157,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
         auto a = load_frag<T>(&xs[ti * 16 + (l & 15)][kk + (l >> 4) * M::KPL]);
         auto b = load_frag<T>(&ys[tj * 16 + (l & 15)][kk + (l >> 4) * M::KPL]);
         acc[t] = M::run(a, b, acc[t]);
+        if constexpr (SPLIT) {
+          auto al = load_frag<T>(&xl[ti * 16 + (l & 15)][kk + (l >> 4) * M::KPL]);
+          acc[t] = M::run(al, b, acc[t]);
+        }
       }
     }
     __syncthreads();
@@ -211,39 +185,44 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
   }
 }
 
-template <typename T, int TS, int REV>
+template <typename T, int TS, int REV, int SPLIT>
 static hipError_t launch_cs(const Plan& p, int mode, const void* X, const void* Y,
                             const float* cum, const float* init, const float* seg_in,
-                            void* st_t, void* st_n, float* end_out, float* seg_out,
-                            hipStream_t s) {
+                            void* st_t, void* st_n, void* st_n_lo, float* end_out,
+                            float* seg_out, hipStream_t s) {
   dim3 grid(p.dv / TS, p.dk / TS, p.BH * p.NSEG);
-  hipLaunchKernelGGL((k_chunk_state<T, TS, REV>), grid, dim3(kThreads), 0, s,
-                     (const T*)X, (const T*)Y, cum, init, seg_in, (T*)st_t, (T*)st_n, end_out,
-                     seg_out, p.L, p.dk, p.dv, p.C, p.NC, p.NSEG, p.seg_chunks, mode);
+  hipLaunchKernelGGL((k_chunk_state<T, TS, REV, SPLIT>), grid, dim3(kThreads), 0, s,
+                     (const T*)X, (const T*)Y, cum, init, seg_in, (T*)st_t, (T*)st_n,
+                     (T*)st_n_lo, end_out, seg_out, p.L, p.dk, p.dv, p.C, p.NC, p.NSEG,
+                     p.seg_chunks, mode);
   return hipGetLastError();
 }
 
-template <typename T, int REV>
+template <typename T, int REV, int SPLIT>
 static hipError_t launch_cs_ts(const Plan& p, int mode, const void* X, const void* Y,
                                const float* cum, const float* init, const float* seg_in,
-                               void* st_t, void* st_n, float* end_out, float* seg_out,
-                               hipStream_t s) {
+                               void* st_t, void* st_n, void* st_n_lo, float* end_out,
+                               float* seg_out, hipStream_t s) {
   switch (p.TS) {
-    case 64: return launch_cs<T, 64, REV>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, end_out, seg_out, s);
-    case 32: return launch_cs<T, 32, REV>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, end_out, seg_out, s);
-    default: return launch_cs<T, 16, REV>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, end_out, seg_out, s);
+    case 64: return launch_cs<T, 64, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
+    case 32: return launch_cs<T, 32, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
+    default: return launch_cs<T, 16, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
   }
 }
 
-hipError_t launch_chunk_state(const Plan& p, int rev, int mode, const void* X, const void* Y,
-                              const float* cum, const float* init, const float* seg_in,
-                              void* st_t, void* st_n, float* end_out, float* seg_out,
-                              hipStream_t s) {
-  if (p.bf16)
-    return rev ? launch_cs_ts<bf16, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, end_out, seg_out, s)
-               : launch_cs_ts<bf16, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, end_out, seg_out, s);
-  return rev ? launch_cs_ts<float, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, end_out, seg_out, s)
-             : launch_cs_ts<float, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, end_out, seg_out, s);
+hipError_t launch_chunk_state(const Plan& p, int rev, int mode, int split, const void* X,
+                              const void* Y, const float* cum, const float* init,
+                              const float* seg_in, void* st_t, void* st_n, void* st_n_lo,
+                              float* end_out, float* seg_out, hipStream_t s) {
+  if (p.bf16) {
+    if (split)
+      return rev ? launch_cs_ts<bf16, 1, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s)
+                 : launch_cs_ts<bf16, 0, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
+    return rev ? launch_cs_ts<bf16, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s)
+               : launch_cs_ts<bf16, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s);
+  }
+  return rev ? launch_cs_ts<float, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s)
+             : launch_cs_ts<float, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s);
 }
 
 // ------------------------------------------------------------------ segment scan
@@ -267,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void k_segment_scan(
       float G = 0.f;
       const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks);
       for (int n = nb; n < ne; ++n) G += crow[(size_t)(min(L, (n + 1) * C) - 1) * dk];
-      S = fast_exp(G) * S + seg_u[so];
+      S = expf(G) * S + seg_u[so];
     }
     if (end_out) end_out[((size_t)bh * dk + i) * dv + j] = S;
   }
@@ -300,35 +279,27 @@ hipError_t launch_copy_state(const Plan& p, const float* src, float* dst, hipStr
 // ------------------------------------------------------------------ K3: chunk output
 // One workgroup per (batch-head, chunk, d_v tile).  Walks d_k in slices:
 //  * inter-chunk term (Q ⊙ Lambda) S_{n-1} on MFMA (papercache.org notes §4.2,
-//    the Lambda factor carries the decay from the chunk start);
-//  * off-diagonal sub-chunk blocks of P on MFMA with the query sub-chunk's
-//    first row z as reference: (Q_j ⊙ e^{B_j - z}) (K_u ⊙ e^{z - B_u})^T,
-//    both factors <= 1 (notes §4.3 / Figure 3, inter-sub-chunk in half
-//    precision; App. B listing);
-//  * diagonal sub-chunk blocks in fp32 on the vector ALUs (Figure 3, the
-//    intra-sub-chunk part in full precision).  The decay between rows
-//    r <= m is formed as the running product alpha_{r+1}...alpha_m of
-//    per-row gates alpha = e^{B_r - B_{r-1}}, which equals e^{B_m - B_r}
-//    up to rounding, never divides and cannot overflow.
-// Then P V on MFMA (the diagonal blocks of P split into a bf16 high part and
-// a bf16 low part so that they keep ~16 bits) and the result is stored.
+//    Lambda carries the decay from the chunk start);
+//  * the chunk's gated score matrix P (gla_pblock.h): off-diagonal sub-chunk
+//    blocks on MFMA, diagonal blocks in fp32 on the vector ALUs (notes §4.3 /
+//    Figure 3).
+// Then P V on MFMA and the store.  Off-diagonal P is rounded to the I/O type
+// before P V (half-precision inter-sub-chunk products); the diagonal blocks
+// are split into a high and a low part so that they keep ~16 mantissa bits.
 template <typename T, int C, int TVO>
 __global__ __launch_bounds__(kThreads) void k_chunk_output(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ cum, const T* __restrict__ st_t, T* __restrict__ o, int L, int dk,
     int dv, int NC) {
   using M = Mma<T>;
-  constexpr bool BF = sizeof(T) == 2;
-  constexpr int KS = BF ? 32 : 16;
-  constexpr int PT = 16 / (int)sizeof(T);
-  constexpr int LDT = KS + PT, LDF = KS + 4, LDP = C + PT, LDV = C + PT;
+  using PB = PBuilder<T, C>;
+  constexpr bool BF = PB::BF;
+  constexpr int KS = PB::KS, LDT = PB::LDT, LDF = PB::LDF, PT = PB::PT;
+  constexpr int LDP = C + PT, LDV = C + PT;
   constexpr int NRT = C / 16, NCT = TVO / 16;
   constexpr int WC = NCT < 4 ? NCT : 4, WR = 4 / WC;
   constexpr int NCW = NCT / WC, NRW = (NRT + WR - 1) / WR;
-  constexpr int NP = NRT * (NRT - 1) / 2, NPW = (NP + 3) / 4;
-  constexpr int WPB = 4 / NRT, NG = 8 * WPB;
-  constexpr int CPL = KS / NG > 0 ? KS / NG : 1;
-  constexpr int SLICE_BYTES = 3 * C * LDT * (int)sizeof(T) + 2 * C * LDF * 4;
+  constexpr int SLICE_BYTES = PB::SLICE_BYTES + C * LDT * (int)sizeof(T);
   constexpr int VT_BYTES = TVO * LDV * (int)sizeof(T);
   constexpr int REGION = SLICE_BYTES > VT_BYTES ? SLICE_BYTES : VT_BYTES;
 
@@ -338,9 +309,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
   __shared__ float pd[4][16][17];
   T* qs = reinterpret_cast<T*>(smem);
   T* ks = qs + C * LDT;
-  T* qts = ks + C * LDT;
-  float* bs = reinterpret_cast<float*>(qts + C * LDT);
+  float* bs = reinterpret_cast<float*>(ks + C * LDT);
   float* als = bs + C * LDF;
+  T* qts = reinterpret_cast<T*>(als + C * LDF);
   T* vt = reinterpret_cast<T*>(smem);
 
   const int n = blockIdx.x, j0 = blockIdx.y * TVO, bh = blockIdx.z;
@@ -350,18 +321,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
 
   for (int it = tid; it < C * LDP; it += kThreads) {
     (&p_hi[0][0])[it] = from_f32<T>(0.f);
-    if (BF) (&p_lo[0][0])[it] = from_f32<T>(0.f);
+    if constexpr (BF) (&p_lo[0][0])[it] = from_f32<T>(0.f);
   }
 
-  // roles
-  const int db = w / WPB, tb = (w % WPB) * kWave + l, dp = tb & 7, dg = tb >> 3;
+  PB pb;
+  pb.init();
   const int wc = w % WC, wr = w / WC;
-  float dout[17];
-#pragma unroll
-  for (int i = 0; i < 17; ++i) dout[i] = 0.f;
-  floatx4 pacc[NPW > 0 ? NPW : 1];
-#pragma unroll
-  for (int t = 0; t < (NPW > 0 ? NPW : 1); ++t) pacc[t] = zero4();
   floatx4 acc[NRW][NCW];
 #pragma unroll
   for (int a = 0; a < NRW; ++a)
@@ -372,33 +337,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
 
   for (int s0 = 0; s0 < dk; s0 += KS) {
     __syncthreads();
-    for (int it = tid; it < C * (KS / 8); it += kThreads) {
-      const int row = it / (KS / 8), c8 = (it % (KS / 8)) * 8;
-      const bool valid = row < rv;
-      const int crow = valid ? r0 + row : r0 + rv - 1;
-      float qv[8], kv[8], bv[8];
-      load8(cum + qo + (size_t)crow * dk + s0 + c8, bv);
-      if (valid) {
-        load8(q + qo + (size_t)crow * dk + s0 + c8, qv);
-        load8(k + qo + (size_t)crow * dk + s0 + c8, kv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = kv[e] = 0.f;
-      }
-      store8(qs + row * LDT + c8, qv);
-      store8(ks + row * LDT + c8, kv);
-      store8(bs + row * LDF + c8, bv);
-      float qt[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qt[e] = qv[e] * fast_exp(bv[e]);
-      store8(qts + row * LDT + c8, qt);
-    }
+    PB::stage(q, k, cum, qo, r0, rv, dk, s0, qs, ks, bs, qts);
     __syncthreads();
-    for (int it = tid; it < C * KS; it += kThreads) {
-      const int row = it / KS, c = it % KS;
-      als[row * LDF + c] = (row & 15) ? fast_exp(bs[row * LDF + c] - bs[(row - 1) * LDF + c]) : 1.f;
-    }
-
+    PB::gates(bs, als);
     // inter-chunk term
     for (int kk = 0; kk < KS; kk += M::K) {
       typename M::frag bf[NCW];
@@ -416,95 +357,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
         for (int ct = 0; ct < NCW; ++ct) acc[rt][ct] = M::run(a, bf[ct], acc[rt][ct]);
       }
     }
-
-    // off-diagonal sub-chunk blocks of P
-#pragma unroll
-    for (int t = 0; t < NPW; ++t) {
-      const int pi = w + 4 * t;
-      if (pi >= NP) continue;
-      int jq, ju;
-      pair_of(pi, jq, ju);
-      const int m = l & 15;
-      for (int kk = 0; kk < KS; kk += M::K) {
-        const int cq = kk + (l >> 4) * M::KPL;
-        float sa[M::KPL], sb[M::KPL];
-#pragma unroll
-        for (int e = 0; e < M::KPL; ++e) {
-          const float z = bs[(jq * 16) * LDF + cq + e];
-          sa[e] = fast_exp(bs[(jq * 16 + m) * LDF + cq + e] - z);
-          sb[e] = fast_exp(z - bs[(ju * 16 + m) * LDF + cq + e]);
-        }
-        auto a = scaled_frag<T>(qs + (jq * 16 + m) * LDT + cq, sa);
-        auto b = scaled_frag<T>(ks + (ju * 16 + m) * LDT + cq, sb);
-        pacc[t] = M::run(a, b, pacc[t]);
-      }
-    }
+    pb.offdiag(qs, ks, bs);
     __syncthreads();
-
-    // diagonal sub-chunk blocks of P: fp32, running gate products
-    if (dg * CPL < KS) {
-      const int cb = dg * CPL;
-      const int m1 = dp, m2 = 15 - dp;
-      float wv[CPL];
-#pragma unroll
-      for (int i = 0; i < 17; ++i) {
-        const bool first = i <= dp;
-        const int m = first ? m1 : m2;
-        const int r = first ? (dp - i) : (m2 - (i - dp - 1));
-        const bool reset = (i == 0) || (i == dp + 1);
-        const int R = db * 16 + m, Rk = db * 16 + r;
-        float part = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const float qv = to_f32(qs[R * LDT + cb + c]);
-          const float al = als[(Rk + 1 < C ? Rk + 1 : Rk) * LDF + cb + c];
-          wv[c] = reset ? qv : wv[c] * al;
-          part += wv[c] * to_f32(ks[Rk * LDT + cb + c]);
-        }
-        dout[i] += part;
-      }
-    }
+    pb.diag(qs, ks, als);
   }
   __syncthreads();
-
-  // reduce diagonal partials over the 8 channel groups of a wave
-#pragma unroll
-  for (int i = 0; i < 17; ++i) {
-    dout[i] += __shfl_xor(dout[i], 8);
-    dout[i] += __shfl_xor(dout[i], 16);
-    dout[i] += __shfl_xor(dout[i], 32);
-  }
-  if ((l >> 3) == 0) {
-#pragma unroll
-    for (int i = 0; i < 17; ++i) {
-      const bool first = i <= dp;
-      const int m = first ? dp : 15 - dp;
-      const int r = first ? (dp - i) : (15 - dp - (i - dp - 1));
-      pd[w][m][r] = dout[i];
-    }
-  }
-  // off-diagonal blocks to LDS (bf16 / fp32)
-#pragma unroll
-  for (int t = 0; t < NPW; ++t) {
-    const int pi = w + 4 * t;
-    if (pi >= NP) continue;
-    int jq, ju;
-    pair_of(pi, jq, ju);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      p_hi[jq * 16 + (l >> 4) * 4 + r][ju * 16 + (l & 15)] = from_f32<T>(pacc[t][r]);
-  }
-  __syncthreads();
-  for (int it = tid; it < NRT * 256; it += kThreads) {
-    const int b = it >> 8, m = (it >> 4) & 15, r = it & 15;
-    if (r > m) continue;
-    float val = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < WPB; ++ww) val += pd[b * WPB + ww][m][r];
+  pb.finish(pd, [&](int m, int r, float val) {
     const T hi = from_f32<T>(val);
-    p_hi[b * 16 + m][b * 16 + r] = hi;
-    if (BF) p_lo[b * 16 + m][b * 16 + r] = from_f32<T>(val - to_f32(hi));
-  }
+    p_hi[m][r] = hi;
+    if constexpr (BF) {
+      if ((m >> 4) == (r >> 4)) p_lo[m][r] = from_f32<T>(val - to_f32(hi));
+    }
+  });
   // V tile, transposed: vt[col][token]
   for (int it = tid; it < C * (TVO / 8); it += kThreads) {
     const int row = it / (TVO / 8), c8 = (it % (TVO / 8)) * 8;
@@ -533,9 +397,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
         acc[rt][ct] = M::run(a, b, acc[rt][ct]);
       }
     }
-    if (BF) {
+    if constexpr (BF) {
       const int kd = (rti * 16 / M::K) * M::K;
-      auto a = load_frag<T>(&p_lo[BF ? rti * 16 + (l & 15) : 0][BF ? kd + (l >> 4) * M::KPL : 0]);
+      auto a = load_frag<T>(&p_lo[rti * 16 + (l & 15)][kd + (l >> 4) * M::KPL]);
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         auto b = load_frag<T>(vt + ((wc + WC * ct) * 16 + (l & 15)) * LDV + kd + (l >> 4) * M::KPL);

@@ -21,6 +21,7 @@ struct Plan {
   size_t esize;      // bytes per I/O element
   // workspace layout (byte offsets); 0-sized regions have offset 0
   size_t off_cum, off_st, off_st2, off_seg_u, off_seg_in, off_end, off_dlt, off_rs;
+  size_t off_A, off_dA, off_stlo, off_dstlo;
   size_t ws_fwd, ws_bwd;
 };
 
@@ -39,10 +40,12 @@ hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t 
 //   mode SEG_FILL  : start from seg_in[seg] (or init / zeros if NSEG == 1),
 //                    writes per-chunk states, end state -> end_out (last seg)
 enum StateMode { SEG_LOCAL = 0, SEG_FILL = 1 };
-hipError_t launch_chunk_state(const Plan& p, int rev, int mode, const void* X, const void* Y,
-                              const float* cum, const float* init, const float* seg_u_in,
-                              void* st_t, void* st_n, float* end_out, float* seg_u_out,
-                              hipStream_t s);
+// split (bf16 only): hi/lo operand split, and st_n_lo receives the low part of
+// the states written to st_n.
+hipError_t launch_chunk_state(const Plan& p, int rev, int mode, int split, const void* X,
+                              const void* Y, const float* cum, const float* init,
+                              const float* seg_u_in, void* st_t, void* st_n, void* st_n_lo,
+                              float* end_out, float* seg_u_out, hipStream_t s);
 // Combine per-segment local states: seg_in[seg] = state entering segment seg
 // (forward order, or reverse order when rev), end_out = final state.
 hipError_t launch_segment_scan(const Plan& p, int rev, const float* cum, const float* init,
@@ -53,10 +56,19 @@ hipError_t launch_chunk_output(const Plan& p, const void* q, const void* k, cons
 hipError_t launch_copy_state(const Plan& p, const float* src, float* dst, hipStream_t s);
 
 // ---- backward kernels (gla_bwd.hip) ----
-hipError_t launch_chunk_grad(const Plan& p, const void* q, const void* k, const void* v,
+// A (chunk score matrix) and dA = (dO V^T) ⊙ M per chunk, fp32 C x C blocks.
+hipError_t launch_chunk_attn(const Plan& p, const void* q, const void* k, const void* v,
+                             const void* dout, const float* cum, float* Aw, float* dAw,
+                             hipStream_t s);
+// dq, dk, chunk-local reverse cumsum of dlog b (into dla) and chunk totals.
+// st_lo / dst_lo: low parts of the states (bf16 split), or null.
+hipError_t launch_chunk_dqdk(const Plan& p, const void* q, const void* k, const void* v,
                              const void* dout, const float* cum, const void* st_n,
-                             const void* dst_n, const void* dst_t, void* dq, void* dk,
-                             void* dv, float* dla_local, float* dlt, hipStream_t s);
+                             const void* st_lo, const void* dst_n, const void* dst_lo,
+                             const float* dAw, void* dq, void* dk, float* dla, float* dlt,
+                             hipStream_t s);
+hipError_t launch_chunk_dv(const Plan& p, const void* k, const void* dout, const float* cum,
+                           const void* dst_t, const float* Aw, void* dv, hipStream_t s);
 hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT, float* rs,
                                hipStream_t s);
 hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,

@@ -1,0 +1,231 @@
+// gla_pblock.h -- building the chunk's causal gated score matrix
+//   P[m][r] = sum_k q_mk k_rk exp(B_mk - B_rk),  r <= m  (0 above the diagonal)
+// for one chunk of C rows, walking d_k in slices of KS channels (papercache.org
+// notes §4.1 log-space parallel form restricted to a chunk; §4.3 / Figure 3
+// secondary chunking).
+//
+//  * Off-diagonal sub-chunk blocks (query sub-chunk j, key sub-chunk u < j):
+//    MFMA on (Q_j ⊙ e^{B_j - z}) (K_u ⊙ e^{z - B_u})^T with z = B at the
+//    first row of sub-chunk j (the App. B listing's reference row), so both
+//    factors are <= 1.
+//  * Diagonal 16 x 16 blocks: fp32 on the vector ALUs.  The decay between rows
+//    r <= m is the running product alpha_{r+1} ... alpha_m of the per-row gates
+//    alpha_s = e^{B_s - B_{s-1}}: equal to e^{B_m - B_r} up to rounding, no
+//    division, no overflow.  Lane (p, g) of a block team owns rows p and
+//    15 - p (17 (row, key) pairs in all) over a channel group g.
+#pragma once
+
+#include "gla_common.h"
+
+namespace gla {
+
+// Off-diagonal sub-chunk pair number pi -> (query sub-chunk j, key sub-chunk u < j).
+__device__ inline void pair_of(int pi, int& j, int& u) {
+  j = 1;
+  while (pi >= j) { pi -= j; ++j; }
+  u = pi;
+}
+
+// Load / store 8 consecutive elements as fp32.
+__device__ inline void load8(const float* p, float* o) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { o[e] = a[e]; o[e + 4] = b[e]; }
+}
+__device__ inline void load8(const bf16* p, float* o) {
+  bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = static_cast<float>(a[e]);
+}
+__device__ inline void store8(float* p, const float* x) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = x[e]; b[e] = x[e + 4]; }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+__device__ inline void store8(bf16* p, const float* x) {
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = static_cast<bf16>(x[e]);
+  *reinterpret_cast<bf16x8*>(p) = a;
+}
+__device__ inline void store4(float* p, floatx4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ inline void store4(bf16* p, floatx4 x) {
+  bf16x4 a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] = static_cast<bf16>(x[e]);
+  *reinterpret_cast<bf16x4*>(p) = a;
+}
+
+template <typename T, int C>
+struct PBuilder {
+  using M = Mma<T>;
+  static constexpr bool BF = sizeof(T) == 2;
+  static constexpr int KS = BF ? 32 : 16;          // d_k slice
+  static constexpr int PT = 16 / (int)sizeof(T);
+  static constexpr int LDT = KS + PT;              // row length of T slice arrays
+  static constexpr int LDF = KS + 4;               // row length of fp32 slice arrays
+  static constexpr int NRT = C / 16;               // sub-chunks per chunk
+  static constexpr int NP = NRT * (NRT - 1) / 2;   // off-diagonal pairs
+  static constexpr int NPW = (NP + 3) / 4;
+  static constexpr int NPA = NPW > 0 ? NPW : 1;
+  static constexpr int WPB = 4 / NRT;              // waves per diagonal block
+  static constexpr int NG = 8 * WPB;               // channel groups per block
+  static constexpr int CPL = KS / NG > 0 ? KS / NG : 1;
+  // LDS: q, k (T), cumsum and gates (fp32), one slice
+  static constexpr int SLICE_BYTES = 2 * C * LDT * (int)sizeof(T) + 2 * C * LDF * 4;
+
+  float dsum[17];
+  floatx4 pacc[NPA];
+  int db, dp, dg, w, l;
+
+  __device__ void init() {
+    w = wave_id();
+    l = lane_id();
+    const int tb = (w % WPB) * kWave + l;
+    db = w / WPB;
+    dp = tb & 7;
+    dg = tb >> 3;
+#pragma unroll
+    for (int i = 0; i < 17; ++i) dsum[i] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NPA; ++t) pacc[t] = zero4();
+  }
+
+  // Stage rows [r0, r0 + C) x channels [s0, s0 + KS) of q, k and the chunk-local
+  // cumsum into LDS.  Rows >= rv are padding: q = k = 0 and the cumsum of the
+  // last valid row (log alpha = 0 there).  Optionally also writes
+  // qt = T(q ⊙ e^B) (row-major, LDT) for the inter-chunk MFMA.
+  __device__ static void stage(const T* q, const T* k, const float* cum, size_t qo, int r0,
+                               int rv, int dk, int s0, T* qs, T* ks, float* bs, T* qt) {
+    for (int it = threadIdx.x; it < C * (KS / 8); it += kThreads) {
+      const int row = it / (KS / 8), c8 = (it % (KS / 8)) * 8;
+      const bool valid = row < rv;
+      const int crow = valid ? r0 + row : r0 + rv - 1;
+      float qv[8], kv[8], bv[8];
+      load8(cum + qo + (size_t)crow * dk + s0 + c8, bv);
+      if (valid) {
+        load8(q + qo + (size_t)crow * dk + s0 + c8, qv);
+        load8(k + qo + (size_t)crow * dk + s0 + c8, kv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = kv[e] = 0.f;
+      }
+      store8(qs + row * LDT + c8, qv);
+      store8(ks + row * LDT + c8, kv);
+      store8(bs + row * LDF + c8, bv);
+      if (qt) {
+        float t8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t8[e] = qv[e] * gexp<T>(bv[e]);
+        store8(qt + row * LDT + c8, t8);
+      }
+    }
+  }
+
+  // Per-row gates within each sub-chunk: als[row] = e^{B_row - B_{row-1}}
+  // (1 at a sub-chunk's first row, where it is never used).
+  __device__ static void gates(const float* bs, float* als) {
+    for (int it = threadIdx.x; it < C * KS; it += kThreads) {
+      const int row = it / KS, c = it % KS;
+      als[row * LDF + c] =
+          (row & 15) ? gexp<T>(bs[row * LDF + c] - bs[(row - 1) * LDF + c]) : 1.f;
+    }
+  }
+
+  // Off-diagonal blocks, MFMA, accumulated over slices.  Needs qs, ks, bs.
+  __device__ void offdiag(const T* qs, const T* ks, const float* bs) {
+#pragma unroll
+    for (int t = 0; t < NPW; ++t) {
+      const int pi = w + 4 * t;
+      if (pi >= NP) continue;
+      int jq, ju;
+      pair_of(pi, jq, ju);
+      const int m = l & 15;
+      for (int kk = 0; kk < KS; kk += M::K) {
+        const int cq = kk + (l >> 4) * M::KPL;
+        float sa[M::KPL], sb[M::KPL];
+#pragma unroll
+        for (int e = 0; e < M::KPL; ++e) {
+          const float z = bs[(jq * 16) * LDF + cq + e];
+          sa[e] = gexp<T>(bs[(jq * 16 + m) * LDF + cq + e] - z);
+          sb[e] = gexp<T>(z - bs[(ju * 16 + m) * LDF + cq + e]);
+        }
+        auto a = scaled_frag<T>(qs + (jq * 16 + m) * LDT + cq, sa);
+        auto b = scaled_frag<T>(ks + (ju * 16 + m) * LDT + cq, sb);
+        pacc[t] = M::run(a, b, pacc[t]);
+      }
+    }
+  }
+
+  // Diagonal blocks, fp32 VALU, accumulated over slices.  Needs qs, ks, als.
+  __device__ void diag(const T* qs, const T* ks, const float* als) {
+    if (dg * CPL >= KS) return;
+    const int cb = dg * CPL;
+    const int m1 = dp, m2 = 15 - dp;
+    float wv[CPL];
+#pragma unroll
+    for (int i = 0; i < 17; ++i) {
+      const bool first = i <= dp;
+      const int m = first ? m1 : m2;
+      const int r = first ? (dp - i) : (m2 - (i - dp - 1));
+      const bool reset = (i == 0) || (i == dp + 1);
+      const int R = db * 16 + m, Rk = db * 16 + r;
+      const int Ra = (Rk + 1 < C) ? Rk + 1 : Rk;
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const float qv = to_f32(qs[R * LDT + cb + c]);
+        const float al = als[Ra * LDF + cb + c];
+        wv[c] = reset ? qv : wv[c] * al;
+        part += wv[c] * to_f32(ks[Rk * LDT + cb + c]);
+      }
+      dsum[i] += part;
+    }
+  }
+
+  // After the last slice (and a barrier): reduce the diagonal partials and
+  // hand every entry of P to emit(m, r, value), r <= m.  Off-diagonal entries
+  // are emitted by the wave that owns the block, diagonal ones after a
+  // cross-wave sum through pd (4 x 16 x 17 floats of LDS).
+  template <typename Emit>
+  __device__ void finish(float (*pd)[16][17], Emit emit) {
+#pragma unroll
+    for (int i = 0; i < 17; ++i) {
+      dsum[i] += __shfl_xor(dsum[i], 8);
+      dsum[i] += __shfl_xor(dsum[i], 16);
+      dsum[i] += __shfl_xor(dsum[i], 32);
+    }
+    if ((l >> 3) == 0) {
+#pragma unroll
+      for (int i = 0; i < 17; ++i) {
+        const bool first = i <= dp;
+        const int m = first ? dp : 15 - dp;
+        const int r = first ? (dp - i) : (15 - dp - (i - dp - 1));
+        pd[w][m][r] = dsum[i];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NPW; ++t) {
+      const int pi = w + 4 * t;
+      if (pi >= NP) continue;
+      int jq, ju;
+      pair_of(pi, jq, ju);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) emit(jq * 16 + (l >> 4) * 4 + r, ju * 16 + (l & 15), pacc[t][r]);
+    }
+    __syncthreads();
+    for (int it = threadIdx.x; it < NRT * 256; it += kThreads) {
+      const int b = it >> 8, m = (it >> 4) & 15, r = it & 15;
+      if (r > m) continue;
+      float val = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WPB; ++ww) val += pd[b * WPB + ww][m][r];
+      emit(b * 16 + m, b * 16 + r, val);
+    }
+  }
+};
+
+}  // namespace gla

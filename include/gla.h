@@ -117,6 +117,27 @@ gla_status gla_bwd(const gla_dims *dims, int dtype,
                    void *dq, void *dk, void *dv, float *dlog_alpha, float *dh0,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- launch profiling (measurement support; not part of the computation) ----
+ * While enabled, every kernel launch made by gla_fwd / gla_bwd is bracketed by
+ * two HIP events recorded on the launch stream, so per-kernel GPU durations can
+ * be read back after the caller synchronises.  Records beyond `capacity` are
+ * dropped (and counted).  Enabling creates the events (host-side HIP calls);
+ * it must not be done inside a captured stream.  Not thread-safe: one
+ * profiling session per process at a time.
+ *   gla_profile_begin : enable and clear; capacity >= 1 records.
+ *                       GLA_ERR_SHAPE if capacity < 1, GLA_ERR_HIP if the
+ *                       events cannot be created.
+ *   gla_profile_end   : disable (records stay readable until the next begin).
+ *   gla_profile_count : number of records kept so far (dropped ones excluded).
+ *   gla_profile_get   : name of the i-th record's kernel (static string) and its
+ *                       duration in ms; GLA_ERR_SHAPE for a bad index,
+ *                       GLA_ERR_NULL for NULL outputs, GLA_ERR_HIP if the
+ *                       events have not completed (caller did not sync). */
+gla_status gla_profile_begin(int capacity);
+void gla_profile_end(void);
+int gla_profile_count(void);
+gla_status gla_profile_get(int index, const char **kernel, float *ms);
+
 #ifdef __cplusplus
 }
 #endif
