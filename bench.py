@@ -42,6 +42,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def fused_segments(w, nc):
+    """Segments of the fused forward, as the library plans them: enough
+    (batch-head, segment, d_v tile) workgroups to give each compute unit one."""
+    dvt = 256 if (w.dtype == "bf16" and w.dk <= 128 and w.dv % 256 == 0) else 128
+    units = w.B * w.H * (w.dv // dvt)
+    want = 1 if units >= 256 else -(-256 // units)
+    want = min(want, nc)
+    seg_chunks = -(-nc // max(want, 1))
+    return -(-nc // seg_chunks)
+
+
 def kernel_bytes(name, w, esize, nc):
     """Algorithmic bytes of one launch of a forward kernel: each input byte read
     once and each output byte written once (re-reads are not counted)."""
@@ -51,10 +62,15 @@ def kernel_bytes(name, w, esize, nc):
     a = cum = BH * L * dk * 4
     states = BH * nc * dk * dv * esize
     hT = BH * dk * dv * 4
+    nseg = fused_segments(w, nc)
+    seg = BH * nseg * dk * dv * 4 if nseg > 1 else 0
     return {
         "chunk_cumsum": a + cum,
         "chunk_state": k + v + cum + states + hT,
         "chunk_output": q + k + v + cum + states + o,
+        "chunk_state_local": k + v + cum + seg,
+        "segment_scan": 2 * seg + hT,
+        "seg_output": q + k + v + cum + seg + o,
     }.get(name)
 
 

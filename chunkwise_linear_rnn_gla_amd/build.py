@@ -11,6 +11,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -30,11 +31,27 @@ CFLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")
+    _check_no_scratch(src, r.stderr)
     return obj
+
+
+def _check_no_scratch(src: str, remarks: str) -> None:
+    """Every kernel must keep its working set in registers and LDS: a kernel
+    that spills to scratch is rejected at build time."""
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            raise RuntimeError(f"{os.path.basename(src)}: kernel {name} uses "
+                               f"{m.group(1)} bytes/lane of scratch (register spill)")
 
 
 def build(verbose: bool = False) -> str:

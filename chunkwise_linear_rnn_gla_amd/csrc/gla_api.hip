@@ -2,6 +2,7 @@
 // layout and the stream-ordered launch sequences.
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "../../include/gla.h"
 #include "gla_internal.h"
@@ -43,13 +44,36 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     P.seg_chunks = (int)((P.NC + want - 1) / want);
     P.NSEG = (P.NC + P.seg_chunks - 1) / P.seg_chunks;
   }
+  // Fused forward: one workgroup per (batch-head, segment, d_v tile); enough
+  // segments to give every compute unit a workgroup.
+  P.fused = fused_supported(bf16, C, dk, dv);
+  const char* env = getenv("GLA_FORWARD");
+  if (env && strcmp(env, "materialized") == 0) P.fused = 0;
+  P.DVTF = fused_dv_tile(bf16, dk, dv);
+  P.NSEGF = 1;
+  P.segf_chunks = P.NC > 0 ? P.NC : 1;
+  if (P.fused && P.NC > 1 && P.BH > 0) {
+    const int64_t units = (int64_t)P.BH * (dv / P.DVTF);
+    int64_t want = units >= 256 ? 1 : (256 + units - 1) / units;
+    if (want > P.NC) want = P.NC;
+    P.segf_chunks = (int)((P.NC + want - 1) / want);
+    P.NSEGF = (P.NC + P.segf_chunks - 1) / P.segf_chunks;
+  }
   const size_t BH = (size_t)P.BH, S = (size_t)dk * dv;
   size_t off = 0;
   P.off_cum = off; off = align_up(off + BH * L * dk * 4);
+  P.off_sg = off; off = align_up(off + BH * (size_t)(P.NSEG > P.NSEGF ? P.NSEG : P.NSEGF) * dk * 4);
   P.off_st = off; off = align_up(off + BH * P.NC * S * P.esize);
   P.off_seg_u = off; off = align_up(off + (P.NSEG > 1 ? BH * P.NSEG * S * 4 : 0));
   P.off_seg_in = off; off = align_up(off + (P.NSEG > 1 ? BH * P.NSEG * S * 4 : 0));
-  P.ws_fwd = off;
+  {
+    // the fused forward reuses the cumsum region and needs its own segment states
+    size_t f = P.off_st;
+    P.off_fu = f; f = align_up(f + (P.NSEGF > 1 ? BH * P.NSEGF * S * 4 : 0));
+    P.off_fi = f; f = align_up(f + (P.NSEGF > 1 ? BH * P.NSEGF * S * 4 : 0));
+    P.ws_fwd = off > f ? off : f;
+  }
+  off = P.ws_fwd;
   // backward extras: dS per chunk in two layouts, hT, chunk totals of
   // dlog b, rowsum(hT * dhT)
   P.off_st2 = off; off = align_up(off + 2 * BH * P.NC * S * P.esize);
@@ -175,17 +199,33 @@ gla_status gla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k
 
   char* ws = (char*)workspace;
   float* cum = (float*)(ws + p.off_cum);
+  float* sg = (float*)(ws + p.off_sg);
   void* states = ws + p.off_st;
   float* seg_u = (float*)(ws + p.off_seg_u);
   float* seg_in = (float*)(ws + p.off_seg_in);
 
   GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
+  if (p.fused) {
+    // segment entry states from the segments' local states, then one fused
+    // pass per segment that keeps the state on chip
+    float* fu = (float*)(ws + p.off_fu);
+    float* fi = (float*)(ws + p.off_fi);
+    if (p.NSEGF > 1) {
+      Plan ps = p;
+      ps.NSEG = p.NSEGF;
+      ps.seg_chunks = p.segf_chunks;
+      GLA_LAUNCH("chunk_state_local", launch_chunk_state(ps, 0, SEG_LOCAL, 0, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, fu, sg, s));
+      GLA_LAUNCH("segment_scan", launch_segment_scan(ps, 0, sg, h0, fu, fi, hT, s));
+    }
+    GLA_LAUNCH("seg_output", launch_seg_output(p, q, k, v, cum, h0, fi, o, hT, s));
+    return GLA_OK;
+  }
   if (p.NSEG > 1) {
-    GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, 0, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, s));
-    GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, cum, h0, seg_u, seg_in, hT, s));
-    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, 0, k, v, cum, h0, seg_in, states, nullptr, nullptr, nullptr, nullptr, s));
+    GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, 0, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, sg, s));
+    GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, sg, h0, seg_u, seg_in, hT, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, 0, k, v, cum, h0, seg_in, states, nullptr, nullptr, nullptr, nullptr, nullptr, s));
   } else {
-    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, 0, k, v, cum, h0, nullptr, states, nullptr, nullptr, hT, nullptr, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, 0, k, v, cum, h0, nullptr, states, nullptr, nullptr, hT, nullptr, nullptr, s));
   }
   GLA_LAUNCH("chunk_output", launch_chunk_output(p, q, k, v, cum, states, o, s));
   return GLA_OK;
@@ -213,6 +253,7 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
 
   char* ws = (char*)workspace;
   float* cum = (float*)(ws + p.off_cum);
+  float* sg = (float*)(ws + p.off_sg);
   void* st_n = ws + p.off_st;                       // S_{n-1}, [dk][dv]
   void* dst_n = ws + p.off_st2;                     // dS_n, [dk][dv]
   void* dst_t = ws + p.off_st2 + (size_t)p.BH * p.NC * p.dk * p.dv * p.esize;  // dS_n, [dv][dk]
@@ -229,19 +270,19 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
   // recompute the chunk states (not stored by the forward)
   GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
   if (p.NSEG > 1) {
-    GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, p.bf16, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, s));
-    GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, cum, h0, seg_u, seg_in, hT, s));
-    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, seg_in, nullptr, st_n, st_lo, nullptr, nullptr, s));
+    GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, p.bf16, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, sg, s));
+    GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, sg, h0, seg_u, seg_in, hT, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, seg_in, nullptr, st_n, st_lo, nullptr, nullptr, nullptr, s));
   } else {
-    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, nullptr, nullptr, st_n, st_lo, hT, nullptr, s));
+    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, nullptr, nullptr, st_n, st_lo, hT, nullptr, nullptr, s));
   }
   // reverse recurrence of the state gradient
   if (p.NSEG > 1) {
-    GLA_LAUNCH("chunk_state_rev_local", launch_chunk_state(p, 1, SEG_LOCAL, p.bf16, q, dout, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, s));
-    GLA_LAUNCH("segment_scan_rev", launch_segment_scan(p, 1, cum, dhT, seg_u, seg_in, dh0, s));
-    GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, seg_in, dst_t, dst_n, dst_lo, nullptr, nullptr, s));
+    GLA_LAUNCH("chunk_state_rev_local", launch_chunk_state(p, 1, SEG_LOCAL, p.bf16, q, dout, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, sg, s));
+    GLA_LAUNCH("segment_scan_rev", launch_segment_scan(p, 1, sg, dhT, seg_u, seg_in, dh0, s));
+    GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, seg_in, dst_t, dst_n, dst_lo, nullptr, nullptr, nullptr, s));
   } else {
-    GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, nullptr, dst_t, dst_n, dst_lo, dh0, nullptr, s));
+    GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, nullptr, dst_t, dst_n, dst_lo, dh0, nullptr, nullptr, s));
   }
   GLA_LAUNCH("chunk_attn", launch_chunk_attn(p, q, k, v, dout, cum, Aw, dAw, s));
   GLA_LAUNCH("chunk_dqdk", launch_chunk_dqdk(p, q, k, v, dout, cum, st_n, st_lo, dst_n,

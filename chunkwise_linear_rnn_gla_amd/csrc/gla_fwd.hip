@@ -19,26 +19,54 @@ namespace gla {
 // ------------------------------------------------------------------ K1: chunk cumsum
 // Chunk-local inclusive cumsum of log alpha (the App. B listing's "cumsum of
 // log decay within a chunk"; its printed loop indexes a[i] where the
-// chunk-local position is meant).  One thread per (chunk, key channel).
+// chunk-local position is meant).  A thread owns 4 adjacent key channels of
+// 16 consecutive rows (16 independent 16-byte loads in flight); the 16-row
+// group totals are combined through LDS.  Within a row group the sum runs in
+// row order, and group offsets are added in group order.
+constexpr int kCumRows = 16;
+
 __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ a,
                                                      float* __restrict__ cum, int L, int dk,
-                                                     int C, int NC, int cpb) {
-  const int sub = threadIdx.x / dk, col = threadIdx.x % dk;
-  const int n = blockIdx.x * cpb + sub;
-  if (sub >= cpb || n >= NC) return;
-  const size_t base = (size_t)blockIdx.y * L * dk + col;
-  const int r0 = n * C, r1 = min(L, r0 + C);
-  float acc = 0.f;
-  for (int r = r0; r < r1; ++r) {
-    acc += a[base + (size_t)r * dk];
-    cum[base + (size_t)r * dk] = acc;
+                                                     int C, int NC, int BH) {
+  __shared__ f32x4 tot[kThreads];
+  const int quads = dk / 4, groups = C / kCumRows;      // per chunk
+  const int per_chunk = quads * groups;                 // threads per chunk (<= 256)
+  const int cpb = kThreads / per_chunk;                 // chunks per block
+  const int t = threadIdx.x, sub = t / per_chunk, rem = t % per_chunk;
+  const int gq = rem % quads, rg = rem / quads;
+  const long chunk = (long)blockIdx.x * cpb + sub;      // global chunk id over BH * NC
+  const bool active = sub < cpb && chunk < (long)BH * NC;
+  const int bh = active ? (int)(chunk / NC) : 0, n = active ? (int)(chunk % NC) : 0;
+  const int r0 = n * C + rg * kCumRows;
+  const int r1 = active ? min(L, r0 + kCumRows) : r0;
+  const size_t base = (size_t)bh * L * dk + 4 * gq;
+  f32x4 v[kCumRows];
+#pragma unroll
+  for (int i = 0; i < kCumRows; ++i)
+    if (r0 + i < r1) v[i] = *reinterpret_cast<const f32x4*>(a + base + (size_t)(r0 + i) * dk);
+  f32x4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kCumRows; ++i) {
+    if (r0 + i < r1) {
+      run += v[i];
+      v[i] = run;
+    }
   }
+  tot[t] = run;
+  __syncthreads();
+  f32x4 off = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < rg; ++g) off += tot[sub * per_chunk + g * quads + gq];
+#pragma unroll
+  for (int i = 0; i < kCumRows; ++i)
+    if (r0 + i < r1) *reinterpret_cast<f32x4*>(cum + base + (size_t)(r0 + i) * dk) = v[i] + off;
 }
 
 hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t s) {
-  const int cpb = kThreads / p.dk;
-  dim3 grid((p.NC + cpb - 1) / cpb, p.BH);
-  hipLaunchKernelGGL(k_cumsum, grid, dim3(cpb * p.dk), 0, s, a, cum, p.L, p.dk, p.C, p.NC, cpb);
+  const int per_chunk = (p.dk / 4) * (p.C / kCumRows);
+  const int cpb = kThreads / per_chunk;
+  const long chunks = (long)p.BH * p.NC;
+  dim3 grid((unsigned)((chunks + cpb - 1) / cpb));
+  hipLaunchKernelGGL(k_cumsum, grid, dim3(kThreads), 0, s, a, cum, p.L, p.dk, p.C, p.NC, p.BH);
   return hipGetLastError();
 }
 
@@ -47,30 +75,40 @@ hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t 
 // and walks the chunks of one sequence segment in order (reverse order for the
 // backward's dS recurrence).  The tile lives in MFMA accumulators (fp32); each
 // chunk's operands are staged transposed through LDS so that both MFMA
-// operands read contiguous token runs.
+// operands read contiguous token runs.  The next chunk's raw inputs are
+// loaded into registers while the current chunk updates the state.
 //
 // SPLIT (bf16 only): the scaled operand X ⊙ e^{...} is held as a high and a
 // low bf16 part (two MFMAs), and st_n_lo receives the low part of every
 // written state, so that the backward's gradients see ~16-bit operands.
+//
+// Workgroups are numbered so that the tiles of one (batch, head) are
+// consecutive within one XCD (workgroup w runs on XCD w % 8): the tiles that
+// re-read the same k / v / cumsum rows then share an L2.
 template <typename T, int TS, int REV, int SPLIT>
 __global__ __launch_bounds__(kThreads) void k_chunk_state(
     const T* __restrict__ X, const T* __restrict__ Y, const float* __restrict__ cum,
     const float* __restrict__ init, const float* __restrict__ seg_in, T* __restrict__ st_t,
     T* __restrict__ st_n, T* __restrict__ st_n_lo, float* __restrict__ end_out,
-    float* __restrict__ seg_out, int L, int dk, int dv, int C, int NC, int NSEG, int seg_chunks,
-    int mode) {
+    float* __restrict__ seg_out, float* __restrict__ seg_g, int L, int dk, int dv, int C, int NC,
+    int NSEG, int seg_chunks, int mode) {
   using M = Mma<T>;
   constexpr int NT1 = TS / 16, NTT = NT1 * NT1, NW = (NTT + 3) / 4;
-  constexpr int LDC = 64 + 16 / (int)sizeof(T);  // chunk <= 64 tokens, padded rows
-  constexpr int CG = TS / 8;
-  __shared__ __attribute__((aligned(16))) T xs[TS][LDC];
-  __shared__ __attribute__((aligned(16))) T xl[SPLIT ? TS : 1][SPLIT ? LDC : 8];
-  __shared__ __attribute__((aligned(16))) T ys[TS][LDC];
+  constexpr int LDX = TS + gather_pad<T>(TS);    // row-major [token][channel], padded
+  constexpr int CG = TS / 8;                     // 8-channel column groups
+  constexpr int RS = kThreads / CG;              // row stride between a thread's rows
+  constexpr int RPT = (64 + RS - 1) / RS;        // rows per thread (chunk <= 64)
+  __shared__ __attribute__((aligned(16))) T xs[64][LDX];
+  __shared__ __attribute__((aligned(16))) T xl[SPLIT ? 64 : 1][SPLIT ? LDX : 8];
+  __shared__ __attribute__((aligned(16))) T ys[64][LDX];
   __shared__ float gam[TS];
 
-  const int j0 = blockIdx.x * TS, i0 = blockIdx.y * TS;
-  const int bh = blockIdx.z / NSEG, seg = blockIdx.z % NSEG;
-  const int w = wave_id(), l = lane_id();
+  const int ntj = dv / TS, nti = dk / TS;
+  const int lid = xcd_logical(blockIdx.x, gridDim.x);
+  const int j0 = (lid % ntj) * TS, i0 = ((lid / ntj) % nti) * TS;
+  const int z = lid / (ntj * nti), bh = z / NSEG, seg = z % NSEG;
+  const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int cg = tid % CG, rbase = tid / CG, c0 = cg * 8;
   const size_t xo = (size_t)bh * L * dk, yo = (size_t)bh * L * dv;
 
   const float* src = nullptr;
@@ -94,35 +132,64 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
     }
   }
 
-  const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks);
-  for (int step = 0; step < ne - nb; ++step) {
+  const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks), nsteps = max(0, ne - nb);
+  // prefetch registers: this thread's rows of X, Y, cumsum and the chunk total
+  Raw8<T> rx[RPT], ry[RPT];
+  f32x4 rb[RPT][2], rg[2];
+#define GLA_STATE_FETCH(NCH)                                                              \
+  do {                                                                                     \
+    const int fr0 = (NCH) * C, frv = min(C, L - fr0);                                      \
+    const float* glast = cum + xo + (size_t)(fr0 + frv - 1) * dk + i0 + c0;                \
+    rg[0] = *reinterpret_cast<const f32x4*>(glast);                                        \
+    rg[1] = *reinterpret_cast<const f32x4*>(glast + 4);                                    \
+    _Pragma("unroll") for (int u = 0; u < RPT; ++u) {                                      \
+      const int row = rbase + u * RS;                                                      \
+      if (row < frv) {                                                                     \
+        raw_load(rx[u], X + xo + (size_t)(fr0 + row) * dk + i0 + c0);                      \
+        raw_load(ry[u], Y + yo + (size_t)(fr0 + row) * dv + j0 + c0);                      \
+        const float* bp = cum + xo + (size_t)(fr0 + row) * dk + i0 + c0;                   \
+        rb[u][0] = *reinterpret_cast<const f32x4*>(bp);                                    \
+        rb[u][1] = *reinterpret_cast<const f32x4*>(bp + 4);                                \
+      } else {                                                                             \
+        raw_zero(rx[u]);                                                                   \
+        raw_zero(ry[u]);                                                                   \
+        rb[u][0] = rb[u][1] = f32x4{};                                                     \
+      }                                                                                    \
+    }                                                                                      \
+  } while (0)
+  if (nsteps > 0) GLA_STATE_FETCH(REV ? ne - 1 : nb);
+  float gsum[8];  // this segment's total log decay for the thread's 8 channels
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gsum[e] = 0.f;
+
+  for (int step = 0; step < nsteps; ++step) {
     const int n = REV ? (ne - 1 - step) : (nb + step);
-    const int r0 = n * C, rv = min(C, L - r0);
-    const float* glast = cum + xo + (size_t)(r0 + rv - 1) * dk + i0;
-    for (int it = threadIdx.x; it < C * CG; it += kThreads) {
-      const int row = it / CG, c0 = (it % CG) * 8;
-      float xv[8], yv[8];
-      if (row < rv) {
-        float bv[8], gv[8];
-        load8(X + xo + (size_t)(r0 + row) * dk + i0 + c0, xv);
-        load8(Y + yo + (size_t)(r0 + row) * dv + j0 + c0, yv);
-        load8(cum + xo + (size_t)(r0 + row) * dk + i0 + c0, bv);
-        load8(glast + c0, gv);
+    // stage this chunk (registers -> LDS, row-major, X scaled)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] *= gexp<T>(REV ? bv[e] : gv[e] - bv[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = yv[e] = 0.f;
-      }
+    for (int u = 0; u < RPT; ++u) {
+      const int row = rbase + u * RS;
+      if (row >= C) continue;
+      float xv[8], xlo[8], yv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const T hi = from_f32<T>(xv[e]);
-        xs[c0 + e][row] = hi;
-        if constexpr (SPLIT) xl[c0 + e][row] = from_f32<T>(xv[e] - to_f32(hi));
-        ys[c0 + e][row] = from_f32<T>(yv[e]);
+        const float b = rb[u][e >> 2][e & 3], g = rg[e >> 2][e & 3];
+        xv[e] = raw_get(rx[u], e) * gexp<T>(REV ? b : g - b);
+        xlo[e] = xv[e] - to_f32(from_f32<T>(xv[e]));
+        yv[e] = raw_get(ry[u], e);
+      }
+      store8_aligned8(&xs[row][c0], xv);
+      if constexpr (SPLIT) store8_aligned8(&xl[row][c0], xlo);
+      store8_aligned8(&ys[row][c0], yv);
+    }
+    if (rbase == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        gam[c0 + e] = gexp<T>(rg[e >> 2][e & 3]);
+        gsum[e] += rg[e >> 2][e & 3];
       }
     }
-    if (threadIdx.x < TS) gam[threadIdx.x] = gexp<T>(glast[threadIdx.x]);
+    // prefetch the next chunk while this one is consumed
+    if (step + 1 < nsteps) GLA_STATE_FETCH(REV ? n - 1 : n + 1);
     __syncthreads();
 
     // The state entering this chunk's update: S_{n-1} (forward) or dS_n (reverse).
@@ -154,11 +221,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[t][r] *= gam[ti * 16 + (l >> 4) * 4 + r];
       for (int kk = 0; kk < C; kk += M::K) {
-        auto a = load_frag<T>(&xs[ti * 16 + (l & 15)][kk + (l >> 4) * M::KPL]);
-        auto b = load_frag<T>(&ys[tj * 16 + (l & 15)][kk + (l >> 4) * M::KPL]);
+        const int kr = kk + (l >> 4) * M::KPL;
+        auto a = gather_frag<T>(&xs[kr][ti * 16 + (l & 15)], LDX);
+        auto b = gather_frag<T>(&ys[kr][tj * 16 + (l & 15)], LDX);
         acc[t] = M::run(a, b, acc[t]);
         if constexpr (SPLIT) {
-          auto al = load_frag<T>(&xl[ti * 16 + (l & 15)][kk + (l >> 4) * M::KPL]);
+          auto al = gather_frag<T>(&xl[kr][ti * 16 + (l & 15)], LDX);
           acc[t] = M::run(al, b, acc[t]);
         }
       }
@@ -166,6 +234,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
     __syncthreads();
   }
 
+  if (mode == SEG_LOCAL && seg_g && j0 == 0 && rbase == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) seg_g[((size_t)bh * NSEG + seg) * dk + i0 + c0 + e] = gsum[e];
+  }
   float* dst = nullptr;
   if (mode == SEG_LOCAL) dst = seg_out + ((size_t)bh * NSEG + seg) * dk * dv;
   else if (NSEG == 1 && end_out) dst = end_out + (size_t)bh * dk * dv;
@@ -185,15 +257,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
   }
 }
 
+#undef GLA_STATE_FETCH
+
 template <typename T, int TS, int REV, int SPLIT>
 static hipError_t launch_cs(const Plan& p, int mode, const void* X, const void* Y,
                             const float* cum, const float* init, const float* seg_in,
                             void* st_t, void* st_n, void* st_n_lo, float* end_out,
-                            float* seg_out, hipStream_t s) {
-  dim3 grid(p.dv / TS, p.dk / TS, p.BH * p.NSEG);
+                            float* seg_out, float* seg_g, hipStream_t s) {
+  dim3 grid((p.dv / TS) * (p.dk / TS) * p.BH * p.NSEG);
   hipLaunchKernelGGL((k_chunk_state<T, TS, REV, SPLIT>), grid, dim3(kThreads), 0, s,
                      (const T*)X, (const T*)Y, cum, init, seg_in, (T*)st_t, (T*)st_n,
-                     (T*)st_n_lo, end_out, seg_out, p.L, p.dk, p.dv, p.C, p.NC, p.NSEG,
+                     (T*)st_n_lo, end_out, seg_out, seg_g, p.L, p.dk, p.dv, p.C, p.NC, p.NSEG,
                      p.seg_chunks, mode);
   return hipGetLastError();
 }
@@ -202,63 +276,81 @@ template <typename T, int REV, int SPLIT>
 static hipError_t launch_cs_ts(const Plan& p, int mode, const void* X, const void* Y,
                                const float* cum, const float* init, const float* seg_in,
                                void* st_t, void* st_n, void* st_n_lo, float* end_out,
-                               float* seg_out, hipStream_t s) {
+                               float* seg_out, float* seg_g, hipStream_t s) {
   switch (p.TS) {
-    case 64: return launch_cs<T, 64, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
-    case 32: return launch_cs<T, 32, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
-    default: return launch_cs<T, 16, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
+    case 64: return launch_cs<T, 64, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
+    case 32: return launch_cs<T, 32, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
+    default: return launch_cs<T, 16, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
   }
 }
 
 hipError_t launch_chunk_state(const Plan& p, int rev, int mode, int split, const void* X,
                               const void* Y, const float* cum, const float* init,
                               const float* seg_in, void* st_t, void* st_n, void* st_n_lo,
-                              float* end_out, float* seg_out, hipStream_t s) {
+                              float* end_out, float* seg_out, float* seg_g, hipStream_t s) {
   if (p.bf16) {
     if (split)
-      return rev ? launch_cs_ts<bf16, 1, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s)
-                 : launch_cs_ts<bf16, 0, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, s);
-    return rev ? launch_cs_ts<bf16, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s)
-               : launch_cs_ts<bf16, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s);
+      return rev ? launch_cs_ts<bf16, 1, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s)
+                 : launch_cs_ts<bf16, 0, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
+    return rev ? launch_cs_ts<bf16, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s)
+               : launch_cs_ts<bf16, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s);
   }
-  return rev ? launch_cs_ts<float, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s)
-             : launch_cs_ts<float, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, s);
+  return rev ? launch_cs_ts<float, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s)
+             : launch_cs_ts<float, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s);
 }
 
 // ------------------------------------------------------------------ segment scan
 // Sequence-level parallelism for long sequences: each segment's local state
 // (zero start) is combined with the state entering it,
-//   S_in(s+1) = e^{G_s} ⊙ S_in(s) + U_s,  G_s = sum of the segment's chunk totals,
+//   S_in(s+1) = e^{G_s} ⊙ S_in(s) + U_s,  G_s = the segment's total log decay,
 // the associative step of the chunk recurrence (papercache.org notes §2.2,
-// chunk-level recurrence, applied to groups of chunks).
+// chunk-level recurrence, applied to groups of chunks).  A thread owns 4
+// adjacent state entries of one row; the U loads of 8 segments are issued
+// before they are combined.
 __global__ __launch_bounds__(kThreads) void k_segment_scan(
-    const float* __restrict__ cum, const float* __restrict__ init, const float* __restrict__ seg_u,
-    float* __restrict__ seg_in, float* __restrict__ end_out, int L, int dk, int dv, int C, int NC,
-    int NSEG, int seg_chunks, int rev) {
-  const int i = blockIdx.x, bh = blockIdx.y;
-  const float* crow = cum + (size_t)bh * L * dk + i;
-  for (int j = threadIdx.x; j < dv; j += blockDim.x) {
-    float S = init ? init[((size_t)bh * dk + i) * dv + j] : 0.f;
-    for (int t = 0; t < NSEG; ++t) {
-      const int seg = rev ? NSEG - 1 - t : t;
-      const size_t so = (((size_t)bh * NSEG + seg) * dk + i) * dv + j;
-      seg_in[so] = S;
-      float G = 0.f;
-      const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks);
-      for (int n = nb; n < ne; ++n) G += crow[(size_t)(min(L, (n + 1) * C) - 1) * dk];
-      S = expf(G) * S + seg_u[so];
+    const float* __restrict__ seg_g, const float* __restrict__ init,
+    const float* __restrict__ seg_u, float* __restrict__ seg_in, float* __restrict__ end_out,
+    int dk, int dv, int NSEG, int rev, long total4) {
+  const long t = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= total4) return;
+  const int dv4 = dv / 4, j = (int)(t % dv4) * 4;
+  const long r = t / dv4;
+  const int i = (int)(r % dk), bh = (int)(r / dk);
+  const size_t off = ((size_t)bh * dk + i) * dv + j;
+  f32x4 S = init ? *reinterpret_cast<const f32x4*>(init + off) : f32x4{};
+  for (int t0 = 0; t0 < NSEG; t0 += 8) {
+    f32x4 U[8];
+    float G[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tt = t0 + u;
+      if (tt < NSEG) {
+        const int seg = rev ? NSEG - 1 - tt : tt;
+        U[u] = *reinterpret_cast<const f32x4*>(seg_u + (((size_t)bh * NSEG + seg) * dk + i) * dv + j);
+        G[u] = seg_g[((size_t)bh * NSEG + seg) * dk + i];
+      }
     }
-    if (end_out) end_out[((size_t)bh * dk + i) * dv + j] = S;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tt = t0 + u;
+      if (tt < NSEG) {
+        const int seg = rev ? NSEG - 1 - tt : tt;
+        *reinterpret_cast<f32x4*>(seg_in + (((size_t)bh * NSEG + seg) * dk + i) * dv + j) = S;
+        S = expf(G[u]) * S + U[u];
+      }
+    }
   }
+  if (end_out) *reinterpret_cast<f32x4*>(end_out + off) = S;
 }
 
-hipError_t launch_segment_scan(const Plan& p, int rev, const float* cum, const float* init,
+hipError_t launch_segment_scan(const Plan& p, int rev, const float* seg_g, const float* init,
                                const float* seg_u, float* seg_in, float* end_out,
                                hipStream_t s) {
-  dim3 grid(p.dk, p.BH);
-  const int threads = p.dv < kThreads ? p.dv : kThreads;
-  hipLaunchKernelGGL(k_segment_scan, grid, dim3(threads), 0, s, cum, init, seg_u, seg_in,
-                     end_out, p.L, p.dk, p.dv, p.C, p.NC, p.NSEG, p.seg_chunks, rev);
+  const long total4 = (long)p.BH * p.dk * (p.dv / 4);
+  if (total4 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_segment_scan, dim3((unsigned)((total4 + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, seg_g, init, seg_u, seg_in, end_out, p.dk, p.dv,
+                     p.NSEG, rev, total4);
   return hipGetLastError();
 }
 
@@ -335,31 +427,85 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
 
   const T* stp = st_t + ((size_t)bh * NC + n) * dv * dk;
 
+  // Slice s of (q, k, cumsum) and the state fragments are fetched into
+  // registers one slice ahead of their use.
+  constexpr int SITEMS = C * (KS / 8);  // 8-element items per slice
+  constexpr int KSTEPS = KS / M::K;
+  const int srow = tid / (KS / 8), sc8 = (tid % (KS / 8)) * 8;
+  const bool sact = tid < SITEMS;
+  const bool svalid = sact && srow < rv;
+  const int scrow = r0 + (srow < rv ? srow : rv - 1);
+  Raw8<T> pq, pk;
+  f32x4 pb2[2];
+  typename M::frag fnext[KSTEPS][NCW];
+#define GLA_SLICE_FETCH(S0)                                                               \
+  do {                                                                                     \
+    if (sact) {                                                                            \
+      const float* bp = cum + qo + (size_t)scrow * dk + (S0) + sc8;                        \
+      pb2[0] = *reinterpret_cast<const f32x4*>(bp);                                        \
+      pb2[1] = *reinterpret_cast<const f32x4*>(bp + 4);                                    \
+      if (svalid) {                                                                        \
+        raw_load(pq, q + qo + (size_t)scrow * dk + (S0) + sc8);                            \
+        raw_load(pk, k + qo + (size_t)scrow * dk + (S0) + sc8);                            \
+      } else {                                                                             \
+        raw_zero(pq);                                                                      \
+        raw_zero(pk);                                                                      \
+      }                                                                                    \
+    }                                                                                      \
+    _Pragma("unroll") for (int ks = 0; ks < KSTEPS; ++ks)                                  \
+    _Pragma("unroll") for (int ct = 0; ct < NCW; ++ct) {                                   \
+      const int col = j0 + (wc + WC * ct) * 16 + (l & 15);                                \
+      fnext[ks][ct] =                                                                      \
+          load_frag<T>(stp + (size_t)col * dk + (S0) + ks * M::K + (l >> 4) * M::KPL);     \
+    }                                                                                      \
+  } while (0)
+  GLA_SLICE_FETCH(0);
+
   for (int s0 = 0; s0 < dk; s0 += KS) {
     __syncthreads();
-    PB::stage(q, k, cum, qo, r0, rv, dk, s0, qs, ks, bs, qts);
+    if (sact) {
+      float qv[8], kv[8], bv[8], qt[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[e] = raw_get(pq, e);
+        kv[e] = raw_get(pk, e);
+        bv[e] = pb2[e >> 2][e & 3];
+        qt[e] = qv[e] * gexp<T>(bv[e]);
+      }
+      store8(qs + srow * LDT + sc8, qv);
+      store8(ks + srow * LDT + sc8, kv);
+      store8(bs + srow * LDF + sc8, bv);
+      store8(qts + srow * LDT + sc8, qt);
+    }
     __syncthreads();
     PB::gates(bs, als);
     // inter-chunk term
-    for (int kk = 0; kk < KS; kk += M::K) {
-      typename M::frag bf[NCW];
 #pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) {
-        const int col = j0 + (wc + WC * ct) * 16 + (l & 15);
-        bf[ct] = load_frag<T>(stp + (size_t)col * dk + s0 + kk + (l >> 4) * M::KPL);
-      }
+    for (int ks2 = 0; ks2 < KSTEPS; ++ks2) {
 #pragma unroll
       for (int rt = 0; rt < NRW; ++rt) {
         const int rti = wr + WR * rt;
         if (rti >= NRT) continue;
-        auto a = load_frag<T>(qts + (rti * 16 + (l & 15)) * LDT + kk + (l >> 4) * M::KPL);
+        auto a = load_frag<T>(qts + (rti * 16 + (l & 15)) * LDT + ks2 * M::K + (l >> 4) * M::KPL);
 #pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) acc[rt][ct] = M::run(a, bf[ct], acc[rt][ct]);
+        for (int ct = 0; ct < NCW; ++ct) acc[rt][ct] = M::run(a, fnext[ks2][ct], acc[rt][ct]);
       }
     }
+    // next slice's loads overlap the score-matrix work below
+    if (s0 + KS < dk) GLA_SLICE_FETCH(s0 + KS);
     pb.offdiag(qs, ks, bs);
     __syncthreads();
     pb.diag(qs, ks, als);
+  }
+  // V tile loads in flight while the score matrix is reduced
+  constexpr int VITEMS = (C * (TVO / 8) + kThreads - 1) / kThreads;
+  Raw8<T> pv[VITEMS];
+#pragma unroll
+  for (int u = 0; u < VITEMS; ++u) {
+    const int it = tid + u * kThreads;
+    const int row = it / (TVO / 8), c8 = (it % (TVO / 8)) * 8;
+    if (it < C * (TVO / 8) && row < rv) raw_load(pv[u], v + vo + (size_t)(r0 + row) * dv + j0 + c8);
+    else raw_zero(pv[u]);
   }
   __syncthreads();
   pb.finish(pd, [&](int m, int r, float val) {
@@ -370,17 +516,13 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
     }
   });
   // V tile, transposed: vt[col][token]
-  for (int it = tid; it < C * (TVO / 8); it += kThreads) {
+#pragma unroll
+  for (int u = 0; u < VITEMS; ++u) {
+    const int it = tid + u * kThreads;
+    if (it >= C * (TVO / 8)) continue;
     const int row = it / (TVO / 8), c8 = (it % (TVO / 8)) * 8;
-    float vv[8];
-    if (row < rv) {
-      load8(v + vo + (size_t)(r0 + row) * dv + j0 + c8, vv);
-    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vv[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(c8 + e) * LDV + row] = from_f32<T>(vv[e]);
+    for (int e = 0; e < 8; ++e) vt[(c8 + e) * LDV + row] = from_f32<T>(raw_get(pv[u], e));
   }
   __syncthreads();
 
@@ -424,6 +566,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_output(
     }
   }
 }
+
+#undef GLA_SLICE_FETCH
 
 template <typename T, int C, int TVO>
 static hipError_t launch_co(const Plan& p, const void* q, const void* k, const void* v,

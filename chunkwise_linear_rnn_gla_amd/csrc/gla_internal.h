@@ -18,10 +18,16 @@ struct Plan {
   int NSEG;          // sequence segments for the chunk-state recurrence
   int seg_chunks;    // chunks per segment
   int TVO;           // output column tile of the output kernels
+  int fused;         // forward runs the fused segment kernel (else materialised states)
+  int NSEGF;         // sequence segments of the fused forward
+  int segf_chunks;   // chunks per fused segment
+  int DVTF;          // d_v tile of the fused segment kernel
   size_t esize;      // bytes per I/O element
   // workspace layout (byte offsets); 0-sized regions have offset 0
   size_t off_cum, off_st, off_st2, off_seg_u, off_seg_in, off_end, off_dlt, off_rs;
   size_t off_A, off_dA, off_stlo, off_dstlo;
+  size_t off_fu, off_fi;   // fused forward: segment local states, segment entry states
+  size_t off_sg;           // segment total log decays [BH][max(NSEG, NSEGF)][dk]
   size_t ws_fwd, ws_bwd;
 };
 
@@ -42,18 +48,30 @@ hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t 
 enum StateMode { SEG_LOCAL = 0, SEG_FILL = 1 };
 // split (bf16 only): hi/lo operand split, and st_n_lo receives the low part of
 // the states written to st_n.
+// In SEG_LOCAL mode seg_g (if not null) receives each segment's total log decay
+// per key channel, [BH][NSEG][dk].
 hipError_t launch_chunk_state(const Plan& p, int rev, int mode, int split, const void* X,
                               const void* Y, const float* cum, const float* init,
                               const float* seg_u_in, void* st_t, void* st_n, void* st_n_lo,
-                              float* end_out, float* seg_u_out, hipStream_t s);
+                              float* end_out, float* seg_u_out, float* seg_g, hipStream_t s);
 // Combine per-segment local states: seg_in[seg] = state entering segment seg
 // (forward order, or reverse order when rev), end_out = final state.
-hipError_t launch_segment_scan(const Plan& p, int rev, const float* cum, const float* init,
+hipError_t launch_segment_scan(const Plan& p, int rev, const float* seg_g, const float* init,
                                const float* seg_u, float* seg_in, float* end_out,
                                hipStream_t s);
 hipError_t launch_chunk_output(const Plan& p, const void* q, const void* k, const void* v,
                                const float* cum, const void* st_t, void* o, hipStream_t s);
 hipError_t launch_copy_state(const Plan& p, const float* src, float* dst, hipStream_t s);
+
+// ---- fused segment forward (gla_fused.hip) ----
+bool fused_supported(int bf16, int C, int dk, int dv);
+int fused_dv_tile(int bf16, int dk, int dv);
+// Per (batch-head, segment p.NSEGF, d_v tile p.DVTF): o for the segment's
+// chunks from the segment entry state (seg_in, or h0 when NSEGF == 1, when
+// hT also receives the final state).
+hipError_t launch_seg_output(const Plan& p, const void* q, const void* k, const void* v,
+                             const float* cum, const float* h0, const float* seg_in, void* o,
+                             float* hT, hipStream_t s);
 
 // ---- backward kernels (gla_bwd.hip) ----
 // A (chunk score matrix) and dA = (dO V^T) ⊙ M per chunk, fp32 C x C blocks.

@@ -51,6 +51,23 @@ __device__ inline void store8(bf16* p, const float* x) {
   for (int e = 0; e < 8; ++e) a[e] = static_cast<bf16>(x[e]);
   *reinterpret_cast<bf16x8*>(p) = a;
 }
+// Store 8 consecutive elements to a destination that is only 8-byte aligned.
+__device__ inline void store8_aligned8(float* p, const float* x) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    float2 v2 = {x[e], x[e + 1]};
+    *reinterpret_cast<float2*>(p + e) = v2;
+  }
+}
+__device__ inline void store8_aligned8(bf16* p, const float* x) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 4) {
+    bf16x4 a;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) a[f] = static_cast<bf16>(x[e + f]);
+    *reinterpret_cast<bf16x4*>(p + e) = a;
+  }
+}
 __device__ inline void store4(float* p, floatx4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ inline void store4(bf16* p, floatx4 x) {
   bf16x4 a;
@@ -59,8 +76,60 @@ __device__ inline void store4(bf16* p, floatx4 x) {
   *reinterpret_cast<bf16x4*>(p) = a;
 }
 
-template <typename T, int C>
+// Register staging of 8 consecutive elements of T (one 16- or 32-byte load).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> { bf16x8 v; };
+template <> struct Raw8<float> { f32x4 v[2]; };
+__device__ inline void raw_load(Raw8<bf16>& r, const bf16* p) { r.v = *reinterpret_cast<const bf16x8*>(p); }
+__device__ inline void raw_load(Raw8<float>& r, const float* p) {
+  r.v[0] = *reinterpret_cast<const f32x4*>(p);
+  r.v[1] = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ inline float raw_get(const Raw8<bf16>& r, int e) { return static_cast<float>(r.v[e]); }
+__device__ inline float raw_get(const Raw8<float>& r, int e) { return r.v[e >> 2][e & 3]; }
+__device__ inline void raw_zero(Raw8<bf16>& r) { r.v = bf16x8{}; }
+__device__ inline void raw_zero(Raw8<float>& r) { r.v[0] = f32x4{}; r.v[1] = f32x4{}; }
+
+// XCD-aware renumbering of a 1-D grid of n workgroups: consecutive logical
+// ids land on the same XCD.
+__device__ inline int xcd_logical(int w, int n) {
+  const int per = n / 8, rem = n % 8, x = w % 8, i = w / 8;
+  // XCDs 0..rem-1 own per+1 logical ids, the others per
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
+}
+
+// Gather a fragment of KPL elements spaced `stride` apart (a column read of a
+// row-major LDS array: the MFMA operand wants consecutive K per lane, and K
+// runs down the rows).
+template <typename T>
+__device__ inline typename Mma<T>::frag gather_frag(const T* p, int stride);
+template <> __device__ inline bf16x8 gather_frag<bf16>(const bf16* p, int stride) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = p[e * stride];
+  return r;
+}
+template <> __device__ inline float gather_frag<float>(const float* p, int stride) { return p[0]; }
+
+// Row padding (elements) of a row-major LDS array of width W read by
+// gather_frag: the four 16-lane groups of a wave read rows KPL apart, and the
+// padding puts their 64-byte (fp32) / 32-byte (bf16) column windows in
+// disjoint LDS banks.
+template <typename T> constexpr int gather_pad(int W) {
+  if (sizeof(T) == 2) {
+    // stride s dwords with 8 s = 16 (mod 64)
+    for (int p = 0; p < 64; p += 2)
+      if ((((W + p) / 2) * 8) % 64 == 16) return p;
+    return 0;
+  }
+  for (int p = 0; p < 64; p += 4)
+    if ((W + p) % 64 == 16 || (W + p) % 64 == 48) return p;
+  return 0;
+}
+
+template <typename T, int C, int NWV = 4>
 struct PBuilder {
+  static constexpr int NTH = NWV * kWave;          // threads of the workgroup
   using M = Mma<T>;
   static constexpr bool BF = sizeof(T) == 2;
   static constexpr int KS = BF ? 32 : 16;          // d_k slice
@@ -69,9 +138,9 @@ struct PBuilder {
   static constexpr int LDF = KS + 4;               // row length of fp32 slice arrays
   static constexpr int NRT = C / 16;               // sub-chunks per chunk
   static constexpr int NP = NRT * (NRT - 1) / 2;   // off-diagonal pairs
-  static constexpr int NPW = (NP + 3) / 4;
+  static constexpr int NPW = (NP + NWV - 1) / NWV;
   static constexpr int NPA = NPW > 0 ? NPW : 1;
-  static constexpr int WPB = 4 / NRT;              // waves per diagonal block
+  static constexpr int WPB = NWV / NRT;            // waves per diagonal block
   static constexpr int NG = 8 * WPB;               // channel groups per block
   static constexpr int CPL = KS / NG > 0 ? KS / NG : 1;
   // LDS: q, k (T), cumsum and gates (fp32), one slice
@@ -100,7 +169,7 @@ struct PBuilder {
   // qt = T(q ⊙ e^B) (row-major, LDT) for the inter-chunk MFMA.
   __device__ static void stage(const T* q, const T* k, const float* cum, size_t qo, int r0,
                                int rv, int dk, int s0, T* qs, T* ks, float* bs, T* qt) {
-    for (int it = threadIdx.x; it < C * (KS / 8); it += kThreads) {
+    for (int it = threadIdx.x; it < C * (KS / 8); it += NTH) {
       const int row = it / (KS / 8), c8 = (it % (KS / 8)) * 8;
       const bool valid = row < rv;
       const int crow = valid ? r0 + row : r0 + rv - 1;
@@ -128,7 +197,7 @@ struct PBuilder {
   // Per-row gates within each sub-chunk: als[row] = e^{B_row - B_{row-1}}
   // (1 at a sub-chunk's first row, where it is never used).
   __device__ static void gates(const float* bs, float* als) {
-    for (int it = threadIdx.x; it < C * KS; it += kThreads) {
+    for (int it = threadIdx.x; it < C * KS; it += NTH) {
       const int row = it / KS, c = it % KS;
       als[row * LDF + c] =
           (row & 15) ? gexp<T>(bs[row * LDF + c] - bs[(row - 1) * LDF + c]) : 1.f;
@@ -139,7 +208,7 @@ struct PBuilder {
   __device__ void offdiag(const T* qs, const T* ks, const float* bs) {
 #pragma unroll
     for (int t = 0; t < NPW; ++t) {
-      const int pi = w + 4 * t;
+      const int pi = w + NWV * t;
       if (pi >= NP) continue;
       int jq, ju;
       pair_of(pi, jq, ju);
@@ -160,27 +229,57 @@ struct PBuilder {
     }
   }
 
+  // CPL consecutive channels as fp32 (vector LDS loads).
+  __device__ static inline void ldc(const float* p, float* o) {
+    if constexpr (CPL == 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = v[c];
+    } else if constexpr (CPL == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      o[0] = v.x;
+      o[1] = v.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[c] = p[c];
+    }
+  }
+  __device__ static inline void ldc(const bf16* p, float* o) {
+    if constexpr (CPL == 4) {
+      const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = static_cast<float>(v[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[c] = static_cast<float>(p[c]);
+    }
+  }
+
   // Diagonal blocks, fp32 VALU, accumulated over slices.  Needs qs, ks, als.
+  // The lane's two query rows are loaded once; each step then reads one key
+  // row and one gate row (vector loads) and extends the running gate product.
   __device__ void diag(const T* qs, const T* ks, const float* als) {
     if (dg * CPL >= KS) return;
     const int cb = dg * CPL;
-    const int m1 = dp, m2 = 15 - dp;
-    float wv[CPL];
+    const int m2 = 15 - dp;
+    float q1[CPL], q2[CPL], wv[CPL];
+    ldc(qs + (db * 16 + dp) * LDT + cb, q1);
+    ldc(qs + (db * 16 + m2) * LDT + cb, q2);
 #pragma unroll
     for (int i = 0; i < 17; ++i) {
       const bool first = i <= dp;
-      const int m = first ? m1 : m2;
       const int r = first ? (dp - i) : (m2 - (i - dp - 1));
-      const bool reset = (i == 0) || (i == dp + 1);
-      const int R = db * 16 + m, Rk = db * 16 + r;
+      const int Rk = db * 16 + r;
       const int Ra = (Rk + 1 < C) ? Rk + 1 : Rk;
+      float kv[CPL], av[CPL];
+      ldc(ks + Rk * LDT + cb, kv);
+      ldc(als + Ra * LDF + cb, av);
       float part = 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        const float qv = to_f32(qs[R * LDT + cb + c]);
-        const float al = als[Ra * LDF + cb + c];
-        wv[c] = reset ? qv : wv[c] * al;
-        part += wv[c] * to_f32(ks[Rk * LDT + cb + c]);
+        if (i == 0) wv[c] = q1[c];
+        else wv[c] = (i == dp + 1) ? q2[c] : wv[c] * av[c];
+        part += wv[c] * kv[c];
       }
       dsum[i] += part;
     }
@@ -189,7 +288,7 @@ struct PBuilder {
   // After the last slice (and a barrier): reduce the diagonal partials and
   // hand every entry of P to emit(m, r, value), r <= m.  Off-diagonal entries
   // are emitted by the wave that owns the block, diagonal ones after a
-  // cross-wave sum through pd (4 x 16 x 17 floats of LDS).
+  // cross-wave sum through pd (NWV x 16 x 17 floats of LDS).
   template <typename Emit>
   __device__ void finish(float (*pd)[16][17], Emit emit) {
 #pragma unroll
@@ -209,7 +308,7 @@ struct PBuilder {
     }
 #pragma unroll
     for (int t = 0; t < NPW; ++t) {
-      const int pi = w + 4 * t;
+      const int pi = w + NWV * t;
       if (pi >= NP) continue;
       int jq, ju;
       pair_of(pi, jq, ju);
@@ -217,7 +316,7 @@ struct PBuilder {
       for (int r = 0; r < 4; ++r) emit(jq * 16 + (l >> 4) * 4 + r, ju * 16 + (l & 15), pacc[t][r]);
     }
     __syncthreads();
-    for (int it = threadIdx.x; it < NRT * 256; it += kThreads) {
+    for (int it = threadIdx.x; it < NRT * 256; it += NTH) {
       const int b = it >> 8, m = (it >> 4) & 15, r = it & 15;
       if (r > m) continue;
       float val = 0.f;

@@ -1,6 +1,8 @@
 """GPU parity of the forward: the HIP path (through the C ABI) against the fp64
 oracle on the same seeded inputs, element by element (relative L2 per output
 tensor: <= 1e-5 for fp32 I/O, <= 5e-3 for bf16 I/O)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -9,6 +11,18 @@ from chunkwise_linear_rnn_gla_amd.inputs import WORKLOADS, make_inputs, workload
 from gpu_util import TOL, dtype_name, oracle_fwd, rel_l2, run_fwd, say
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["auto", "materialized"], autouse=True)
+def forward_path(request, monkeypatch):
+    """Run every forward case through both forward paths: the default (the
+    fused segment kernel wherever it applies) and the materialised-state
+    kernels (GLA_FORWARD=materialized)."""
+    if request.param == "materialized":
+        monkeypatch.setenv("GLA_FORWARD", "materialized")
+    else:
+        monkeypatch.delenv("GLA_FORWARD", raising=False)
+    return request.param
 
 
 def check_fwd(x, chunk, tag=""):
@@ -57,10 +71,21 @@ def test_segmented_state_recurrence(dt):
 
 
 @pytest.mark.parametrize("gate", ["zero", "extreme", "const", "channel_const"])
-def test_gate_edge_cases(gate):
-    x = make_inputs(2, 2, 192, 32, 32, "fp32", seed=303, gate=gate, h0_std=0.2,
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128)])
+def test_gate_edge_cases(gate, dk, dv):
+    x = make_inputs(2, 2, 192, dk, dv, "fp32", seed=303, gate=gate, h0_std=0.2,
                     gate_value=-0.3)
     check_fwd(x, 64, f"gate-{gate}")
+
+
+@pytest.mark.parametrize("dt,dk,dv,L", [("fp32", 64, 128, 1000), ("fp32", 128, 128, 333),
+                                        ("bf16", 128, 256, 700), ("bf16", 64, 256, 1100),
+                                        ("bf16", 256, 512, 450)])
+def test_fused_segments(dt, dk, dv, L):
+    # few heads, many chunks: the fused forward splits the sequence into
+    # segments whose entry states come from the local-state pass and scan
+    x = make_inputs(1, 2, L, dk, dv, dt, seed=311 + dk + L, h0_std=0.3)
+    check_fwd(x, 64, "fused-segments")
 
 
 def test_single_chunk_and_single_token():
