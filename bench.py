@@ -46,31 +46,66 @@ def fused_segments(w, nc):
     """Segments of the fused forward, as the library plans them: enough
     (batch-head, segment, d_v tile) workgroups to give each compute unit one."""
     dvt = 256 if (w.dtype == "bf16" and w.dk <= 128 and w.dv % 256 == 0) else 128
-    units = w.B * w.H * (w.dv // dvt)
+    units = max(1, w.B * w.H * (w.dv // dvt))
     want = 1 if units >= 256 else -(-256 // units)
     want = min(want, nc)
     seg_chunks = -(-nc // max(want, 1))
     return -(-nc // seg_chunks)
 
 
+def recur_plan(w, nc):
+    """(waves per workgroup, sequence segments) of the two-pass forward's
+    recurrence, as the library plans them: 16 state columns per wave, the
+    largest workgroup that still gives 256 workgroups, segments only when
+    fewer than 128 workgroups remain."""
+    bf16 = w.dtype == "bf16"
+    wmin = 2 if (w.dk >= 256 if bf16 else w.dk >= 128) else 1
+    bh = w.B * w.H
+    nwv = wmin
+    for cand in (4, 2, 1):
+        if cand < wmin or w.dv % (16 * cand):
+            continue
+        nwv = cand
+        if bh * (w.dv // (16 * cand)) >= 256:
+            break
+    units = bh * (w.dv // (16 * nwv))
+    nseg = 1
+    if nc > 1 and units < 128:
+        want = min(-(-256 // units), nc)
+        seg_chunks = -(-nc // want)
+        nseg = -(-nc // seg_chunks)
+    return nwv, nseg
+
+
 def kernel_bytes(name, w, esize, nc):
     """Algorithmic bytes of one launch of a forward kernel: each input byte read
     once and each output byte written once (re-reads are not counted)."""
-    BH, L, dk, dv = w.B * w.H, w.L, w.dk, w.dv
+    BH, L, dk, dv, C = w.B * w.H, w.L, w.dk, w.dv, w.chunk
     q = k = BH * L * dk * esize
     v = o = BH * L * dv * esize
     a = cum = BH * L * dk * 4
     states = BH * nc * dk * dv * esize
     hT = BH * dk * dv * 4
+    h0 = hT if w.h0_std else 0
     nseg = fused_segments(w, nc)
     seg = BH * nseg * dk * dv * 4 if nseg > 1 else 0
+    # two-pass forward: Q~, K~ (rows padded to whole chunks), P (+ the low part
+    # of its diagonal blocks for bf16), chunk log decays
+    qg = kg = BH * nc * C * dk * esize
+    pm = BH * nc * C * C * esize + (BH * nc * C * 16 * esize if esize == 2 else 0)
+    gl = BH * nc * dk * 4
+    _, nsegr = recur_plan(w, nc)
+    segr = BH * nsegr * dk * dv * 4 if nsegr > 1 else 0
     return {
         "chunk_cumsum": a + cum,
         "chunk_state": k + v + cum + states + hT,
         "chunk_output": q + k + v + cum + states + o,
         "chunk_state_local": k + v + cum + seg,
-        "segment_scan": 2 * seg + hT,
+        "segment_scan": 2 * (segr or seg) + hT,
         "seg_output": q + k + v + cum + seg + o,
+        "chunk_prep": q + k + a + qg + kg + pm + gl,
+        "recur_local": kg + gl + v + segr,
+        "chunk_recur": qg + kg + pm + gl + v + (segr or h0) + o + (0 if segr else hT),
     }.get(name)
 
 

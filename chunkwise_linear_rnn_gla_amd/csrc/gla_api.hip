@@ -46,9 +46,14 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   }
   // Fused forward: one workgroup per (batch-head, segment, d_v tile); enough
   // segments to give every compute unit a workgroup.
-  P.fused = fused_supported(bf16, C, dk, dv);
+  // Forward path: the two-pass forward (chunk prep + recurrence) wherever its
+  // kernels are instantiated; GLA_FORWARD=fused | materialized selects the
+  // single-pass fused segment kernel or the materialised-state kernels.
   const char* env = getenv("GLA_FORWARD");
-  if (env && strcmp(env, "materialized") == 0) P.fused = 0;
+  const bool want_fused = env && strcmp(env, "fused") == 0;
+  const bool want_mat = env && strcmp(env, "materialized") == 0;
+  P.recur = !want_fused && !want_mat && recur_supported(bf16, C, dk, dv);
+  P.fused = !P.recur && !want_mat && fused_supported(bf16, C, dk, dv);
   P.DVTF = fused_dv_tile(bf16, dk, dv);
   P.NSEGF = 1;
   P.segf_chunks = P.NC > 0 ? P.NC : 1;
@@ -58,6 +63,31 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     if (want > P.NC) want = P.NC;
     P.segf_chunks = (int)((P.NC + want - 1) / want);
     P.NSEGF = (P.NC + P.segf_chunks - 1) / P.segf_chunks;
+  }
+  // Recurrence: 16 state columns per wave; the largest workgroup that still
+  // gives 256 workgroups, and sequence segments when even one wave per
+  // workgroup leaves the chip mostly idle.
+  const int wmin = recur_min_waves(bf16, dk);
+  P.NWVR = wmin;
+  for (int w = 4; w >= wmin; w /= 2) {
+    if (dv % (16 * w)) continue;
+    P.NWVR = w;
+    if ((int64_t)P.BH * (dv / (16 * w)) >= 256) break;
+  }
+  if (const char* e = getenv("GLA_RECUR_WAVES")) {
+    const int w = atoi(e);
+    if ((w == 1 || w == 2 || w == 4) && w >= wmin && dv % (16 * w) == 0) P.NWVR = w;
+  }
+  P.NSEGR = 1;
+  P.segr_chunks = P.NC > 0 ? P.NC : 1;
+  if (P.recur && P.NC > 1 && P.BH > 0) {
+    const int64_t units = (int64_t)P.BH * (dv / (16 * P.NWVR));
+    if (units < 128) {
+      int64_t want = (256 + units - 1) / units;
+      if (want > P.NC) want = P.NC;
+      P.segr_chunks = (int)((P.NC + want - 1) / want);
+      P.NSEGR = (P.NC + P.segr_chunks - 1) / P.segr_chunks;
+    }
   }
   const size_t BH = (size_t)P.BH, S = (size_t)dk * dv;
   size_t off = 0;
@@ -72,6 +102,20 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     P.off_fu = f; f = align_up(f + (P.NSEGF > 1 ? BH * P.NSEGF * S * 4 : 0));
     P.off_fi = f; f = align_up(f + (P.NSEGF > 1 ? BH * P.NSEGF * S * 4 : 0));
     P.ws_fwd = off > f ? off : f;
+  }
+  {
+    // the two-pass forward's buffers (its own region from the start)
+    const size_t NCC = (size_t)P.NC * C;
+    size_t f = 0;
+    P.off_qg = f; f = align_up(f + BH * NCC * dk * P.esize);
+    P.off_kg = f; f = align_up(f + BH * NCC * dk * P.esize);
+    P.off_ph = f; f = align_up(f + BH * NCC * C * P.esize);
+    P.off_pl = f; f = align_up(f + (bf16 ? BH * NCC * 16 * P.esize : 0));
+    P.off_gl = f; f = align_up(f + BH * P.NC * dk * 4);
+    P.off_ru = f; f = align_up(f + (P.NSEGR > 1 ? BH * P.NSEGR * S * 4 : 0));
+    P.off_ri = f; f = align_up(f + (P.NSEGR > 1 ? BH * P.NSEGR * S * 4 : 0));
+    P.off_rg = f; f = align_up(f + (P.NSEGR > 1 ? BH * P.NSEGR * dk * 4 : 0));
+    if (P.recur && f > P.ws_fwd) P.ws_fwd = f;
   }
   off = P.ws_fwd;
   // backward extras: dS per chunk in two layouts, hT, chunk totals of
@@ -204,6 +248,29 @@ gla_status gla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k
   float* seg_u = (float*)(ws + p.off_seg_u);
   float* seg_in = (float*)(ws + p.off_seg_in);
 
+  if (p.recur) {
+    // pass 1: per-chunk operands and score matrices; pass 2: the recurrence
+    // (segment local states and a scan over segments first when segmented)
+    void* qg = ws + p.off_qg;
+    void* kg = ws + p.off_kg;
+    void* ph = ws + p.off_ph;
+    void* pl = ws + p.off_pl;
+    float* gl = (float*)(ws + p.off_gl);
+    float* ru = (float*)(ws + p.off_ru);
+    float* ri = (float*)(ws + p.off_ri);
+    float* rg = (float*)(ws + p.off_rg);
+    GLA_LAUNCH("chunk_prep", launch_chunk_prep(p, q, k, log_alpha, qg, kg, gl, ph, pl, s));
+    if (p.NSEGR > 1) {
+      GLA_LAUNCH("recur_local", launch_chunk_recur(p, 0, qg, kg, ph, pl, gl, v, nullptr, nullptr, ru, rg, s));
+      Plan ps = p;
+      ps.NSEG = p.NSEGR;
+      GLA_LAUNCH("segment_scan", launch_segment_scan(ps, 0, rg, h0, ru, ri, hT, s));
+      GLA_LAUNCH("chunk_recur", launch_chunk_recur(p, 1, qg, kg, ph, pl, gl, v, ri, o, nullptr, nullptr, s));
+    } else {
+      GLA_LAUNCH("chunk_recur", launch_chunk_recur(p, 1, qg, kg, ph, pl, gl, v, h0, o, hT, nullptr, s));
+    }
+    return GLA_OK;
+  }
   GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
   if (p.fused) {
     // segment entry states from the segments' local states, then one fused

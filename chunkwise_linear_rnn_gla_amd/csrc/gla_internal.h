@@ -22,12 +22,20 @@ struct Plan {
   int NSEGF;         // sequence segments of the fused forward
   int segf_chunks;   // chunks per fused segment
   int DVTF;          // d_v tile of the fused segment kernel
+  int recur;         // forward runs chunk prep + chunk recurrence (two passes)
+  int NWVR;          // waves (16 state columns each) per recurrence workgroup
+  int NSEGR;         // sequence segments of the recurrence
+  int segr_chunks;   // chunks per recurrence segment
   size_t esize;      // bytes per I/O element
   // workspace layout (byte offsets); 0-sized regions have offset 0
   size_t off_cum, off_st, off_st2, off_seg_u, off_seg_in, off_end, off_dlt, off_rs;
   size_t off_A, off_dA, off_stlo, off_dstlo;
   size_t off_fu, off_fi;   // fused forward: segment local states, segment entry states
   size_t off_sg;           // segment total log decays [BH][max(NSEG, NSEGF)][dk]
+  // two-pass forward: Q~, K~ [BH][NC*C][dk], P [BH][NC][C][C], low part of P's
+  // diagonal blocks [BH][NC][C][16], chunk log decays [BH][NC][dk], segment
+  // local states / entry states [BH][NSEGR][dk][dv], segment log decays
+  size_t off_qg, off_kg, off_ph, off_pl, off_gl, off_ru, off_ri, off_rg;
   size_t ws_fwd, ws_bwd;
 };
 
@@ -72,6 +80,27 @@ int fused_dv_tile(int bf16, int dk, int dv);
 hipError_t launch_seg_output(const Plan& p, const void* q, const void* k, const void* v,
                              const float* cum, const float* h0, const float* seg_in, void* o,
                              float* hT, hipStream_t s);
+
+// ---- two-pass forward (gla_recur.hip) ----
+// Waves per recurrence workgroup needed to hold the state slice: one wave's
+// 16 columns of a 256-channel bf16 or 128-channel fp32 state leave too few
+// registers for the operands.
+constexpr int recur_min_waves(bool bf16, int dk) { return (bf16 ? dk >= 256 : dk >= 128) ? 2 : 1; }
+bool recur_supported(int bf16, int C, int dk, int dv);
+// Per (batch-head, chunk): Q~ = Q ⊙ e^B, K~ = K ⊙ e^{b - B} (padded rows are
+// zero), b, and the chunk's gated score matrix P (+ low part of its diagonal
+// blocks for bf16).
+hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,
+                             void* qg, void* kg, float* glog, void* ph, void* pl, hipStream_t s);
+// Per (batch-head, segment p.NSEGR, d_v tile of 16 p.NWVR columns).
+//   out = 1: o from the segment entry state (init = seg_in when NSEGR > 1,
+//            else h0 or null); fin receives the final state when NSEGR == 1.
+//   out = 0: the segment's local state from zero -> fin [BH][NSEGR][dk][dv],
+//            its total log decay -> seg_g [BH][NSEGR][dk].
+hipError_t launch_chunk_recur(const Plan& p, int out, const void* qg, const void* kg,
+                              const void* ph, const void* pl, const float* glog, const void* v,
+                              const float* init, void* o, float* fin, float* seg_g,
+                              hipStream_t s);
 
 // ---- backward kernels (gla_bwd.hip) ----
 // A (chunk score matrix) and dA = (dO V^T) ⊙ M per chunk, fp32 C x C blocks.

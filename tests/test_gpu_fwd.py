@@ -13,15 +13,16 @@ from gpu_util import TOL, dtype_name, oracle_fwd, rel_l2, run_fwd, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["auto", "materialized"], autouse=True)
+@pytest.fixture(params=["auto", "fused", "materialized"], autouse=True)
 def forward_path(request, monkeypatch):
-    """Run every forward case through both forward paths: the default (the
-    fused segment kernel wherever it applies) and the materialised-state
-    kernels (GLA_FORWARD=materialized)."""
-    if request.param == "materialized":
-        monkeypatch.setenv("GLA_FORWARD", "materialized")
-    else:
+    """Run every forward case through each forward path: the default (the
+    two-pass chunk prep + recurrence wherever it applies), the single-pass
+    fused segment kernel (GLA_FORWARD=fused, where it applies) and the
+    materialised-state kernels (GLA_FORWARD=materialized)."""
+    if request.param == "auto":
         monkeypatch.delenv("GLA_FORWARD", raising=False)
+    else:
+        monkeypatch.setenv("GLA_FORWARD", request.param)
     return request.param
 
 
@@ -86,6 +87,16 @@ def test_fused_segments(dt, dk, dv, L):
     # segments whose entry states come from the local-state pass and scan
     x = make_inputs(1, 2, L, dk, dv, dt, seed=311 + dk + L, h0_std=0.3)
     check_fwd(x, 64, "fused-segments")
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4])
+@pytest.mark.parametrize("dt,dk", [("fp32", 64), ("bf16", 128)])
+def test_recurrence_workgroup_shapes(waves, dt, dk, monkeypatch):
+    # 32 (batch, head) pairs: one segment per sequence, 16 state columns per
+    # wave and 1, 2 or 4 waves per workgroup
+    monkeypatch.setenv("GLA_RECUR_WAVES", str(waves))
+    x = make_inputs(4, 8, 300, dk, 128, dt, seed=320 + waves + dk, h0_std=0.3)
+    check_fwd(x, 64, f"recur-waves{waves}")
 
 
 def test_single_chunk_and_single_token():
