@@ -87,18 +87,21 @@ hipError_t launch_seg_output(const Plan& p, const void* q, const void* k, const 
 // registers for the operands.
 constexpr int recur_min_waves(bool bf16, int dk) { return (bf16 ? dk >= 256 : dk >= 128) ? 2 : 1; }
 bool recur_supported(int bf16, int C, int dk, int dv);
-// Per (batch-head, chunk): Q~ = Q ⊙ e^B, K~ = K ⊙ e^{b - B} (padded rows are
-// zero), b, and the chunk's gated score matrix P (+ low part of its diagonal
-// blocks for bf16).
+// Per (batch-head, chunk) records, in the fragment-blocked layouts of
+// gla_recur.hip: Q~ = Q ⊙ e^B and K~ = K ⊙ e^{b - B} (C x dk each, rows past
+// the sequence zero), the chunk's gated score matrix P (C x C) and, for bf16,
+// the low part of its diagonal blocks (C x 16); grec holds e^b then b per key
+// channel, recur_grec_bytes(dk) bytes per chunk.
+size_t recur_grec_bytes(int dk);
 hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,
-                             void* qg, void* kg, float* glog, void* ph, void* pl, hipStream_t s);
+                             void* qg, void* kg, float* grec, void* ph, void* pl, hipStream_t s);
 // Per (batch-head, segment p.NSEGR, d_v tile of 16 p.NWVR columns).
 //   out = 1: o from the segment entry state (init = seg_in when NSEGR > 1,
 //            else h0 or null); fin receives the final state when NSEGR == 1.
 //   out = 0: the segment's local state from zero -> fin [BH][NSEGR][dk][dv],
 //            its total log decay -> seg_g [BH][NSEGR][dk].
 hipError_t launch_chunk_recur(const Plan& p, int out, const void* qg, const void* kg,
-                              const void* ph, const void* pl, const float* glog, const void* v,
+                              const void* ph, const void* pl, const float* grec, const void* v,
                               const float* init, void* o, float* fin, float* seg_g,
                               hipStream_t s);
 

@@ -55,56 +55,112 @@ __device__ inline void dma16(const void* g, void* lds_wave_base) {
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16,
                                    0, 0);
 }
+// The same through a buffer resource: 16 bytes at rsrc base + soff + voff
+// (voff per lane, soff wave-uniform) into LDS at lds_wave_base + 16 * lane.
+// The copy is issued from inline assembly: the instruction writes no
+// register, and the compiler, which cannot tell which LDS bytes a copy
+// writes, would otherwise wait for every outstanding copy (including the
+// prefetch of a later chunk) before the next LDS read.  Completion is waited
+// for explicitly (wait_vm) before a staged buffer is read.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline i32x4 make_rsrc(const void* base) {
+  // raw buffer: stride 0, range 2 GiB, 32-bit data format
+  const unsigned long long a = (unsigned long long)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
+  r[2] = 0x7fffffff;
+  r[3] = 0x00020000;
+  return r;
+}
+// lds_wave_base: LDS byte address (wave-uniform).  M0 carries it; no other
+// code in the kernels that use this sets or reads M0.
+__device__ inline void dma16b(const i32x4& r, unsigned voff, unsigned soff, unsigned lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(voff), "s"(r),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory");
+}
+// LDS byte address of a __shared__ object.
+template <typename P>
+__device__ inline unsigned lds_addr(P* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) void*)p;
+}
 // Wait for this wave's outstanding global memory operations (LDS copies too).
 __device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// ---- LDS tile swizzles --------------------------------------------------
-// Tiles are row-major arrays of 16-byte units; unit u of row r is stored at
-// unit slot u ^ swz(r) of that row (an involution within the row, since every
-// row holds a power-of-two number of units and the mask stays below it).
-// Each mask spreads the rows that one MFMA operand read touches over distinct
-// LDS bank windows.  W = 16-element column windows per row.
+// ---- fragment-blocked layouts ---------------------------------------------
+// chunk_prep writes each chunk's Q~, K~, P (and P's diagonal low parts) as
+// blocks of 16-byte units laid out the way the recurrence's MFMA operand
+// reads want them, so that chunk_recur stages a chunk with contiguous
+// 1 KB copies and reads every operand at a lane-constant LDS offset.  The
+// unit orders below are involutions (applying one twice gives the identity),
+// chosen so that each operand read is free of LDS bank conflicts (64 banks of
+// 4 bytes; one 256-byte bank span per pass).
 //
-// Row reads (the 16 rows of a tile, one window each): bf16 windows are 32 B,
-// fp32 windows 64 B; rows sharing a 256-byte bank span are told apart by the
-// row bits below the span, the rest by the XOR.
-template <int ES, int W>
-__device__ inline int swz_rows(int r) {
-  constexpr int WPS = ES == 2 ? 8 : 4;      // windows per 256-byte bank span
-  constexpr int RP = W >= WPS ? 1 : WPS / W;  // rows per bank span
-  constexpr int MW = W >= WPS ? WPS : W;
-  return ((r / RP) & (MW - 1)) * (ES == 2 ? 2 : 4);
+// Row block (Q~, P): 16 rows x 4 units.  A 16x16 MFMA operand read has lane
+// (g, n) load unit g of row n; the 16 lanes of one g then cover 16 distinct
+// units of a 256-byte span.
+__device__ inline int row_slot(int n, int g) { return n * 4 + (g ^ ((n >> 2) & 3)); }
+// Diagonal-block low part (bf16): 16 rows x 2 units (columns 0-7, 8-15).
+__device__ inline int lo_slot(int n, int gd) { return n * 2 + (gd ^ ((n >> 3) & 1)); }
+// Token-run block (bf16, transposed reads): 32 rows x UPR units.  A
+// ds_read_b64_tr_b16 operand read touches rows 8 g + j (+ 4), j < 4, 32 bytes
+// each; half a wave (g = 0, 1) then covers 8 distinct 32-byte windows.
+template <int UPR>
+__device__ inline int run_slot(int rho, int u) {
+  int m;
+  if constexpr (UPR == 2) m = ((rho >> 3) & 1) << 3;
+  else if constexpr (UPR == 4) m = ((rho >> 3) & 1) << 1;
+  else m = (((rho >> 1) & 1) | (((rho >> 3) & 1) << 1)) << 1;
+  return (rho * UPR + u) ^ m;
 }
-// Token-run reads: rows 8 g + j (+ 4) for bf16 transposed reads (j < 4, lane
-// group g), rows 16 b + 4 g + i for fp32 scalar reads (fixed i).
-template <int ES, int W>
-__device__ inline int swz_runs(int r) {
-  if constexpr (ES == 2) {
-    int m = 0;
-    if constexpr (W >= 8) m = (r & 3) | (((r >> 3) & 1) << 2);
-    else if constexpr (W == 4) m = ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
-    else if constexpr (W == 2) m = (r >> 3) & 1;
-    return 2 * m;
-  } else {
-    int m = 0;
-    if constexpr (W >= 4) m = (r >> 2) & 3;
-    else if constexpr (W == 2) m = (r >> 2) & 1;
-    return 4 * m;
-  }
-}
+// Scalar-read block (fp32): 16 rows x UPR units.  A 16x16x4 operand read has
+// lane group g read row 4 g + i (fixed i), 64 bytes; the XOR puts the four
+// rows in distinct 64-byte windows of a 256-byte span.
+template <int UPR>
+__device__ inline int scal_slot(int rho, int u) { return (rho * UPR + u) ^ (((rho >> 2) & 3) << 2); }
+
+// Per-chunk record sizes (bytes).  GW: elements per 64-byte column group
+// (one unit of 4 per row of a row block).
+template <typename T>
+struct RecDims {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr bool BF = ES == 2;
+  static constexpr int EPU = 16 / ES;
+  static constexpr int GW = 64 / ES;
+  __host__ __device__ static constexpr int gbytes(int dk) { return ((8 * dk + 1023) / 1024) * 1024; }
+};
 
 constexpr int kLdsLimit = 160 * 1024;
 
-// Issue the NW wave copies of one staged tile across the workgroup's NWV
-// waves: copy c (64 units of 16 bytes) lands at LDS unit slots off + 64 c ..;
-// src(s) is the global address of the unit for slot s.
-template <int NW, int NWV, typename F>
-__device__ inline void stage_tile(unsigned char* base, int off, int w, int l, F src) {
+// Store one 16-byte unit of EPU values rounded to T.
+template <typename T> __device__ inline void store_unit(unsigned char* p, const float* x);
+template <> __device__ inline void store_unit<bf16>(unsigned char* p, const float* x) {
+  bf16x8 a;
 #pragma unroll
-  for (int i = 0; i < (NW + NWV - 1) / NWV; ++i) {
+  for (int e = 0; e < 8; ++e) a[e] = static_cast<bf16>(x[e]);
+  *reinterpret_cast<bf16x8*>(p) = a;
+}
+template <> __device__ inline void store_unit<float>(unsigned char* p, const float* x) {
+  f32x4 a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a[e] = x[e];
+  *reinterpret_cast<f32x4*>(p) = a;
+}
+
+// Issue copies [w, w + NWV, ...) < NCOPY of a contiguous tile: copy c moves the
+// 1 KB at src + 1024 c into LDS at dst + 1024 c.
+template <int NCOPY, int NWV>
+__device__ inline void copy_tile(const unsigned char* src, unsigned dst, int w, int l) {
+  const i32x4 r = make_rsrc(src);
+  const unsigned loff = (unsigned)l * 16u;
+#pragma unroll
+  for (int i = 0; i < (NCOPY + NWV - 1) / NWV; ++i) {
     const int c = w + i * NWV;
-    if (NW % NWV != 0 && c >= NW) break;
-    dma16(src(c * 64 + l), base + (off + c * 64) * 16);
+    if (NCOPY % NWV != 0 && c >= NCOPY) break;
+    dma16b(r, loff, (unsigned)c * 1024u, dst + (unsigned)c * 1024u);
   }
 }
 
@@ -114,12 +170,15 @@ __device__ inline void stage_tile(unsigned char* base, int off, int w, int l, F 
 template <typename T, int C>
 __global__ __launch_bounds__(kThreads) void k_chunk_prep(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ la,
-    T* __restrict__ qg, T* __restrict__ kg, float* __restrict__ glog, T* __restrict__ ph,
-    T* __restrict__ pl, int L, int dk, int NC) {
+    unsigned char* __restrict__ qrec, unsigned char* __restrict__ krec,
+    unsigned char* __restrict__ prec, unsigned char* __restrict__ lrec,
+    float* __restrict__ grec, int L, int dk, int NC) {
   using PB = PBuilder<T, C>;
+  using RD = RecDims<T>;
   constexpr bool BF = PB::BF;
   constexpr int KS = PB::KS, LDT = PB::LDT, LDF = PB::LDF;
-  constexpr int EPU = 16 / (int)sizeof(T);
+  constexpr int EPU = RD::EPU;
+  static_assert(KS == RD::GW, "one d_k slice is one column group");
   constexpr int RG = kThreads / KS;  // row groups of the slice cumsum
   constexpr int RPT = C / RG;        // rows per thread
   static_assert(RPT >= 1 && C % RG == 0, "cumsum row split");
@@ -135,9 +194,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
 
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int r0 = n * C, rv = min(C, L - r0);
+  const int NG = dk / KS;                                     // column groups per row
   const size_t io = (size_t)bh * L * dk;                      // q, k, log alpha
   const size_t cb = (size_t)bh * NC + n;                      // chunk id
-  const size_t go = cb * C * dk;                              // Q~, K~ (padded rows)
+  unsigned char* qr = qrec + cb * C * dk * RD::ES;
+  unsigned char* kr = krec + cb * C * dk * RD::ES;
+  float* gr = grec + cb * (RD::gbytes(dk) / 4);
 
   for (int it = tid; it < C * C; it += kThreads) ps[it] = from_f32<T>(0.f);
   if constexpr (BF)
@@ -146,7 +208,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
   PB pb;
   pb.init();
   const int ch = tid % KS, rg = tid / KS;
-  for (int s0 = 0; s0 < dk; s0 += KS) {
+  for (int grp = 0; grp < NG; ++grp) {
+    const int s0 = grp * KS;
     // log alpha of the thread's rows (0 past the end of the sequence)
     float av[RPT];
 #pragma unroll
@@ -182,23 +245,35 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) bs[(rg * RPT + i) * LDF + ch] = av[i] + off;
     __syncthreads();
-    // Q~ = Q ⊙ e^B, K~ = K ⊙ e^{b - B}, b
-    for (int it = tid; it < C * (KS / 8); it += kThreads) {
-      const int row = it / (KS / 8), c8 = (it % (KS / 8)) * 8;
-      float qv[8], kv[8], bv[8], gv[8];
-      load8(qs + row * LDT + c8, qv);
-      load8(ks + row * LDT + c8, kv);
-      load8(bs + row * LDF + c8, bv);
-      load8(bs + (C - 1) * LDF + c8, gv);
+    // Q~ = Q ⊙ e^B and K~ = K ⊙ e^{b - B}, one 16-byte unit per thread each.
+    // Q~ unit g of a row holds (bf16) columns 4g..4g+3 and 16+4g..16+4g+3 of
+    // the group, the channels of the state rows that lane group g holds in
+    // its accumulators; (fp32) columns 4g..4g+3.
+    for (int it = tid; it < C * 4; it += kThreads) {
+      const int row = it >> 2, g = it & 3;
+      float x[EPU];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qv[e] *= gexp<T>(bv[e]);
-        kv[e] *= gexp<T>(gv[e] - bv[e]);
+      for (int e = 0; e < EPU; ++e) {
+        const int c = BF ? (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4) : 4 * g + e;
+        x[e] = to_f32(qs[row * LDT + c]) * gexp<T>(bs[row * LDF + c]);
       }
-      store8(qg + go + (size_t)row * dk + s0 + c8, qv);
-      store8(kg + go + (size_t)row * dk + s0 + c8, kv);
+      store_unit<T>(qr + (((row >> 4) * NG + grp) * 1024 + row_slot(row & 15, g) * 16), x);
+      // K~: unit u = columns EPU u .. EPU u + EPU - 1
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) {
+        const int c = EPU * g + e;
+        x[e] = to_f32(ks[row * LDT + c]) * gexp<T>(bs[(C - 1) * LDF + c] - bs[row * LDF + c]);
+      }
+      int kofs;
+      if constexpr (BF) kofs = ((row >> 5) * NG + grp) * 2048 + run_slot<4>(row & 31, g) * 16;
+      else kofs = ((row >> 4) * NG + grp) * 1024 + scal_slot<4>(row & 15, g) * 16;
+      store_unit<T>(kr + kofs, x);
     }
-    if (tid < KS) glog[cb * dk + s0 + tid] = bs[(C - 1) * LDF + tid];
+    if (tid < KS) {
+      const float b = bs[(C - 1) * LDF + tid];
+      gr[s0 + tid] = gexp<T>(b);  // the chunk's decay of state row s0 + tid
+      gr[dk + s0 + tid] = b;      // and its log
+    }
     PB::gates(bs, als);
     pb.offdiag(qs, ks, bs);
     __syncthreads();
@@ -213,62 +288,75 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
     }
   });
   __syncthreads();
-  typedef f32x4 unit_t;
-  unit_t* pout = reinterpret_cast<unit_t*>(ph + cb * C * C);
-  const unit_t* pin = reinterpret_cast<const unit_t*>(ps);
-  for (int it = tid; it < C * C / EPU; it += kThreads) pout[it] = pin[it];
+  // P as row blocks (jt, column group); unit g of a row = its EPU columns
+  constexpr int PUR = C / EPU, NPG = C / KS;
+  unsigned char* pr = prec + cb * C * C * RD::ES;
+  for (int it = tid; it < C * PUR; it += kThreads) {
+    const int row = it / PUR, uu = it % PUR;
+    const f32x4 val = *reinterpret_cast<const f32x4*>(&ps[row * C + uu * EPU]);
+    *reinterpret_cast<f32x4*>(pr + ((row >> 4) * NPG + (uu >> 2)) * 1024 +
+                              row_slot(row & 15, uu & 3) * 16) = val;
+  }
   if constexpr (BF) {
-    unit_t* lout = reinterpret_cast<unit_t*>(pl + cb * C * 16);
-    const unit_t* lin = reinterpret_cast<const unit_t*>(ls);
-    for (int it = tid; it < C * 16 / EPU; it += kThreads) lout[it] = lin[it];
+    unsigned char* lr = lrec + cb * C * 16 * RD::ES;
+    for (int it = tid; it < C * 2; it += kThreads) {
+      const int row = it >> 1, gd = it & 1;
+      const f32x4 val = *reinterpret_cast<const f32x4*>(&ls[row * 16 + 8 * gd]);
+      *reinterpret_cast<f32x4*>(lr + (row >> 4) * 512 + lo_slot(row & 15, gd) * 16) = val;
+    }
   }
 }
 
 // =========================================================== pass 2: recurrence
 template <typename T, int C, int DK, int NWV, int OUT>
 struct RecurLayout {
-  static constexpr int ES = (int)sizeof(T);
-  static constexpr bool BF = ES == 2;
-  static constexpr int EPU = 16 / ES;           // elements per 16-byte unit
+  using RD = RecDims<T>;
+  static constexpr int ES = RD::ES;
+  static constexpr bool BF = RD::BF;
   static constexpr int DVT = 16 * NWV;          // d_v tile: 16 columns per wave
-  static constexpr int QUR = DK / EPU;          // units per Q~ / K~ row
-  static constexpr int PUR = C / EPU;           // units per P row
-  static constexpr int VUR = DVT / EPU;         // units per V row
-  static constexpr int QUN = OUT ? C * QUR : 0;
-  static constexpr int KUN = C * QUR;
-  static constexpr int PUN = OUT ? C * PUR : 0;
-  static constexpr int LUN = (OUT && BF) ? C * 16 / EPU : 0;
-  static constexpr int GUN = DK / 4 < 64 ? 64 : DK / 4;  // padded to a wave
-  static constexpr int VUN = C * VUR;
-  static constexpr int oQ = 0, oK = oQ + QUN, oP = oK + KUN, oL = oP + PUN, oG = oL + LUN,
-                       oV = oG + GUN, UN = oV + VUN;
-  static constexpr int BUF = UN * 16;
+  static constexpr int NG = DK / RD::GW;        // column groups of a Q~ / K~ row
+  static constexpr int NPG = C / RD::GW;        // column groups of a P row
+  static constexpr int VUPR = DVT * ES / 16;    // units per V row
+  static constexpr int QB = OUT ? C * DK * ES : 0;
+  static constexpr int KB = C * DK * ES;
+  static constexpr int PB = OUT ? C * C * ES : 0;
+  static constexpr int LB = (OUT && BF) ? C * 16 * ES : 0;
+  static constexpr int GB = RD::gbytes(DK);
+  static constexpr int VB = C * DVT * ES;
+  static constexpr int VBLK = BF ? 32 * VUPR * 16 : 16 * VUPR * 16;  // bytes per V block
+  static constexpr int oQ = 0, oK = oQ + QB, oP = oK + KB, oL = oP + PB, oG = oL + LB,
+                       oV = oG + GB, BUF = oV + VB;
   static constexpr int NBUF = 2 * BUF <= kLdsLimit ? 2 : 1;
-  static_assert(QUN % 64 == 0 && KUN % 64 == 0 && PUN % 64 == 0 && LUN % 64 == 0 &&
-                    GUN % 64 == 0 && VUN % 64 == 0,
-                "every staged tile is a whole number of wave copies");
+  static constexpr int VCOPY = VB / 1024, VCW = (VCOPY + NWV - 1) / NWV;  // V copies (per wave)
+  static_assert(QB % 1024 == 0 && KB % 1024 == 0 && PB % 1024 == 0 && LB % 1024 == 0 &&
+                    VB % 1024 == 0,
+                "every staged tile is a whole number of 1 KB copies");
   static_assert(BUF <= kLdsLimit, "staged chunk exceeds LDS");
 };
 
 template <typename T, int C, int DK, int NWV, int OUT>
 __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
-    const T* __restrict__ qg, const T* __restrict__ kg, const T* __restrict__ ph,
-    const T* __restrict__ pl, const float* __restrict__ glog, const T* __restrict__ v,
-    const float* __restrict__ init, T* __restrict__ o, float* __restrict__ fin,
-    float* __restrict__ seg_g, int L, int dv, int NC, int NSEG, int seg_chunks) {
+    const unsigned char* __restrict__ qrec, const unsigned char* __restrict__ krec,
+    const unsigned char* __restrict__ prec, const unsigned char* __restrict__ lrec,
+    const float* __restrict__ grec, const T* __restrict__ v, const float* __restrict__ init,
+    T* __restrict__ o, float* __restrict__ fin, float* __restrict__ seg_g, int L, int dv, int NC,
+    int NSEG, int seg_chunks) {
   using Lay = RecurLayout<T, C, DK, NWV, OUT>;
   constexpr bool BF = Lay::BF;
-  constexpr int EPU = Lay::EPU, DVT = Lay::DVT, NTH = NWV * kWave;
-  constexpr int NRT = C / 16, NKT = DK / 16;
-  constexpr int WQ = DK / 16, WV = DVT / 16, WP = C / 16;  // 16-column windows per row
+  constexpr int ES = Lay::ES, DVT = Lay::DVT, NTH = NWV * kWave, VUPR = Lay::VUPR;
+  constexpr int NRT = C / 16, NKT = DK / 16, NG = Lay::NG, NPG = Lay::NPG;
   __shared__ __attribute__((aligned(16))) unsigned char lds[Lay::NBUF * Lay::BUF];
 
   const int ntv = dv / DVT;
   const int lid = xcd_logical(blockIdx.x, gridDim.x);
   const int tile = lid % ntv, seg = (lid / ntv) % NSEG, bh = lid / (ntv * NSEG);
   const int j0 = tile * DVT;
-  const int w = wave_id(), l = lane_id(), g = l >> 4, ln = l & 15;
-  const int col = j0 + 16 * w + ln;  // this lane's state / output column
+  // the wave index as a scalar: copy and column offsets derived from it stay
+  // in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int l = lane_id(), g = l >> 4, ln = l & 15;
+  const int vc = 16 * w;             // this wave's first column within the tile
+  const int col = j0 + vc + ln;      // this lane's state column
   const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks);
 
   // ---- state slice: lane holds S[16 a + 4 g + r][col]
@@ -291,87 +379,101 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
 #pragma unroll
   for (int i = 0; i < NGS; ++i) gsum[i] = 0.f;
 
-  // ---- stage chunk n into buffer b: every tile as whole wave copies
+  // ---- V copies: per-lane (row, byte column) of each of this wave's copies
+  int vrow[Lay::VCW], vcolb[Lay::VCW];
+  unsigned vrow_off[Lay::VCW];
+#pragma unroll
+  for (int i = 0; i < Lay::VCW; ++i) {
+    const int c = w + i * NWV;
+    const int s = c * 64 + l;
+    int rho, u, blk;
+    if constexpr (BF) {
+      blk = s / (32 * VUPR);
+      const int lg = run_slot<VUPR>((s % (32 * VUPR)) / VUPR, s % VUPR);
+      rho = blk * 32 + lg / VUPR;
+      u = lg % VUPR;
+    } else {
+      blk = s / (16 * VUPR);
+      const int lg = scal_slot<VUPR>((s % (16 * VUPR)) / VUPR, s % VUPR);
+      rho = blk * 16 + lg / VUPR;
+      u = lg % VUPR;
+    }
+    vrow[i] = rho;
+    vcolb[i] = u * 16;
+    vrow_off[i] = (unsigned)(rho * dv * ES + u * 16);
+  }
+
+  const unsigned lds0 = lds_addr(lds);
   auto issue = [&](int n, int b) {
-    unsigned char* base = lds + b * Lay::BUF;
+    const unsigned base = lds0 + (unsigned)(b * Lay::BUF);
     const size_t cb = (size_t)bh * NC + n;
     if constexpr (OUT) {
-      const T* qb = qg + cb * C * DK;
-      stage_tile<Lay::QUN / 64, NWV>(base, Lay::oQ, w, l, [&](int s) {
-        const int r = s / Lay::QUR, u = (s % Lay::QUR) ^ swz_rows<Lay::ES, WQ>(r);
-        return qb + r * DK + u * EPU;
-      });
-      const T* pb = ph + cb * C * C;
-      stage_tile<Lay::PUN / 64, NWV>(base, Lay::oP, w, l, [&](int s) {
-        const int r = s / Lay::PUR, u = (s % Lay::PUR) ^ swz_rows<Lay::ES, WP>(r);
-        return pb + r * C + u * EPU;
-      });
-      if constexpr (BF) {
-        const T* lb = pl + cb * C * 16;
-        stage_tile<Lay::LUN / 64, NWV>(base, Lay::oL, w, l, [&](int s) { return lb + s * EPU; });
-      }
+      copy_tile<Lay::QB / 1024, NWV>(qrec + cb * Lay::QB, base + Lay::oQ, w, l);
+      copy_tile<Lay::PB / 1024, NWV>(prec + cb * Lay::PB, base + Lay::oP, w, l);
+      if constexpr (BF) copy_tile<Lay::LB / 1024, NWV>(lrec + cb * Lay::LB, base + Lay::oL, w, l);
     }
-    const T* kb = kg + cb * C * DK;
-    stage_tile<Lay::KUN / 64, NWV>(base, Lay::oK, w, l, [&](int s) {
-      const int r = s / Lay::QUR, u = (s % Lay::QUR) ^ swz_runs<Lay::ES, WQ>(r);
-      return kb + r * DK + u * EPU;
-    });
-    // chunk log decays: DK / 4 units, the rest of the wave copy repeats unit 0
-    const float* gb = glog + cb * DK;
-    stage_tile<Lay::GUN / 64, NWV>(base, Lay::oG, w, l,
-                                   [&](int s) { return gb + (s < DK / 4 ? s : 0) * 4; });
+    copy_tile<Lay::KB / 1024, NWV>(krec + cb * Lay::KB, base + Lay::oK, w, l);
+    copy_tile<Lay::GB / 1024, NWV>(reinterpret_cast<const unsigned char*>(grec) + cb * Lay::GB,
+                                   base + Lay::oG, w, l);
     // V rows past the end of the sequence repeat the last row (their K~ rows
     // and P columns are zero)
-    const int r0 = n * C, last = L - 1;
-    const T* vb = v + (size_t)bh * L * dv + j0;
-    stage_tile<Lay::VUN / 64, NWV>(base, Lay::oV, w, l, [&](int s) {
-      const int r = s / Lay::VUR, u = (s % Lay::VUR) ^ swz_runs<Lay::ES, WV>(r);
-      return vb + (size_t)min(r0 + r, last) * dv + u * EPU;
-    });
+    const int r0 = n * C;
+    const i32x4 vr = make_rsrc(v + ((size_t)bh * L + r0) * dv + j0);
+    const bool full = r0 + C <= L;
+#pragma unroll
+    for (int i = 0; i < Lay::VCW; ++i) {
+      const int c = w + i * NWV;
+      if (Lay::VCOPY % NWV != 0 && c >= Lay::VCOPY) break;
+      const unsigned vo = full ? vrow_off[i] : (unsigned)(min(vrow[i], L - 1 - r0) * dv * ES + vcolb[i]);
+      dma16b(vr, vo, 0u, base + (unsigned)(Lay::oV + c * 1024));
+    }
   };
 
-  if (nb < ne) issue(nb, 0);
-  for (int n = nb; n < ne; ++n) {
-    const int b = Lay::NBUF == 2 ? ((n - nb) & 1) : 0;
-    wait_vm();
-    __syncthreads();  // chunk n staged; every wave is done with the other buffer
-    if (Lay::NBUF == 2 && n + 1 < ne) issue(n + 1, b ^ 1);
-    const unsigned char* base = lds + b * Lay::BUF;
-    const T* Qs = reinterpret_cast<const T*>(base + Lay::oQ * 16);
-    const T* Ks = reinterpret_cast<const T*>(base + Lay::oK * 16);
-    const T* Ps = reinterpret_cast<const T*>(base + Lay::oP * 16);
-    const T* Ls = reinterpret_cast<const T*>(base + Lay::oL * 16);
-    const float* Gs = reinterpret_cast<const float*>(base + Lay::oG * 16);
-    const T* Vs = reinterpret_cast<const T*>(base + Lay::oV * 16);
-    // element (row, c) of a swizzled tile with RU units per row
-    auto qx = [&](int row, int c) {
-      return row * DK + (((c / EPU) ^ swz_rows<Lay::ES, WQ>(row)) * EPU) + c % EPU;
-    };
-    auto kx = [&](int row, int c) {
-      return row * DK + (((c / EPU) ^ swz_runs<Lay::ES, WQ>(row)) * EPU) + c % EPU;
-    };
-    auto px = [&](int row, int c) {
-      return row * C + (((c / EPU) ^ swz_rows<Lay::ES, WP>(row)) * EPU) + c % EPU;
-    };
-    auto vx = [&](int row, int c) {
-      return row * DVT + (((c / EPU) ^ swz_runs<Lay::ES, WV>(row)) * EPU) + c % EPU;
-    };
-    const int vc = 16 * w;  // this wave's first column within the tile
+  // ---- lane-constant LDS offsets of the operand reads
+  const int qoff = row_slot(ln, g) * 16;                  // Q~ and P row blocks
+  const int loff = lo_slot(ln, g & 1) * 16;               // P low part, lanes g = 2 (jt & 1) + gd
+  int voff[2], koff[2][2], vsoff[4], ksoff[4];
+  if constexpr (BF) {
+    const int rho = 8 * g + (ln >> 2), half = (ln & 1) * 8, ub = (ln & 3) >> 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      voff[h] = run_slot<VUPR>(rho + 4 * h, 2 * w + ub) * 16 + half;
+#pragma unroll
+      for (int ap = 0; ap < 2; ++ap) koff[ap][h] = run_slot<4>(rho + 4 * h, 2 * ap + ub) * 16 + half;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vsoff[i] = scal_slot<VUPR>(4 * g + i, 4 * w + (ln >> 2)) * 16 + (ln & 3) * 4;
+      ksoff[i] = scal_slot<4>(4 * g + i, ln >> 2) * 16 + (ln & 3) * 4;
+    }
+  }
 
+  // One chunk from buffer b: O^T of the chunk into ot (stored by the caller
+  // once the next copies are issued), then the state update.
+  auto body = [&](int n, int b, floatx4 (&ot)[NRT]) {
+    const unsigned char* base = lds + b * Lay::BUF;
+    const unsigned char* Qs = base + Lay::oQ;
+    const unsigned char* Ks = base + Lay::oK;
+    const unsigned char* Ps = base + Lay::oP;
+    const unsigned char* Ls = base + Lay::oL;
+    const float* Gs = reinterpret_cast<const float*>(base + Lay::oG);
+    const unsigned char* Vs = base + Lay::oV;
     if constexpr (BF) {
       // V fragments over token runs 32 kt + 8 g + e at column vc + ln
       bf16x8 vf[C / 32];
 #pragma unroll
       for (int kt = 0; kt < C / 32; ++kt) {
-        const int ra = 32 * kt + 8 * g + (ln >> 2), c = vc + 4 * (ln & 3);
-        vf[kt] = join8(ds_read_tr(Vs + vx(ra, c)), ds_read_tr(Vs + vx(ra + 4, c)));
+        const bf16* vb = reinterpret_cast<const bf16*>(Vs + kt * Lay::VBLK);
+        vf[kt] = join8(ds_read_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const unsigned char*>(vb) + voff[0])),
+                       ds_read_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const unsigned char*>(vb) + voff[1])));
       }
       if constexpr (OUT) {
-        floatx4 ot[NRT];
 #pragma unroll
         for (int jt = 0; jt < NRT; ++jt) ot[jt] = zero4();
         // O^T += S^T Q~^T over pairs of 16-channel tiles; the MFMA's K index
         // 8 g + e maps to channel 32 a2 + 4 g + e (e < 4) or + 16 + 4 g + e - 4
+        // (the order of the Q~ units)
 #pragma unroll
         for (int a2 = 0; a2 < NKT / 2; ++a2) {
           bf16x8 A;
@@ -382,32 +484,21 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
           }
 #pragma unroll
           for (int jt = 0; jt < NRT; ++jt) {
-            const int row = 16 * jt + ln;
-            const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(Qs + qx(row, 32 * a2 + 4 * g));
-            const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(Qs + qx(row, 32 * a2 + 16 + 4 * g));
-            ot[jt] = Mma<bf16>::run(A, join8(x0, x1), ot[jt]);
+            const bf16x8 B = *reinterpret_cast<const bf16x8*>(Qs + (jt * NG + a2) * 1024 + qoff);
+            ot[jt] = Mma<bf16>::run(A, B, ot[jt]);
           }
         }
         // O^T += V^T P^T (P rounded; its diagonal blocks also carry a low part)
 #pragma unroll
         for (int jt = 0; jt < NRT; ++jt) {
-          const int row = 16 * jt + ln;
 #pragma unroll
           for (int kt = 0; kt <= (jt >> 1); ++kt) {
-            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(Ps + px(row, 32 * kt + 8 * g));
+            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(Ps + (jt * NPG + kt) * 1024 + qoff);
             ot[jt] = Mma<bf16>::run(vf[kt], pf, ot[jt]);
           }
-          const int gd = g - 2 * (jt & 1);  // lane group inside the diagonal block
           bf16x8 lf = bf16x8{};
-          if (gd == 0 || gd == 1) lf = *reinterpret_cast<const bf16x8*>(Ls + row * 16 + 8 * gd);
+          if ((g >> 1) == (jt & 1)) lf = *reinterpret_cast<const bf16x8*>(Ls + jt * 512 + loff);
           ot[jt] = Mma<bf16>::run(vf[jt >> 1], lf, ot[jt]);
-        }
-        const int rv = min(C, L - n * C);
-#pragma unroll
-        for (int jt = 0; jt < NRT; ++jt) {
-          const int row = 16 * jt + ln;
-          if (row < rv)
-            store4(o + ((size_t)bh * L + n * C + row) * dv + j0 + vc + 4 * g, ot[jt]);
         }
       }
       // S = diag(e^b) S + K~^T V
@@ -415,34 +506,35 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
       for (int a = 0; a < NKT; ++a) {
         const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + 16 * a + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[a][r] *= gexp<T>(gv[r]);
+        for (int r = 0; r < 4; ++r) S[a][r] *= gv[r];
       }
 #pragma unroll
       for (int kt = 0; kt < C / 32; ++kt) {
 #pragma unroll
         for (int a = 0; a < NKT; ++a) {
-          const int ra = 32 * kt + 8 * g + (ln >> 2), c = 16 * a + 4 * (ln & 3);
-          const bf16x8 kf = join8(ds_read_tr(Ks + kx(ra, c)), ds_read_tr(Ks + kx(ra + 4, c)));
+          const unsigned char* kb = Ks + (kt * NG + (a >> 1)) * 2048;
+          const bf16x8 kf = join8(ds_read_tr(reinterpret_cast<const bf16*>(kb + koff[a & 1][0])),
+                                  ds_read_tr(reinterpret_cast<const bf16*>(kb + koff[a & 1][1])));
           S[a] = Mma<bf16>::run(kf, vf[kt], S[a]);
         }
       }
     } else {
-      // fp32: 16x16x4 MFMAs; within each 16-token block b the MFMA i takes
-      // tokens 16 b + 4 g + i (K index g)
+      // fp32: 16x16x4 MFMAs; within each 16-token block bb the MFMA i takes
+      // tokens 16 bb + 4 g + i (K index g)
       float vf[NRT][4];
 #pragma unroll
       for (int bb = 0; bb < NRT; ++bb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vf[bb][i] = Vs[vx(16 * bb + 4 * g + i, vc + ln)];
+        for (int i = 0; i < 4; ++i)
+          vf[bb][i] = *reinterpret_cast<const float*>(Vs + bb * Lay::VBLK + vsoff[i]);
       if constexpr (OUT) {
-        floatx4 ot[NRT];
 #pragma unroll
         for (int jt = 0; jt < NRT; ++jt) ot[jt] = zero4();
 #pragma unroll
         for (int a = 0; a < NKT; ++a)
 #pragma unroll
           for (int jt = 0; jt < NRT; ++jt) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(Qs + qx(16 * jt + ln, 16 * a + 4 * g));
+            const f32x4 x = *reinterpret_cast<const f32x4*>(Qs + (jt * NG + a) * 1024 + qoff);
 #pragma unroll
             for (int r = 0; r < 4; ++r) ot[jt] = Mma<float>::run(S[a][r], x[r], ot[jt]);
           }
@@ -450,42 +542,81 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
         for (int jt = 0; jt < NRT; ++jt)
 #pragma unroll
           for (int bb = 0; bb <= jt; ++bb) {
-            const f32x4 pf = *reinterpret_cast<const f32x4*>(Ps + px(16 * jt + ln, 16 * bb + 4 * g));
+            const f32x4 pf = *reinterpret_cast<const f32x4*>(Ps + (jt * NPG + bb) * 1024 + qoff);
 #pragma unroll
             for (int i = 0; i < 4; ++i) ot[jt] = Mma<float>::run(vf[bb][i], pf[i], ot[jt]);
           }
-        const int rv = min(C, L - n * C);
-#pragma unroll
-        for (int jt = 0; jt < NRT; ++jt) {
-          const int row = 16 * jt + ln;
-          if (row < rv)
-            store4(o + ((size_t)bh * L + n * C + row) * dv + j0 + vc + 4 * g, ot[jt]);
-        }
       }
 #pragma unroll
       for (int a = 0; a < NKT; ++a) {
         const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + 16 * a + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[a][r] *= gexp<T>(gv[r]);
+        for (int r = 0; r < 4; ++r) S[a][r] *= gv[r];
       }
 #pragma unroll
       for (int bb = 0; bb < NRT; ++bb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int a = 0; a < NKT; ++a)
-            S[a] = Mma<float>::run(Ks[kx(16 * bb + 4 * g + i, 16 * a + ln)], vf[bb][i], S[a]);
+          for (int a = 0; a < NKT; ++a) {
+            const float kv = *reinterpret_cast<const float*>(Ks + (bb * NG + a) * 1024 + ksoff[i]);
+            S[a] = Mma<float>::run(kv, vf[bb][i], S[a]);
+          }
     }
     if constexpr (!OUT) {
 #pragma unroll
       for (int i = 0; i < NGS; ++i) {
         const int t = threadIdx.x + i * NTH;
-        if (t < DK) gsum[i] += Gs[t];
+        if (t < DK) gsum[i] += Gs[DK + t];
       }
     }
-    if (Lay::NBUF == 1) {
+  };
+
+  auto store_out = [&](int n, const floatx4 (&ot)[NRT]) {
+    if constexpr (OUT) {
+      const int rv = min(C, L - n * C);
+      T* orow = o + ((size_t)bh * L + n * C + ln) * dv + j0 + vc + 4 * g;
+#pragma unroll
+      for (int jt = 0; jt < NRT; ++jt)
+        if (16 * jt + ln < rv) store4(orow + (size_t)16 * jt * dv, ot[jt]);
+    }
+  };
+
+  // ---- walk the segment's chunks.  Per chunk: compute from its buffer,
+  // then wait for the next chunk's copies (issued a chunk earlier) and for
+  // the previous chunk's stores, barrier, issue the copies of the chunk after
+  // next into the buffer just released, and only then store this chunk's
+  // output, so that its stores complete during the next chunk's compute.
+  // Buffer indices are literals at every body call.
+  floatx4 ot[NRT];
+  if constexpr (Lay::NBUF == 2) {
+    if (nb < ne) issue(nb, 0);
+    if (nb + 1 < ne) issue(nb + 1, 1);
+    wait_vm();
+    __syncthreads();
+    for (int n = nb; n < ne; n += 2) {
+      body(n, 0, ot);
+      wait_vm();
+      __syncthreads();  // chunk n + 1 staged; every wave is done with buffer 0
+      if (n + 2 < ne) issue(n + 2, 0);
+      store_out(n, ot);
+      if (n + 1 < ne) {
+        body(n + 1, 1, ot);
+        wait_vm();
+        __syncthreads();  // chunk n + 2 staged; every wave is done with buffer 1
+        if (n + 3 < ne) issue(n + 3, 1);
+        store_out(n + 1, ot);
+      }
+    }
+  } else {
+    if (nb < ne) issue(nb, 0);
+    for (int n = nb; n < ne; ++n) {
+      wait_vm();
+      __syncthreads();  // chunk n staged
+      body(n, 0, ot);
       __syncthreads();  // every wave is done with the buffer
       if (n + 1 < ne) issue(n + 1, 0);
+      store_out(n, ot);
     }
   }
 
@@ -511,64 +642,65 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
 // =========================================================== launchers
 template <typename T, int C>
 static hipError_t launch_prep_t(const Plan& p, const void* q, const void* k, const float* la,
-                                void* qg, void* kg, float* glog, void* ph, void* pl,
+                                void* qg, void* kg, float* grec, void* ph, void* pl,
                                 hipStream_t s) {
   hipLaunchKernelGGL((k_chunk_prep<T, C>), dim3(p.NC, p.BH), dim3(kThreads), 0, s, (const T*)q,
-                     (const T*)k, la, (T*)qg, (T*)kg, glog, (T*)ph, (T*)pl, p.L, p.dk, p.NC);
+                     (const T*)k, la, (unsigned char*)qg, (unsigned char*)kg, (unsigned char*)ph,
+                     (unsigned char*)pl, grec, p.L, p.dk, p.NC);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,
-                             void* qg, void* kg, float* glog, void* ph, void* pl, hipStream_t s) {
+                             void* qg, void* kg, float* grec, void* ph, void* pl, hipStream_t s) {
   if (p.bf16) {
-    if (p.C == 64) return launch_prep_t<bf16, 64>(p, q, k, la, qg, kg, glog, ph, pl, s);
-    return launch_prep_t<bf16, 32>(p, q, k, la, qg, kg, glog, ph, pl, s);
+    if (p.C == 64) return launch_prep_t<bf16, 64>(p, q, k, la, qg, kg, grec, ph, pl, s);
+    return launch_prep_t<bf16, 32>(p, q, k, la, qg, kg, grec, ph, pl, s);
   }
-  if (p.C == 64) return launch_prep_t<float, 64>(p, q, k, la, qg, kg, glog, ph, pl, s);
-  if (p.C == 32) return launch_prep_t<float, 32>(p, q, k, la, qg, kg, glog, ph, pl, s);
-  return launch_prep_t<float, 16>(p, q, k, la, qg, kg, glog, ph, pl, s);
+  if (p.C == 64) return launch_prep_t<float, 64>(p, q, k, la, qg, kg, grec, ph, pl, s);
+  if (p.C == 32) return launch_prep_t<float, 32>(p, q, k, la, qg, kg, grec, ph, pl, s);
+  return launch_prep_t<float, 16>(p, q, k, la, qg, kg, grec, ph, pl, s);
 }
 
 template <typename T, int C, int DK, int NWV>
 static hipError_t launch_recur_w(const Plan& p, int out, const void* qg, const void* kg,
-                                 const void* ph, const void* pl, const float* glog,
+                                 const void* ph, const void* pl, const float* grec,
                                  const void* v, const float* init, void* o, float* fin,
                                  float* seg_g, hipStream_t s) {
   const dim3 grid(p.BH * p.NSEGR * (p.dv / (16 * NWV)));
+  const unsigned char *q8 = (const unsigned char*)qg, *k8 = (const unsigned char*)kg,
+                      *p8 = (const unsigned char*)ph, *l8 = (const unsigned char*)pl;
   if (out)
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1>), grid, dim3(NWV * kWave), 0, s,
-                       (const T*)qg, (const T*)kg, (const T*)ph, (const T*)pl, glog,
-                       (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC, p.NSEGR,
-                       p.segr_chunks);
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1>), grid, dim3(NWV * kWave), 0, s, q8, k8,
+                       p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
+                       p.NSEGR, p.segr_chunks);
   else
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0>), grid, dim3(NWV * kWave), 0, s,
-                       (const T*)qg, (const T*)kg, (const T*)ph, (const T*)pl, glog,
-                       (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC, p.NSEGR,
-                       p.segr_chunks);
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0>), grid, dim3(NWV * kWave), 0, s, q8, k8,
+                       p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
+                       p.NSEGR, p.segr_chunks);
   return hipGetLastError();
 }
 
 template <typename T, int C, int DK>
 static hipError_t launch_recur_d(const Plan& p, int out, const void* qg, const void* kg,
-                                 const void* ph, const void* pl, const float* glog,
+                                 const void* ph, const void* pl, const float* grec,
                                  const void* v, const float* init, void* o, float* fin,
                                  float* seg_g, hipStream_t s) {
   if (p.NWVR == 4)
-    return launch_recur_w<T, C, DK, 4>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
+    return launch_recur_w<T, C, DK, 4>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   if (p.NWVR == 2)
-    return launch_recur_w<T, C, DK, 2>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
+    return launch_recur_w<T, C, DK, 2>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   if constexpr (recur_min_waves(sizeof(T) == 2, DK) == 1)
-    return launch_recur_w<T, C, DK, 1>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
+    return launch_recur_w<T, C, DK, 1>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   return hipErrorInvalidValue;
 }
 
 template <typename T, int C>
 static hipError_t launch_recur_c(const Plan& p, int out, const void* qg, const void* kg,
-                                 const void* ph, const void* pl, const float* glog,
+                                 const void* ph, const void* pl, const float* grec,
                                  const void* v, const float* init, void* o, float* fin,
                                  float* seg_g, hipStream_t s) {
 #define GLA_RECUR_DK(D) \
-  if (p.dk == D) return launch_recur_d<T, C, D>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s)
+  if (p.dk == D) return launch_recur_d<T, C, D>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s)
   if constexpr (sizeof(T) == 2) {
     GLA_RECUR_DK(32);
     GLA_RECUR_DK(64);
@@ -584,6 +716,8 @@ static hipError_t launch_recur_c(const Plan& p, int out, const void* qg, const v
   return hipErrorInvalidValue;
 }
 
+size_t recur_grec_bytes(int dk) { return RecDims<float>::gbytes(dk); }
+
 bool recur_supported(int bf16, int C, int dk, int dv) {
   const bool shape = bf16 ? (C == 32 || C == 64) && (dk == 32 || dk == 64 || dk == 128 || dk == 256)
                           : (C == 16 || C == 32 || C == 64) && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
@@ -591,19 +725,19 @@ bool recur_supported(int bf16, int C, int dk, int dv) {
 }
 
 hipError_t launch_chunk_recur(const Plan& p, int out, const void* qg, const void* kg,
-                              const void* ph, const void* pl, const float* glog, const void* v,
+                              const void* ph, const void* pl, const float* grec, const void* v,
                               const float* init, void* o, float* fin, float* seg_g,
                               hipStream_t s) {
   if (p.bf16) {
     if (p.C == 64)
-      return launch_recur_c<bf16, 64>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
-    return launch_recur_c<bf16, 32>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
+      return launch_recur_c<bf16, 64>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
+    return launch_recur_c<bf16, 32>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   }
   if (p.C == 64)
-    return launch_recur_c<float, 64>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
+    return launch_recur_c<float, 64>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   if (p.C == 32)
-    return launch_recur_c<float, 32>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
-  return launch_recur_c<float, 16>(p, out, qg, kg, ph, pl, glog, v, init, o, fin, seg_g, s);
+    return launch_recur_c<float, 32>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
+  return launch_recur_c<float, 16>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
 }
 
 }  // namespace gla
