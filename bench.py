@@ -21,6 +21,7 @@ Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -36,6 +37,34 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 INFINITY_CACHE_BYTES = 256 << 20
 
 METRIC = "GLA chunkwise fwd TFLOP/s + tokens/s, B8 H4 L2048 dk128 dv256 bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CALIBRATE_BYTES = 1 << 30     # plain device copy used to scale the HBM byte counters
+
+
+def sources_digest(paths):
+    """sha256 over the given repository files (the sources of a kernel)."""
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE record, or None when there is none or
+    the kernel's sources changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for e in rec.get("entries", []):
+        if e.get("kernel") == kernel and e.get("workload") == workload:
+            if e.get("sources_sha256") != sources_digest(e.get("sources", [])):
+                return None
+            return e
+    return None
 
 
 def log(*a):
@@ -118,7 +147,21 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd figure")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times), the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        dev = torch.device("cuda:0")
+        src = torch.ones(CALIBRATE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration: 3 copies of {CALIBRATE_BYTES} bytes")
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
@@ -234,10 +277,23 @@ def main():
     dom_avg_s = sum(per_kernel[dom]) / len(per_kernel[dom]) * 1e-3
     dom_bytes = kernel_bytes(dom, w, esize, nc)
     achieved = dom_bytes / dom_avg_s / 1e9
+    tr = measured_traffic(dom, w.name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None, "algorithmic_bytes_per_launch": dom_bytes,
+                "traffic": tr["bytes_per_launch"] if tr else None,
+                "traffic_read": tr["read_bytes_per_launch"] if tr else None,
+                "traffic_write": tr["write_bytes_per_launch"] if tr else None,
+                "algorithmic_bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+    # the whole step against the method's compulsory HBM bytes (q, k, v, log
+    # alpha read once, o and hT written once, h0 read if given)
+    BHs = w.B * w.H
+    compulsory = (2 * BHs * w.L * w.dk * esize + 2 * BHs * w.L * w.dv * esize +
+                  BHs * w.L * w.dk * 4 + BHs * w.dk * w.dv * 4 * (2 if w.h0_std else 1))
+    step_gbps = compulsory / (ms_per_step * 1e-3) / 1e9
+    step_roofline = {"bound": "hbm", "compulsory_bytes": compulsory,
+                     "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(step_gbps / HBM_PEAK_GBPS, 4)}
     log(f"[bench] {value:.3e} tokens/s, {tflops:.1f} TFLOP/s; dominant {dom} "
         f"{dom_avg_s * 1e6:.1f} us, {achieved:.0f} GB/s")
 
@@ -306,7 +362,7 @@ def main():
         "tflops": round(tflops, 2), "frac_bf16_mfma_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
         "warm": {"ms_per_step": round(warm_ms, 5),
                  "tokens_per_s": round(tokens / (warm_ms * 1e-3), 1)},
-        "roofline": roofline, "kernels": kernels, "copy_gbps": round(copy_gbps, 1),
+        "roofline": roofline, "step_roofline": step_roofline, "kernels": kernels, "copy_gbps": round(copy_gbps, 1),
         "fwd_bwd": fwd_bwd, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -89,9 +89,13 @@ gla_status gla_bwd_workspace_size(const gla_dims *dims, int dtype, size_t *bytes
  *        fp32 (entries <= 0 expected; not checked); h0 [B,H,dk,dv] fp32 or
  *        NULL for zeros.
  *   out: o [B,H,L,dv] in `dtype`; hT [B,H,dk,dv] fp32, or NULL to skip.
- *   Steps on `stream`: chunk-local cumsum of log_alpha; inter-chunk state
- *   recurrence materialising the state entering every chunk; intra-chunk
- *   output (MFMA between sub-chunks, fp32 on diagonal sub-blocks).
+ *   Steps on `stream` (default path): one pass over all chunks in parallel
+ *   forms the chunk-local cumsum of log_alpha, Q ⊙ e^B, K ⊙ e^{b-B}, the
+ *   chunk decay and the chunk's gated score matrix (MFMA between
+ *   sub-chunks, fp32 on diagonal sub-blocks); a second pass walks the chunks
+ *   in order with the state on chip and writes o (and hT).  Long sequences
+ *   with few (batch, head) pairs are split into segments whose entry states
+ *   come from a scan of the segments' local states.
  *   workspace: device memory of at least gla_fwd_workspace_size bytes,
  *   16-byte aligned, contents on entry irrelevant, clobbered on exit. */
 gla_status gla_fwd(const gla_dims *dims, int dtype,
