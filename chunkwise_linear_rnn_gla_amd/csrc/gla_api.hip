@@ -82,9 +82,14 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   P.segr_chunks = P.NC > 0 ? P.NC : 1;
   if (P.recur && P.NC > 1 && P.BH > 0) {
     const int64_t units = (int64_t)P.BH * (dv / (16 * P.NWVR));
-    if (units < 128) {
-      int64_t want = (256 + units - 1) / units;
-      if (want > P.NC) want = P.NC;
+    int64_t want = 1;
+    if (units < 128) want = (256 + units - 1) / units;
+    if (const char* e = getenv("GLA_RECUR_SEGMENTS")) {
+      const int v = atoi(e);
+      if (v >= 1) want = v;
+    }
+    if (want > P.NC) want = P.NC;
+    if (want > 1) {
       P.segr_chunks = (int)((P.NC + want - 1) / want);
       P.NSEGR = (P.NC + P.segr_chunks - 1) / P.segr_chunks;
     }

@@ -76,6 +76,20 @@ template <> __device__ inline bf16x8 scaled_frag<bf16>(const bf16* x, const floa
 template <> __device__ inline float scaled_frag<float>(const float* x, const float* s) {
   return x[0] * s[0];
 }
+// The same for bf16 operands from fp32 values x (rounded once after scaling).
+__device__ inline bf16x8 scaled_frag_from_f32(const float* x, const float* s) {
+  const f32x4 x0 = *reinterpret_cast<const f32x4*>(x);
+  const f32x4 x1 = *reinterpret_cast<const f32x4*>(x + 4);
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(s);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + 4);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = static_cast<bf16>(x0[e] * s0[e]);
+    r[e + 4] = static_cast<bf16>(x1[e] * s1[e]);
+  }
+  return r;
+}
 
 __device__ inline floatx4 zero4() {
   floatx4 z = {0.f, 0.f, 0.f, 0.f};

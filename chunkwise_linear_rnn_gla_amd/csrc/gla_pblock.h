@@ -69,6 +69,14 @@ __device__ inline void store8_aligned8(bf16* p, const float* x) {
   }
 }
 __device__ inline void store4(float* p, floatx4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ inline floatx4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ inline floatx4 load4(const bf16* p) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  floatx4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = static_cast<float>(a[e]);
+  return r;
+}
 __device__ inline void store4(bf16* p, floatx4 x) {
   bf16x4 a;
 #pragma unroll
@@ -127,14 +135,16 @@ template <typename T> constexpr int gather_pad(int W) {
   return 0;
 }
 
-template <typename T, int C, int NWV = 4>
+// S: element type of the q / k slice arrays in LDS (T, or fp32 so that the
+// vector-ALU reads need no conversion).
+template <typename T, int C, int NWV = 4, typename S = T>
 struct PBuilder {
   static constexpr int NTH = NWV * kWave;          // threads of the workgroup
   using M = Mma<T>;
   static constexpr bool BF = sizeof(T) == 2;
   static constexpr int KS = BF ? 32 : 16;          // d_k slice
-  static constexpr int PT = 16 / (int)sizeof(T);
-  static constexpr int LDT = KS + PT;              // row length of T slice arrays
+  static constexpr int PT = 16 / (int)sizeof(S);
+  static constexpr int LDT = KS + PT;              // row length of the S slice arrays
   static constexpr int LDF = KS + 4;               // row length of fp32 slice arrays
   static constexpr int NRT = C / 16;               // sub-chunks per chunk
   static constexpr int NP = NRT * (NRT - 1) / 2;   // off-diagonal pairs
@@ -144,7 +154,7 @@ struct PBuilder {
   static constexpr int NG = 8 * WPB;               // channel groups per block
   static constexpr int CPL = KS / NG > 0 ? KS / NG : 1;
   // LDS: q, k (T), cumsum and gates (fp32), one slice
-  static constexpr int SLICE_BYTES = 2 * C * LDT * (int)sizeof(T) + 2 * C * LDF * 4;
+  static constexpr int SLICE_BYTES = 2 * C * LDT * (int)sizeof(S) + 2 * C * LDF * 4;
 
   float dsum[17];
   floatx4 pacc[NPA];
@@ -168,7 +178,7 @@ struct PBuilder {
   // last valid row (log alpha = 0 there).  Optionally also writes
   // qt = T(q ⊙ e^B) (row-major, LDT) for the inter-chunk MFMA.
   __device__ static void stage(const T* q, const T* k, const float* cum, size_t qo, int r0,
-                               int rv, int dk, int s0, T* qs, T* ks, float* bs, T* qt) {
+                               int rv, int dk, int s0, S* qs, S* ks, float* bs, T* qt) {
     for (int it = threadIdx.x; it < C * (KS / 8); it += NTH) {
       const int row = it / (KS / 8), c8 = (it % (KS / 8)) * 8;
       const bool valid = row < rv;
@@ -205,7 +215,7 @@ struct PBuilder {
   }
 
   // Off-diagonal blocks, MFMA, accumulated over slices.  Needs qs, ks, bs.
-  __device__ void offdiag(const T* qs, const T* ks, const float* bs) {
+  __device__ void offdiag(const S* qs, const S* ks, const float* bs) {
 #pragma unroll
     for (int t = 0; t < NPW; ++t) {
       const int pi = w + NWV * t;
@@ -222,8 +232,14 @@ struct PBuilder {
           sa[e] = gexp<T>(bs[(jq * 16 + m) * LDF + cq + e] - z);
           sb[e] = gexp<T>(z - bs[(ju * 16 + m) * LDF + cq + e]);
         }
-        auto a = scaled_frag<T>(qs + (jq * 16 + m) * LDT + cq, sa);
-        auto b = scaled_frag<T>(ks + (ju * 16 + m) * LDT + cq, sb);
+        typename M::frag a, b;
+        if constexpr (BF && sizeof(S) == 4) {
+          a = scaled_frag_from_f32(qs + (jq * 16 + m) * LDT + cq, sa);
+          b = scaled_frag_from_f32(ks + (ju * 16 + m) * LDT + cq, sb);
+        } else {
+          a = scaled_frag<T>(qs + (jq * 16 + m) * LDT + cq, sa);
+          b = scaled_frag<T>(ks + (ju * 16 + m) * LDT + cq, sb);
+        }
         pacc[t] = M::run(a, b, pacc[t]);
       }
     }
@@ -258,7 +274,7 @@ struct PBuilder {
   // Diagonal blocks, fp32 VALU, accumulated over slices.  Needs qs, ks, als.
   // The lane's two query rows are loaded once; each step then reads one key
   // row and one gate row (vector loads) and extends the running gate product.
-  __device__ void diag(const T* qs, const T* ks, const float* als) {
+  __device__ void diag(const S* qs, const S* ks, const float* als) {
     if (dg * CPL >= KS) return;
     const int cb = dg * CPL;
     const int m2 = 15 - dp;

@@ -173,7 +173,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
     unsigned char* __restrict__ qrec, unsigned char* __restrict__ krec,
     unsigned char* __restrict__ prec, unsigned char* __restrict__ lrec,
     float* __restrict__ grec, int L, int dk, int NC) {
-  using PB = PBuilder<T, C>;
+  // q, k slices staged in fp32: the diagonal blocks' vector-ALU reads and the
+  // scaled MFMA operands then need no conversion
+  using PB = PBuilder<T, C, 4, float>;
   using RD = RecDims<T>;
   constexpr bool BF = PB::BF;
   constexpr int KS = PB::KS, LDT = PB::LDT, LDF = PB::LDF;
@@ -187,9 +189,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
   __shared__ float tot[RG][KS];
   __shared__ __attribute__((aligned(16))) T ps[C * C];
   __shared__ __attribute__((aligned(16))) T ls[BF ? C * 16 : EPU];
-  T* qs = reinterpret_cast<T*>(smem);
-  T* ks = qs + C * LDT;
-  float* bs = reinterpret_cast<float*>(ks + C * LDT);
+  float* qs = reinterpret_cast<float*>(smem);
+  float* ks = qs + C * LDT;
+  float* bs = ks + C * LDT;
   float* als = bs + C * LDF;
 
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -208,28 +210,48 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
   PB pb;
   pb.init();
   const int ch = tid % KS, rg = tid / KS;
-  for (int grp = 0; grp < NG; ++grp) {
+  // The next slice's q, k (one 8-element unit each per thread) and log alpha
+  // (RPT rows of one channel per thread) are loaded into registers while the
+  // current slice is processed.  Rows past the end of the sequence read as 0.
+  constexpr int NU = C * (KS / 8);
+  static_assert(NU <= kThreads, "one q / k unit per thread");
+  const int urow = tid / (KS / 8), uc8 = (tid % (KS / 8)) * 8;
+  const bool uld = tid < NU && urow < rv;
+  Raw8<T> rq, rk;
+  float ra[RPT];
+  auto fetch = [&](int grp) __attribute__((always_inline)) {
     const int s0 = grp * KS;
-    // log alpha of the thread's rows (0 past the end of the sequence)
-    float av[RPT];
+    if (uld) {
+      raw_load(rq, q + io + (size_t)(r0 + urow) * dk + s0 + uc8);
+      raw_load(rk, k + io + (size_t)(r0 + urow) * dk + s0 + uc8);
+    } else {
+      raw_zero(rq);
+      raw_zero(rk);
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg * RPT + i;
-      av[i] = row < rv ? la[io + (size_t)(r0 + row) * dk + s0 + ch] : 0.f;
+      ra[i] = row < rv ? la[io + (size_t)(r0 + row) * dk + s0 + ch] : 0.f;
     }
-    __syncthreads();  // previous slice's readers of qs, ks, bs, tot are done
-    for (int it = tid; it < C * (KS / 8); it += kThreads) {
-      const int row = it / (KS / 8), c8 = (it % (KS / 8)) * 8;
-      float qv[8], kv[8];
-      if (row < rv) {
-        load8(q + io + (size_t)(r0 + row) * dk + s0 + c8, qv);
-        load8(k + io + (size_t)(r0 + row) * dk + s0 + c8, kv);
-      } else {
+  };
+  fetch(0);
+  for (int grp = 0; grp < NG; ++grp) {
+    const int s0 = grp * KS;
+    const Raw8<T> cq = rq, ck = rk;
+    float av[RPT];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = kv[e] = 0.f;
+    for (int i = 0; i < RPT; ++i) av[i] = ra[i];
+    if (grp + 1 < NG) fetch(grp + 1);
+    __syncthreads();  // previous slice's readers of qs, ks, bs, tot are done
+    if (tid < NU) {
+      float qv[8], kv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qv[e] = raw_get(cq, e);
+        kv[e] = raw_get(ck, e);
       }
-      store8(qs + row * LDT + c8, qv);
-      store8(ks + row * LDT + c8, kv);
+      store8(qs + urow * LDT + uc8, qv);
+      store8(ks + urow * LDT + uc8, kv);
     }
     // chunk-local cumsum: RPT rows per thread, then the preceding groups' totals
     float run = 0.f;
