@@ -27,11 +27,18 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
 ]
+# Per-source extras.  The forward's kernels keep their MFMA accumulators in
+# ordinary VGPRs (no accumulator-register moves around every use of the
+# state); the backward's kernels are faster with the default allocation.
+EXTRA_FLAGS = {
+    "gla_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, *CFLAGS, *extra, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")

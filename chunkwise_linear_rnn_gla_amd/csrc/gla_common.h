@@ -105,6 +105,13 @@ template <typename T> __device__ inline float gexp(float x);
 template <> __device__ inline float gexp<float>(float x) { return expf(x); }
 template <> __device__ inline float gexp<bf16>(float x) { return __expf(x); }
 
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS (and scalar
+// memory) operations, then for every wave.  Unlike __syncthreads(), whose
+// release fence also waits for the wave's outstanding global stores, it does
+// not make global stores visible; use it only where the data handed over
+// lives in LDS (or was waited for explicitly, as LDS-DMA copies are).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ inline int wave_id() { return threadIdx.x / kWave; }
 

@@ -331,7 +331,7 @@ struct PBuilder {
 #pragma unroll
       for (int r = 0; r < 4; ++r) emit(jq * 16 + (l >> 4) * 4 + r, ju * 16 + (l & 15), pacc[t][r]);
     }
-    __syncthreads();
+    lds_barrier();
     for (int it = threadIdx.x; it < NRT * 256; it += NTH) {
       const int b = it >> 8, m = (it >> 4) & 15, r = it & 15;
       if (r > m) continue;

@@ -87,6 +87,11 @@ template <typename P>
 __device__ inline unsigned lds_addr(P* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) void*)p;
 }
+// Wait until at most N of this wave's global memory operations are
+// outstanding.  Loads complete in issue order, so in a wave that issues only
+// loads this waits for all but the last N.
+template <int N>
+__device__ inline void wait_vm_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory"); }
 // Wait for this wave's outstanding global memory operations (LDS copies too).
 __device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -242,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) av[i] = ra[i];
     if (grp + 1 < NG) fetch(grp + 1);
-    __syncthreads();  // previous slice's readers of qs, ks, bs, tot are done
+    lds_barrier();  // previous slice's readers of qs, ks, bs, tot are done
     if (tid < NU) {
       float qv[8], kv[8];
 #pragma unroll
@@ -261,12 +266,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
       av[i] = run;
     }
     tot[rg][ch] = run;
-    __syncthreads();
+    lds_barrier();
     float off = 0.f;
     for (int g = 0; g < rg; ++g) off += tot[g][ch];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) bs[(rg * RPT + i) * LDF + ch] = av[i] + off;
-    __syncthreads();
+    lds_barrier();
     // Q~ = Q ⊙ e^B and K~ = K ⊙ e^{b - B}, one 16-byte unit per thread each.
     // Q~ unit g of a row holds (bf16) columns 4g..4g+3 and 16+4g..16+4g+3 of
     // the group, the channels of the state rows that lane group g holds in
@@ -298,10 +303,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
     }
     PB::gates(bs, als);
     pb.offdiag(qs, ks, bs);
-    __syncthreads();
+    lds_barrier();
     pb.diag(qs, ks, als);
   }
-  __syncthreads();
+  lds_barrier();
   pb.finish(pd, [&](int m, int r, float val) {
     const T hi = from_f32<T>(val);
     ps[m * C + r] = hi;
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
       if ((m >> 4) == (r >> 4)) ls[m * 16 + (r & 15)] = from_f32<T>(val - to_f32(hi));
     }
   });
-  __syncthreads();
+  lds_barrier();
   // P as row blocks (jt, column group); unit g of a row = its EPU columns
   constexpr int PUR = C / EPU, NPG = C / KS;
   unsigned char* pr = prec + cb * C * C * RD::ES;
@@ -348,16 +353,23 @@ struct RecurLayout {
   static constexpr int VBLK = BF ? 32 * VUPR * 16 : 16 * VUPR * 16;  // bytes per V block
   static constexpr int oQ = 0, oK = oQ + QB, oP = oK + KB, oL = oP + PB, oG = oL + LB,
                        oV = oG + GB, BUF = oV + VB;
-  static constexpr int NBUF = 2 * BUF <= kLdsLimit ? 2 : 1;
-  static constexpr int VCOPY = VB / 1024, VCW = (VCOPY + NWV - 1) / NWV;  // V copies (per wave)
+  static constexpr int VCOPY = VB / 1024;       // V copies per chunk
+  static constexpr int CPC = BUF / 1024;        // copies per chunk
+  // Staging buffers: three (copies run two chunks ahead) when they fit and
+  // a chunk's copy count fits the 6-bit vmcnt field, else two, else one.
+  static constexpr int NBUF = (CPC <= 63 && 3 * BUF <= kLdsLimit) ? 3 : (2 * BUF <= kLdsLimit ? 2 : 1);
   static_assert(QB % 1024 == 0 && KB % 1024 == 0 && PB % 1024 == 0 && LB % 1024 == 0 &&
                     VB % 1024 == 0,
                 "every staged tile is a whole number of 1 KB copies");
   static_assert(BUF <= kLdsLimit, "staged chunk exceeds LDS");
 };
 
+// Waves 0 .. NWV-1 compute (16 state columns each); wave NWV only issues the
+// LDS copies and waits for them, so that its memory counter holds nothing but
+// loads (a partial wait is exact) and the computing waves, which store the
+// output, never wait on memory.
 template <typename T, int C, int DK, int NWV, int OUT>
-__global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
+__global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
     const unsigned char* __restrict__ qrec, const unsigned char* __restrict__ krec,
     const unsigned char* __restrict__ prec, const unsigned char* __restrict__ lrec,
     const float* __restrict__ grec, const T* __restrict__ v, const float* __restrict__ init,
@@ -376,17 +388,18 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
   // the wave index as a scalar: copy and column offsets derived from it stay
   // in scalar registers
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const bool loader = w == NWV;
   const int l = lane_id(), g = l >> 4, ln = l & 15;
-  const int vc = 16 * w;             // this wave's first column within the tile
-  const int col = j0 + vc + ln;      // this lane's state column
+  const int vc = 16 * (loader ? 0 : w);  // this wave's first column within the tile
+  const int col = j0 + vc + ln;          // this lane's state column
   const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks);
 
   // ---- state slice: lane holds S[16 a + 4 g + r][col]
   floatx4 S[NKT];
   {
     const float* src = nullptr;
-    if (OUT) src = NSEG > 1 ? init + ((size_t)bh * NSEG + seg) * DK * dv
-                            : (init ? init + (size_t)bh * DK * dv : nullptr);
+    if (OUT && !loader) src = NSEG > 1 ? init + ((size_t)bh * NSEG + seg) * DK * dv
+                                       : (init ? init + (size_t)bh * DK * dv : nullptr);
 #pragma unroll
     for (int a = 0; a < NKT; ++a) {
       S[a] = zero4();
@@ -401,53 +414,47 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
 #pragma unroll
   for (int i = 0; i < NGS; ++i) gsum[i] = 0.f;
 
-  // ---- V copies: per-lane (row, byte column) of each of this wave's copies
-  int vrow[Lay::VCW], vcolb[Lay::VCW];
-  unsigned vrow_off[Lay::VCW];
-#pragma unroll
-  for (int i = 0; i < Lay::VCW; ++i) {
-    const int c = w + i * NWV;
+  // ---- V copies: the tile row and 16-byte unit that lane l's slot of copy c
+  // holds
+  auto vslot = [&](int c, int& rho, int& u) __attribute__((always_inline)) {
     const int s = c * 64 + l;
-    int rho, u, blk;
     if constexpr (BF) {
-      blk = s / (32 * VUPR);
+      const int blk = s / (32 * VUPR);
       const int lg = run_slot<VUPR>((s % (32 * VUPR)) / VUPR, s % VUPR);
       rho = blk * 32 + lg / VUPR;
       u = lg % VUPR;
     } else {
-      blk = s / (16 * VUPR);
+      const int blk = s / (16 * VUPR);
       const int lg = scal_slot<VUPR>((s % (16 * VUPR)) / VUPR, s % VUPR);
       rho = blk * 16 + lg / VUPR;
       u = lg % VUPR;
     }
-    vrow[i] = rho;
-    vcolb[i] = u * 16;
-    vrow_off[i] = (unsigned)(rho * dv * ES + u * 16);
-  }
+  };
 
   const unsigned lds0 = lds_addr(lds);
-  auto issue = [&](int n, int b) {
+  // Stage chunk n into buffer b (the loading wave only).
+  auto issue = [&](int n, int b) __attribute__((always_inline)) {
     const unsigned base = lds0 + (unsigned)(b * Lay::BUF);
     const size_t cb = (size_t)bh * NC + n;
     if constexpr (OUT) {
-      copy_tile<Lay::QB / 1024, NWV>(qrec + cb * Lay::QB, base + Lay::oQ, w, l);
-      copy_tile<Lay::PB / 1024, NWV>(prec + cb * Lay::PB, base + Lay::oP, w, l);
-      if constexpr (BF) copy_tile<Lay::LB / 1024, NWV>(lrec + cb * Lay::LB, base + Lay::oL, w, l);
+      copy_tile<Lay::QB / 1024, 1>(qrec + cb * Lay::QB, base + Lay::oQ, 0, l);
+      copy_tile<Lay::PB / 1024, 1>(prec + cb * Lay::PB, base + Lay::oP, 0, l);
+      if constexpr (BF) copy_tile<Lay::LB / 1024, 1>(lrec + cb * Lay::LB, base + Lay::oL, 0, l);
     }
-    copy_tile<Lay::KB / 1024, NWV>(krec + cb * Lay::KB, base + Lay::oK, w, l);
-    copy_tile<Lay::GB / 1024, NWV>(reinterpret_cast<const unsigned char*>(grec) + cb * Lay::GB,
-                                   base + Lay::oG, w, l);
+    copy_tile<Lay::KB / 1024, 1>(krec + cb * Lay::KB, base + Lay::oK, 0, l);
+    copy_tile<Lay::GB / 1024, 1>(reinterpret_cast<const unsigned char*>(grec) + cb * Lay::GB,
+                                 base + Lay::oG, 0, l);
     // V rows past the end of the sequence repeat the last row (their K~ rows
     // and P columns are zero)
     const int r0 = n * C;
     const i32x4 vr = make_rsrc(v + ((size_t)bh * L + r0) * dv + j0);
     const bool full = r0 + C <= L;
 #pragma unroll
-    for (int i = 0; i < Lay::VCW; ++i) {
-      const int c = w + i * NWV;
-      if (Lay::VCOPY % NWV != 0 && c >= Lay::VCOPY) break;
-      const unsigned vo = full ? vrow_off[i] : (unsigned)(min(vrow[i], L - 1 - r0) * dv * ES + vcolb[i]);
-      dma16b(vr, vo, 0u, base + (unsigned)(Lay::oV + c * 1024));
+    for (int c = 0; c < Lay::VCOPY; ++c) {
+      int rho, u;
+      vslot(c, rho, u);
+      if (!full) rho = min(rho, L - 1 - r0);
+      dma16b(vr, (unsigned)(rho * dv * ES + u * 16), 0u, base + (unsigned)(Lay::oV + c * 1024));
     }
   };
 
@@ -473,7 +480,7 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
 
   // One chunk from buffer b: O^T of the chunk into ot (stored by the caller
   // once the next copies are issued), then the state update.
-  auto body = [&](int n, int b, floatx4 (&ot)[NRT]) {
+  auto body = [&](int n, int b, floatx4 (&ot)[NRT]) __attribute__((always_inline)) {
     const unsigned char* base = lds + b * Lay::BUF;
     const unsigned char* Qs = base + Lay::oQ;
     const unsigned char* Ks = base + Lay::oK;
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
     }
   };
 
-  auto store_out = [&](int n, const floatx4 (&ot)[NRT]) {
+  auto store_out = [&](int n, const floatx4 (&ot)[NRT]) __attribute__((always_inline)) {
     if constexpr (OUT) {
       const int rv = min(C, L - n * C);
       T* orow = o + ((size_t)bh * L + n * C + ln) * dv + j0 + vc + 4 * g;
@@ -604,41 +611,62 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
     }
   };
 
-  // ---- walk the segment's chunks.  Per chunk: compute from its buffer,
-  // then wait for the next chunk's copies (issued a chunk earlier) and for
-  // the previous chunk's stores, barrier, issue the copies of the chunk after
-  // next into the buffer just released, and only then store this chunk's
-  // output, so that its stores complete during the next chunk's compute.
-  // Buffer indices are literals at every body call.
+  // ---- walk the segment's chunks.  Chunk n + D (D = NBUF - 1) is staged into
+  // the buffer that chunk n - 1 used while chunk n computes; before the
+  // chunk's closing barrier the loading wave waits until chunk n + 1 has
+  // landed (with D = 2 the copies of chunk n + 2 may still be in flight).
+  // The computing waves store each chunk's output as soon as it is computed.
+  // Buffer indices are literals at every step call.
+  constexpr int D = Lay::NBUF - 1;
   floatx4 ot[NRT];
-  if constexpr (Lay::NBUF == 2) {
-    if (nb < ne) issue(nb, 0);
-    if (nb + 1 < ne) issue(nb + 1, 1);
-    wait_vm();
-    __syncthreads();
-    for (int n = nb; n < ne; n += 2) {
-      body(n, 0, ot);
+  auto wait_through = [&](int m) __attribute__((always_inline)) {  // chunk m landed
+    if constexpr (D == 2) {
+      if (m + 1 < ne) wait_vm_le<Lay::CPC>();
+      else wait_vm();
+    } else {
       wait_vm();
-      __syncthreads();  // chunk n + 1 staged; every wave is done with buffer 0
-      if (n + 2 < ne) issue(n + 2, 0);
-      store_out(n, ot);
-      if (n + 1 < ne) {
-        body(n + 1, 1, ot);
-        wait_vm();
-        __syncthreads();  // chunk n + 2 staged; every wave is done with buffer 1
-        if (n + 3 < ne) issue(n + 3, 1);
-        store_out(n + 1, ot);
-      }
     }
-  } else {
-    if (nb < ne) issue(nb, 0);
-    for (int n = nb; n < ne; ++n) {
-      wait_vm();
-      __syncthreads();  // chunk n staged
-      body(n, 0, ot);
-      __syncthreads();  // every wave is done with the buffer
-      if (n + 1 < ne) issue(n + 1, 0);
-      store_out(n, ot);
+  };
+  auto step = [&](int n, int b) __attribute__((always_inline)) {
+    if constexpr (D > 0) {
+      if (loader) {
+        if (n + D < ne) issue(n + D, (b + D) % Lay::NBUF);
+        if (n + 1 < ne) wait_through(n + 1);
+      } else {
+        body(n, b, ot);
+        store_out(n, ot);
+      }
+      lds_barrier();  // chunk n + 1 staged; everyone is done with buffer b
+    } else {
+      if (!loader) {
+        body(n, 0, ot);
+        store_out(n, ot);
+      }
+      lds_barrier();  // everyone is done with the buffer
+      if (loader && n + 1 < ne) {
+        issue(n + 1, 0);
+        wait_vm();
+      }
+      lds_barrier();  // chunk n + 1 staged
+    }
+  };
+
+  if (nb < ne) {
+    if (loader) {
+#pragma unroll
+      for (int i = 0; i < (D > 0 ? D : 1); ++i)
+        if (nb + i < ne) issue(nb + i, i);
+      wait_through(nb);
+    }
+    lds_barrier();  // chunk nb staged
+  }
+  for (int n = nb; n < ne; n += Lay::NBUF) {
+    step(n, 0);
+    if constexpr (Lay::NBUF >= 2) {
+      if (n + 1 < ne) step(n + 1, 1);
+    }
+    if constexpr (Lay::NBUF == 3) {
+      if (n + 2 < ne) step(n + 2, 2);
     }
   }
 
@@ -646,13 +674,13 @@ __global__ __launch_bounds__(NWV * kWave) void k_chunk_recur(
   float* dst = nullptr;
   if (OUT) dst = (NSEG == 1 && fin) ? fin + (size_t)bh * DK * dv : nullptr;
   else dst = fin + ((size_t)bh * NSEG + seg) * DK * dv;
-  if (dst) {
+  if (dst && !loader) {
 #pragma unroll
     for (int a = 0; a < NKT; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(size_t)(a * 16 + 4 * g + r) * dv + col] = S[a][r];
   }
-  if (!OUT && tile == 0) {
+  if (!OUT && tile == 0 && !loader) {
 #pragma unroll
     for (int i = 0; i < NGS; ++i) {
       const int t = threadIdx.x + i * NTH;
@@ -692,11 +720,11 @@ static hipError_t launch_recur_w(const Plan& p, int out, const void* qg, const v
   const unsigned char *q8 = (const unsigned char*)qg, *k8 = (const unsigned char*)kg,
                       *p8 = (const unsigned char*)ph, *l8 = (const unsigned char*)pl;
   if (out)
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1>), grid, dim3(NWV * kWave), 0, s, q8, k8,
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1>), grid, dim3((NWV + 1) * kWave), 0, s, q8, k8,
                        p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
                        p.NSEGR, p.segr_chunks);
   else
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0>), grid, dim3(NWV * kWave), 0, s, q8, k8,
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0>), grid, dim3((NWV + 1) * kWave), 0, s, q8, k8,
                        p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
                        p.NSEGR, p.segr_chunks);
   return hipGetLastError();
