@@ -155,6 +155,24 @@ template <> __device__ inline void store_unit<float>(unsigned char* p, const flo
   *reinterpret_cast<f32x4*>(p) = a;
 }
 
+// Copy one 16-byte unit of T from LDS to global memory, with element e
+// replaced by 0 where e > last (last < 0: all zero, without reading).
+template <typename T>
+__device__ inline void store_masked(unsigned char* dst, const T* src, int last) {
+  constexpr int EPU = 16 / (int)sizeof(T);
+  f32x4 val = f32x4{};
+  if (last >= 0) {
+    val = *reinterpret_cast<const f32x4*>(src);
+    if (last < EPU - 1) {
+      T* e = reinterpret_cast<T*>(&val);
+#pragma unroll
+      for (int i = 0; i < EPU; ++i)
+        if (i > last) e[i] = from_f32<T>(0.f);
+    }
+  }
+  *reinterpret_cast<f32x4*>(dst) = val;
+}
+
 // Issue copies [w, w + NWV, ...) < NCOPY of a contiguous tile: copy c moves the
 // 1 KB at src + 1024 c into LDS at dst + 1024 c.
 template <int NCOPY, int NWV>
@@ -172,8 +190,12 @@ __device__ inline void copy_tile(const unsigned char* src, unsigned dst, int w, 
 }  // namespace
 
 // =========================================================== pass 1: chunk prep
+// LDS per workgroup stays under a quarter of the CU's 160 KB and registers
+// under 128 per lane, so that four workgroups (one wave per SIMD each) are
+// resident per CU: the usual grid (one workgroup per chunk, a few per CU) then
+// runs in a single round.
 template <typename T, int C>
-__global__ __launch_bounds__(kThreads) void k_chunk_prep(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_chunk_prep(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ la,
     unsigned char* __restrict__ qrec, unsigned char* __restrict__ krec,
     unsigned char* __restrict__ prec, unsigned char* __restrict__ lrec,
@@ -189,15 +211,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
   constexpr int RG = kThreads / KS;  // row groups of the slice cumsum
   constexpr int RPT = C / RG;        // rows per thread
   static_assert(RPT >= 1 && C % RG == 0, "cumsum row split");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[PB::SLICE_BYTES];
-  __shared__ float pd[4][16][17];
+  // The slice arrays (qs, ks, bs, als) are dead after the last slice; the
+  // P staging (ps), the diagonal low parts (ls) and the diagonal partial sums
+  // (pd) then reuse their space.
+  constexpr int PS_BYTES = C * C * (int)sizeof(T);
+  constexpr int LS_BYTES = BF ? C * 16 * (int)sizeof(T) : 0;
+  constexpr int PD_BYTES = 4 * 16 * 17 * 4;
+  constexpr int TAIL_BYTES = PS_BYTES + LS_BYTES + PD_BYTES;
+  constexpr int SMEM_BYTES = PB::SLICE_BYTES > TAIL_BYTES ? PB::SLICE_BYTES : TAIL_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
   __shared__ float tot[RG][KS];
-  __shared__ __attribute__((aligned(16))) T ps[C * C];
-  __shared__ __attribute__((aligned(16))) T ls[BF ? C * 16 : EPU];
   float* qs = reinterpret_cast<float*>(smem);
   float* ks = qs + C * LDT;
   float* bs = ks + C * LDT;
   float* als = bs + C * LDF;
+  T* ps = reinterpret_cast<T*>(smem);
+  T* ls = reinterpret_cast<T*>(smem + PS_BYTES);
+  auto pd = reinterpret_cast<float(*)[16][17]>(smem + PS_BYTES + LS_BYTES);
 
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int r0 = n * C, rv = min(C, L - r0);
@@ -207,10 +237,6 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
   unsigned char* qr = qrec + cb * C * dk * RD::ES;
   unsigned char* kr = krec + cb * C * dk * RD::ES;
   float* gr = grec + cb * (RD::gbytes(dk) / 4);
-
-  for (int it = tid; it < C * C; it += kThreads) ps[it] = from_f32<T>(0.f);
-  if constexpr (BF)
-    for (int it = tid; it < C * 16; it += kThreads) ls[it] = from_f32<T>(0.f);
 
   PB pb;
   pb.init();
@@ -222,13 +248,21 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
   static_assert(NU <= kThreads, "one q / k unit per thread");
   const int urow = tid / (KS / 8), uc8 = (tid % (KS / 8)) * 8;
   const bool uld = tid < NU && urow < rv;
+  // chunk-uniform bases and 32-bit per-thread offsets (one address register
+  // per lane instead of a 64-bit pointer per load)
+  const size_t cbase = io + (size_t)r0 * dk;
+  const T* qc = q + cbase;
+  const T* kc = k + cbase;
+  const float* lc = la + cbase;
+  const unsigned uoff = (unsigned)(urow * dk + uc8);
+  const unsigned aoff = (unsigned)(rg * RPT * dk + ch);
   Raw8<T> rq, rk;
   float ra[RPT];
   auto fetch = [&](int grp) __attribute__((always_inline)) {
-    const int s0 = grp * KS;
+    const unsigned s0 = (unsigned)(grp * KS);
     if (uld) {
-      raw_load(rq, q + io + (size_t)(r0 + urow) * dk + s0 + uc8);
-      raw_load(rk, k + io + (size_t)(r0 + urow) * dk + s0 + uc8);
+      raw_load(rq, qc + (uoff + s0));
+      raw_load(rk, kc + (uoff + s0));
     } else {
       raw_zero(rq);
       raw_zero(rk);
@@ -236,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg * RPT + i;
-      ra[i] = row < rv ? la[io + (size_t)(r0 + row) * dk + s0 + ch] : 0.f;
+      ra[i] = row < rv ? lc[aoff + (unsigned)(i * dk) + s0] : 0.f;
     }
   };
   fetch(0);
@@ -306,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
     lds_barrier();
     pb.diag(qs, ks, als);
   }
-  lds_barrier();
+  lds_barrier();  // the slice arrays are dead from here on
   pb.finish(pd, [&](int m, int r, float val) {
     const T hi = from_f32<T>(val);
     ps[m * C + r] = hi;
@@ -315,21 +349,22 @@ __global__ __launch_bounds__(kThreads) void k_chunk_prep(
     }
   });
   lds_barrier();
-  // P as row blocks (jt, column group); unit g of a row = its EPU columns
+  // P as row blocks (jt, column group); unit g of a row = its EPU columns.
+  // Entries above the diagonal were never written to ps: they are stored as
+  // 0 here.
   constexpr int PUR = C / EPU, NPG = C / KS;
   unsigned char* pr = prec + cb * C * C * RD::ES;
   for (int it = tid; it < C * PUR; it += kThreads) {
     const int row = it / PUR, uu = it % PUR;
-    const f32x4 val = *reinterpret_cast<const f32x4*>(&ps[row * C + uu * EPU]);
-    *reinterpret_cast<f32x4*>(pr + ((row >> 4) * NPG + (uu >> 2)) * 1024 +
-                              row_slot(row & 15, uu & 3) * 16) = val;
+    store_masked<T>(pr + ((row >> 4) * NPG + (uu >> 2)) * 1024 + row_slot(row & 15, uu & 3) * 16,
+                    &ps[row * C + uu * EPU], row - uu * EPU);
   }
   if constexpr (BF) {
     unsigned char* lr = lrec + cb * C * 16 * RD::ES;
     for (int it = tid; it < C * 2; it += kThreads) {
       const int row = it >> 1, gd = it & 1;
-      const f32x4 val = *reinterpret_cast<const f32x4*>(&ls[row * 16 + 8 * gd]);
-      *reinterpret_cast<f32x4*>(lr + (row >> 4) * 512 + lo_slot(row & 15, gd) * 16) = val;
+      store_masked<T>(lr + (row >> 4) * 512 + lo_slot(row & 15, gd) * 16,
+                      &ls[row * 16 + 8 * gd], (row & 15) - 8 * gd);
     }
   }
 }
