@@ -560,8 +560,10 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
             const bf16x8 pf = *reinterpret_cast<const bf16x8*>(Ps + (jt * NPG + kt) * 1024 + qoff);
             ot[jt] = Mma<bf16>::run(vf[kt], pf, ot[jt]);
           }
-          bf16x8 lf = bf16x8{};
-          if ((g >> 1) == (jt & 1)) lf = *reinterpret_cast<const bf16x8*>(Ls + jt * 512 + loff);
+          // every lane reads (a branch would force a wait for the read), the
+          // lanes whose K range is not this block's diagonal drop the value
+          bf16x8 lf = *reinterpret_cast<const bf16x8*>(Ls + jt * 512 + loff);
+          if ((g >> 1) != (jt & 1)) lf = bf16x8{};
           ot[jt] = Mma<bf16>::run(vf[jt >> 1], lf, ot[jt]);
         }
       }
@@ -653,7 +655,19 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
   // The computing waves store each chunk's output as soon as it is computed.
   // Buffer indices are literals at every step call.
   constexpr int D = Lay::NBUF - 1;
-  floatx4 ot[NRT];
+  // ot: the chunk being computed; op: the previous chunk's output, stored
+  // after the next chunk's products are issued so that the stores never wait
+  // for the matrix pipeline
+  floatx4 ot[NRT], op[NRT];
+  int pn = -1;
+  auto store_prev = [&]() __attribute__((always_inline)) {
+    if (pn >= 0) store_out(pn, op);
+  };
+  auto keep = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jt = 0; jt < NRT; ++jt) op[jt] = ot[jt];
+    pn = n;
+  };
   auto wait_through = [&](int m) __attribute__((always_inline)) {  // chunk m landed
     if constexpr (D == 2) {
       if (m + 1 < ne) wait_vm_le<Lay::CPC>();
@@ -669,13 +683,15 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
         if (n + 1 < ne) wait_through(n + 1);
       } else {
         body(n, b, ot);
-        store_out(n, ot);
+        store_prev();
+        keep(n);
       }
       lds_barrier();  // chunk n + 1 staged; everyone is done with buffer b
     } else {
       if (!loader) {
         body(n, 0, ot);
-        store_out(n, ot);
+        store_prev();
+        keep(n);
       }
       lds_barrier();  // everyone is done with the buffer
       if (loader && n + 1 < ne) {
@@ -704,6 +720,8 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
       if (n + 2 < ne) step(n + 2, 2);
     }
   }
+
+  if (!loader) store_prev();
 
   // ---- end of the segment
   float* dst = nullptr;
