@@ -31,7 +31,11 @@ CFLAGS = [
 # ordinary VGPRs (no accumulator-register moves around every use of the
 # state); the backward's kernels are faster with the default allocation.
 EXTRA_FLAGS = {
-    "gla_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gla_prep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the recurrence's chunk body is one long block of LDS reads and MFMAs;
+    # the ILP-oriented scheduler interleaves them far better than the default
+    # occupancy-oriented one (one wave per SIMD runs there anyway)
+    "gla_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 

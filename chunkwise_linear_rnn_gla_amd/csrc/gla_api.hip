@@ -52,7 +52,7 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   const char* env = getenv("GLA_FORWARD");
   const bool want_fused = env && strcmp(env, "fused") == 0;
   const bool want_mat = env && strcmp(env, "materialized") == 0;
-  P.recur = !want_fused && !want_mat && recur_supported(bf16, C, dk, dv);
+  P.recur = !want_fused && !want_mat && recur_supported(bf16, C, dk, dv, L);
   P.fused = !P.recur && !want_mat && fused_supported(bf16, C, dk, dv);
   P.DVTF = fused_dv_tile(bf16, dk, dv);
   P.NSEGF = 1;
@@ -67,16 +67,16 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   // Recurrence: 16 state columns per wave; the largest workgroup that still
   // gives 256 workgroups, and sequence segments when even one wave per
   // workgroup leaves the chip mostly idle.
-  const int wmin = recur_min_waves(bf16, dk);
+  const int wmin = recur_min_waves(bf16, dk), wmax = recur_max_waves(bf16, dk);
   P.NWVR = wmin;
-  for (int w = 4; w >= wmin; w /= 2) {
+  for (int w = wmax; w >= wmin; w /= 2) {
     if (dv % (16 * w)) continue;
     P.NWVR = w;
     if ((int64_t)P.BH * (dv / (16 * w)) >= 256) break;
   }
   if (const char* e = getenv("GLA_RECUR_WAVES")) {
     const int w = atoi(e);
-    if ((w == 1 || w == 2 || w == 4) && w >= wmin && dv % (16 * w) == 0) P.NWVR = w;
+    if ((w == 1 || w == 2 || w == 4) && w >= wmin && w <= wmax && dv % (16 * w) == 0) P.NWVR = w;
   }
   P.NSEGR = 1;
   P.segr_chunks = P.NC > 0 ? P.NC : 1;

@@ -86,7 +86,10 @@ hipError_t launch_seg_output(const Plan& p, const void* q, const void* k, const 
 // 16 columns of a 256-channel bf16 or 128-channel fp32 state leave too few
 // registers for the operands.
 constexpr int recur_min_waves(bool bf16, int dk) { return (bf16 ? dk >= 256 : dk >= 128) ? 2 : 1; }
-bool recur_supported(int bf16, int C, int dk, int dv);
+// ... and at most: with four computing waves and the loading wave, a
+// 256-channel bf16 state slice leaves too few registers.
+constexpr int recur_max_waves(bool bf16, int dk) { return (bf16 && dk >= 256) ? 2 : 4; }
+bool recur_supported(int bf16, int C, int dk, int dv, int L);
 // Per (batch-head, chunk) records, in the fragment-blocked layouts of
 // gla_recur.hip: Q~ = Q ⊙ e^B and K~ = K ⊙ e^{b - B} (C x dk each, rows past
 // the sequence zero), the chunk's gated score matrix P (C x C) and, for bf16,

@@ -1,30 +1,21 @@
-// gla_recur.hip -- two-pass forward of the GLA chunkwise layer (gfx950).
+// gla_recur.hip -- pass 2 of the two-pass forward of the GLA chunkwise layer
+// (gfx950).
 //
-// Pass 1, k_chunk_prep: one workgroup per (batch-head, chunk), all chunks in
-// parallel.  From q, k and log alpha of the chunk it forms
-//   B      = chunk-local inclusive cumsum of log alpha  (per key channel)
-//   Q~     = Q ⊙ e^{B}            (rows of the chunk, I/O type)
-//   K~     = K ⊙ e^{b - B}        (b = B at the chunk's last row)
-//   b      = the chunk's total log decay
-//   P      = the causal gated score matrix of the chunk (gla_pblock.h):
-//            P[m][r] = sum_k q_mk k_rk e^{B_mk - B_rk}, r <= m
-// (papercache.org notes §4.2 chunkwise form with Lambda, Gamma, gamma; §4.3 /
-// Figure 3 for P).  For bf16 I/O, P is stored rounded to bf16 plus the low
-// part of its diagonal 16 x 16 blocks.
-//
-// Pass 2, k_chunk_recur: one workgroup per (batch-head, sequence segment,
-// d_v tile), walking the segment's chunks in order with its d_k x d_v_tile
-// slice of the state in MFMA accumulators (fp32):
+// k_chunk_recur: one workgroup per (batch-head, sequence segment, d_v tile),
+// walking the segment's chunks in order with its d_k x d_v_tile slice of the
+// state in MFMA accumulators (fp32):
 //   O[n]^T = S_{n-1}^T Q~^T + V^T P^T                 (output, transposed)
 //   S_n    = diag(e^{b_n}) S_{n-1} + K~^T V           (state)
-// (notes §4.2; §3.3 / Figure 1a keeps the state on chip).  Every chunk's
-// Q~, K~, P, b and V tile stream into LDS with LDS-DMA (global_load_lds)
-// while the previous chunk computes; each wave owns 16 state columns.  In
-// its local mode (no output) the same walk starts from zero and leaves each
-// segment's own state contribution and total log decay for the segment scan.
+// (papercache.org notes §4.2; §3.3 / Figure 1a keeps the state on chip).
+// Every chunk's Q~, K~, P, b (written by pass 1, gla_prep.hip, in the layouts
+// of gla_records.h) and V tile stream into LDS with LDS-DMA while the
+// previous chunk computes; each wave owns 16 state columns.  In its local mode
+// (no output) the same walk starts from zero and leaves each segment's own
+// state contribution and total log decay for the segment scan.
 #include "gla_common.h"
 #include "gla_internal.h"
 #include "gla_pblock.h"
+#include "gla_records.h"
 
 namespace gla {
 
@@ -47,22 +38,16 @@ __device__ inline bf16x8 join8(bf16x4 a, bf16x4 b) {
   return r;
 }
 
-// Asynchronous global -> LDS copy of one 16-byte unit per lane: lane i of the
-// wave writes LDS bytes [lds_wave_base + 16 i, + 16).  lds_wave_base must be
-// the same for the whole wave.
-__device__ inline void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16,
-                                   0, 0);
-}
-// The same through a buffer resource: 16 bytes at rsrc base + soff + voff
-// (voff per lane, soff wave-uniform) into LDS at lds_wave_base + 16 * lane.
+// Asynchronous global -> LDS copy through a buffer resource: 16 bytes at
+// rsrc base + soff + voff (voff per lane, soff wave-uniform) into LDS at
+// lds_wave_base + 16 * lane.
 // The copy is issued from inline assembly: the instruction writes no
 // register, and the compiler, which cannot tell which LDS bytes a copy
 // writes, would otherwise wait for every outstanding copy (including the
 // prefetch of a later chunk) before the next LDS read.  Completion is waited
 // for explicitly (wait_vm) before a staged buffer is read.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 __device__ inline i32x4 make_rsrc(const void* base) {
   // raw buffer: stride 0, range 2 GiB, 32-bit data format
   const unsigned long long a = (unsigned long long)base;
@@ -95,279 +80,26 @@ __device__ inline void wait_vm_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N
 // Wait for this wave's outstanding global memory operations (LDS copies too).
 __device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// ---- fragment-blocked layouts ---------------------------------------------
-// chunk_prep writes each chunk's Q~, K~, P (and P's diagonal low parts) as
-// blocks of 16-byte units laid out the way the recurrence's MFMA operand
-// reads want them, so that chunk_recur stages a chunk with contiguous
-// 1 KB copies and reads every operand at a lane-constant LDS offset.  The
-// unit orders below are involutions (applying one twice gives the identity),
-// chosen so that each operand read is free of LDS bank conflicts (64 banks of
-// 4 bytes; one 256-byte bank span per pass).
-//
-// Row block (Q~, P): 16 rows x 4 units.  A 16x16 MFMA operand read has lane
-// (g, n) load unit g of row n; the 16 lanes of one g then cover 16 distinct
-// units of a 256-byte span.
-__device__ inline int row_slot(int n, int g) { return n * 4 + (g ^ ((n >> 2) & 3)); }
-// Diagonal-block low part (bf16): 16 rows x 2 units (columns 0-7, 8-15).
-__device__ inline int lo_slot(int n, int gd) { return n * 2 + (gd ^ ((n >> 3) & 1)); }
-// Token-run block (bf16, transposed reads): 32 rows x UPR units.  A
-// ds_read_b64_tr_b16 operand read touches rows 8 g + j (+ 4), j < 4, 32 bytes
-// each; half a wave (g = 0, 1) then covers 8 distinct 32-byte windows.
-template <int UPR>
-__device__ inline int run_slot(int rho, int u) {
-  int m;
-  if constexpr (UPR == 2) m = ((rho >> 3) & 1) << 3;
-  else if constexpr (UPR == 4) m = ((rho >> 3) & 1) << 1;
-  else m = (((rho >> 1) & 1) | (((rho >> 3) & 1) << 1)) << 1;
-  return (rho * UPR + u) ^ m;
-}
-// Scalar-read block (fp32): 16 rows x UPR units.  A 16x16x4 operand read has
-// lane group g read row 4 g + i (fixed i), 64 bytes; the XOR puts the four
-// rows in distinct 64-byte windows of a 256-byte span.
-template <int UPR>
-__device__ inline int scal_slot(int rho, int u) { return (rho * UPR + u) ^ (((rho >> 2) & 3) << 2); }
-
-// Per-chunk record sizes (bytes).  GW: elements per 64-byte column group
-// (one unit of 4 per row of a row block).
-template <typename T>
-struct RecDims {
-  static constexpr int ES = (int)sizeof(T);
-  static constexpr bool BF = ES == 2;
-  static constexpr int EPU = 16 / ES;
-  static constexpr int GW = 64 / ES;
-  __host__ __device__ static constexpr int gbytes(int dk) { return ((8 * dk + 1023) / 1024) * 1024; }
-};
-
-constexpr int kLdsLimit = 160 * 1024;
-
-// Store one 16-byte unit of EPU values rounded to T.
-template <typename T> __device__ inline void store_unit(unsigned char* p, const float* x);
-template <> __device__ inline void store_unit<bf16>(unsigned char* p, const float* x) {
-  bf16x8 a;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] = static_cast<bf16>(x[e]);
-  *reinterpret_cast<bf16x8*>(p) = a;
-}
-template <> __device__ inline void store_unit<float>(unsigned char* p, const float* x) {
-  f32x4 a;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) a[e] = x[e];
-  *reinterpret_cast<f32x4*>(p) = a;
-}
-
-// Copy one 16-byte unit of T from LDS to global memory, with element e
-// replaced by 0 where e > last (last < 0: all zero, without reading).
-template <typename T>
-__device__ inline void store_masked(unsigned char* dst, const T* src, int last) {
-  constexpr int EPU = 16 / (int)sizeof(T);
-  f32x4 val = f32x4{};
-  if (last >= 0) {
-    val = *reinterpret_cast<const f32x4*>(src);
-    if (last < EPU - 1) {
-      T* e = reinterpret_cast<T*>(&val);
-#pragma unroll
-      for (int i = 0; i < EPU; ++i)
-        if (i > last) e[i] = from_f32<T>(0.f);
-    }
-  }
-  *reinterpret_cast<f32x4*>(dst) = val;
-}
-
-// Issue copies [w, w + NWV, ...) < NCOPY of a contiguous tile: copy c moves the
+// Loading wave li of NLD issues copies li, li + NLD, ... of a contiguous tile
+// of NCOPY copies (all NLD waves issue a one-copy tile); copy c moves the
 // 1 KB at src + 1024 c into LDS at dst + 1024 c.
-template <int NCOPY, int NWV>
-__device__ inline void copy_tile(const unsigned char* src, unsigned dst, int w, int l) {
+template <int NCOPY, int NLD>
+__device__ inline void copy_tile(const unsigned char* src, unsigned dst, int li, int l) {
+  static_assert(NCOPY <= 1 || NCOPY % NLD == 0, "uneven split");
   const i32x4 r = make_rsrc(src);
   const unsigned loff = (unsigned)l * 16u;
+  if constexpr (NCOPY == 1) {
+    dma16b(r, loff, 0u, dst);
+  } else {
 #pragma unroll
-  for (int i = 0; i < (NCOPY + NWV - 1) / NWV; ++i) {
-    const int c = w + i * NWV;
-    if (NCOPY % NWV != 0 && c >= NCOPY) break;
-    dma16b(r, loff, (unsigned)c * 1024u, dst + (unsigned)c * 1024u);
+    for (int i = 0; i < NCOPY / NLD; ++i) {
+      const int c = li + i * NLD;
+      dma16b(r, loff, (unsigned)c * 1024u, dst + (unsigned)c * 1024u);
+    }
   }
 }
 
 }  // namespace
-
-// =========================================================== pass 1: chunk prep
-// LDS per workgroup stays under a quarter of the CU's 160 KB and registers
-// under 128 per lane, so that four workgroups (one wave per SIMD each) are
-// resident per CU: the usual grid (one workgroup per chunk, a few per CU) then
-// runs in a single round.
-template <typename T, int C>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_chunk_prep(
-    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ la,
-    unsigned char* __restrict__ qrec, unsigned char* __restrict__ krec,
-    unsigned char* __restrict__ prec, unsigned char* __restrict__ lrec,
-    float* __restrict__ grec, int L, int dk, int NC) {
-  // q, k slices staged in fp32: the diagonal blocks' vector-ALU reads and the
-  // scaled MFMA operands then need no conversion
-  using PB = PBuilder<T, C, 4, float>;
-  using RD = RecDims<T>;
-  constexpr bool BF = PB::BF;
-  constexpr int KS = PB::KS, LDT = PB::LDT, LDF = PB::LDF;
-  constexpr int EPU = RD::EPU;
-  static_assert(KS == RD::GW, "one d_k slice is one column group");
-  constexpr int RG = kThreads / KS;  // row groups of the slice cumsum
-  constexpr int RPT = C / RG;        // rows per thread
-  static_assert(RPT >= 1 && C % RG == 0, "cumsum row split");
-  // The slice arrays (qs, ks, bs, als) are dead after the last slice; the
-  // P staging (ps), the diagonal low parts (ls) and the diagonal partial sums
-  // (pd) then reuse their space.
-  constexpr int PS_BYTES = C * C * (int)sizeof(T);
-  constexpr int LS_BYTES = BF ? C * 16 * (int)sizeof(T) : 0;
-  constexpr int PD_BYTES = 4 * 16 * 17 * 4;
-  constexpr int TAIL_BYTES = PS_BYTES + LS_BYTES + PD_BYTES;
-  constexpr int SMEM_BYTES = PB::SLICE_BYTES > TAIL_BYTES ? PB::SLICE_BYTES : TAIL_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
-  __shared__ float tot[RG][KS];
-  float* qs = reinterpret_cast<float*>(smem);
-  float* ks = qs + C * LDT;
-  float* bs = ks + C * LDT;
-  float* als = bs + C * LDF;
-  T* ps = reinterpret_cast<T*>(smem);
-  T* ls = reinterpret_cast<T*>(smem + PS_BYTES);
-  auto pd = reinterpret_cast<float(*)[16][17]>(smem + PS_BYTES + LS_BYTES);
-
-  const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int r0 = n * C, rv = min(C, L - r0);
-  const int NG = dk / KS;                                     // column groups per row
-  const size_t io = (size_t)bh * L * dk;                      // q, k, log alpha
-  const size_t cb = (size_t)bh * NC + n;                      // chunk id
-  unsigned char* qr = qrec + cb * C * dk * RD::ES;
-  unsigned char* kr = krec + cb * C * dk * RD::ES;
-  float* gr = grec + cb * (RD::gbytes(dk) / 4);
-
-  PB pb;
-  pb.init();
-  const int ch = tid % KS, rg = tid / KS;
-  // The next slice's q, k (one 8-element unit each per thread) and log alpha
-  // (RPT rows of one channel per thread) are loaded into registers while the
-  // current slice is processed.  Rows past the end of the sequence read as 0.
-  constexpr int NU = C * (KS / 8);
-  static_assert(NU <= kThreads, "one q / k unit per thread");
-  const int urow = tid / (KS / 8), uc8 = (tid % (KS / 8)) * 8;
-  const bool uld = tid < NU && urow < rv;
-  // chunk-uniform bases and 32-bit per-thread offsets (one address register
-  // per lane instead of a 64-bit pointer per load)
-  const size_t cbase = io + (size_t)r0 * dk;
-  const T* qc = q + cbase;
-  const T* kc = k + cbase;
-  const float* lc = la + cbase;
-  const unsigned uoff = (unsigned)(urow * dk + uc8);
-  const unsigned aoff = (unsigned)(rg * RPT * dk + ch);
-  Raw8<T> rq, rk;
-  float ra[RPT];
-  auto fetch = [&](int grp) __attribute__((always_inline)) {
-    const unsigned s0 = (unsigned)(grp * KS);
-    if (uld) {
-      raw_load(rq, qc + (uoff + s0));
-      raw_load(rk, kc + (uoff + s0));
-    } else {
-      raw_zero(rq);
-      raw_zero(rk);
-    }
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = rg * RPT + i;
-      ra[i] = row < rv ? lc[aoff + (unsigned)(i * dk) + s0] : 0.f;
-    }
-  };
-  fetch(0);
-  for (int grp = 0; grp < NG; ++grp) {
-    const int s0 = grp * KS;
-    const Raw8<T> cq = rq, ck = rk;
-    float av[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) av[i] = ra[i];
-    if (grp + 1 < NG) fetch(grp + 1);
-    lds_barrier();  // previous slice's readers of qs, ks, bs, tot are done
-    if (tid < NU) {
-      float qv[8], kv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qv[e] = raw_get(cq, e);
-        kv[e] = raw_get(ck, e);
-      }
-      store8(qs + urow * LDT + uc8, qv);
-      store8(ks + urow * LDT + uc8, kv);
-    }
-    // chunk-local cumsum: RPT rows per thread, then the preceding groups' totals
-    float run = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      run += av[i];
-      av[i] = run;
-    }
-    tot[rg][ch] = run;
-    lds_barrier();
-    float off = 0.f;
-    for (int g = 0; g < rg; ++g) off += tot[g][ch];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) bs[(rg * RPT + i) * LDF + ch] = av[i] + off;
-    lds_barrier();
-    // Q~ = Q ⊙ e^B and K~ = K ⊙ e^{b - B}, one 16-byte unit per thread each.
-    // Q~ unit g of a row holds (bf16) columns 4g..4g+3 and 16+4g..16+4g+3 of
-    // the group, the channels of the state rows that lane group g holds in
-    // its accumulators; (fp32) columns 4g..4g+3.
-    for (int it = tid; it < C * 4; it += kThreads) {
-      const int row = it >> 2, g = it & 3;
-      float x[EPU];
-#pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        const int c = BF ? (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4) : 4 * g + e;
-        x[e] = to_f32(qs[row * LDT + c]) * gexp<T>(bs[row * LDF + c]);
-      }
-      store_unit<T>(qr + (((row >> 4) * NG + grp) * 1024 + row_slot(row & 15, g) * 16), x);
-      // K~: unit u = columns EPU u .. EPU u + EPU - 1
-#pragma unroll
-      for (int e = 0; e < EPU; ++e) {
-        const int c = EPU * g + e;
-        x[e] = to_f32(ks[row * LDT + c]) * gexp<T>(bs[(C - 1) * LDF + c] - bs[row * LDF + c]);
-      }
-      int kofs;
-      if constexpr (BF) kofs = ((row >> 5) * NG + grp) * 2048 + run_slot<4>(row & 31, g) * 16;
-      else kofs = ((row >> 4) * NG + grp) * 1024 + scal_slot<4>(row & 15, g) * 16;
-      store_unit<T>(kr + kofs, x);
-    }
-    if (tid < KS) {
-      const float b = bs[(C - 1) * LDF + tid];
-      gr[s0 + tid] = gexp<T>(b);  // the chunk's decay of state row s0 + tid
-      gr[dk + s0 + tid] = b;      // and its log
-    }
-    PB::gates(bs, als);
-    pb.offdiag(qs, ks, bs);
-    lds_barrier();
-    pb.diag(qs, ks, als);
-  }
-  lds_barrier();  // the slice arrays are dead from here on
-  pb.finish(pd, [&](int m, int r, float val) {
-    const T hi = from_f32<T>(val);
-    ps[m * C + r] = hi;
-    if constexpr (BF) {
-      if ((m >> 4) == (r >> 4)) ls[m * 16 + (r & 15)] = from_f32<T>(val - to_f32(hi));
-    }
-  });
-  lds_barrier();
-  // P as row blocks (jt, column group); unit g of a row = its EPU columns.
-  // Entries above the diagonal were never written to ps: they are stored as
-  // 0 here.
-  constexpr int PUR = C / EPU, NPG = C / KS;
-  unsigned char* pr = prec + cb * C * C * RD::ES;
-  for (int it = tid; it < C * PUR; it += kThreads) {
-    const int row = it / PUR, uu = it % PUR;
-    store_masked<T>(pr + ((row >> 4) * NPG + (uu >> 2)) * 1024 + row_slot(row & 15, uu & 3) * 16,
-                    &ps[row * C + uu * EPU], row - uu * EPU);
-  }
-  if constexpr (BF) {
-    unsigned char* lr = lrec + cb * C * 16 * RD::ES;
-    for (int it = tid; it < C * 2; it += kThreads) {
-      const int row = it >> 1, gd = it & 1;
-      store_masked<T>(lr + (row >> 4) * 512 + lo_slot(row & 15, gd) * 16,
-                      &ls[row * 16 + 8 * gd], (row & 15) - 8 * gd);
-    }
-  }
-}
 
 // =========================================================== pass 2: recurrence
 template <typename T, int C, int DK, int NWV, int OUT>
@@ -386,25 +118,56 @@ struct RecurLayout {
   static constexpr int GB = RD::gbytes(DK);
   static constexpr int VB = C * DVT * ES;
   static constexpr int VBLK = BF ? 32 * VUPR * 16 : 16 * VUPR * 16;  // bytes per V block
+  // one record buffer: Q~, K~, P, P's low part, gates
   static constexpr int oQ = 0, oK = oQ + QB, oP = oK + KB, oL = oP + PB, oG = oL + LB,
-                       oV = oG + GB, BUF = oV + VB;
-  static constexpr int VCOPY = VB / 1024;       // V copies per chunk
-  static constexpr int CPC = BUF / 1024;        // copies per chunk
-  // Staging buffers: three (copies run two chunks ahead) when they fit and
-  // a chunk's copy count fits the 6-bit vmcnt field, else two, else one.
-  static constexpr int NBUF = (CPC <= 63 && 3 * BUF <= kLdsLimit) ? 3 : (2 * BUF <= kLdsLimit ? 2 : 1);
+                       RBUF = oG + GB;
+  // NLD loading waves share each chunk's copies: a tile of n > 1 copies (a
+  // power of two) gives each n / NLD, a one-copy tile is issued by all (the
+  // same bytes to the same place), so all issue the same number of copies per
+  // chunk and each has its own 6-bit vmcnt of copies in flight.  One is
+  // enough where the copies' latency is the limit rather than that counter.
+  static constexpr int NLD = 1;
+  static constexpr int NWAVES = NWV + NLD;
+  static constexpr int per_loader(int bytes) {
+    return bytes == 0 ? 0 : (bytes == 1024 ? 1 : bytes / 1024 / NLD);
+  }
+  static constexpr int VCOPY = per_loader(VB);  // V copies per chunk and loading wave
+  static constexpr int RCPC =                   // record copies per chunk and loading wave
+      per_loader(QB) + per_loader(KB) + per_loader(PB) + per_loader(LB) + per_loader(GB);
+  static constexpr int CPC = RCPC + VCOPY;      // copies per chunk and loading wave
+  // Record buffers: three (copies run two chunks ahead) when they fit and a
+  // chunk's copy count fits the 6-bit vmcnt field, else two, else one.
+  static constexpr int NBUF = (CPC <= 63 && 3 * (RBUF + VB) <= kLdsLimit)
+                                  ? 3
+                                  : (2 * (RBUF + VB) <= kLdsLimit ? 2 : 1);
+  // V buffers: V comes straight from HBM (the records were just written by
+  // the prep pass), so its copies run further ahead in a ring of their own
+  // while the LDS and the vmcnt field allow (see the loader's waits).
+  static constexpr int vnb_max(int n) {
+    return (n < 6 && NBUF * RBUF + (n + 1) * VB <= kLdsLimit &&
+            (NBUF == 3 ? 2 * VCOPY + RCPC : VCOPY) <= 63)
+               ? vnb_max(n + 1)
+               : n;
+  }
+  static constexpr int VNB = NBUF == 1 ? 1 : vnb_max(NBUF);
+  static constexpr int oV = NBUF * RBUF;        // V ring after the record buffers
+  static constexpr int LDS = oV + VNB * VB;
   static_assert(QB % 1024 == 0 && KB % 1024 == 0 && PB % 1024 == 0 && LB % 1024 == 0 &&
-                    VB % 1024 == 0,
+                    VB % 1024 == 0 && GB % 1024 == 0,
                 "every staged tile is a whole number of 1 KB copies");
-  static_assert(BUF <= kLdsLimit, "staged chunk exceeds LDS");
+  static constexpr bool split_ok(int bytes) { return bytes <= 1024 || (bytes / 1024) % NLD == 0; }
+  static_assert(split_ok(QB) && split_ok(KB) && split_ok(PB) && split_ok(LB) && split_ok(GB) &&
+                    split_ok(VB),
+                "every tile splits evenly over the loading waves");
+  static_assert(LDS <= kLdsLimit, "staged chunk exceeds LDS");
 };
 
-// Waves 0 .. NWV-1 compute (16 state columns each); wave NWV only issues the
-// LDS copies and waits for them, so that its memory counter holds nothing but
-// loads (a partial wait is exact) and the computing waves, which store the
-// output, never wait on memory.
+// Waves 0 .. NWV-1 compute (16 state columns each); waves NWV .. NWV+NLD-1
+// only issue the LDS copies and wait for them, so that their memory counters
+// hold nothing but loads (a partial wait is exact) and the computing waves,
+// which store the output, never wait on memory.
 template <typename T, int C, int DK, int NWV, int OUT>
-__global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
+__global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) void k_chunk_recur(
     const unsigned char* __restrict__ qrec, const unsigned char* __restrict__ krec,
     const unsigned char* __restrict__ prec, const unsigned char* __restrict__ lrec,
     const float* __restrict__ grec, const T* __restrict__ v, const float* __restrict__ init,
@@ -414,7 +177,7 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
   constexpr bool BF = Lay::BF;
   constexpr int ES = Lay::ES, DVT = Lay::DVT, NTH = NWV * kWave, VUPR = Lay::VUPR;
   constexpr int NRT = C / 16, NKT = DK / 16, NG = Lay::NG, NPG = Lay::NPG;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[Lay::NBUF * Lay::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Lay::LDS];
 
   const int ntv = dv / DVT;
   const int lid = xcd_logical(blockIdx.x, gridDim.x);
@@ -423,9 +186,11 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
   // the wave index as a scalar: copy and column offsets derived from it stay
   // in scalar registers
   const int w = __builtin_amdgcn_readfirstlane(wave_id());
-  const bool loader = w == NWV;
+  const bool loader = w >= NWV;
+  const bool computer = !loader;
+  const int li = (Lay::NLD > 1 && loader) ? w - NWV : 0;  // loading wave index
   const int l = lane_id(), g = l >> 4, ln = l & 15;
-  const int vc = 16 * (loader ? 0 : w);  // this wave's first column within the tile
+  const int vc = computer ? 16 * w : 0;  // this wave's first column within the tile
   const int col = j0 + vc + ln;          // this lane's state column
   const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks);
 
@@ -433,7 +198,7 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
   floatx4 S[NKT];
   {
     const float* src = nullptr;
-    if (OUT && !loader) src = NSEG > 1 ? init + ((size_t)bh * NSEG + seg) * DK * dv
+    if (OUT && computer) src = NSEG > 1 ? init + ((size_t)bh * NSEG + seg) * DK * dv
                                        : (init ? init + (size_t)bh * DK * dv : nullptr);
 #pragma unroll
     for (int a = 0; a < NKT; ++a) {
@@ -467,29 +232,37 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
   };
 
   const unsigned lds0 = lds_addr(lds);
-  // Stage chunk n into buffer b (the loading wave only).
-  auto issue = [&](int n, int b) __attribute__((always_inline)) {
-    const unsigned base = lds0 + (unsigned)(b * Lay::BUF);
+  // Stage chunk n's records into record buffer (n - nb) % NBUF (the loading
+  // waves only).
+  auto issue_r = [&](int n) __attribute__((always_inline)) {
+    const unsigned base = lds0 + (unsigned)(((n - nb) % Lay::NBUF) * Lay::RBUF);
     const size_t cb = (size_t)bh * NC + n;
+    constexpr int NLD = Lay::NLD;
     if constexpr (OUT) {
-      copy_tile<Lay::QB / 1024, 1>(qrec + cb * Lay::QB, base + Lay::oQ, 0, l);
-      copy_tile<Lay::PB / 1024, 1>(prec + cb * Lay::PB, base + Lay::oP, 0, l);
-      if constexpr (BF) copy_tile<Lay::LB / 1024, 1>(lrec + cb * Lay::LB, base + Lay::oL, 0, l);
+      copy_tile<Lay::QB / 1024, NLD>(qrec + cb * Lay::QB, base + Lay::oQ, li, l);
+      copy_tile<Lay::PB / 1024, NLD>(prec + cb * Lay::PB, base + Lay::oP, li, l);
+      if constexpr (BF) copy_tile<Lay::LB / 1024, NLD>(lrec + cb * Lay::LB, base + Lay::oL, li, l);
     }
-    copy_tile<Lay::KB / 1024, 1>(krec + cb * Lay::KB, base + Lay::oK, 0, l);
-    copy_tile<Lay::GB / 1024, 1>(reinterpret_cast<const unsigned char*>(grec) + cb * Lay::GB,
-                                 base + Lay::oG, 0, l);
+    copy_tile<Lay::KB / 1024, NLD>(krec + cb * Lay::KB, base + Lay::oK, li, l);
+    copy_tile<Lay::GB / 1024, NLD>(reinterpret_cast<const unsigned char*>(grec) + cb * Lay::GB,
+                                   base + Lay::oG, li, l);
+  };
+  // Stage chunk n's V tile into V buffer n % VNB (the loading waves only).
+  auto issue_v = [&](int n) __attribute__((always_inline)) {
+    const unsigned base = lds0 + (unsigned)(Lay::oV + (n % Lay::VNB) * Lay::VB);
     // V rows past the end of the sequence repeat the last row (their K~ rows
     // and P columns are zero)
     const int r0 = n * C;
     const i32x4 vr = make_rsrc(v + ((size_t)bh * L + r0) * dv + j0);
     const bool full = r0 + C <= L;
+    constexpr int NVC = Lay::VB / 1024;
 #pragma unroll
-    for (int c = 0; c < Lay::VCOPY; ++c) {
+    for (int i = 0; i < (NVC == 1 ? 1 : NVC / Lay::NLD); ++i) {
+      const int c = NVC == 1 ? 0 : li + i * Lay::NLD;
       int rho, u;
       vslot(c, rho, u);
       if (!full) rho = min(rho, L - 1 - r0);
-      dma16b(vr, (unsigned)(rho * dv * ES + u * 16), 0u, base + (unsigned)(Lay::oV + c * 1024));
+      dma16b(vr, (unsigned)(rho * dv * ES + u * 16), 0u, base + (unsigned)(c * 1024));
     }
   };
 
@@ -513,16 +286,52 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
     }
   }
 
-  // One chunk from buffer b: O^T of the chunk into ot (stored by the caller
-  // once the next copies are issued), then the state update.
-  auto body = [&](int n, int b, floatx4 (&ot)[NRT]) __attribute__((always_inline)) {
-    const unsigned char* base = lds + b * Lay::BUF;
+  // Output stores go through a buffer resource spanning the head's L rows:
+  // rows past the end of the sequence fall outside it and are dropped by the
+  // hardware, so the stores need no branch.
+  const __amdgpu_buffer_rsrc_t orsrc =
+      __builtin_amdgcn_make_buffer_rsrc(OUT ? o + (size_t)bh * L * dv : o, 0, L * dv * ES, 0x00020000);
+  auto store_out = [&](int n, const floatx4 (&ot)[NRT]) __attribute__((always_inline)) {
+    if constexpr (OUT) {
+      const int off0 = ((n * C + ln) * dv + j0 + vc + 4 * g) * ES;
+#pragma unroll
+      for (int jt = 0; jt < NRT; ++jt) {
+        const int off = off0 + 16 * jt * dv * ES;
+        if constexpr (BF) {
+          bf16x4 h;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = static_cast<bf16>(ot[jt][r]);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, h), orsrc, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, ot[jt]), orsrc, off, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ot holds the output of chunk pn (-1: none yet), stored during the next
+  // chunk's body, once that chunk's first products are issued, so that the
+  // stores do not wait for the matrix pipeline.
+  floatx4 ot[NRT];
+  int pn = -1;
+  auto flush_out = [&](int n) __attribute__((always_inline)) {
+    if (pn >= 0) store_out(pn, ot);
+    pn = n;
+  };
+
+  // One chunk from record buffer b.  bf16: the state update first (from the
+  // bf16 copy of S_{n-1} that the output products use), so that the next
+  // chunk's products, which need S_n, never wait for this chunk's output
+  // products; then the previous chunk's output is stored and this chunk's
+  // computed into ot.  fp32: output first, then the update.
+  auto body = [&](int n, int b) __attribute__((always_inline)) {
+    const unsigned char* base = lds + b * Lay::RBUF;
     const unsigned char* Qs = base + Lay::oQ;
     const unsigned char* Ks = base + Lay::oK;
     const unsigned char* Ps = base + Lay::oP;
     const unsigned char* Ls = base + Lay::oL;
     const float* Gs = reinterpret_cast<const float*>(base + Lay::oG);
-    const unsigned char* Vs = base + Lay::oV;
+    const unsigned char* Vs = lds + Lay::oV + (n % Lay::VNB) * Lay::VB;
     if constexpr (BF) {
       // V fragments over token runs 32 kt + 8 g + e at column vc + ln
       bf16x8 vf[C / 32];
@@ -532,40 +341,18 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
         vf[kt] = join8(ds_read_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const unsigned char*>(vb) + voff[0])),
                        ds_read_tr(reinterpret_cast<const bf16*>(reinterpret_cast<const unsigned char*>(vb) + voff[1])));
       }
+      // S_{n-1}^T as the output products' A operands: the MFMA's K index
+      // 8 g + e maps to channel 32 a2 + 4 g + e (e < 4) or + 16 + 4 g + e - 4
+      // (the order of the Q~ units)
+      bf16x8 A[OUT ? NKT / 2 : 1];
       if constexpr (OUT) {
 #pragma unroll
-        for (int jt = 0; jt < NRT; ++jt) ot[jt] = zero4();
-        // O^T += S^T Q~^T over pairs of 16-channel tiles; the MFMA's K index
-        // 8 g + e maps to channel 32 a2 + 4 g + e (e < 4) or + 16 + 4 g + e - 4
-        // (the order of the Q~ units)
-#pragma unroll
-        for (int a2 = 0; a2 < NKT / 2; ++a2) {
-          bf16x8 A;
+        for (int a2 = 0; a2 < NKT / 2; ++a2)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            A[r] = static_cast<bf16>(S[2 * a2][r]);
-            A[r + 4] = static_cast<bf16>(S[2 * a2 + 1][r]);
+            A[a2][r] = static_cast<bf16>(S[2 * a2][r]);
+            A[a2][r + 4] = static_cast<bf16>(S[2 * a2 + 1][r]);
           }
-#pragma unroll
-          for (int jt = 0; jt < NRT; ++jt) {
-            const bf16x8 B = *reinterpret_cast<const bf16x8*>(Qs + (jt * NG + a2) * 1024 + qoff);
-            ot[jt] = Mma<bf16>::run(A, B, ot[jt]);
-          }
-        }
-        // O^T += V^T P^T (P rounded; its diagonal blocks also carry a low part)
-#pragma unroll
-        for (int jt = 0; jt < NRT; ++jt) {
-#pragma unroll
-          for (int kt = 0; kt <= (jt >> 1); ++kt) {
-            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(Ps + (jt * NPG + kt) * 1024 + qoff);
-            ot[jt] = Mma<bf16>::run(vf[kt], pf, ot[jt]);
-          }
-          // every lane reads (a branch would force a wait for the read), the
-          // lanes whose K range is not this block's diagonal drop the value
-          bf16x8 lf = *reinterpret_cast<const bf16x8*>(Ls + jt * 512 + loff);
-          if ((g >> 1) != (jt & 1)) lf = bf16x8{};
-          ot[jt] = Mma<bf16>::run(vf[jt >> 1], lf, ot[jt]);
-        }
       }
       // S = diag(e^b) S + K~^T V
 #pragma unroll
@@ -584,6 +371,34 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
           S[a] = Mma<bf16>::run(kf, vf[kt], S[a]);
         }
       }
+      if constexpr (OUT) {
+        flush_out(n);
+#pragma unroll
+        for (int jt = 0; jt < NRT; ++jt) ot[jt] = zero4();
+        // O^T += S_{n-1}^T Q~^T over pairs of 16-channel tiles
+#pragma unroll
+        for (int a2 = 0; a2 < NKT / 2; ++a2) {
+#pragma unroll
+          for (int jt = 0; jt < NRT; ++jt) {
+            const bf16x8 B = *reinterpret_cast<const bf16x8*>(Qs + (jt * NG + a2) * 1024 + qoff);
+            ot[jt] = Mma<bf16>::run(A[a2], B, ot[jt]);
+          }
+        }
+        // O^T += V^T P^T (P rounded; its diagonal blocks also carry a low part)
+#pragma unroll
+        for (int jt = 0; jt < NRT; ++jt) {
+#pragma unroll
+          for (int kt = 0; kt <= (jt >> 1); ++kt) {
+            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(Ps + (jt * NPG + kt) * 1024 + qoff);
+            ot[jt] = Mma<bf16>::run(vf[kt], pf, ot[jt]);
+          }
+          // every lane reads (a branch would force a wait for the read), the
+          // lanes whose K range is not this block's diagonal drop the value
+          bf16x8 lf = *reinterpret_cast<const bf16x8*>(Ls + jt * 512 + loff);
+          if ((g >> 1) != (jt & 1)) lf = bf16x8{};
+          ot[jt] = Mma<bf16>::run(vf[jt >> 1], lf, ot[jt]);
+        }
+      }
     } else {
       // fp32: 16x16x4 MFMAs; within each 16-token block bb the MFMA i takes
       // tokens 16 bb + 4 g + i (K index g)
@@ -594,6 +409,7 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
         for (int i = 0; i < 4; ++i)
           vf[bb][i] = *reinterpret_cast<const float*>(Vs + bb * Lay::VBLK + vsoff[i]);
       if constexpr (OUT) {
+        flush_out(n);
 #pragma unroll
         for (int jt = 0; jt < NRT; ++jt) ot[jt] = zero4();
 #pragma unroll
@@ -638,39 +454,38 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
     }
   };
 
-  auto store_out = [&](int n, const floatx4 (&ot)[NRT]) __attribute__((always_inline)) {
-    if constexpr (OUT) {
-      const int rv = min(C, L - n * C);
-      T* orow = o + ((size_t)bh * L + n * C + ln) * dv + j0 + vc + 4 * g;
-#pragma unroll
-      for (int jt = 0; jt < NRT; ++jt)
-        if (16 * jt + ln < rv) store4(orow + (size_t)16 * jt * dv, ot[jt]);
-    }
-  };
-
-  // ---- walk the segment's chunks.  Chunk n + D (D = NBUF - 1) is staged into
-  // the buffer that chunk n - 1 used while chunk n computes; before the
-  // chunk's closing barrier the loading wave waits until chunk n + 1 has
-  // landed (with D = 2 the copies of chunk n + 2 may still be in flight).
-  // The computing waves store each chunk's output as soon as it is computed.
-  // Buffer indices are literals at every step call.
+  // ---- walk the segment's chunks.  While chunk n computes, the loading wave
+  // stages the records of chunk n + D (D = NBUF - 1) into the record buffer
+  // that chunk n - 1 used and the V tile of chunk n + VD (VD = VNB - 1) into
+  // the V buffer that chunk n - 1 used, then waits until chunk n + 1 has
+  // landed, and the step ends with a barrier.  Record buffer indices are
+  // literals at every step call.
   constexpr int D = Lay::NBUF - 1;
-  // ot: the chunk being computed; op: the previous chunk's output, stored
-  // after the next chunk's products are issued so that the stores never wait
-  // for the matrix pipeline
-  floatx4 ot[NRT], op[NRT];
-  int pn = -1;
-  auto store_prev = [&]() __attribute__((always_inline)) {
-    if (pn >= 0) store_out(pn, op);
+  constexpr int VD = Lay::VNB - 1;
+  // The copies of step s: chunk s + D's records, then chunk s + VD's V tile
+  // (steps before nb issue only what belongs to the segment).
+  auto issue_step = [&](int s) __attribute__((always_inline)) {
+    if (s + D >= nb && s + D < ne) issue_r(s + D);
+    if (s + VD < ne) issue_v(s + VD);
   };
-  auto keep = [&](int n) __attribute__((always_inline)) {
-#pragma unroll
-    for (int jt = 0; jt < NRT; ++jt) op[jt] = ot[jt];
-    pn = n;
-  };
-  auto wait_through = [&](int m) __attribute__((always_inline)) {  // chunk m landed
-    if constexpr (D == 2) {
-      if (m + 1 < ne) wait_vm_le<Lay::CPC>();
+  // At step n, after its copies: wait until chunk n + 1 has landed.  A
+  // loading wave issues only loads, which complete in issue order, so each
+  // waits until no more of its copies are outstanding than it issued after
+  // its last one of chunk n + 1: with VD > D that is its records (issued at
+  // step n + 1 - D), followed by that step's V copies and the copies of the
+  // steps after it; with VD = D it is its V tile, followed by the later
+  // steps' copies.  Copies past the end of the segment are never issued.
+  auto wait_next = [&](int n) __attribute__((always_inline)) {
+    if constexpr (D == 2 && VD > 2) {
+      if (n + VD < ne) wait_vm_le<2 * Lay::VCOPY + Lay::RCPC>();
+      else if (n - 1 + VD < ne) wait_vm_le<Lay::VCOPY + Lay::RCPC>();
+      else if (n + 2 < ne) wait_vm_le<Lay::RCPC>();
+      else wait_vm();
+    } else if constexpr (D == 2) {
+      if (n + 2 < ne) wait_vm_le<Lay::CPC>();
+      else wait_vm();
+    } else if constexpr (D == 1 && VD > 1) {
+      if (n + VD < ne) wait_vm_le<Lay::VCOPY>();
       else wait_vm();
     } else {
       wait_vm();
@@ -679,23 +494,18 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
   auto step = [&](int n, int b) __attribute__((always_inline)) {
     if constexpr (D > 0) {
       if (loader) {
-        if (n + D < ne) issue(n + D, (b + D) % Lay::NBUF);
-        if (n + 1 < ne) wait_through(n + 1);
+        issue_step(n);
+        if (n + 1 < ne) wait_next(n);
       } else {
-        body(n, b, ot);
-        store_prev();
-        keep(n);
+        body(n, b);
       }
       lds_barrier();  // chunk n + 1 staged; everyone is done with buffer b
     } else {
-      if (!loader) {
-        body(n, 0, ot);
-        store_prev();
-        keep(n);
-      }
+      if (computer) body(n, 0);
       lds_barrier();  // everyone is done with the buffer
       if (loader && n + 1 < ne) {
-        issue(n + 1, 0);
+        issue_r(n + 1);
+        issue_v(n + 1);
         wait_vm();
       }
       lds_barrier();  // chunk n + 1 staged
@@ -704,10 +514,16 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
 
   if (nb < ne) {
     if (loader) {
+      if constexpr (D > 0) {
+        // the copies that steps nb - VD .. nb - 1 would have issued
 #pragma unroll
-      for (int i = 0; i < (D > 0 ? D : 1); ++i)
-        if (nb + i < ne) issue(nb + i, i);
-      wait_through(nb);
+        for (int i = VD; i > 0; --i) issue_step(nb - i);
+        wait_next(nb - 1);
+      } else {
+        issue_r(nb);
+        issue_v(nb);
+        wait_vm();
+      }
     }
     lds_barrier();  // chunk nb staged
   }
@@ -721,19 +537,19 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
     }
   }
 
-  if (!loader) store_prev();
+  if (OUT && computer && pn >= 0) store_out(pn, ot);
 
   // ---- end of the segment
   float* dst = nullptr;
   if (OUT) dst = (NSEG == 1 && fin) ? fin + (size_t)bh * DK * dv : nullptr;
   else dst = fin + ((size_t)bh * NSEG + seg) * DK * dv;
-  if (dst && !loader) {
+  if (dst && computer) {
 #pragma unroll
     for (int a = 0; a < NKT; ++a)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(size_t)(a * 16 + 4 * g + r) * dv + col] = S[a][r];
   }
-  if (!OUT && tile == 0 && !loader) {
+  if (!OUT && tile == 0 && computer) {
 #pragma unroll
     for (int i = 0; i < NGS; ++i) {
       const int t = threadIdx.x + i * NTH;
@@ -743,27 +559,6 @@ __global__ __launch_bounds__((NWV + 1) * kWave) void k_chunk_recur(
 }
 
 // =========================================================== launchers
-template <typename T, int C>
-static hipError_t launch_prep_t(const Plan& p, const void* q, const void* k, const float* la,
-                                void* qg, void* kg, float* grec, void* ph, void* pl,
-                                hipStream_t s) {
-  hipLaunchKernelGGL((k_chunk_prep<T, C>), dim3(p.NC, p.BH), dim3(kThreads), 0, s, (const T*)q,
-                     (const T*)k, la, (unsigned char*)qg, (unsigned char*)kg, (unsigned char*)ph,
-                     (unsigned char*)pl, grec, p.L, p.dk, p.NC);
-  return hipGetLastError();
-}
-
-hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,
-                             void* qg, void* kg, float* grec, void* ph, void* pl, hipStream_t s) {
-  if (p.bf16) {
-    if (p.C == 64) return launch_prep_t<bf16, 64>(p, q, k, la, qg, kg, grec, ph, pl, s);
-    return launch_prep_t<bf16, 32>(p, q, k, la, qg, kg, grec, ph, pl, s);
-  }
-  if (p.C == 64) return launch_prep_t<float, 64>(p, q, k, la, qg, kg, grec, ph, pl, s);
-  if (p.C == 32) return launch_prep_t<float, 32>(p, q, k, la, qg, kg, grec, ph, pl, s);
-  return launch_prep_t<float, 16>(p, q, k, la, qg, kg, grec, ph, pl, s);
-}
-
 template <typename T, int C, int DK, int NWV>
 static hipError_t launch_recur_w(const Plan& p, int out, const void* qg, const void* kg,
                                  const void* ph, const void* pl, const float* grec,
@@ -773,11 +568,13 @@ static hipError_t launch_recur_w(const Plan& p, int out, const void* qg, const v
   const unsigned char *q8 = (const unsigned char*)qg, *k8 = (const unsigned char*)kg,
                       *p8 = (const unsigned char*)ph, *l8 = (const unsigned char*)pl;
   if (out)
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1>), grid, dim3((NWV + 1) * kWave), 0, s, q8, k8,
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1>), grid,
+                       dim3(RecurLayout<T, C, DK, NWV, 1>::NWAVES * kWave), 0, s, q8, k8,
                        p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
                        p.NSEGR, p.segr_chunks);
   else
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0>), grid, dim3((NWV + 1) * kWave), 0, s, q8, k8,
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0>), grid,
+                       dim3(RecurLayout<T, C, DK, NWV, 0>::NWAVES * kWave), 0, s, q8, k8,
                        p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
                        p.NSEGR, p.segr_chunks);
   return hipGetLastError();
@@ -788,8 +585,9 @@ static hipError_t launch_recur_d(const Plan& p, int out, const void* qg, const v
                                  const void* ph, const void* pl, const float* grec,
                                  const void* v, const float* init, void* o, float* fin,
                                  float* seg_g, hipStream_t s) {
-  if (p.NWVR == 4)
-    return launch_recur_w<T, C, DK, 4>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
+  if constexpr (recur_max_waves(sizeof(T) == 2, DK) == 4)
+    if (p.NWVR == 4)
+      return launch_recur_w<T, C, DK, 4>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   if (p.NWVR == 2)
     return launch_recur_w<T, C, DK, 2>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   if constexpr (recur_min_waves(sizeof(T) == 2, DK) == 1)
@@ -821,10 +619,12 @@ static hipError_t launch_recur_c(const Plan& p, int out, const void* qg, const v
 
 size_t recur_grec_bytes(int dk) { return RecDims<float>::gbytes(dk); }
 
-bool recur_supported(int bf16, int C, int dk, int dv) {
+bool recur_supported(int bf16, int C, int dk, int dv, int L) {
   const bool shape = bf16 ? (C == 32 || C == 64) && (dk == 32 || dk == 64 || dk == 128 || dk == 256)
                           : (C == 16 || C == 32 || C == 64) && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
-  return shape && dv % (16 * recur_min_waves(bf16, dk)) == 0;
+  // a head's output must be addressable with 32-bit byte offsets
+  const bool range = (long long)L * dv * (bf16 ? 2 : 4) <= 0x7fffffffLL;
+  return shape && range && dv % (16 * recur_min_waves(bf16, dk)) == 0;
 }
 
 hipError_t launch_chunk_recur(const Plan& p, int out, const void* qg, const void* kg,
