@@ -93,6 +93,32 @@ __global__ __launch_bounds__(kThreads) void k_chunk_attn(
 }
 
 // ------------------------------------------------------------------ B3b: dq, dk, dlog b
+// Column layout of the off-diagonal intra operands of k_chunk_dqdk.  For query
+// sub-chunk j >= 1 the dq operand holds K ⊙ e^{z_j - B} over key rows
+// [0, KQ(j)) (z_j = B at row 16 j; rows >= 16 j are 0), at columns
+// [OQ(j), OQ(j) + KQ(j)); for key sub-chunk u < NRT - 1 the dk operand holds
+// Q ⊙ e^{B - z'_u} over query rows [MLO(u), C) (z'_u = B at row 16 u + 15;
+// rows < 16 (u + 1) are 0), at columns [OK(u), OK(u) + C - MLO(u)).  K spans
+// are whole MFMA K steps.
+template <int K, int C>
+struct OffCols {
+  static constexpr int NRT = C / 16;
+  static constexpr int KQ(int j) { return ((16 * j + K - 1) / K) * K; }
+  static constexpr int MLO(int u) { return ((16 * (u + 1)) / K) * K; }
+  static constexpr int OQ(int j) {
+    int o = 0;
+    for (int i = 1; i < j; ++i) o += KQ(i);
+    return o;
+  }
+  static constexpr int OK(int u) {
+    int o = 0;
+    for (int i = 0; i < u; ++i) o += C - MLO(i);
+    return o;
+  }
+  static constexpr int WQ = OQ(NRT) > 0 ? OQ(NRT) : K;       // dq operand columns
+  static constexpr int WK = OK(NRT - 1) > 0 ? OK(NRT - 1) : K;  // dk operand columns
+};
+
 // One workgroup per (batch-head, chunk, d_k tile of TK channels).
 template <typename T, int C, int TK>
 __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
@@ -114,9 +140,15 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   __shared__ __attribute__((aligned(16))) T dath[C][LDA];   // transposed: [r][m]
   __shared__ __attribute__((aligned(16))) T datl[BF ? C : 1][BF ? LDA : 8];
   __shared__ float dad[C][17];                              // diagonal blocks, fp32
+  __shared__ float dgo[2][C][TK + 4];                       // diagonal-block terms of dq, dk
   __shared__ float qf[C][LDK], kf[C][LDK], bt[C][LDK], al[C][LDK];
-  __shared__ __attribute__((aligned(16))) T opT[TK][LDA];   // scaled operand, [ch][row]
-  __shared__ __attribute__((aligned(16))) T opL[BF ? TK : 1][BF ? LDA : 8];  // its low part
+  // off-diagonal intra operands, [ch][column] (OffCols), and their low parts
+  using OC = OffCols<M::K, C>;
+  constexpr int LDQ = OC::WQ + PT, LDKO = OC::WK + PT;
+  __shared__ __attribute__((aligned(16))) T opq[TK][LDQ];
+  __shared__ __attribute__((aligned(16))) T opk[TK][LDKO];
+  __shared__ __attribute__((aligned(16))) T opql[BF ? TK : 1][BF ? LDQ : 8];
+  __shared__ __attribute__((aligned(16))) T opkl[BF ? TK : 1][BF ? LDKO : 8];
 
   const int n = blockIdx.x, c0 = blockIdx.y * TK, bh = blockIdx.z;
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -217,83 +249,124 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     }
   }
 
-  // intra dq, off-diagonal sub-chunks: rows of sub-chunk j, keys r < 16 j,
-  // reference z_j = B at the first row of j:
-  //   e^{B_m - z_j} ⊙ [dA_off (K ⊙ e^{z_j - B})]
-  for (int j = 1; j < NRT; ++j) {
-    __syncthreads();
-    for (int it = tid; it < C * TK; it += kThreads) {
-      const int r = it / TK, c = it % TK;
+  // intra terms of the off-diagonal sub-chunk blocks, with the reference row
+  // of each block (both factors <= 1):
+  //   dq rows of sub-chunk j:  e^{B_m - z_j} ⊙ [dA_off (K ⊙ e^{z_j - B})]
+  //   dk rows of sub-chunk u:  e^{z'_u - B_r} ⊙ [dA_off^T (Q ⊙ e^{B - z'_u})]
+  // All operands are formed in one pass; each wave then handles the blocks of
+  // its own row tiles.
+  if constexpr (NRT > 1) {
+    for (int it = tid; it < TK * OC::WQ; it += kThreads) {
+      const int c = it / OC::WQ, col = it % OC::WQ;
+      int j = 1;
+      while (j + 1 < NRT && col >= OC::OQ(j + 1)) ++j;
+      const int r = col - OC::OQ(j);
       const float x = r < 16 * j ? kf[r][c] * gexp<T>(bt[16 * j][c] - bt[r][c]) : 0.f;
       const T hi = from_f32<T>(x);
-      opT[c][r] = hi;
-      if constexpr (BF) opL[c][r] = from_f32<T>(x - to_f32(hi));
+      opq[c][col] = hi;
+      if constexpr (BF) opql[c][col] = from_f32<T>(x - to_f32(hi));
     }
-    __syncthreads();
-#pragma unroll
-    for (int rt = 0; rt < NRW; ++rt) {
-      if (wr + WR * rt != j) continue;
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) {
-        const int c = (wc + WC * ct) * 16 + (l & 15);
-        floatx4 t4 = zero4();
-        for (int kk = 0; kk < 16 * j; kk += M::K) {
-          const int kc = kk + (l >> 4) * M::KPL;
-          auto b = load_frag<T>(&opT[c][kc]);
-          auto ah = load_frag<T>(&dah[j * 16 + (l & 15)][kc]);
-          t4 = M::run(ah, b, t4);
-          if constexpr (BF) {
-            t4 = M::run(load_frag<T>(&dal[j * 16 + (l & 15)][kc]), b, t4);
-            t4 = M::run(ah, load_frag<T>(&opL[c][kc]), t4);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = j * 16 + (l >> 4) * 4 + r;
-          aq[rt][ct][r] += gexp<T>(bt[row][c] - bt[16 * j][c]) * t4[r];
-        }
-      }
-    }
-  }
-  // intra dk, off-diagonal sub-chunks: key rows of sub-chunk u, queries
-  // m > last(u), reference z = B at the last row of u:
-  //   e^{z - B_r} ⊙ [dA_off^T (Q ⊙ e^{B - z})]
-  for (int u = 0; u + 1 < NRT; ++u) {
-    __syncthreads();
-    for (int it = tid; it < C * TK; it += kThreads) {
-      const int m = it / TK, c = it % TK;
+    for (int it = tid; it < TK * OC::WK; it += kThreads) {
+      const int c = it / OC::WK, col = it % OC::WK;
+      int u = 0;
+      while (u + 2 < NRT && col >= OC::OK(u + 1)) ++u;
+      const int m = OC::MLO(u) + col - OC::OK(u);
       const float x = m >= 16 * (u + 1) ? qf[m][c] * gexp<T>(bt[m][c] - bt[16 * u + 15][c]) : 0.f;
       const T hi = from_f32<T>(x);
-      opT[c][m] = hi;
-      if constexpr (BF) opL[c][m] = from_f32<T>(x - to_f32(hi));
+      opk[c][col] = hi;
+      if constexpr (BF) opkl[c][col] = from_f32<T>(x - to_f32(hi));
     }
     __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
-      if (wr + WR * rt != u) continue;
+      const int rti = wr + WR * rt;
+      if (rti >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
-        floatx4 t4 = zero4();
-        for (int kk = ((16 * (u + 1)) / M::K) * M::K; kk < C; kk += M::K) {
-          const int kc = kk + (l >> 4) * M::KPL;
-          auto b = load_frag<T>(&opT[c][kc]);
-          auto ah = load_frag<T>(&dath[u * 16 + (l & 15)][kc]);
-          t4 = M::run(ah, b, t4);
-          if constexpr (BF) {
-            t4 = M::run(load_frag<T>(&datl[u * 16 + (l & 15)][kc]), b, t4);
-            t4 = M::run(ah, load_frag<T>(&opL[c][kc]), t4);
+        if (rti >= 1) {
+          const int j = rti;
+          floatx4 t4 = zero4();
+          for (int kk = 0; kk < OC::KQ(j); kk += M::K) {
+            const int kc = kk + (l >> 4) * M::KPL;
+            auto b = load_frag<T>(&opq[c][OC::OQ(j) + kc]);
+            auto ah = load_frag<T>(&dah[j * 16 + (l & 15)][kc]);
+            t4 = M::run(ah, b, t4);
+            if constexpr (BF) {
+              t4 = M::run(load_frag<T>(&dal[j * 16 + (l & 15)][kc]), b, t4);
+              t4 = M::run(ah, load_frag<T>(&opql[c][OC::OQ(j) + kc]), t4);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = j * 16 + (l >> 4) * 4 + r;
+            aq[rt][ct][r] += gexp<T>(bt[row][c] - bt[16 * j][c]) * t4[r];
           }
         }
+        if (rti + 1 < NRT) {
+          const int u = rti;
+          floatx4 t4 = zero4();
+          for (int kk = OC::MLO(u); kk < C; kk += M::K) {
+            const int kc = kk + (l >> 4) * M::KPL;
+            const int oc = OC::OK(u) + kc - OC::MLO(u);
+            auto b = load_frag<T>(&opk[c][oc]);
+            auto ah = load_frag<T>(&dath[u * 16 + (l & 15)][kc]);
+            t4 = M::run(ah, b, t4);
+            if constexpr (BF) {
+              t4 = M::run(load_frag<T>(&datl[u * 16 + (l & 15)][kc]), b, t4);
+              t4 = M::run(ah, load_frag<T>(&opkl[c][oc]), t4);
+            }
+          }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = u * 16 + (l >> 4) * 4 + r;
-          ak[rt][ct][r] += gexp<T>(bt[16 * u + 15][c] - bt[row][c]) * t4[r];
+          for (int r = 0; r < 4; ++r) {
+            const int row = u * 16 + (l >> 4) * 4 + r;
+            ak[rt][ct][r] += gexp<T>(bt[16 * u + 15][c] - bt[row][c]) * t4[r];
+          }
         }
       }
     }
   }
-  // diagonal sub-chunk blocks, fp32 VALU with running gate products
+  // diagonal sub-chunk blocks, fp32 VALU with running gate products.  Thread
+  // (dq or dk, block b, channel c) keeps the block's 16 gates and its 16 k (or
+  // q) values of channel c in registers and forms all 16 rows of the block's
+  // term; the terms go through LDS to the waves that own the rows.
+  static_assert(2 * NRT * TK <= kThreads || (2 * NRT * TK) % kThreads == 0, "diagonal split");
+  for (int it = tid; it < 2 * NRT * TK; it += kThreads) {
+    const int which = it / (NRT * TK), b = (it / TK) % NRT, c = it % TK;
+    float a[16], x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a[i] = al[16 * b + i][c];
+      x[i] = which ? qf[16 * b + i][c] : kf[16 * b + i][c];
+    }
+    const float* dd = &dad[16 * b][0];  // [16][17]: dA[16 b + m][16 b + s]
+    if (which == 0) {
+      // dq row m: sum over keys s <= m of dA[m][s] k_s e^{B_m - B_s}
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        float E = 1.f, sum = 0.f;
+#pragma unroll
+        for (int s2 = m; s2 >= 0; --s2) {
+          if (s2 < m) E *= a[s2 + 1];
+          sum += dd[m * 17 + s2] * x[s2] * E;
+        }
+        dgo[0][16 * b + m][c] = sum;
+      }
+    } else {
+      // dk row r: sum over queries s >= r of dA[s][r] q_s e^{B_s - B_r}
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float F = 1.f, sum = 0.f;
+#pragma unroll
+        for (int s2 = r; s2 < 16; ++s2) {
+          if (s2 > r) F *= a[s2];
+          sum += dd[s2 * 17 + r] * x[s2] * F;
+        }
+        dgo[1][16 * b + r][c] = sum;
+      }
+    }
+  }
+  __syncthreads();
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
     const int rti = wr + WR * rt;
@@ -303,28 +376,13 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       const int c = (wc + WC * ct) * 16 + (l & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int mi = (l >> 4) * 4 + r;           // row within the block
-        const int row = rti * 16 + mi;
-        // dq: sum over keys s <= mi of dA[row][s] k_s E(row, s), E built downwards
-        float E = 1.f, sq = 0.f;
-#pragma unroll
-        for (int s = 15; s >= 0; --s) {
-          if (s < mi) E *= al[rti * 16 + s + 1][c];
-          if (s <= mi) sq += dad[row][s] * kf[rti * 16 + s][c] * E;
-        }
-        aq[rt][ct][r] += sq;
-        // dk: sum over queries s >= mi of dA[s][row] q_s E(s, row), E built upwards
-        float F = 1.f, sk = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          if (s > mi) F *= al[rti * 16 + s][c];
-          if (s >= mi) sk += dad[rti * 16 + s][mi] * qf[rti * 16 + s][c] * F;
-        }
-        ak[rt][ct][r] += sk;
+        const int row = rti * 16 + (l >> 4) * 4 + r;
+        aq[rt][ct][r] += dgo[0][row][c];
+        ak[rt][ct][r] += dgo[1][row][c];
       }
     }
   }
-  __syncthreads();  // everyone is done with bt / al / opT
+  __syncthreads();  // everyone is done with bt / al / the operands
   float* dlb = &al[0][0];  // reuse: dlog b of the tile, [C][LDK]
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
@@ -346,14 +404,32 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     }
   }
   __syncthreads();
-  // chunk-local reverse cumsum of dlog b, and the chunk total
-  for (int c = tid; c < TK; c += kThreads) {
+  // chunk-local reverse cumsum of dlog b, and the chunk total: thread
+  // (row group g, channel c) sums its RPG rows from the bottom, then adds the
+  // totals of the row groups below it
+  constexpr int NGR = kThreads / TK, RPG = C / NGR;
+  static_assert(NGR * TK == kThreads && RPG * NGR == C, "row groups of the reverse cumsum");
+  float* gtot = &bt[0][0];  // reuse: [NGR][TK] group totals
+  {
+    const int c = tid % TK, g = tid / TK;
+    float part[RPG];
     float s = 0.f;
-    for (int row = rv - 1; row >= 0; --row) {
-      s += dlb[row * LDK + c];
-      dla[qo + (size_t)(r0 + row) * dk + c0 + c] = s;
+#pragma unroll
+    for (int i = RPG - 1; i >= 0; --i) {
+      const int row = g * RPG + i;
+      s += row < rv ? dlb[row * LDK + c] : 0.f;
+      part[i] = s;
     }
-    dlt[((size_t)bh * NC + n) * dk + c0 + c] = s;
+    gtot[g * TK + c] = s;
+    __syncthreads();
+    float off = 0.f;
+    for (int g2 = g + 1; g2 < NGR; ++g2) off += gtot[g2 * TK + c];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int row = g * RPG + i;
+      if (row < rv) dla[qo + (size_t)(r0 + row) * dk + c0 + c] = part[i] + off;
+    }
+    if (g == 0) dlt[((size_t)bh * NC + n) * dk + c0 + c] = part[0] + off;
   }
 }
 
@@ -493,10 +569,23 @@ __global__ __launch_bounds__(kThreads) void k_dla_carry(const float* __restrict_
                                                         int C, int NC) {
   const int n = blockIdx.x, bh = blockIdx.y;
   const int r0 = n * C, r1 = min(L, r0 + C);
-  for (int c = threadIdx.x; c < dk; c += blockDim.x) {
+  // threads (row phase p, channel c): dk channels, blockDim / dk row phases
+  const int nph = blockDim.x >= dk ? blockDim.x / dk : 1;
+  for (int t = threadIdx.x; t < nph * dk; t += blockDim.x) {
+    const int c = t % dk, p = t / dk;
     float off = rs[(size_t)bh * dk + c];
     for (int m = n + 1; m < NC; ++m) off += dlt[((size_t)bh * NC + m) * dk + c];
-    for (int r = r0; r < r1; ++r) dla[((size_t)bh * L + r) * dk + c] += off;
+    float* d = dla + ((size_t)bh * L + r0) * dk + c;
+    int r = r0 + p;
+    for (; r + 3 * nph < r1; r += 4 * nph) {
+      const float a0 = d[(size_t)(r - r0) * dk], a1 = d[(size_t)(r - r0 + nph) * dk],
+                  a2 = d[(size_t)(r - r0 + 2 * nph) * dk], a3 = d[(size_t)(r - r0 + 3 * nph) * dk];
+      d[(size_t)(r - r0) * dk] = a0 + off;
+      d[(size_t)(r - r0 + nph) * dk] = a1 + off;
+      d[(size_t)(r - r0 + 2 * nph) * dk] = a2 + off;
+      d[(size_t)(r - r0 + 3 * nph) * dk] = a3 + off;
+    }
+    for (; r < r1; r += nph) d[(size_t)(r - r0) * dk] += off;
   }
 }
 
