@@ -156,29 +156,56 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   const size_t qo = (size_t)bh * L * dk, vo = (size_t)bh * L * dv;
   const float* dAb = dAw + ((size_t)bh * NC + n) * C * C;
 
-  for (int it = tid; it < C * C; it += kThreads) {
-    const int m = it / C, r = it % C;
-    const float x = dAb[it];
-    const bool dgb = (m >> 4) == (r >> 4);
-    const float xo = dgb ? 0.f : x;
-    const T hi = from_f32<T>(xo);
-    dah[m][r] = hi;
-    dath[r][m] = hi;
-    if constexpr (BF) {
-      const T lo = from_f32<T>(xo - to_f32(hi));
-      dal[m][r] = lo;
-      datl[r][m] = lo;
+  // dA in 4 x 4 blocks per thread: rows and (transposed) columns of a block
+  // are written as 4-element vectors
+  for (int it = tid; it < (C / 4) * (C / 4); it += kThreads) {
+    const int m0 = (it / (C / 4)) * 4, c4 = (it % (C / 4)) * 4;
+    const bool dgb = (m0 >> 4) == (c4 >> 4);  // inside a diagonal 16 x 16 block
+    floatx4 hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const floatx4 x = *reinterpret_cast<const f32x4*>(dAb + (m0 + i) * C + c4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (dgb) dad[m0 + i][(c4 + e) & 15] = x[e];
+        const float xo = dgb ? 0.f : x[e];
+        hi[i][e] = to_f32(from_f32<T>(xo));
+        lo[i][e] = xo - hi[i][e];
+      }
+      store4(&dah[m0 + i][c4], hi[i]);
+      if constexpr (BF) store4(&dal[m0 + i][c4], lo[i]);
     }
-    if (dgb) dad[m][r & 15] = x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      floatx4 th, tl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        th[i] = hi[i][e];
+        tl[i] = lo[i][e];
+      }
+      store4(&dath[c4 + e][m0], th);
+      if constexpr (BF) store4(&datl[c4 + e][m0], tl);
+    }
   }
-  for (int it = tid; it < C * TK; it += kThreads) {
-    const int row = it / TK, c = it % TK;
+  // q, k, cumsum of the tile, 8 channels per unit
+  for (int it = tid; it < C * (TK / 8); it += kThreads) {
+    const int row = it / (TK / 8), c = (it % (TK / 8)) * 8;
     const bool valid = row < rv;
     const int crow = valid ? r0 + row : r0 + rv - 1;
     const size_t gi = qo + (size_t)crow * dk + c0 + c;
-    qf[row][c] = valid ? to_f32(q[gi]) : 0.f;
-    kf[row][c] = valid ? to_f32(k[gi]) : 0.f;
-    bt[row][c] = cum[gi];
+    float x[8];
+    load8(q + gi, x);
+    if (!valid)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    store8(&qf[row][c], x);
+    load8(k + gi, x);
+    if (!valid)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    store8(&kf[row][c], x);
+    load8(cum + gi, x);
+    store8(&bt[row][c], x);
   }
   __syncthreads();
   for (int it = tid; it < C * TK; it += kThreads) {
@@ -198,36 +225,52 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   const T* sp = st_n + so;
   const T* dsp = dst_n + so;
   const bool lo_s = st_lo != nullptr, lo_d = dst_lo != nullptr;
-  for (int kk = 0; kk < dv; kk += M::K) {
-    const int cc = kk + (l >> 4) * M::KPL;
-    typename M::frag bs_[NCW], bd_[NCW], bsl[NCW], bdl[NCW];
+  // The operands of KG consecutive K steps are loaded before their products
+  // are issued, so that a group pays the global-load latency once.
+  constexpr int KG = 8;
+  for (int kk0 = 0; kk0 < dv; kk0 += KG * M::K) {
+    typename M::frag bs_[KG][NCW], bd_[KG][NCW], bsl[KG][NCW], bdl[KG][NCW];
+    typename M::frag ao[KG][NRW], av[KG][NRW];
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct) {
-      const int ch = c0 + (wc + WC * ct) * 16 + (l & 15);
-      bs_[ct] = load_frag<T>(sp + (size_t)ch * dv + cc);
-      bd_[ct] = load_frag<T>(dsp + (size_t)ch * dv + cc);
-      if (lo_s) bsl[ct] = load_frag<T>(st_lo + so + (size_t)ch * dv + cc);
-      if (lo_d) bdl[ct] = load_frag<T>(dst_lo + so + (size_t)ch * dv + cc);
-    }
-#pragma unroll
-    for (int rt = 0; rt < NRW; ++rt) {
-      const int rti = wr + WR * rt;
-      if (rti >= NRT) continue;
-      const int row = rti * 16 + (l & 15);
-      typename M::frag ao, av;
-      if (row < rv) {
-        ao = load_frag<T>(dout + vo + (size_t)(r0 + row) * dv + cc);
-        av = load_frag<T>(v + vo + (size_t)(r0 + row) * dv + cc);
-      } else {
-        ao = typename M::frag{};
-        av = typename M::frag{};
-      }
+    for (int gk = 0; gk < KG; ++gk) {
+      const int kk = kk0 + gk * M::K;
+      if (kk >= dv) break;
+      const int cc = kk + (l >> 4) * M::KPL;
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
-        aq[rt][ct] = M::run(ao, bs_[ct], aq[rt][ct]);
-        ak[rt][ct] = M::run(av, bd_[ct], ak[rt][ct]);
-        if (lo_s) aq[rt][ct] = M::run(ao, bsl[ct], aq[rt][ct]);
-        if (lo_d) ak[rt][ct] = M::run(av, bdl[ct], ak[rt][ct]);
+        const int ch = c0 + (wc + WC * ct) * 16 + (l & 15);
+        bs_[gk][ct] = load_frag<T>(sp + (size_t)ch * dv + cc);
+        bd_[gk][ct] = load_frag<T>(dsp + (size_t)ch * dv + cc);
+        if (lo_s) bsl[gk][ct] = load_frag<T>(st_lo + so + (size_t)ch * dv + cc);
+        if (lo_d) bdl[gk][ct] = load_frag<T>(dst_lo + so + (size_t)ch * dv + cc);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRW; ++rt) {
+        const int rti = wr + WR * rt;
+        if (rti >= NRT) continue;
+        // rows past the end of the sequence read the last row and drop it
+        const int row = rti * 16 + (l & 15), rr = row < rv ? row : rv - 1;
+        ao[gk][rt] = load_frag<T>(dout + vo + (size_t)(r0 + rr) * dv + cc);
+        av[gk][rt] = load_frag<T>(v + vo + (size_t)(r0 + rr) * dv + cc);
+        if (row >= rv) {
+          ao[gk][rt] = typename M::frag{};
+          av[gk][rt] = typename M::frag{};
+        }
+      }
+    }
+#pragma unroll
+    for (int gk = 0; gk < KG; ++gk) {
+      if (kk0 + gk * M::K >= dv) break;
+#pragma unroll
+      for (int rt = 0; rt < NRW; ++rt) {
+        if (wr + WR * rt >= NRT) continue;
+#pragma unroll
+        for (int ct = 0; ct < NCW; ++ct) {
+          aq[rt][ct] = M::run(ao[gk][rt], bs_[gk][ct], aq[rt][ct]);
+          ak[rt][ct] = M::run(av[gk][rt], bd_[gk][ct], ak[rt][ct]);
+          if (lo_s) aq[rt][ct] = M::run(ao[gk][rt], bsl[gk][ct], aq[rt][ct]);
+          if (lo_d) ak[rt][ct] = M::run(av[gk][rt], bdl[gk][ct], ak[rt][ct]);
+        }
       }
     }
   }
@@ -256,25 +299,38 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   // All operands are formed in one pass; each wave then handles the blocks of
   // its own row tiles.
   if constexpr (NRT > 1) {
-    for (int it = tid; it < TK * OC::WQ; it += kThreads) {
-      const int c = it / OC::WQ, col = it % OC::WQ;
+    // 8 consecutive columns (rows of the chunk) of one channel per unit; the
+    // block boundaries of the column layout are multiples of 8
+    static_assert(OC::WQ % 8 == 0 && OC::WK % 8 == 0, "8-column units");
+    for (int it = tid; it < TK * (OC::WQ / 8); it += kThreads) {
+      const int c = it % TK, col = (it / TK) * 8;
       int j = 1;
       while (j + 1 < NRT && col >= OC::OQ(j + 1)) ++j;
       const int r = col - OC::OQ(j);
-      const float x = r < 16 * j ? kf[r][c] * gexp<T>(bt[16 * j][c] - bt[r][c]) : 0.f;
-      const T hi = from_f32<T>(x);
-      opq[c][col] = hi;
-      if constexpr (BF) opql[c][col] = from_f32<T>(x - to_f32(hi));
+      const float z = bt[16 * j][c];
+      float x[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = r + e < 16 * j ? kf[r + e][c] * gexp<T>(z - bt[r + e][c]) : 0.f;
+        lo[e] = x[e] - to_f32(from_f32<T>(x[e]));
+      }
+      store8(&opq[c][col], x);
+      if constexpr (BF) store8(&opql[c][col], lo);
     }
-    for (int it = tid; it < TK * OC::WK; it += kThreads) {
-      const int c = it / OC::WK, col = it % OC::WK;
+    for (int it = tid; it < TK * (OC::WK / 8); it += kThreads) {
+      const int c = it % TK, col = (it / TK) * 8;
       int u = 0;
       while (u + 2 < NRT && col >= OC::OK(u + 1)) ++u;
       const int m = OC::MLO(u) + col - OC::OK(u);
-      const float x = m >= 16 * (u + 1) ? qf[m][c] * gexp<T>(bt[m][c] - bt[16 * u + 15][c]) : 0.f;
-      const T hi = from_f32<T>(x);
-      opk[c][col] = hi;
-      if constexpr (BF) opkl[c][col] = from_f32<T>(x - to_f32(hi));
+      const float z = bt[16 * u + 15][c];
+      float x[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = m + e >= 16 * (u + 1) ? qf[m + e][c] * gexp<T>(bt[m + e][c] - z) : 0.f;
+        lo[e] = x[e] - to_f32(from_f32<T>(x[e]));
+      }
+      store8(&opk[c][col], x);
+      if constexpr (BF) store8(&opkl[c][col], lo);
     }
     __syncthreads();
 #pragma unroll
