@@ -516,16 +516,40 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dv(
   const size_t qo = (size_t)bh * L * dk, vo = (size_t)bh * L * dv;
   const float* Ab = Aw + ((size_t)bh * NC + n) * C * C;
 
-  for (int it = tid; it < C * C; it += kThreads) {
-    const int m = it / C, r = it % C;
-    const float x = Ab[it];
-    const T hi = from_f32<T>(x);
-    ath[r][m] = hi;
-    if constexpr (BF) atl[r][m] = from_f32<T>(x - to_f32(hi));
+  // A^T and dO^T, staged in 4 x 4 blocks per thread (4-element writes)
+  for (int it = tid; it < (C / 4) * (C / 4); it += kThreads) {
+    const int m0 = (it / (C / 4)) * 4, c4 = (it % (C / 4)) * 4;
+    floatx4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = *reinterpret_cast<const f32x4*>(Ab + (m0 + i) * C + c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      floatx4 hi, lo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = to_f32(from_f32<T>(x[i][e]));
+        lo[i] = x[i][e] - hi[i];
+      }
+      store4(&ath[c4 + e][m0], hi);
+      if constexpr (BF) store4(&atl[c4 + e][m0], lo);
+    }
   }
-  for (int it = tid; it < C * TVD; it += kThreads) {
-    const int m = it / TVD, c = it % TVD;
-    dot[c][m] = m < rv ? dout[vo + (size_t)(r0 + m) * dv + j0 + c] : from_f32<T>(0.f);
+  for (int it = tid; it < (C / 4) * (TVD / 4); it += kThreads) {
+    const int m0 = (it / (TVD / 4)) * 4, c4 = (it % (TVD / 4)) * 4;
+    floatx4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + i < rv ? m0 + i : rv - 1;  // rows past the end: read, then 0
+      x[i] = load4(dout + vo + (size_t)(r0 + m) * dv + j0 + c4);
+      if (m0 + i >= rv) x[i] = zero4();
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      floatx4 t;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = x[i][e];
+      store4(&dot[c4 + e][m0], t);
+    }
   }
 
   const int wc = w % WC, wr = w / WC;
@@ -540,14 +564,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dv(
   for (int s0 = 0; s0 < dk; s0 += KSL) {
     const int ks = min(KSL, dk - s0);
     __syncthreads();
-    for (int it = tid; it < C * ks; it += kThreads) {
-      const int m = it / ks, c = it % ks;
-      float x = 0.f;
-      if (m < rv) {
-        const size_t gi = qo + (size_t)(r0 + m) * dk + s0 + c;
-        x = to_f32(k[gi]) * gexp<T>(blast[s0 + c] - cum[gi]);
-      }
-      kt[m][c] = from_f32<T>(x);
+    for (int it = tid; it < C * (ks / 8); it += kThreads) {
+      const int m = it / (ks / 8), c = (it % (ks / 8)) * 8;
+      const int mm = m < rv ? m : rv - 1;
+      const size_t gi = qo + (size_t)(r0 + mm) * dk + s0 + c;
+      float kv[8], bv[8], bl[8], x[8];
+      load8(k + gi, kv);
+      load8(cum + gi, bv);
+      load8(blast + s0 + c, bl);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = m < rv ? kv[e] * gexp<T>(bl[e] - bv[e]) : 0.f;
+      store8(&kt[m][c], x);
     }
     __syncthreads();
     for (int kk = 0; kk < ks; kk += M::K) {
