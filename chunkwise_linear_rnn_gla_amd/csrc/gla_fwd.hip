@@ -102,6 +102,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
   __shared__ __attribute__((aligned(16))) T xl[SPLIT ? 64 : 1][SPLIT ? LDX : 8];
   __shared__ __attribute__((aligned(16))) T ys[64][LDX];
   __shared__ float gam[TS];
+  // The state entering each update, staged for stores of whole row
+  // segments: [i][j] (hi, and lo when split) and, for the transposed copy,
+  // [j][i].
+  constexpr int LDS_ = TS + 16 / (int)sizeof(T);
+  __shared__ __attribute__((aligned(16))) T stg[SPLIT ? 2 : 1][TS][LDS_];
+  __shared__ __attribute__((aligned(16))) T stgT[TS][LDS_];
 
   const int ntj = dv / TS, nti = dk / TS;
   const int lid = xcd_logical(blockIdx.x, gridDim.x);
@@ -190,27 +196,43 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
     }
     // prefetch the next chunk while this one is consumed
     if (step + 1 < nsteps) GLA_STATE_FETCH(REV ? n - 1 : n + 1);
-    __syncthreads();
 
-    // The state entering this chunk's update: S_{n-1} (forward) or dS_n (reverse).
-    if (mode == SEG_FILL && (st_t || st_n)) {
+    // The state entering this chunk's update: S_{n-1} (forward) or dS_n
+    // (reverse), staged in LDS, then stored as 16-byte units of rows.
+    const bool emit = mode == SEG_FILL && (st_t || st_n);
+    if (emit) {
 #pragma unroll
       for (int t = 0; t < NW; ++t) {
         const int tt = w + 4 * t;
         if (tt >= NTT) continue;
         const int ti = tt / NT1, tj = tt % NT1;
-        const int j = j0 + tj * 16 + (l & 15);
-        const int ib = i0 + ti * 16 + (l >> 4) * 4;
-        if (st_t) store4(st_t + (((size_t)bh * NC + n) * dv + j) * dk + ib, acc[t]);
+        const int jl = tj * 16 + (l & 15), il = ti * 16 + (l >> 4) * 4;
+        if (st_t) store4(&stgT[jl][il], acc[t]);
         if (st_n) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const size_t idx = (((size_t)bh * NC + n) * dk + ib + r) * dv + j;
             const T hi = from_f32<T>(acc[t][r]);
-            st_n[idx] = hi;
-            if (SPLIT && st_n_lo) st_n_lo[idx] = from_f32<T>(acc[t][r] - to_f32(hi));
+            stg[0][il + r][jl] = hi;
+            if constexpr (SPLIT) stg[1][il + r][jl] = from_f32<T>(acc[t][r] - to_f32(hi));
           }
         }
+      }
+    }
+    __syncthreads();
+    if (emit) {
+      constexpr int EPU = 16 / (int)sizeof(T);
+      for (int it = tid; it < TS * (TS / EPU); it += kThreads) {
+        const int row = it / (TS / EPU), u = (it % (TS / EPU)) * EPU;
+        if (st_n) {
+          const size_t idx = (((size_t)bh * NC + n) * dk + i0 + row) * dv + j0 + u;
+          *reinterpret_cast<f32x4*>(st_n + idx) = *reinterpret_cast<const f32x4*>(&stg[0][row][u]);
+          if (SPLIT && st_n_lo)
+            *reinterpret_cast<f32x4*>(st_n_lo + idx) =
+                *reinterpret_cast<const f32x4*>(&stg[SPLIT ? 1 : 0][row][u]);
+        }
+        if (st_t)
+          *reinterpret_cast<f32x4*>(st_t + (((size_t)bh * NC + n) * dv + j0 + row) * dk + i0 + u) =
+              *reinterpret_cast<const f32x4*>(&stgT[row][u]);
       }
     }
 #pragma unroll
