@@ -112,6 +112,31 @@ template <> __device__ inline float gexp<bf16>(float x) { return __expf(x); }
 // lives in LDS (or was waited for explicitly, as LDS-DMA copies are).
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4 a + b receives
+// element b of the 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12.
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+__device__ inline bf16x4 ds_read_tr(const bf16* p) {
+  const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s16*)(const_cast<bf16*>(p)));
+  bf16x4 o;
+  __builtin_memcpy(&o, &r, 8);
+  return o;
+}
+__device__ inline bf16x8 join8(bf16x4 a, bf16x4 b) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[e + 4] = b[e]; }
+  return r;
+}
+// The 16x16x32 bf16 MFMA operand of lane (g, n) over K: rows k0 + 8 g .. + 7
+// of column c0 + n of a row-major LDS array (leading dimension ld elements,
+// rows 8-byte aligned), with two transposed reads.
+__device__ inline bf16x8 col_frag_tr(const bf16* x, int ld, int k0, int c0, int l) {
+  const int n = l & 15, g = l >> 4;
+  const bf16* p = x + (k0 + 8 * g + (n >> 2)) * ld + c0 + 4 * (n & 3);
+  return join8(ds_read_tr(p), ds_read_tr(p + 4 * ld));
+}
+
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ inline int wave_id() { return threadIdx.x / kWave; }
 

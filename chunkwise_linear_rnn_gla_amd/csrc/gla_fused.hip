@@ -43,23 +43,6 @@ __device__ inline floatx4 state_times_q(floatx4 s, const float* qrow, floatx4 ac
   return acc;
 }
 
-// ds_read_b64_tr_b16: within each 16-lane group, lane 4 a + b receives
-// element b of the 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12.
-typedef short v4s16 __attribute__((ext_vector_type(4)));
-__device__ inline bf16x4 ds_read_tr(const bf16* p) {
-  const v4s16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4s16*)(const_cast<bf16*>(p)));
-  bf16x4 o;
-  __builtin_memcpy(&o, &r, 8);
-  return o;
-}
-__device__ inline bf16x8 join8(bf16x4 a, bf16x4 b) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { r[e] = a[e]; r[e + 4] = b[e]; }
-  return r;
-}
-
 }  // namespace
 
 // Asynchronous global -> LDS copy of one 16-byte unit per lane: lane i of the

@@ -244,11 +244,19 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
       for (int r = 0; r < 4; ++r) acc[t][r] *= gam[ti * 16 + (l >> 4) * 4 + r];
       for (int kk = 0; kk < C; kk += M::K) {
         const int kr = kk + (l >> 4) * M::KPL;
-        auto a = gather_frag<T>(&xs[kr][ti * 16 + (l & 15)], LDX);
-        auto b = gather_frag<T>(&ys[kr][tj * 16 + (l & 15)], LDX);
+        typename M::frag a, b;
+        if constexpr (sizeof(T) == 2) {  // K runs down the rows: transposed reads
+          a = col_frag_tr(&xs[0][0], LDX, kk, ti * 16, l);
+          b = col_frag_tr(&ys[0][0], LDX, kk, tj * 16, l);
+        } else {
+          a = gather_frag<T>(&xs[kr][ti * 16 + (l & 15)], LDX);
+          b = gather_frag<T>(&ys[kr][tj * 16 + (l & 15)], LDX);
+        }
         acc[t] = M::run(a, b, acc[t]);
         if constexpr (SPLIT) {
-          auto al = gather_frag<T>(&xl[kr][ti * 16 + (l & 15)], LDX);
+          typename M::frag al;
+          if constexpr (sizeof(T) == 2) al = col_frag_tr(&xl[0][0], LDX, kk, ti * 16, l);
+          else al = gather_frag<T>(&xl[kr][ti * 16 + (l & 15)], LDX);
           acc[t] = M::run(al, b, acc[t]);
         }
       }

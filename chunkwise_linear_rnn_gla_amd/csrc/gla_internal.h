@@ -81,7 +81,7 @@ hipError_t launch_seg_output(const Plan& p, const void* q, const void* k, const 
                              const float* cum, const float* h0, const float* seg_in, void* o,
                              float* hT, hipStream_t s);
 
-// ---- two-pass forward (gla_recur.hip) ----
+// ---- two-pass forward (gla_prep.hip, gla_recur.hip) ----
 // Waves per recurrence workgroup needed to hold the state slice: one wave's
 // 16 columns of a 256-channel bf16 or 128-channel fp32 state leave too few
 // registers for the operands.
@@ -91,7 +91,7 @@ constexpr int recur_min_waves(bool bf16, int dk) { return (bf16 ? dk >= 256 : dk
 constexpr int recur_max_waves(bool bf16, int dk) { return (bf16 && dk >= 256) ? 2 : 4; }
 bool recur_supported(int bf16, int C, int dk, int dv, int L);
 // Per (batch-head, chunk) records, in the fragment-blocked layouts of
-// gla_recur.hip: Q~ = Q ⊙ e^B and K~ = K ⊙ e^{b - B} (C x dk each, rows past
+// gla_records.h: Q~ = Q ⊙ e^B and K~ = K ⊙ e^{b - B} (C x dk each, rows past
 // the sequence zero), the chunk's gated score matrix P (C x C) and, for bf16,
 // the low part of its diagonal blocks (C x 16); grec holds e^b then b per key
 // channel, recur_grec_bytes(dk) bytes per chunk.
