@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int i = 0; i < RPT; ++i) av[i] = ra[i];
     if (grp + 1 < NG) fetch(grp + 1);
-    lds_barrier();  // previous slice's readers of qs, ks, bs, tot are done
+    lds_barrier();  // previous slice's readers of qs, ks, bs, als, tot are done
     if (tid < NU) {
       float qv[8], kv[8];
 #pragma unroll
@@ -159,6 +159,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       }
       store8(qs + urow * LDT + uc8, qv);
       store8(ks + urow * LDT + uc8, kv);
+    }
+    // per-row gates alpha = e^{log alpha} (1 at a sub-chunk's first row, where
+    // the diagonal blocks never use it), from the log gates in registers
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = rg * RPT + i;
+      als[row * LDF + ch] = (row & 15) ? gexp<T>(av[i]) : 1.f;
     }
     // chunk-local cumsum: RPT rows per thread, then the preceding groups' totals
     float run = 0.f;
@@ -203,9 +210,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       gr[s0 + tid] = gexp<T>(b);  // the chunk's decay of state row s0 + tid
       gr[dk + s0 + tid] = b;      // and its log
     }
-    PB::gates(bs, als);
+    // both read only what the two barriers above published
     pb.offdiag(qs, ks, bs);
-    lds_barrier();
     pb.diag(qs, ks, als);
   }
   lds_barrier();  // the slice arrays are dead from here on
