@@ -292,9 +292,9 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
     }
   };
 
-  // ot holds the output of chunk pn (-1: none yet), stored during the next
-  // chunk's body, once that chunk's first products are issued, so that the
-  // stores do not wait for the matrix pipeline.
+  // ot holds the output of chunk pn (-1: none yet), stored at the start of
+  // the next chunk's body: its products finished during the barrier, and
+  // the stores are then in flight while that body's products run.
   floatx4 ot[NRT];
   int pn = -1;
   auto flush_out = [&](int n) __attribute__((always_inline)) {
@@ -302,11 +302,11 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
     pn = n;
   };
 
-  // One chunk from record buffer b.  bf16: the state update first (from the
-  // bf16 copy of S_{n-1} that the output products use), so that the next
-  // chunk's products, which need S_n, never wait for this chunk's output
-  // products; then the previous chunk's output is stored and this chunk's
-  // computed into ot.  fp32: output first, then the update.
+  // One chunk from record buffer b, after the previous chunk's output is
+  // stored.  bf16: the state update first (from the bf16 copy of S_{n-1} that
+  // the output products use), so that the next chunk's products, which need
+  // S_n, never wait for this chunk's output products; then this chunk's
+  // output into ot.  fp32: output first, then the update.
   auto body = [&](int n, int b) __attribute__((always_inline)) {
     const unsigned char* base = lds + b * Lay::RBUF;
     const unsigned char* Qs = base + Lay::oQ;
@@ -316,6 +316,7 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
     const float* Gs = reinterpret_cast<const float*>(base + Lay::oG);
     const unsigned char* Vs = lds + Lay::oV + (n % Lay::VNB) * Lay::VB;
     if constexpr (BF) {
+      if constexpr (OUT) flush_out(n);
       // V fragments over token runs 32 kt + 8 g + e at column vc + ln
       bf16x8 vf[C / 32];
 #pragma unroll
@@ -355,7 +356,6 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
         }
       }
       if constexpr (OUT) {
-        flush_out(n);
 #pragma unroll
         for (int jt = 0; jt < NRT; ++jt) ot[jt] = zero4();
         // O^T += S_{n-1}^T Q~^T over pairs of 16-channel tiles
