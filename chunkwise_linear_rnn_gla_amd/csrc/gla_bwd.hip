@@ -155,20 +155,101 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   const int r0 = n * C, rv = min(C, L - r0);
   const size_t qo = (size_t)bh * L * dk, vo = (size_t)bh * L * dv;
   const float* dAb = dAw + ((size_t)bh * NC + n) * C * C;
+  const int wc = w % WC, wr = w / WC;
+  floatx4 aq[NRW][NCW], ak[NRW][NCW];
+#pragma unroll
+  for (int a = 0; a < NRW; ++a)
+#pragma unroll
+    for (int b = 0; b < NCW; ++b) aq[a][b] = ak[a][b] = zero4();
 
-  // dA in 4 x 4 blocks per thread: rows and (transposed) columns of a block
-  // are written as 4-element vectors
-  for (int it = tid; it < (C / 4) * (C / 4); it += kThreads) {
-    const int m0 = (it / (C / 4)) * 4, c4 = (it % (C / 4)) * 4;
+  // Operands of the inter-chunk products for KG K steps at kk0: states (and
+  // their low halves) of this wave's channels, dO and V of its rows.
+  const size_t so = ((size_t)bh * NC + n) * dk * dv;
+  const T* sp = st_n + so;
+  const T* dsp = dst_n + so;
+  const bool lo_s = st_lo != nullptr, lo_d = dst_lo != nullptr;
+  constexpr int KG = 4;
+  struct InterFrags {
+    typename M::frag bs_[KG][NCW], bd_[KG][NCW], bsl[KG][NCW], bdl[KG][NCW];
+    typename M::frag ao[KG][NRW], av[KG][NRW];
+  };
+  auto inter_load = [&](InterFrags& f, int kk0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int gk = 0; gk < KG; ++gk) {
+      const int kk = kk0 + gk * M::K;
+      if (kk >= dv) break;
+      const int cc = kk + (l >> 4) * M::KPL;
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int ch = c0 + (wc + WC * ct) * 16 + (l & 15);
+        f.bs_[gk][ct] = load_frag<T>(sp + (size_t)ch * dv + cc);
+        f.bd_[gk][ct] = load_frag<T>(dsp + (size_t)ch * dv + cc);
+        if (lo_s) f.bsl[gk][ct] = load_frag<T>(st_lo + so + (size_t)ch * dv + cc);
+        if (lo_d) f.bdl[gk][ct] = load_frag<T>(dst_lo + so + (size_t)ch * dv + cc);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRW; ++rt) {
+        const int rti = wr + WR * rt;
+        if (rti >= NRT) continue;
+        // rows past the end of the sequence read the last row and drop it
+        const int row = rti * 16 + (l & 15), rr = row < rv ? row : rv - 1;
+        f.ao[gk][rt] = load_frag<T>(dout + vo + (size_t)(r0 + rr) * dv + cc);
+        f.av[gk][rt] = load_frag<T>(v + vo + (size_t)(r0 + rr) * dv + cc);
+        if (row >= rv) {
+          f.ao[gk][rt] = typename M::frag{};
+          f.av[gk][rt] = typename M::frag{};
+        }
+      }
+    }
+  };
+  auto inter_mma = [&](const InterFrags& f, int gk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt) {
+      if (wr + WR * rt >= NRT) continue;
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        aq[rt][ct] = M::run(f.ao[gk][rt], f.bs_[gk][ct], aq[rt][ct]);
+        ak[rt][ct] = M::run(f.av[gk][rt], f.bd_[gk][ct], ak[rt][ct]);
+        if (lo_s) aq[rt][ct] = M::run(f.ao[gk][rt], f.bsl[gk][ct], aq[rt][ct]);
+        if (lo_d) ak[rt][ct] = M::run(f.av[gk][rt], f.bdl[gk][ct], ak[rt][ct]);
+      }
+    }
+  };
+  // Loads first: this thread's 4 x 4 block of dA and 8-channel unit of the
+  // q, k, cumsum tile (at most one of each per thread), then the first group
+  // of inter-chunk operands, which stays in flight while dA, q, k and the
+  // gates are staged (loads complete in order, so consuming the earlier ones
+  // does not wait for it, and the barriers until its products are LDS-only).
+  static_assert((C / 4) * (C / 4) <= kThreads && C * (TK / 8) <= kThreads, "one unit per thread");
+  const bool has_da = tid < (C / 4) * (C / 4), has_tile = tid < C * (TK / 8);
+  const int m0 = (tid / (C / 4)) * 4, c4 = (tid % (C / 4)) * 4;
+  floatx4 xda[4];
+  if (has_da)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xda[i] = *reinterpret_cast<const f32x4*>(dAb + (m0 + i) * C + c4);
+  const int trow = tid / (TK / 8), tc = (tid % (TK / 8)) * 8;
+  const bool tvalid = trow < rv;
+  const size_t tgi = qo + (size_t)(tvalid ? r0 + trow : r0 + rv - 1) * dk + c0 + tc;
+  Raw8<T> tq_, tk_;
+  Raw8<float> tb_;
+  if (has_tile) {
+    raw_load(tq_, q + tgi);
+    raw_load(tk_, k + tgi);
+    raw_load(tb_, cum + tgi);
+  }
+  InterFrags f0;
+  inter_load(f0, 0);
+
+  // dA rows and (transposed) columns of the block, as 4-element vectors
+  if (has_da) {
     const bool dgb = (m0 >> 4) == (c4 >> 4);  // inside a diagonal 16 x 16 block
     floatx4 hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const floatx4 x = *reinterpret_cast<const f32x4*>(dAb + (m0 + i) * C + c4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (dgb) dad[m0 + i][(c4 + e) & 15] = x[e];
-        const float xo = dgb ? 0.f : x[e];
+        if (dgb) dad[m0 + i][(c4 + e) & 15] = xda[i][e];
+        const float xo = dgb ? 0.f : xda[i][e];
         hi[i][e] = to_f32(from_f32<T>(xo));
         lo[i][e] = xo - hi[i][e];
       }
@@ -187,92 +268,37 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       if constexpr (BF) store4(&datl[c4 + e][m0], tl);
     }
   }
-  // q, k, cumsum of the tile, 8 channels per unit
-  for (int it = tid; it < C * (TK / 8); it += kThreads) {
-    const int row = it / (TK / 8), c = (it % (TK / 8)) * 8;
-    const bool valid = row < rv;
-    const int crow = valid ? r0 + row : r0 + rv - 1;
-    const size_t gi = qo + (size_t)crow * dk + c0 + c;
+  // q, k (0 past the end of the sequence) and the cumsum of the tile
+  if (has_tile) {
     float x[8];
-    load8(q + gi, x);
-    if (!valid)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    store8(&qf[row][c], x);
-    load8(k + gi, x);
-    if (!valid)
+    for (int e = 0; e < 8; ++e) x[e] = tvalid ? raw_get(tq_, e) : 0.f;
+    store8(&qf[trow][tc], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    store8(&kf[row][c], x);
-    load8(cum + gi, x);
-    store8(&bt[row][c], x);
+    for (int e = 0; e < 8; ++e) x[e] = tvalid ? raw_get(tk_, e) : 0.f;
+    store8(&kf[trow][tc], x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = raw_get(tb_, e);
+    store8(&bt[trow][tc], x);
   }
-  __syncthreads();
+  lds_barrier();
   for (int it = tid; it < C * TK; it += kThreads) {
     const int row = it / TK, c = it % TK;
     al[row][c] = (row & 15) ? gexp<T>(bt[row][c] - bt[row - 1][c]) : 1.f;
   }
 
-  const int wc = w % WC, wr = w / WC;
-  floatx4 aq[NRW][NCW], ak[NRW][NCW];
+  // inter-chunk terms: dO S_{n-1}^T and V dS_n^T, reduction over d_v, in
+  // groups of KG K steps whose operands are loaded before their products are
+  // issued.  The first group's loads were issued at the start of the kernel.
 #pragma unroll
-  for (int a = 0; a < NRW; ++a)
+  for (int gk = 0; gk < KG; ++gk)
+    if (gk * M::K < dv) inter_mma(f0, gk);
+  for (int kk0 = KG * M::K; kk0 < dv; kk0 += KG * M::K) {
+    InterFrags f;
+    inter_load(f, kk0);
 #pragma unroll
-    for (int b = 0; b < NCW; ++b) aq[a][b] = ak[a][b] = zero4();
-
-  // inter-chunk terms: dO S_{n-1}^T and V dS_n^T, reduction over d_v
-  const size_t so = ((size_t)bh * NC + n) * dk * dv;
-  const T* sp = st_n + so;
-  const T* dsp = dst_n + so;
-  const bool lo_s = st_lo != nullptr, lo_d = dst_lo != nullptr;
-  // The operands of KG consecutive K steps are loaded before their products
-  // are issued, so that a group pays the global-load latency once.
-  constexpr int KG = 8;
-  for (int kk0 = 0; kk0 < dv; kk0 += KG * M::K) {
-    typename M::frag bs_[KG][NCW], bd_[KG][NCW], bsl[KG][NCW], bdl[KG][NCW];
-    typename M::frag ao[KG][NRW], av[KG][NRW];
-#pragma unroll
-    for (int gk = 0; gk < KG; ++gk) {
-      const int kk = kk0 + gk * M::K;
-      if (kk >= dv) break;
-      const int cc = kk + (l >> 4) * M::KPL;
-#pragma unroll
-      for (int ct = 0; ct < NCW; ++ct) {
-        const int ch = c0 + (wc + WC * ct) * 16 + (l & 15);
-        bs_[gk][ct] = load_frag<T>(sp + (size_t)ch * dv + cc);
-        bd_[gk][ct] = load_frag<T>(dsp + (size_t)ch * dv + cc);
-        if (lo_s) bsl[gk][ct] = load_frag<T>(st_lo + so + (size_t)ch * dv + cc);
-        if (lo_d) bdl[gk][ct] = load_frag<T>(dst_lo + so + (size_t)ch * dv + cc);
-      }
-#pragma unroll
-      for (int rt = 0; rt < NRW; ++rt) {
-        const int rti = wr + WR * rt;
-        if (rti >= NRT) continue;
-        // rows past the end of the sequence read the last row and drop it
-        const int row = rti * 16 + (l & 15), rr = row < rv ? row : rv - 1;
-        ao[gk][rt] = load_frag<T>(dout + vo + (size_t)(r0 + rr) * dv + cc);
-        av[gk][rt] = load_frag<T>(v + vo + (size_t)(r0 + rr) * dv + cc);
-        if (row >= rv) {
-          ao[gk][rt] = typename M::frag{};
-          av[gk][rt] = typename M::frag{};
-        }
-      }
-    }
-#pragma unroll
-    for (int gk = 0; gk < KG; ++gk) {
-      if (kk0 + gk * M::K >= dv) break;
-#pragma unroll
-      for (int rt = 0; rt < NRW; ++rt) {
-        if (wr + WR * rt >= NRT) continue;
-#pragma unroll
-        for (int ct = 0; ct < NCW; ++ct) {
-          aq[rt][ct] = M::run(ao[gk][rt], bs_[gk][ct], aq[rt][ct]);
-          ak[rt][ct] = M::run(av[gk][rt], bd_[gk][ct], ak[rt][ct]);
-          if (lo_s) aq[rt][ct] = M::run(ao[gk][rt], bsl[gk][ct], aq[rt][ct]);
-          if (lo_d) ak[rt][ct] = M::run(av[gk][rt], bdl[gk][ct], ak[rt][ct]);
-        }
-      }
-    }
+    for (int gk = 0; gk < KG; ++gk)
+      if (kk0 + gk * M::K < dv) inter_mma(f, gk);
   }
   __syncthreads();  // al ready
 #pragma unroll
