@@ -54,14 +54,27 @@ __global__ __launch_bounds__(kThreads) void k_chunk_attn(
     const int tj = rem;
     const int ra = ti * 16 + (l & 15), rb = tj * 16 + (l & 15);
     floatx4 acc = zero4();
-    for (int kk = 0; kk < dv; kk += M::K) {
-      const int c = kk + (l >> 4) * M::KPL;
-      typename M::frag a, b;
-      if (ra < rv) a = load_frag<T>(dout + vo + (size_t)(r0 + ra) * dv + c);
-      else a = typename M::frag{};
-      if (rb < rv) b = load_frag<T>(v + vo + (size_t)(r0 + rb) * dv + c);
-      else b = typename M::frag{};
-      acc = M::run(a, b, acc);
+    // the operands of KG K steps are loaded before their products (rows past
+    // the end of the sequence read the last row and are dropped)
+    constexpr int KG = 8;
+    const int rra = ra < rv ? ra : rv - 1, rrb = rb < rv ? rb : rv - 1;
+    for (int kk0 = 0; kk0 < dv; kk0 += KG * M::K) {
+      typename M::frag a[KG], b[KG];
+#pragma unroll
+      for (int gk = 0; gk < KG; ++gk) {
+        const int kk = kk0 + gk * M::K;
+        if (kk >= dv) break;
+        const int c = kk + (l >> 4) * M::KPL;
+        a[gk] = load_frag<T>(dout + vo + (size_t)(r0 + rra) * dv + c);
+        b[gk] = load_frag<T>(v + vo + (size_t)(r0 + rrb) * dv + c);
+        if (ra >= rv) a[gk] = typename M::frag{};
+        if (rb >= rv) b[gk] = typename M::frag{};
+      }
+#pragma unroll
+      for (int gk = 0; gk < KG; ++gk) {
+        if (kk0 + gk * M::K >= dv) break;
+        acc = M::run(a[gk], b[gk], acc);
+      }
     }
     const int col = tj * 16 + (l & 15);
 #pragma unroll
