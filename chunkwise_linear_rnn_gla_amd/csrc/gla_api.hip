@@ -264,7 +264,7 @@ gla_status gla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k
     float* ru = (float*)(ws + p.off_ru);
     float* ri = (float*)(ws + p.off_ri);
     float* rg = (float*)(ws + p.off_rg);
-    GLA_LAUNCH("chunk_prep", launch_chunk_prep(p, q, k, log_alpha, qg, kg, gl, ph, pl, s));
+    GLA_LAUNCH("chunk_prep", launch_chunk_prep(p, q, k, log_alpha, v, qg, kg, gl, ph, pl, s));
     if (p.NSEGR > 1) {
       GLA_LAUNCH("recur_local", launch_chunk_recur(p, 0, qg, kg, ph, pl, gl, v, nullptr, nullptr, ru, rg, s));
       Plan ps = p;

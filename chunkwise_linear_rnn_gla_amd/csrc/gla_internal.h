@@ -97,7 +97,8 @@ bool recur_supported(int bf16, int C, int dk, int dv, int L);
 // channel, recur_grec_bytes(dk) bytes per chunk.
 size_t recur_grec_bytes(int dk);
 hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,
-                             void* qg, void* kg, float* grec, void* ph, void* pl, hipStream_t s);
+                             const void* v, void* qg, void* kg, float* grec, void* ph, void* pl,
+                             hipStream_t s);
 // Per (batch-head, segment p.NSEGR, d_v tile of 16 p.NWVR columns).
 //   out = 1: o from the segment entry state (init = seg_in when NSEGR > 1,
 //            else h0 or null); fin receives the final state when NSEGR == 1.

@@ -2,7 +2,8 @@
 // (gfx950).
 //
 // k_chunk_prep: one workgroup per (batch-head, chunk), all chunks in
-// parallel.  From q, k and log alpha of the chunk it forms
+// parallel (it also prefetches the chunk's V rows for pass 2).  From q, k and
+// log alpha of the chunk it forms
 //   B      = chunk-local inclusive cumsum of log alpha  (per key channel)
 //   Q~     = Q ⊙ e^{B}            (rows of the chunk, I/O type)
 //   K~     = K ⊙ e^{b - B}        (b = B at the chunk's last row)
@@ -55,6 +56,25 @@ __device__ inline void store_masked(unsigned char* dst, const T* src, int last) 
   *reinterpret_cast<f32x4*>(dst) = val;
 }
 
+// Prefetch into the caches: a 4-byte asynchronous LDS copy per lane from byte
+// 128 l of [base, base + bytes) (lanes past the end read nothing), one per
+// 128-byte line of an 8 KB piece.  The LDS bytes written at lds_dummy +
+// 4 * lane are never read.
+__device__ inline void touch_lines(const void* base, int bytes, int l, unsigned lds_dummy) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const unsigned long long a = (unsigned long long)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_dummy)), "v"((unsigned)l * 128u), "s"(r),
+                 "s"(0u)
+               : "memory");
+}
+
 }  // namespace
 
 // =========================================================== pass 1: chunk prep
@@ -65,9 +85,9 @@ __device__ inline void store_masked(unsigned char* dst, const T* src, int last) 
 template <typename T, int C>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_chunk_prep(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ la,
-    unsigned char* __restrict__ qrec, unsigned char* __restrict__ krec,
+    const T* __restrict__ v, unsigned char* __restrict__ qrec, unsigned char* __restrict__ krec,
     unsigned char* __restrict__ prec, unsigned char* __restrict__ lrec,
-    float* __restrict__ grec, int L, int dk, int NC) {
+    float* __restrict__ grec, int L, int dk, int dv, int NC) {
   // q, k slices staged in fp32: the diagonal blocks' vector-ALU reads and the
   // scaled MFMA operands then need no conversion
   using PB = PBuilder<T, C, 4, float>;
@@ -89,6 +109,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   constexpr int SMEM_BYTES = PB::SLICE_BYTES > TAIL_BYTES ? PB::SLICE_BYTES : TAIL_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
   __shared__ float tot[RG][KS];
+  __shared__ __attribute__((aligned(16))) unsigned char vtouch[256];
   float* qs = reinterpret_cast<float*>(smem);
   float* ks = qs + C * LDT;
   float* bs = ks + C * LDT;
@@ -105,6 +126,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   unsigned char* qr = qrec + cb * C * dk * RD::ES;
   unsigned char* kr = krec + cb * C * dk * RD::ES;
   float* gr = grec + cb * (RD::gbytes(dk) / 4);
+
+  // The recurrence pass reads this chunk's V rows next: bring them from HBM
+  // into the caches (the memory-side cache keeps them until then), 8 KB per
+  // wave and touch.  Issued in the last slice, when this workgroup's input
+  // fetches are done (at the kernel's start they would compete with them),
+  // and waited for at the end of the slice loop.
+  auto touch_v = [&]() __attribute__((always_inline)) {
+    const int vbytes = rv * dv * (int)sizeof(T);
+    const unsigned char* vrow = reinterpret_cast<const unsigned char*>(v + ((size_t)bh * L + r0) * dv);
+    const unsigned dmy = (unsigned)(size_t)(__attribute__((address_space(3))) void*)vtouch;
+    for (int p0 = wave_id() * 8192; p0 < vbytes; p0 += (kThreads / kWave) * 8192)
+      touch_lines(vrow + p0, min(8192, vbytes - p0), lane_id(), dmy);
+  };
 
   PB pb;
   pb.init();
@@ -149,6 +183,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int i = 0; i < RPT; ++i) av[i] = ra[i];
     if (grp + 1 < NG) fetch(grp + 1);
+    if (grp == NG - 1) touch_v();
     lds_barrier();  // previous slice's readers of qs, ks, bs, als, tot are done
     if (tid < NU) {
       float qv[8], kv[8];
@@ -214,6 +249,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     pb.offdiag(qs, ks, bs);
     pb.diag(qs, ks, als);
   }
+  // no touch may be in flight when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();  // the slice arrays are dead from here on
   pb.finish(pd, [&](int m, int r, float val) {
     const T hi = from_f32<T>(val);
@@ -246,23 +283,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // =========================================================== launcher
 template <typename T, int C>
 static hipError_t launch_prep_t(const Plan& p, const void* q, const void* k, const float* la,
-                                void* qg, void* kg, float* grec, void* ph, void* pl,
-                                hipStream_t s) {
+                                const void* v, void* qg, void* kg, float* grec, void* ph,
+                                void* pl, hipStream_t s) {
   hipLaunchKernelGGL((k_chunk_prep<T, C>), dim3(p.NC, p.BH), dim3(kThreads), 0, s, (const T*)q,
-                     (const T*)k, la, (unsigned char*)qg, (unsigned char*)kg, (unsigned char*)ph,
-                     (unsigned char*)pl, grec, p.L, p.dk, p.NC);
+                     (const T*)k, la, (const T*)v, (unsigned char*)qg, (unsigned char*)kg,
+                     (unsigned char*)ph, (unsigned char*)pl, grec, p.L, p.dk, p.dv, p.NC);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,
-                             void* qg, void* kg, float* grec, void* ph, void* pl, hipStream_t s) {
+                             const void* v, void* qg, void* kg, float* grec, void* ph, void* pl,
+                             hipStream_t s) {
   if (p.bf16) {
-    if (p.C == 64) return launch_prep_t<bf16, 64>(p, q, k, la, qg, kg, grec, ph, pl, s);
-    return launch_prep_t<bf16, 32>(p, q, k, la, qg, kg, grec, ph, pl, s);
+    if (p.C == 64) return launch_prep_t<bf16, 64>(p, q, k, la, v, qg, kg, grec, ph, pl, s);
+    return launch_prep_t<bf16, 32>(p, q, k, la, v, qg, kg, grec, ph, pl, s);
   }
-  if (p.C == 64) return launch_prep_t<float, 64>(p, q, k, la, qg, kg, grec, ph, pl, s);
-  if (p.C == 32) return launch_prep_t<float, 32>(p, q, k, la, qg, kg, grec, ph, pl, s);
-  return launch_prep_t<float, 16>(p, q, k, la, qg, kg, grec, ph, pl, s);
+  if (p.C == 64) return launch_prep_t<float, 64>(p, q, k, la, v, qg, kg, grec, ph, pl, s);
+  if (p.C == 32) return launch_prep_t<float, 32>(p, q, k, la, v, qg, kg, grec, ph, pl, s);
+  return launch_prep_t<float, 16>(p, q, k, la, v, qg, kg, grec, ph, pl, s);
 }
 
 }  // namespace gla
