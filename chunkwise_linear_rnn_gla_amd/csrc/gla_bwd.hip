@@ -148,20 +148,24 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   constexpr int NRT = C / 16, NCT = TK / 16;
   constexpr int WC = NCT < 4 ? NCT : 4, WR = 4 / WC;
   constexpr int NCW = NCT / WC, NRW = (NRT + WR - 1) / WR;
-  __shared__ __attribute__((aligned(16))) T dah[C][LDA];    // dA, diagonal blocks zeroed
-  __shared__ __attribute__((aligned(16))) T dal[BF ? C : 1][BF ? LDA : 8];
-  __shared__ __attribute__((aligned(16))) T dath[C][LDA];   // transposed: [r][m]
-  __shared__ __attribute__((aligned(16))) T datl[BF ? C : 1][BF ? LDA : 8];
   __shared__ float dad[C][17];                              // diagonal blocks, fp32
-  __shared__ float dgo[2][C][TK + 4];                       // diagonal-block terms of dq, dk
   __shared__ float qf[C][LDK], kf[C][LDK], bt[C][LDK], al[C][LDK];
-  // off-diagonal intra operands, [ch][column] (OffCols), and their low parts
+  // One region serves, in turn, the dq blocks' dA (diagonal blocks zeroed)
+  // and operand, the dk blocks' dA^T ([r][m]) and operand, and the diagonal
+  // blocks' terms of dq and dk (dgo).  Operands are [ch][column] (OffCols),
+  // each with its low part for bf16.
   using OC = OffCols<M::K, C>;
-  constexpr int LDQ = OC::WQ + PT, LDKO = OC::WK + PT;
-  __shared__ __attribute__((aligned(16))) T opq[TK][LDQ];
-  __shared__ __attribute__((aligned(16))) T opk[TK][LDKO];
-  __shared__ __attribute__((aligned(16))) T opql[BF ? TK : 1][BF ? LDQ : 8];
-  __shared__ __attribute__((aligned(16))) T opkl[BF ? TK : 1][BF ? LDKO : 8];
+  constexpr int LDO = (OC::WQ > OC::WK ? OC::WQ : OC::WK) + PT;
+  constexpr int DA_BYTES = C * LDA * (int)sizeof(T), DAL_BYTES = BF ? DA_BYTES : 0;
+  constexpr int OP_BYTES = TK * LDO * (int)sizeof(T), OPL_BYTES = BF ? OP_BYTES : 0;
+  constexpr int OFF_BYTES = DA_BYTES + DAL_BYTES + OP_BYTES + OPL_BYTES;
+  constexpr int DGO_BYTES = 2 * C * (TK + 4) * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char ubuf[OFF_BYTES > DGO_BYTES ? OFF_BYTES : DGO_BYTES];
+  auto da = reinterpret_cast<T(*)[LDA]>(ubuf);
+  auto dal = reinterpret_cast<T(*)[LDA]>(ubuf + DA_BYTES);
+  auto op = reinterpret_cast<T(*)[LDO]>(ubuf + DA_BYTES + DAL_BYTES);
+  auto opl = reinterpret_cast<T(*)[LDO]>(ubuf + DA_BYTES + DAL_BYTES + OP_BYTES);
+  auto dgo = reinterpret_cast<float(*)[C][TK + 4]>(ubuf);
 
   const int n = blockIdx.x, c0 = blockIdx.y * TK, bh = blockIdx.z;
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -253,34 +257,42 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   InterFrags f0;
   inter_load(f0, 0);
 
-  // dA rows and (transposed) columns of the block, as 4-element vectors
-  if (has_da) {
+  // dA rows of the block as 4-element vectors (hi / lo split, the diagonal
+  // blocks zeroed and kept in fp32 apart); with transpose, its columns
+  auto stage_da = [&](bool transpose) __attribute__((always_inline)) {
+    if (!has_da) return;
     const bool dgb = (m0 >> 4) == (c4 >> 4);  // inside a diagonal 16 x 16 block
     floatx4 hi[4], lo[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (dgb) dad[m0 + i][(c4 + e) & 15] = xda[i][e];
+        if (dgb && !transpose) dad[m0 + i][(c4 + e) & 15] = xda[i][e];
         const float xo = dgb ? 0.f : xda[i][e];
         hi[i][e] = to_f32(from_f32<T>(xo));
         lo[i][e] = xo - hi[i][e];
       }
-      store4(&dah[m0 + i][c4], hi[i]);
-      if constexpr (BF) store4(&dal[m0 + i][c4], lo[i]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      floatx4 th, tl;
+    if (!transpose) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        th[i] = hi[i][e];
-        tl[i] = lo[i][e];
+        store4(&da[m0 + i][c4], hi[i]);
+        if constexpr (BF) store4(&dal[m0 + i][c4], lo[i]);
       }
-      store4(&dath[c4 + e][m0], th);
-      if constexpr (BF) store4(&datl[c4 + e][m0], tl);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        floatx4 th, tl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          th[i] = hi[i][e];
+          tl[i] = lo[i][e];
+        }
+        store4(&da[c4 + e][m0], th);
+        if constexpr (BF) store4(&dal[c4 + e][m0], tl);
+      }
     }
-  }
+  };
+  stage_da(false);
   // q, k (0 past the end of the sequence) and the cumsum of the tile
   if (has_tile) {
     float x[8];
@@ -335,8 +347,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   // of each block (both factors <= 1):
   //   dq rows of sub-chunk j:  e^{B_m - z_j} ⊙ [dA_off (K ⊙ e^{z_j - B})]
   //   dk rows of sub-chunk u:  e^{z'_u - B_r} ⊙ [dA_off^T (Q ⊙ e^{B - z'_u})]
-  // All operands are formed in one pass; each wave then handles the blocks of
-  // its own row tiles.
+  // First the dq blocks, then the dk blocks in the same LDS: each operand is
+  // formed in one pass, then every wave handles the blocks of its row tiles.
   if constexpr (NRT > 1) {
     // 8 consecutive columns (rows of the chunk) of one channel per unit; the
     // block boundaries of the column layout are multiples of 8
@@ -353,9 +365,37 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         x[e] = r + e < 16 * j ? kf[r + e][c] * gexp<T>(z - bt[r + e][c]) : 0.f;
         lo[e] = x[e] - to_f32(from_f32<T>(x[e]));
       }
-      store8(&opq[c][col], x);
-      if constexpr (BF) store8(&opql[c][col], lo);
+      store8(&op[c][col], x);
+      if constexpr (BF) store8(&opl[c][col], lo);
     }
+    __syncthreads();
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt) {
+      const int j = wr + WR * rt;
+      if (j < 1 || j >= NRT) continue;
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int c = (wc + WC * ct) * 16 + (l & 15);
+        floatx4 t4 = zero4();
+        for (int kk = 0; kk < OC::KQ(j); kk += M::K) {
+          const int kc = kk + (l >> 4) * M::KPL;
+          auto b = load_frag<T>(&op[c][OC::OQ(j) + kc]);
+          auto ah = load_frag<T>(&da[j * 16 + (l & 15)][kc]);
+          t4 = M::run(ah, b, t4);
+          if constexpr (BF) {
+            t4 = M::run(load_frag<T>(&dal[j * 16 + (l & 15)][kc]), b, t4);
+            t4 = M::run(ah, load_frag<T>(&opl[c][OC::OQ(j) + kc]), t4);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = j * 16 + (l >> 4) * 4 + r;
+          aq[rt][ct][r] += gexp<T>(bt[row][c] - bt[16 * j][c]) * t4[r];
+        }
+      }
+    }
+    __syncthreads();  // done with dA and the dq operand
+    stage_da(true);
     for (int it = tid; it < TK * (OC::WK / 8); it += kThreads) {
       const int c = it % TK, col = (it / TK) * 8;
       int u = 0;
@@ -368,58 +408,37 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         x[e] = m + e >= 16 * (u + 1) ? qf[m + e][c] * gexp<T>(bt[m + e][c] - z) : 0.f;
         lo[e] = x[e] - to_f32(from_f32<T>(x[e]));
       }
-      store8(&opk[c][col], x);
-      if constexpr (BF) store8(&opkl[c][col], lo);
+      store8(&op[c][col], x);
+      if constexpr (BF) store8(&opl[c][col], lo);
     }
     __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
-      const int rti = wr + WR * rt;
-      if (rti >= NRT) continue;
+      const int u = wr + WR * rt;
+      if (u + 1 >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
-        if (rti >= 1) {
-          const int j = rti;
-          floatx4 t4 = zero4();
-          for (int kk = 0; kk < OC::KQ(j); kk += M::K) {
-            const int kc = kk + (l >> 4) * M::KPL;
-            auto b = load_frag<T>(&opq[c][OC::OQ(j) + kc]);
-            auto ah = load_frag<T>(&dah[j * 16 + (l & 15)][kc]);
-            t4 = M::run(ah, b, t4);
-            if constexpr (BF) {
-              t4 = M::run(load_frag<T>(&dal[j * 16 + (l & 15)][kc]), b, t4);
-              t4 = M::run(ah, load_frag<T>(&opql[c][OC::OQ(j) + kc]), t4);
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = j * 16 + (l >> 4) * 4 + r;
-            aq[rt][ct][r] += gexp<T>(bt[row][c] - bt[16 * j][c]) * t4[r];
+        floatx4 t4 = zero4();
+        for (int kk = OC::MLO(u); kk < C; kk += M::K) {
+          const int kc = kk + (l >> 4) * M::KPL;
+          const int oc = OC::OK(u) + kc - OC::MLO(u);
+          auto b = load_frag<T>(&op[c][oc]);
+          auto ah = load_frag<T>(&da[u * 16 + (l & 15)][kc]);
+          t4 = M::run(ah, b, t4);
+          if constexpr (BF) {
+            t4 = M::run(load_frag<T>(&dal[u * 16 + (l & 15)][kc]), b, t4);
+            t4 = M::run(ah, load_frag<T>(&opl[c][oc]), t4);
           }
         }
-        if (rti + 1 < NRT) {
-          const int u = rti;
-          floatx4 t4 = zero4();
-          for (int kk = OC::MLO(u); kk < C; kk += M::K) {
-            const int kc = kk + (l >> 4) * M::KPL;
-            const int oc = OC::OK(u) + kc - OC::MLO(u);
-            auto b = load_frag<T>(&opk[c][oc]);
-            auto ah = load_frag<T>(&dath[u * 16 + (l & 15)][kc]);
-            t4 = M::run(ah, b, t4);
-            if constexpr (BF) {
-              t4 = M::run(load_frag<T>(&datl[u * 16 + (l & 15)][kc]), b, t4);
-              t4 = M::run(ah, load_frag<T>(&opkl[c][oc]), t4);
-            }
-          }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = u * 16 + (l >> 4) * 4 + r;
-            ak[rt][ct][r] += gexp<T>(bt[16 * u + 15][c] - bt[row][c]) * t4[r];
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int row = u * 16 + (l >> 4) * 4 + r;
+          ak[rt][ct][r] += gexp<T>(bt[16 * u + 15][c] - bt[row][c]) * t4[r];
         }
       }
     }
+    __syncthreads();  // the diagonal terms below reuse the region
   }
   // diagonal sub-chunk blocks, fp32 VALU with running gate products.  Thread
   // (dq or dk, block b, channel c) keeps the block's 16 gates and its 16 k (or
