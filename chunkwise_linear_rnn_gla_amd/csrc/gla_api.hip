@@ -339,22 +339,20 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
   void* st_lo = p.bf16 ? (void*)(ws + p.off_stlo) : nullptr;
   void* dst_lo = p.bf16 ? (void*)(ws + p.off_dstlo) : nullptr;
 
-  // recompute the chunk states (not stored by the forward)
+  // recompute the chunk states (not stored by the forward), and the reverse
+  // recurrence of the state gradient: independent, so one launch runs both
   GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
   if (p.NSEG > 1) {
     GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, p.bf16, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, sg, s));
     GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, sg, h0, seg_u, seg_in, hT, s));
     GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, seg_in, nullptr, st_n, st_lo, nullptr, nullptr, nullptr, s));
-  } else {
-    GLA_LAUNCH("chunk_state", launch_chunk_state(p, 0, SEG_FILL, p.bf16, k, v, cum, h0, nullptr, nullptr, st_n, st_lo, hT, nullptr, nullptr, s));
-  }
-  // reverse recurrence of the state gradient
-  if (p.NSEG > 1) {
     GLA_LAUNCH("chunk_state_rev_local", launch_chunk_state(p, 1, SEG_LOCAL, p.bf16, q, dout, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, sg, s));
     GLA_LAUNCH("segment_scan_rev", launch_segment_scan(p, 1, sg, dhT, seg_u, seg_in, dh0, s));
     GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, seg_in, dst_t, dst_n, dst_lo, nullptr, nullptr, nullptr, s));
   } else {
-    GLA_LAUNCH("chunk_state_rev", launch_chunk_state(p, 1, SEG_FILL, p.bf16, q, dout, cum, dhT, nullptr, dst_t, dst_n, dst_lo, dh0, nullptr, nullptr, s));
+    const StateJob fwd{0, SEG_FILL, k, v, cum, h0, nullptr, nullptr, st_n, st_lo, hT, nullptr, nullptr};
+    const StateJob rev{1, SEG_FILL, q, dout, cum, dhT, nullptr, dst_t, dst_n, dst_lo, dh0, nullptr, nullptr};
+    GLA_LAUNCH("chunk_state_pair", launch_chunk_state_pair(p, p.bf16, fwd, rev, s));
   }
   GLA_LAUNCH("chunk_attn", launch_chunk_attn(p, q, k, v, dout, cum, Aw, dAw, s));
   GLA_LAUNCH("chunk_dqdk", launch_chunk_dqdk(p, q, k, v, dout, cum, st_n, st_lo, dst_n,

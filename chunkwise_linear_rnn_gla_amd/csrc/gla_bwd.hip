@@ -93,15 +93,15 @@ __global__ __launch_bounds__(kThreads) void k_chunk_attn(
   PB pb;
   pb.init();
   for (int s0 = 0; s0 < dk; s0 += KS) {
-    __syncthreads();
+    lds_barrier();
     PB::stage(q, k, cum, qo, r0, rv, dk, s0, qs, ks, bs, nullptr);
-    __syncthreads();
+    lds_barrier();
     PB::gates(bs, als);
     pb.offdiag(qs, ks, bs);
-    __syncthreads();
+    lds_barrier();
     pb.diag(qs, ks, als);
   }
-  __syncthreads();
+  lds_barrier();
   pb.finish(pd, [&](int m, int r, float val) { Ab[m * C + r] = val; });
 }
 
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     for (int gk = 0; gk < KG; ++gk)
       if (kk0 + gk * M::K < dv) inter_mma(f, gk);
   }
-  __syncthreads();  // al ready
+  lds_barrier();  // al ready
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
     const int rti = wr + WR * rt;
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       store8(&op[c][col], x);
       if constexpr (BF) store8(&opl[c][col], lo);
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
       const int j = wr + WR * rt;
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         }
       }
     }
-    __syncthreads();  // done with dA and the dq operand
+    lds_barrier();  // done with dA and the dq operand
     stage_da(true);
     for (int it = tid; it < TK * (OC::WK / 8); it += kThreads) {
       const int c = it % TK, col = (it / TK) * 8;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       store8(&op[c][col], x);
       if constexpr (BF) store8(&opl[c][col], lo);
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
       const int u = wr + WR * rt;
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         }
       }
     }
-    __syncthreads();  // the diagonal terms below reuse the region
+    lds_barrier();  // the diagonal terms below reuse the region
   }
   // diagonal sub-chunk blocks, fp32 VALU with running gate products.  Thread
   // (dq or dk, block b, channel c) keeps the block's 16 gates and its 16 k (or
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
     const int rti = wr + WR * rt;
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       }
     }
   }
-  __syncthreads();  // everyone is done with bt / al / the operands
+  lds_barrier();  // everyone is done with bt / al / the operands
   float* dlb = &al[0][0];  // reuse: dlog b of the tile, [C][LDK]
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // chunk-local reverse cumsum of dlog b, and the chunk total: thread
   // (row group g, channel c) sums its RPG rows from the bottom, then adds the
   // totals of the row groups below it
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       part[i] = s;
     }
     gtot[g * TK + c] = s;
-    __syncthreads();
+    lds_barrier();
     float off = 0.f;
     for (int g2 = g + 1; g2 < NGR; ++g2) off += gtot[g2 * TK + c];
 #pragma unroll
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dv(
   const float* blast = cum + qo + (size_t)(r0 + rv - 1) * dk;
   for (int s0 = 0; s0 < dk; s0 += KSL) {
     const int ks = min(KSL, dk - s0);
-    __syncthreads();
+    lds_barrier();
     for (int it = tid; it < C * (ks / 8); it += kThreads) {
       const int m = it / (ks / 8), c = (it % (ks / 8)) * 8;
       const int mm = m < rv ? m : rv - 1;
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dv(
       for (int e = 0; e < 8; ++e) x[e] = m < rv ? kv[e] * gexp<T>(bl[e] - bv[e]) : 0.f;
       store8(&kt[m][c], x);
     }
-    __syncthreads();
+    lds_barrier();
     for (int kk = 0; kk < ks; kk += M::K) {
       const int kc = kk + (l >> 4) * M::KPL;
       typename M::frag b[NCW];

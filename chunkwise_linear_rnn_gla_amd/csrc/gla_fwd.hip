@@ -85,13 +85,29 @@ hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t 
 // Workgroups are numbered so that the tiles of one (batch, head) are
 // consecutive within one XCD (workgroup w runs on XCD w % 8): the tiles that
 // re-read the same k / v / cumsum rows then share an L2.
-template <typename T, int TS, int REV, int SPLIT>
+//
+// One launch can run two jobs (the forward recurrence of S and the reverse one
+// of dS): workgroups below nblk0 take job0, the rest job1, so that the two
+// chains, each mostly waiting on its own latencies, share the compute units.
+template <typename T, int TS, int SPLIT>
 __global__ __launch_bounds__(kThreads) void k_chunk_state(
-    const T* __restrict__ X, const T* __restrict__ Y, const float* __restrict__ cum,
-    const float* __restrict__ init, const float* __restrict__ seg_in, T* __restrict__ st_t,
-    T* __restrict__ st_n, T* __restrict__ st_n_lo, float* __restrict__ end_out,
-    float* __restrict__ seg_out, float* __restrict__ seg_g, int L, int dk, int dv, int C, int NC,
-    int NSEG, int seg_chunks, int mode) {
+    StateJob job0, StateJob job1, int nblk0, const float* __restrict__ cum, int L, int dk, int dv,
+    int C, int NC, int NSEG, int seg_chunks) {
+  const bool second = blockIdx.x >= (unsigned)nblk0;
+  const StateJob& J = second ? job1 : job0;
+  const int bid = second ? (int)blockIdx.x - nblk0 : (int)blockIdx.x;
+  const int nblk = second ? (int)gridDim.x - nblk0 : nblk0;
+  const int REV = J.rev, mode = J.mode;
+  const T* __restrict__ X = static_cast<const T*>(J.X);
+  const T* __restrict__ Y = static_cast<const T*>(J.Y);
+  const float* __restrict__ init = J.init;
+  const float* __restrict__ seg_in = J.seg_in;
+  T* __restrict__ st_t = static_cast<T*>(J.st_t);
+  T* __restrict__ st_n = static_cast<T*>(J.st_n);
+  T* __restrict__ st_n_lo = static_cast<T*>(J.st_n_lo);
+  float* __restrict__ end_out = J.end_out;
+  float* __restrict__ seg_out = J.seg_out;
+  float* __restrict__ seg_g = J.seg_g;
   using M = Mma<T>;
   constexpr int NT1 = TS / 16, NTT = NT1 * NT1, NW = (NTT + 3) / 4;
   constexpr int LDX = TS + gather_pad<T>(TS);    // row-major [token][channel], padded
@@ -110,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
   __shared__ __attribute__((aligned(16))) T stgT[TS][LDS_];
 
   const int ntj = dv / TS, nti = dk / TS;
-  const int lid = xcd_logical(blockIdx.x, gridDim.x);
+  const int lid = xcd_logical(bid, nblk);
   const int j0 = (lid % ntj) * TS, i0 = ((lid / ntj) % nti) * TS;
   const int z = lid / (ntj * nti), bh = z / NSEG, seg = z % NSEG;
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
@@ -235,29 +251,53 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
               *reinterpret_cast<const f32x4*>(&stgT[row][u]);
       }
     }
+    if constexpr (sizeof(T) == 2) {
+      // bf16: K runs down the rows (transposed reads), at most two K steps
+      // (C <= 64).  Tile t of wave w is (ti, tj) = ((w + 4 t) / NT1, (w + 4 t)
+      // % NT1); every fragment of the step is read before the products.
+      constexpr int KMAX = 64 / M::K;
+      typename M::frag fa[NW][KMAX], fl[NW][KMAX], fb[NW][KMAX];
 #pragma unroll
-    for (int t = 0; t < NW; ++t) {
-      const int tt = w + 4 * t;
-      if (tt >= NTT) continue;
-      const int ti = tt / NT1, tj = tt % NT1;
+      for (int t = 0; t < NW; ++t) {
+        const int tt = w + 4 * t;
+        if (tt >= NTT) continue;
+        const int ti = tt / NT1, tj = tt % NT1;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] *= gam[ti * 16 + (l >> 4) * 4 + r];
-      for (int kk = 0; kk < C; kk += M::K) {
-        const int kr = kk + (l >> 4) * M::KPL;
-        typename M::frag a, b;
-        if constexpr (sizeof(T) == 2) {  // K runs down the rows: transposed reads
-          a = col_frag_tr(&xs[0][0], LDX, kk, ti * 16, l);
-          b = col_frag_tr(&ys[0][0], LDX, kk, tj * 16, l);
-        } else {
-          a = gather_frag<T>(&xs[kr][ti * 16 + (l & 15)], LDX);
-          b = gather_frag<T>(&ys[kr][tj * 16 + (l & 15)], LDX);
+        for (int ks = 0; ks < KMAX; ++ks) {
+          if (ks * M::K >= C) continue;
+          fa[t][ks] = col_frag_tr(&xs[0][0], LDX, ks * M::K, ti * 16, l);
+          fb[t][ks] = col_frag_tr(&ys[0][0], LDX, ks * M::K, tj * 16, l);
+          if constexpr (SPLIT) fl[t][ks] = col_frag_tr(&xl[0][0], LDX, ks * M::K, ti * 16, l);
         }
-        acc[t] = M::run(a, b, acc[t]);
-        if constexpr (SPLIT) {
-          typename M::frag al;
-          if constexpr (sizeof(T) == 2) al = col_frag_tr(&xl[0][0], LDX, kk, ti * 16, l);
-          else al = gather_frag<T>(&xl[kr][ti * 16 + (l & 15)], LDX);
-          acc[t] = M::run(al, b, acc[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
+        const int tt = w + 4 * t;
+        if (tt >= NTT) continue;
+        const int ti = tt / NT1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] *= gam[ti * 16 + (l >> 4) * 4 + r];
+#pragma unroll
+        for (int ks = 0; ks < KMAX; ++ks) {
+          if (ks * M::K >= C) continue;
+          acc[t] = M::run(fa[t][ks], fb[t][ks], acc[t]);
+          if constexpr (SPLIT) acc[t] = M::run(fl[t][ks], fb[t][ks], acc[t]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NW; ++t) {
+        const int tt = w + 4 * t;
+        if (tt >= NTT) continue;
+        const int ti = tt / NT1, tj = tt % NT1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] *= gam[ti * 16 + (l >> 4) * 4 + r];
+        for (int kk = 0; kk < C; kk += M::K) {
+          const int kr = kk + (l >> 4) * M::KPL;
+          const typename M::frag a = gather_frag<T>(&xs[kr][ti * 16 + (l & 15)], LDX);
+          const typename M::frag b = gather_frag<T>(&ys[kr][tj * 16 + (l & 15)], LDX);
+          acc[t] = M::run(a, b, acc[t]);
+          if constexpr (SPLIT) acc[t] = M::run(gather_frag<T>(&xl[kr][ti * 16 + (l & 15)], LDX), b, acc[t]);
         }
       }
     }
@@ -289,44 +329,44 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
 
 #undef GLA_STATE_FETCH
 
-template <typename T, int TS, int REV, int SPLIT>
-static hipError_t launch_cs(const Plan& p, int mode, const void* X, const void* Y,
-                            const float* cum, const float* init, const float* seg_in,
-                            void* st_t, void* st_n, void* st_n_lo, float* end_out,
-                            float* seg_out, float* seg_g, hipStream_t s) {
-  dim3 grid((p.dv / TS) * (p.dk / TS) * p.BH * p.NSEG);
-  hipLaunchKernelGGL((k_chunk_state<T, TS, REV, SPLIT>), grid, dim3(kThreads), 0, s,
-                     (const T*)X, (const T*)Y, cum, init, seg_in, (T*)st_t, (T*)st_n,
-                     (T*)st_n_lo, end_out, seg_out, seg_g, p.L, p.dk, p.dv, p.C, p.NC, p.NSEG,
-                     p.seg_chunks, mode);
+template <typename T, int TS, int SPLIT>
+static hipError_t launch_cs(const Plan& p, const StateJob& a, const StateJob* b, hipStream_t s) {
+  const int per = (p.dv / TS) * (p.dk / TS) * p.BH * p.NSEG;
+  hipLaunchKernelGGL((k_chunk_state<T, TS, SPLIT>), dim3(b ? 2 * per : per), dim3(kThreads), 0, s,
+                     a, b ? *b : a, per, cum_of(a), p.L, p.dk, p.dv, p.C, p.NC, p.NSEG,
+                     p.seg_chunks);
   return hipGetLastError();
 }
 
-template <typename T, int REV, int SPLIT>
-static hipError_t launch_cs_ts(const Plan& p, int mode, const void* X, const void* Y,
-                               const float* cum, const float* init, const float* seg_in,
-                               void* st_t, void* st_n, void* st_n_lo, float* end_out,
-                               float* seg_out, float* seg_g, hipStream_t s) {
+template <typename T, int SPLIT>
+static hipError_t launch_cs_ts(const Plan& p, const StateJob& a, const StateJob* b,
+                               hipStream_t s) {
   switch (p.TS) {
-    case 64: return launch_cs<T, 64, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
-    case 32: return launch_cs<T, 32, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
-    default: return launch_cs<T, 16, REV, SPLIT>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
+    case 64: return launch_cs<T, 64, SPLIT>(p, a, b, s);
+    case 32: return launch_cs<T, 32, SPLIT>(p, a, b, s);
+    default: return launch_cs<T, 16, SPLIT>(p, a, b, s);
   }
+}
+
+static hipError_t launch_state_jobs(const Plan& p, int split, const StateJob& a,
+                                    const StateJob* b, hipStream_t s) {
+  if (p.bf16) return split ? launch_cs_ts<bf16, 1>(p, a, b, s) : launch_cs_ts<bf16, 0>(p, a, b, s);
+  return launch_cs_ts<float, 0>(p, a, b, s);
 }
 
 hipError_t launch_chunk_state(const Plan& p, int rev, int mode, int split, const void* X,
                               const void* Y, const float* cum, const float* init,
                               const float* seg_in, void* st_t, void* st_n, void* st_n_lo,
                               float* end_out, float* seg_out, float* seg_g, hipStream_t s) {
-  if (p.bf16) {
-    if (split)
-      return rev ? launch_cs_ts<bf16, 1, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s)
-                 : launch_cs_ts<bf16, 0, 1>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, st_n_lo, end_out, seg_out, seg_g, s);
-    return rev ? launch_cs_ts<bf16, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s)
-               : launch_cs_ts<bf16, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s);
-  }
-  return rev ? launch_cs_ts<float, 1, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s)
-             : launch_cs_ts<float, 0, 0>(p, mode, X, Y, cum, init, seg_in, st_t, st_n, nullptr, end_out, seg_out, seg_g, s);
+  const StateJob a{rev, mode, X, Y, cum, init, seg_in, st_t, st_n, split ? st_n_lo : nullptr,
+                   end_out, seg_out, seg_g};
+  return launch_state_jobs(p, split, a, nullptr, s);
+}
+
+hipError_t launch_chunk_state_pair(const Plan& p, int split, const StateJob& a, const StateJob& b,
+                                   hipStream_t s) {
+  if (a.cum != b.cum) return hipErrorInvalidValue;
+  return launch_state_jobs(p, split, a, &b, s);
 }
 
 // ------------------------------------------------------------------ segment scan

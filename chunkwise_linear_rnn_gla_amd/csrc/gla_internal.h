@@ -54,6 +54,22 @@ hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t 
 //   mode SEG_FILL  : start from seg_in[seg] (or init / zeros if NSEG == 1),
 //                    writes per-chunk states, end state -> end_out (last seg)
 enum StateMode { SEG_LOCAL = 0, SEG_FILL = 1 };
+// The arguments of one recurrence (as for launch_chunk_state).
+struct StateJob {
+  int rev, mode;
+  const void* X;
+  const void* Y;
+  const float* cum;
+  const float* init;
+  const float* seg_in;
+  void* st_t;
+  void* st_n;
+  void* st_n_lo;
+  float* end_out;
+  float* seg_out;
+  float* seg_g;
+};
+inline const float* cum_of(const StateJob& j) { return j.cum; }
 // split (bf16 only): hi/lo operand split, and st_n_lo receives the low part of
 // the states written to st_n.
 // In SEG_LOCAL mode seg_g (if not null) receives each segment's total log decay
@@ -62,6 +78,11 @@ hipError_t launch_chunk_state(const Plan& p, int rev, int mode, int split, const
                               const void* Y, const float* cum, const float* init,
                               const float* seg_u_in, void* st_t, void* st_n, void* st_n_lo,
                               float* end_out, float* seg_u_out, float* seg_g, hipStream_t s);
+// Two recurrences over the same segments and cumsum in one launch (the
+// workgroups of a first, then those of b), e.g. the forward recurrence of S
+// and the reverse one of dS, which are independent.
+hipError_t launch_chunk_state_pair(const Plan& p, int split, const StateJob& a, const StateJob& b,
+                                   hipStream_t s);
 // Combine per-segment local states: seg_in[seg] = state entering segment seg
 // (forward order, or reverse order when rev), end_out = final state.
 hipError_t launch_segment_scan(const Plan& p, int rev, const float* seg_g, const float* init,
