@@ -114,7 +114,7 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     size_t f = 0;
     P.off_qg = f; f = align_up(f + BH * NCC * dk * P.esize);
     P.off_kg = f; f = align_up(f + BH * NCC * dk * P.esize);
-    P.off_ph = f; f = align_up(f + BH * NCC * C * P.esize);
+    P.off_ph = f; f = align_up(f + BH * P.NC * recur_prec_bytes(bf16, C));
     P.off_pl = f; f = align_up(f + (bf16 ? BH * NCC * 16 * P.esize : 0));
     P.off_gl = f; f = align_up(f + BH * P.NC * recur_grec_bytes(dk));
     P.off_ru = f; f = align_up(f + (P.NSEGR > 1 ? BH * P.NSEGR * S * 4 : 0));

@@ -117,6 +117,8 @@ bool recur_supported(int bf16, int C, int dk, int dv, int L);
 // the low part of its diagonal blocks (C x 16); grec holds e^b then b per key
 // channel, recur_grec_bytes(dk) bytes per chunk.
 size_t recur_grec_bytes(int dk);
+// Bytes of one chunk's packed P record (row blocks above the diagonal left out).
+size_t recur_prec_bytes(int is_bf16, int C);
 hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,
                              const void* v, void* qg, void* kg, float* grec, void* ph, void* pl,
                              hipStream_t s);

@@ -260,14 +260,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
   });
   lds_barrier();
-  // P as row blocks (jt, column group); unit g of a row = its EPU columns.
+  // P as row blocks (jt, column group), the groups wholly above the
+  // diagonal left out (RecDims::pblock); unit g of a row = its EPU columns.
   // Entries above the diagonal were never written to ps: they are stored as
   // 0 here.
-  constexpr int PUR = C / EPU, NPG = C / KS;
-  unsigned char* pr = prec + cb * C * C * RD::ES;
+  constexpr int PUR = C / EPU;
+  unsigned char* pr = prec + cb * RD::pblocks(C) * 1024;
   for (int it = tid; it < C * PUR; it += kThreads) {
-    const int row = it / PUR, uu = it % PUR;
-    store_masked<T>(pr + ((row >> 4) * NPG + (uu >> 2)) * 1024 + row_slot(row & 15, uu & 3) * 16,
+    const int row = it / PUR, uu = it % PUR, jt = row >> 4, cg = uu >> 2;
+    if (cg > RD::plast(jt)) continue;
+    store_masked<T>(pr + RD::pblock(jt, cg) * 1024 + row_slot(row & 15, uu & 3) * 16,
                     &ps[row * C + uu * EPU], row - uu * EPU);
   }
   if constexpr (BF) {

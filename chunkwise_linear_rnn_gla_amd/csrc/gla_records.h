@@ -48,6 +48,16 @@ struct RecDims {
   static constexpr int EPU = 16 / ES;
   static constexpr int GW = 64 / ES;
   __host__ __device__ static constexpr int gbytes(int dk) { return ((8 * dk + 1023) / 1024) * 1024; }
+  // P's row block jt (16 rows) holds column groups 0 .. plast(jt); the
+  // groups after it lie above the diagonal and are not stored.  pblock: the
+  // 1 KB block (jt, cg) in the packed record; pblocks: blocks per chunk.
+  __host__ __device__ static constexpr int plast(int jt) { return (16 * jt + 15) / GW; }
+  __host__ __device__ static constexpr int pblock(int jt, int cg) {
+    static_assert(GW == 32 || GW == 16, "bf16 or fp32 records");
+    // sum over j < jt of plast(j) + 1: j / 2 + 1 (GW 32) or j + 1 (GW 16)
+    return (GW == 32 ? jt + ((jt - 1) >> 1) * (jt >> 1) : jt * (jt + 1) / 2) + cg;
+  }
+  __host__ __device__ static constexpr int pblocks(int C) { return pblock(C / 16, 0); }
 };
 
 constexpr int kLdsLimit = 160 * 1024;

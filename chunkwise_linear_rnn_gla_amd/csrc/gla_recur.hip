@@ -96,7 +96,7 @@ struct RecurLayout {
   static constexpr int VUPR = DVT * ES / 16;    // units per V row
   static constexpr int QB = OUT ? C * DK * ES : 0;
   static constexpr int KB = C * DK * ES;
-  static constexpr int PB = OUT ? C * C * ES : 0;
+  static constexpr int PB = OUT ? RD::pblocks(C) * 1024 : 0;
   static constexpr int LB = (OUT && BF) ? C * 16 * ES : 0;
   static constexpr int GB = RD::gbytes(DK);
   static constexpr int VB = C * DVT * ES;
@@ -372,7 +372,7 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
         for (int jt = 0; jt < NRT; ++jt) {
 #pragma unroll
           for (int kt = 0; kt <= (jt >> 1); ++kt) {
-            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(Ps + (jt * NPG + kt) * 1024 + qoff);
+            const bf16x8 pf = *reinterpret_cast<const bf16x8*>(Ps + RecDims<T>::pblock(jt, kt) * 1024 + qoff);
             ot[jt] = Mma<bf16>::run(vf[kt], pf, ot[jt]);
           }
           // every lane reads (a branch would force a wait for the read), the
@@ -407,7 +407,7 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
         for (int jt = 0; jt < NRT; ++jt)
 #pragma unroll
           for (int bb = 0; bb <= jt; ++bb) {
-            const f32x4 pf = *reinterpret_cast<const f32x4*>(Ps + (jt * NPG + bb) * 1024 + qoff);
+            const f32x4 pf = *reinterpret_cast<const f32x4*>(Ps + RecDims<T>::pblock(jt, bb) * 1024 + qoff);
 #pragma unroll
             for (int i = 0; i < 4; ++i) ot[jt] = Mma<float>::run(vf[bb][i], pf[i], ot[jt]);
           }
@@ -601,6 +601,9 @@ static hipError_t launch_recur_c(const Plan& p, int out, const void* qg, const v
 }
 
 size_t recur_grec_bytes(int dk) { return RecDims<float>::gbytes(dk); }
+size_t recur_prec_bytes(int is_bf16, int C) {
+  return (size_t)(is_bf16 ? RecDims<bf16>::pblocks(C) : RecDims<float>::pblocks(C)) * 1024;
+}
 
 bool recur_supported(int bf16, int C, int dk, int dv, int L) {
   const bool shape = bf16 ? (C == 32 || C == 64) && (dk == 32 || dk == 64 || dk == 128 || dk == 256)
