@@ -126,11 +126,14 @@ def kernel_bytes(name, w, esize, nc):
     h0 = hT if w.h0_std else 0
     nseg = fused_segments(w, nc)
     seg = BH * nseg * dk * dv * 4 if nseg > 1 else 0
-    # two-pass forward: Q~, K~ (rows padded to whole chunks), P (+ the low part
-    # of its diagonal blocks for bf16), chunk log decays
+    # two-pass forward: Q~, K~ (rows padded to whole chunks), P (its 1 KB
+    # blocks of 16 rows x 64 bytes that reach the diagonal or below, + the low
+    # part of its diagonal blocks for bf16), chunk log decays
     qg = kg = BH * nc * C * dk * esize
-    pm = BH * nc * C * C * esize + (BH * nc * C * 16 * esize if esize == 2 else 0)
-    gl = BH * nc * dk * 4
+    jt = C // 16
+    p_blocks = jt + ((jt - 1) >> 1) * (jt >> 1) if esize == 2 else jt * (jt + 1) // 2
+    pm = BH * nc * p_blocks * 1024 + (BH * nc * C * 16 * esize if esize == 2 else 0)
+    gl = BH * nc * 2 * dk * 4  # e^b and b per key channel
     _, nsegr = recur_plan(w, nc)
     segr = BH * nsegr * dk * dv * 4 if nsegr > 1 else 0
     return {
