@@ -704,29 +704,47 @@ __global__ __launch_bounds__(kWave) void k_rowsum_state(const float* __restrict_
 
 // dlog alpha_t = (chunk-local reverse cumsum of dlog b)_t
 //              + sum of the totals of all later chunks + rowsum(hT ⊙ dhT).
+// One workgroup per (chunk, batch-head): its first dk / 4 threads form the
+// chunk's offsets for 4 channels each (independent vector loads of the later
+// chunks' totals), then every thread adds them to 4-channel vectors of the
+// chunk's rows.
 __global__ __launch_bounds__(kThreads) void k_dla_carry(const float* __restrict__ dlt,
                                                         const float* __restrict__ rs,
                                                         float* __restrict__ dla, int L, int dk,
                                                         int C, int NC) {
-  const int n = blockIdx.x, bh = blockIdx.y;
-  const int r0 = n * C, r1 = min(L, r0 + C);
-  // threads (row phase p, channel c): dk channels, blockDim / dk row phases
-  const int nph = blockDim.x >= dk ? blockDim.x / dk : 1;
-  for (int t = threadIdx.x; t < nph * dk; t += blockDim.x) {
-    const int c = t % dk, p = t / dk;
-    float off = rs[(size_t)bh * dk + c];
-    for (int m = n + 1; m < NC; ++m) off += dlt[((size_t)bh * NC + m) * dk + c];
-    float* d = dla + ((size_t)bh * L + r0) * dk + c;
-    int r = r0 + p;
-    for (; r + 3 * nph < r1; r += 4 * nph) {
-      const float a0 = d[(size_t)(r - r0) * dk], a1 = d[(size_t)(r - r0 + nph) * dk],
-                  a2 = d[(size_t)(r - r0 + 2 * nph) * dk], a3 = d[(size_t)(r - r0 + 3 * nph) * dk];
-      d[(size_t)(r - r0) * dk] = a0 + off;
-      d[(size_t)(r - r0 + nph) * dk] = a1 + off;
-      d[(size_t)(r - r0 + 2 * nph) * dk] = a2 + off;
-      d[(size_t)(r - r0 + 3 * nph) * dk] = a3 + off;
+  __shared__ f32x4 off4[kThreads];
+  const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int dk4 = dk / 4;
+  for (int c4 = tid; c4 < dk4; c4 += kThreads) {
+    f32x4 s = *reinterpret_cast<const f32x4*>(rs + (size_t)bh * dk + 4 * c4);
+    const float* base = dlt + (size_t)bh * NC * dk + 4 * c4;
+    int m = n + 1;
+    for (; m + 7 < NC; m += 8) {
+      f32x4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const f32x4*>(base + (size_t)(m + u) * dk);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += x[u];
     }
-    for (; r < r1; r += nph) d[(size_t)(r - r0) * dk] += off;
+    for (; m < NC; ++m) s += *reinterpret_cast<const f32x4*>(base + (size_t)m * dk);
+    off4[c4] = s;
+  }
+  __syncthreads();
+  const int r0 = n * C, rows = min(C, L - r0);
+  float* d = dla + ((size_t)bh * L + r0) * dk;
+  const int total = rows * dk4;
+  for (int e0 = tid; e0 < total; e0 += 4 * kThreads) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kThreads;
+      if (e < total) v[u] = *reinterpret_cast<const f32x4*>(d + (size_t)e * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + u * kThreads;
+      if (e < total) *reinterpret_cast<f32x4*>(d + (size_t)e * 4) = v[u] + off4[e % dk4];
+    }
   }
 }
 
@@ -831,8 +849,7 @@ hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT,
 
 hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,
                             hipStream_t s) {
-  const int threads = p.dk < kThreads ? p.dk : kThreads;
-  hipLaunchKernelGGL(k_dla_carry, dim3(p.NC, p.BH), dim3(threads), 0, s, dlt, rs, dla, p.L, p.dk,
+  hipLaunchKernelGGL(k_dla_carry, dim3(p.NC, p.BH), dim3(kThreads), 0, s, dlt, rs, dla, p.L, p.dk,
                      p.C, p.NC);
   return hipGetLastError();
 }
