@@ -143,7 +143,9 @@ def kernel_bytes(name, w, esize, nc):
         "chunk_state_local": k + v + cum + seg,
         "segment_scan": 2 * (segr or seg) + hT,
         "seg_output": q + k + v + cum + seg + o,
-        "chunk_prep": q + k + a + qg + kg + pm + gl,
+        # chunk_prep also reads V from HBM once (into the caches, for the
+        # recurrence, which then finds it there)
+        "chunk_prep": q + k + a + v + qg + kg + pm + gl,
         "recur_local": kg + gl + v + segr,
         "chunk_recur": qg + kg + pm + gl + v + (segr or h0) + o + (0 if segr else hT),
     }.get(name)
