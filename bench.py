@@ -160,6 +160,7 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd figure")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step figure")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -358,6 +359,65 @@ def main():
             fwd_bwd = {"error": f"{type(e).__name__}: {e}"}
             log(f"[bench] fwd+bwd failed: {e}")
 
+    # ---- one-token decode steps (gla_decode) at the same head shape: each
+    # reads and writes the fp32 state once, so HBM bounds it.  The steps
+    # rotate over enough state buffers (more than the Infinity Cache holds)
+    # that each step's state comes from HBM.
+    decode = None
+    if not args.no_decode:
+        try:
+            g = torch.Generator().manual_seed(5)
+            dq_ = (torch.randn(w.B, w.H, w.dk, generator=g) * w.dk ** -0.5).to(x.q.dtype).to(dev)
+            dk_ = torch.randn(w.B, w.H, w.dk, generator=g).to(x.q.dtype).to(dev)
+            dv_ = torch.randn(w.B, w.H, w.dv, generator=g).to(x.q.dtype).to(dev)
+            da_ = (torch.nn.functional.logsigmoid(torch.randn(w.B, w.H, w.dk, generator=g))
+                   / 16.0).to(dev)
+            sbytes = w.B * w.H * w.dk * w.dv * 4
+            nst = max(2, -(-INFINITY_CACHE_BYTES * 33 // 32 // sbytes))
+            states = [torch.zeros(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+                      for _ in range(nst)]
+            do_ = torch.empty(w.B, w.H, w.dv, dtype=x.q.dtype, device=dev)
+            dd = gla.GlaDims(w.B, w.H, 1, w.dk, w.dv, w.chunk, 16)
+
+            it = [0]
+
+            def dec():
+                it[0] += 1
+                st = gla.gla_decode(dd, code, dq_, dk_, dv_, da_, states[it[0] % nst], do_,
+                                    stream)
+                if st != 0:
+                    raise gla.GlaError(st, "gla_decode")
+
+            for _ in range(200):
+                dec()
+            torch.cuda.synchronize()
+            nd = 2000
+            td = time.perf_counter()
+            for _ in range(nd):
+                dec()
+            torch.cuda.synchronize()
+            dec_us = (time.perf_counter() - td) * 1e6 / nd
+            _abi.gla_profile_begin(nd)
+            for _ in range(nd):
+                dec()
+            torch.cuda.synchronize()
+            _abi.gla_profile_end()
+            ev = [_abi.gla_profile_get(i)[1] * 1e3 for i in range(_abi.gla_profile_count())]
+            ev_us = sum(ev) / len(ev)
+            dbytes = (2 * w.B * w.H * w.dk * w.dv * 4
+                      + w.B * w.H * (2 * w.dk * esize + w.dk * 4 + 2 * w.dv * esize))
+            del states
+            decode = {"workload": f"decode B{w.B} H{w.H} dk{w.dk} dv{w.dv} one token, fp32 state",
+                      "state_buffers": nst,
+                      "us_per_step": round(dec_us, 2), "tokens_per_s": round(w.B / (dec_us * 1e-6), 1),
+                      "kernel_us": round(ev_us, 2), "bytes_per_step": dbytes,
+                      "achieved_gbps": round(dbytes / (ev_us * 1e-6) / 1e9, 1),
+                      "frac_hbm_peak": round(dbytes / (ev_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+            log(f"[bench] decode {dec_us:.2f} us/step, kernel {ev_us:.2f} us")
+        except Exception as e:  # reported, not hidden
+            decode = {"error": f"{type(e).__name__}: {e}"}
+            log(f"[bench] decode failed: {e}")
+
     # ---- the oracle on the host cores (baseline, not target)
     cpu = None
     if not args.no_cpu:
@@ -389,6 +449,7 @@ def main():
         "warm": {"ms_per_step": round(warm_ms, 5),
                  "tokens_per_s": round(tokens / (warm_ms * 1e-3), 1)},
         "roofline": roofline, "step_roofline": step_roofline, "kernels": kernels, "copy_gbps": round(copy_gbps, 1),
+        "decode": decode,
         "fwd_bwd": fwd_bwd, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -11,11 +11,12 @@ from __future__ import annotations
 
 from . import _abi
 from ._abi import (GLA_BF16, GLA_FP32, GlaDims, GlaError, gla_abi_version, gla_bwd,  # noqa: F401
-                   gla_bwd_workspace_size, gla_fwd, gla_fwd_workspace_size, gla_status_string)
+                   gla_bwd_workspace_size, gla_decode, gla_fwd, gla_fwd_workspace_size,
+                   gla_status_string)
 
-__all__ = ["fwd", "bwd", "dims_for", "gla_fwd", "gla_bwd", "gla_fwd_workspace_size",
-           "gla_bwd_workspace_size", "gla_abi_version", "gla_status_string", "GlaDims",
-           "GlaError", "GLA_FP32", "GLA_BF16"]
+__all__ = ["fwd", "bwd", "decode", "dims_for", "gla_fwd", "gla_bwd", "gla_decode",
+           "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_abi_version",
+           "gla_status_string", "GlaDims", "GlaError", "GLA_FP32", "GLA_BF16"]
 
 
 def _torch():
@@ -110,3 +111,25 @@ def bwd(q, k, v, log_alpha, h0, dout, dhT=None, chunk=64, subchunk=16, want_dh0=
     if st != 0:
         raise GlaError(st, "gla_bwd")
     return dq, dkk, dvv, dla, dh0
+
+
+def decode(q, k, v, log_alpha, state, out=None):
+    """One token of the recurrent form, in place on `state`.  q, k [B,H,dk],
+    v [B,H,dv] (fp32 or bf16), log_alpha [B,H,dk] fp32, state [B,H,dk,dv]
+    fp32 (updated).  Returns o [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    _check(q, "q", io)
+    _check(k, "k", io, q.shape)
+    _check(v, "v", io, (B, H, dv))
+    _check(log_alpha, "log_alpha", torch.float32, q.shape)
+    _check(state, "state", torch.float32, (B, H, dk, dv))
+    o = out if out is not None else torch.empty(B, H, dv, dtype=io, device=q.device)
+    _check(o, "out", io, (B, H, dv))
+    st = gla_decode(GlaDims(B, H, 1, dk, dv, 64, 16), _dtype_code(q), q, k, v, log_alpha, state,
+                    o, _stream(q.device))
+    if st != 0:
+        raise GlaError(st, "gla_decode")
+    return o

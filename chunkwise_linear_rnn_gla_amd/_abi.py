@@ -19,8 +19,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_NULL", 2: "GLA_ERR_SHAPE", 3: "GLA_ERR_DTYPE"
 
 # Every symbol include/gla.h declares.
 EXPORTS = ("gla_abi_version", "gla_status_string", "gla_fwd_workspace_size",
-           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_profile_begin", "gla_profile_end",
-           "gla_profile_count", "gla_profile_get")
+           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_decode", "gla_profile_begin",
+           "gla_profile_end", "gla_profile_count", "gla_profile_get")
 
 
 class GlaDims(ctypes.Structure):
@@ -60,6 +60,8 @@ def load():
     lib.gla_fwd.restype = i32
     lib.gla_bwd.argtypes = [dims_p, i32] + [vp] * 12 + [vp, sz, vp]
     lib.gla_bwd.restype = i32
+    lib.gla_decode.argtypes = [dims_p, i32] + [vp] * 6 + [vp]
+    lib.gla_decode.restype = i32
     lib.gla_profile_begin.argtypes = [i32]
     lib.gla_profile_begin.restype = i32
     lib.gla_profile_end.argtypes = []
@@ -120,6 +122,12 @@ def gla_bwd(dims, dtype, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv, dlog_alp
     return load().gla_bwd(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                           _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
                           _ptr(dlog_alpha), _ptr(dh0), _ptr(workspace), workspace_bytes, stream)
+
+
+def gla_decode(dims, dtype, q, k, v, log_alpha, state, o, stream):
+    """Raw call; pointer arguments are tensors, ints or None.  Returns the status."""
+    return load().gla_decode(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(log_alpha), _ptr(state), _ptr(o), stream)
 
 
 def gla_profile_begin(capacity: int) -> None:

@@ -363,6 +363,24 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
   return GLA_OK;
 }
 
+gla_status gla_decode(const gla_dims* dims, int dtype, const void* q, const void* k,
+                      const void* v, const float* log_alpha, float* state, void* o,
+                      void* stream) {
+  if (!dims) return GLA_ERR_NULL;
+  if (dtype != GLA_FP32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
+  // one token: B, H, dk and dv are checked as for gla_fwd (the sequence and
+  // chunk fields of dims do not apply)
+  Plan p;
+  if (!make_plan(dims->B, dims->H, 1, dims->dk, dims->dv, 64, 16, dtype == GLA_BF16, &p))
+    return GLA_ERR_SHAPE;
+  if (p.BH == 0) return GLA_OK;
+  gla_status st = check_ptrs({q, k, v, log_alpha, state, o}, {});
+  if (st != GLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  GLA_LAUNCH("decode", launch_decode(p, q, k, v, log_alpha, state, o, s));
+  return GLA_OK;
+}
+
 gla_status gla_profile_begin(int capacity) {
   if (capacity < 1) return GLA_ERR_SHAPE;
   if (capacity != g_cap) {

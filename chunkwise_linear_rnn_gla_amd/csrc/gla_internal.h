@@ -148,6 +148,12 @@ hipError_t launch_chunk_dv(const Plan& p, const void* k, const void* dout, const
                            const void* dst_t, const float* Aw, void* dv, hipStream_t s);
 hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT, float* rs,
                                hipStream_t s);
+// One token of the recurrent form in place on the state (gla_decode.hip):
+// state <- diag(e^{la}) state + k^T v, o = q state; q, k, la [BH][dk],
+// v, o [BH][dv], state [BH][dk][dv] fp32.
+hipError_t launch_decode(const Plan& p, const void* q, const void* k, const void* v,
+                         const float* la, float* state, void* o, hipStream_t s);
+
 // dla += rs + the dlog b totals of all later chunks (dlt [BH][NC][dk]).
 hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,
                             hipStream_t s);

@@ -121,6 +121,22 @@ gla_status gla_bwd(const gla_dims *dims, int dtype,
                    void *dq, void *dk, void *dv, float *dlog_alpha, float *dh0,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* One token of the recurrent form, in place on the state (papercache.org
+ * notes §2.1 and §4.1, recurrent form: the constant-memory inference step).
+ * Per (batch, head), with a = log_alpha of the token:
+ *     state <- diag(e^{a}) state + k^T v,      o = q state
+ * (the output includes the token, as in gla_fwd).  Repeated calls over the
+ * tokens of a sequence give gla_fwd's o and hT up to rounding.
+ *   dims: B, H, dk, dv with gla_fwd's limits; L, chunk and subchunk are not
+ *         used.
+ *   in : q, k [B,H,dk] and v [B,H,dv] in `dtype`; log_alpha [B,H,dk] fp32.
+ *   in/out: state [B,H,dk,dv] fp32, read and overwritten.
+ *   out: o [B,H,dv] in `dtype` (must not alias the inputs or state).
+ *   No workspace.  Errors as for gla_fwd; B * H == 0 is a no-op. */
+gla_status gla_decode(const gla_dims *dims, int dtype,
+                      const void *q, const void *k, const void *v,
+                      const float *log_alpha, float *state, void *o, void *stream);
+
 /* ---- launch profiling (measurement support; not part of the computation) ----
  * While enabled, every kernel launch made by gla_fwd / gla_bwd is bracketed by
  * two HIP events recorded on the launch stream, so per-kernel GPU durations can

@@ -134,3 +134,15 @@ def test_empty_batch_is_a_no_op():
     d = good_dims(B=0)
     assert _abi.gla_fwd(d, GLA_BF16, None, None, None, None, None, None, None, None, 0, None) == 0
     assert _abi.gla_bwd(d, GLA_BF16, *([None] * 12), None, 0, None) == 0
+
+
+def test_decode_errors():
+    # validation of the one-token step happens before any launch
+    d = good_dims(L=0, chunk=0, subchunk=0)  # sequence and chunk fields are not used
+    assert _abi.gla_decode(d, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert _abi.load().gla_decode(None, GLA_BF16, *([FAKE] * 6), None) == 1
+    assert _abi.gla_decode(good_dims(dk=20), GLA_BF16, *([FAKE] * 6), None) == 2
+    assert _abi.gla_decode(good_dims(dv=1024), GLA_FP32, *([FAKE] * 6), None) == 2
+    assert _abi.gla_decode(d, GLA_BF16, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == 1
+    assert _abi.gla_decode(d, GLA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None) == 4
+    assert _abi.gla_decode(good_dims(B=0), GLA_BF16, *([None] * 6), None) == 0
