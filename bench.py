@@ -23,7 +23,9 @@ count 2*L*C*(dk+dv) + 4*L*dk*dv per head, the dominant kernel's roofline
 (achieved algorithmic GB/s from HIP events recorded around every launch on the
 launch stream, in a second pass of the same K steps: the events add a few
 microseconds per launch, so the step time is taken in a pass without them),
-the fp64 oracle timed on the host cores, and a fwd+bwd figure.
+the fp64 oracle timed on the host cores, a fwd+bwd figure, a one-token decode
+figure and the op-level layer (projections and gates in torch around these
+kernels) at d = 1024 with 4 heads.
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -161,6 +163,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd figure")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step figure")
+    ap.add_argument("--no-layer", action="store_true", help="skip the op-level layer figure")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -418,6 +421,52 @@ def main():
             decode = {"error": f"{type(e).__name__}: {e}"}
             log(f"[bench] decode failed: {e}")
 
+    # ---- the op-level layer (projections, gate, norm and output gate in
+    # torch, the recurrence in the kernels) at d = 1024, 4 heads, which gives
+    # this head shape; seeded random weights
+    layer = None
+    if not args.no_layer:
+        try:
+            from chunkwise_linear_rnn_gla_amd.layer import GlaLayer
+            d_model = w.H * w.dv
+            lay = GlaLayer(d_model, w.H, chunk=w.chunk, seed=9, dtype=x.q.dtype, device=dev)
+            g = torch.Generator().manual_seed(10)
+            xl = torch.randn(w.B, w.L, d_model, generator=g).to(x.q.dtype).to(dev)
+            dyl = torch.randn(w.B, w.L, d_model, generator=g).to(x.q.dtype).to(dev)
+            xg = xl.clone().requires_grad_(True)
+
+            def lf():
+                with torch.no_grad():
+                    lay(xl)
+
+            def lfb():
+                lay(xg).backward(dyl)
+
+            res = {}
+            for name, fn in (("fwd", lf), ("fwd_bwd", lfb)):
+                for _ in range(5):
+                    fn()
+                torch.cuda.synchronize()
+                kl = max(5, args.steps // 10)
+                tl = time.perf_counter()
+                for _ in range(kl):
+                    fn()
+                torch.cuda.synchronize()
+                res[name] = (time.perf_counter() - tl) * 1e3 / kl
+            layer = {"workload": f"GLA layer d{d_model} heads{w.H} B{w.B} L{w.L} {w.dtype}",
+                     "fwd_ms": round(res["fwd"], 4),
+                     "fwd_tokens_per_s": round(tokens / (res["fwd"] * 1e-3), 1),
+                     "fwd_bwd_ms": round(res["fwd_bwd"], 4),
+                     "fwd_bwd_tokens_per_s": round(tokens / (res["fwd_bwd"] * 1e-3), 1),
+                     "core_share_fwd": round(ms_per_step / res["fwd"], 4)}
+            if fwd_bwd and "ms_per_step" in fwd_bwd:
+                layer["core_share_fwd_bwd"] = round(fwd_bwd["ms_per_step"] / res["fwd_bwd"], 4)
+            del lay, xl, dyl, xg
+            log(f"[bench] layer fwd {res['fwd'] * 1e3:.1f} us, fwd+bwd {res['fwd_bwd'] * 1e3:.1f} us")
+        except Exception as e:  # reported, not hidden
+            layer = {"error": f"{type(e).__name__}: {e}"}
+            log(f"[bench] layer failed: {e}")
+
     # ---- the oracle on the host cores (baseline, not target)
     cpu = None
     if not args.no_cpu:
@@ -449,7 +498,7 @@ def main():
         "warm": {"ms_per_step": round(warm_ms, 5),
                  "tokens_per_s": round(tokens / (warm_ms * 1e-3), 1)},
         "roofline": roofline, "step_roofline": step_roofline, "kernels": kernels, "copy_gbps": round(copy_gbps, 1),
-        "decode": decode,
+        "decode": decode, "layer": layer,
         "fwd_bwd": fwd_bwd, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
