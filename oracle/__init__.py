@@ -13,6 +13,9 @@ Contents
   (``chunkwise.py``), an independent formulation used to pin ``fwd``.
 * ``closed_form_dlog_alpha``: the pages' closed-form gate gradient, used to pin
   ``bwd`` (and, through it, the GPU path's use of that closed form).
+* ``ggla_fwd`` / ``ggla_bwd``: the general gate G_t = alpha_t^T beta_t (notes,
+  App. C) as the same token recurrence and BPTT in C;
+  ``closed_form_general``: its closed-form dlog alpha and dlog beta.
 
 All functions take and return NumPy float64 arrays laid out [B, H, L, d]
 (states [B, H, dk, dv]).
@@ -64,6 +67,10 @@ def _load():
         lib.gla_oracle_fwd.restype = i
         lib.gla_oracle_bwd.argtypes = [i, i, i, i, i] + [dp] * 12 + [i]
         lib.gla_oracle_bwd.restype = i
+        lib.ggla_oracle_fwd.argtypes = [i, i, i, i, i] + [dp] * 8 + [i]
+        lib.ggla_oracle_fwd.restype = i
+        lib.ggla_oracle_bwd.argtypes = [i, i, i, i, i] + [dp] * 14 + [i]
+        lib.ggla_oracle_bwd.restype = i
         _lib = lib
     return _lib
 
@@ -141,3 +148,66 @@ def closed_form_dlog_alpha(q, k, dq, dk, hT=None, dhT=None):
     if dhT is not None:
         out = out + np.sum(np.asarray(hT) * np.asarray(dhT), axis=-1)[..., None, :]
     return out
+
+
+def ggla_fwd(q, k, v, log_alpha, log_beta, h0=None, nthreads=None):
+    """Token-by-token forward with the general gate G_t = alpha_t^T beta_t
+    (log_beta [B, H, L, dv]) in fp64.  Returns (o, hT)."""
+    q, k, v, a, b, h0 = (_c64(x) for x in (q, k, v, log_alpha, log_beta, h0))
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and a.shape == q.shape and v.shape == (B, H, L, dv)
+    assert b.shape == v.shape
+    if h0 is not None:
+        assert h0.shape == (B, H, dk, dv)
+    o = np.empty((B, H, L, dv))
+    hT = np.empty((B, H, dk, dv))
+    rc = _load().ggla_oracle_fwd(B, H, L, dk, dv, _p(q), _p(k), _p(v), _p(a), _p(b), _p(h0),
+                                 _p(o), _p(hT), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ggla_oracle_fwd failed ({rc})")
+    return o, hT
+
+
+def ggla_bwd(q, k, v, log_alpha, log_beta, h0, dout, dhT=None, nthreads=None):
+    """BPTT of the general-gate recurrence in fp64.
+    Returns (dq, dk, dv, dlog_alpha, dlog_beta, dh0)."""
+    q, k, v, a, b, h0, do, dhT = (_c64(x) for x in (q, k, v, log_alpha, log_beta, h0, dout,
+                                                    dhT))
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    assert do.shape == v.shape and b.shape == v.shape
+    dq = np.empty_like(q)
+    dkk = np.empty_like(k)
+    dvv = np.empty_like(v)
+    da = np.empty_like(a)
+    db = np.empty_like(b)
+    dh0 = np.empty((B, H, dk, dv))
+    rc = _load().ggla_oracle_bwd(B, H, L, dk, dv, _p(q), _p(k), _p(v), _p(a), _p(b), _p(h0),
+                                 _p(do), _p(dhT), _p(dq), _p(dkk), _p(dvv), _p(da), _p(db),
+                                 _p(dh0), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"ggla_oracle_bwd failed ({rc})")
+    return dq, dkk, dvv, da, db, dh0
+
+
+def closed_form_general(q, k, v, o, dq, dk, dv, dout, hT=None, dhT=None):
+    """Closed-form gate gradients of the general gate, in fp64.
+
+    Notes, App. C (memory-efficient gradients of the general form): with the
+    cumulative products b_t of alpha and d_t of beta, the parallel form puts
+    b_t on q_t, 1/b_s on k_s, 1/d_s on v_s and d_t on o_t, so
+        dlog b_t = q_t ⊙ dq_t - k_t ⊙ dk_t,   dlog d_t = o_t ⊙ do_t - v_t ⊙ dv_t
+    and each dlog gate is the sum of its dlog cumulative product over later
+    tokens.  hT carries b_L and d_L as well, which adds the row sums
+    (alpha) and column sums (beta) of hT ⊙ dhT to the last token's terms.
+    Returns (dlog_alpha, dlog_beta)."""
+    f = lambda x: np.asarray(x, np.float64)
+    rev = lambda x: np.flip(np.cumsum(np.flip(x, axis=-2), axis=-2), axis=-2)
+    da = rev(f(q) * f(dq) - f(k) * f(dk))
+    db = rev(f(o) * f(dout) - f(v) * f(dv))
+    if dhT is not None:
+        P = f(hT) * f(dhT)
+        da = da + np.sum(P, axis=-1)[..., None, :]
+        db = db + np.sum(P, axis=-2)[..., None, :]
+    return da, db

@@ -53,6 +53,17 @@
  * Threads: one (b,h) pair per task, tasks split over `nthreads` pthreads.
  * Each task's arithmetic is independent of the split.
  *
+ * General gate (ggla_oracle_fwd / ggla_oracle_bwd): the same recurrence with
+ * the outer-product gate G_t = alpha_t^T beta_t of the notes' App. C
+ * ("general form"), beta_t acting on the d_v columns:
+ *
+ *           S_t[i][j] = exp(a_t[i]) * exp(b_t[j]) * S_{t-1}[i][j] + k_t[i] * v_t[j]
+ *
+ * with b_t = log beta_t, laid out [B][H][L][dv] like v.  Its BPTT adds
+ *           dlogb_t[j] = sum_i dS[i][j] * G_t[i][j] * S_{t-1}[i][j]
+ * and decays dS by G_t[i][j].  With log_beta == NULL both functions are the
+ * row-gated ones above, operation for operation.
+ *
  * Return value: 0 on success, -1 on bad arguments, -2 on allocation failure.
  */
 #include <math.h>
@@ -64,8 +75,8 @@
 
 typedef struct {
   int B, H, L, dk, dv;
-  const double *q, *k, *v, *la, *h0, *dout, *dhT;
-  double *o, *hT, *dq, *dkk, *dvv, *dla, *dh0;
+  const double *q, *k, *v, *la, *lb, *h0, *dout, *dhT;
+  double *o, *hT, *dq, *dkk, *dvv, *dla, *dlb, *dh0;
   int next;            /* next (b,h) task index, guarded by mu */
   int failed;
   pthread_mutex_t mu;
@@ -78,14 +89,23 @@ static int or_take(or_job *J) {
   return t;
 }
 
-/* One recurrence step: S <- diag(exp(a)) S + k^T v. */
-static void or_step(double *S, const double *a, const double *kt,
+/* One recurrence step: S <- diag(exp(a)) S + k^T v, or with a column gate b
+ * (not NULL): S[i][j] <- exp(a[i]) exp(b[j]) S[i][j] + k[i] v[j]. */
+static void or_step(double *S, const double *a, const double *b, const double *kt,
                     const double *vt, int dk, int dv) {
   for (int i = 0; i < dk; ++i) {
     double g = exp(a[i]);
     double *row = S + (size_t)i * dv;
-    for (int j = 0; j < dv; ++j) row[j] = g * row[j] + kt[i] * vt[j];
+    if (b)
+      for (int j = 0; j < dv; ++j) row[j] = (g * exp(b[j])) * row[j] + kt[i] * vt[j];
+    else
+      for (int j = 0; j < dv; ++j) row[j] = g * row[j] + kt[i] * vt[j];
   }
+}
+
+/* log beta of token t, or NULL for the row-gated recurrence */
+static const double *or_lb(const or_job *J, size_t vo, int t) {
+  return J->lb ? J->lb + vo + (size_t)t * J->dv : NULL;
 }
 
 static void or_fwd_head(or_job *J, int bh) {
@@ -98,7 +118,7 @@ static void or_fwd_head(or_job *J, int bh) {
   else memset(S, 0, sizeof(double) * dk * dv);
   for (int t = 0; t < L; ++t) {
     const double *qt = J->q + qo + (size_t)t * dk;
-    or_step(S, J->la + qo + (size_t)t * dk, J->k + qo + (size_t)t * dk,
+    or_step(S, J->la + qo + (size_t)t * dk, or_lb(J, vo, t), J->k + qo + (size_t)t * dk,
             J->v + vo + (size_t)t * dv, dk, dv);
     double *ot = J->o + vo + (size_t)t * dv;
     for (int j = 0; j < dv; ++j) ot[j] = 0.0;
@@ -130,8 +150,8 @@ static void or_bwd_head(or_job *J, int bh) {
     memcpy(next, ck + SS * c, sizeof(double) * SS);
     int t1 = (c + 1) * OR_CKPT < L ? (c + 1) * OR_CKPT : L;
     for (int t = c * OR_CKPT; t < t1; ++t)
-      or_step(next, J->la + qo + (size_t)t * dk, J->k + qo + (size_t)t * dk,
-              J->v + vo + (size_t)t * dv, dk, dv);
+      or_step(next, J->la + qo + (size_t)t * dk, or_lb(J, vo, t),
+              J->k + qo + (size_t)t * dk, J->v + vo + (size_t)t * dv, dk, dv);
   }
 
   if (J->dhT) memcpy(dS, J->dhT + so, sizeof(double) * SS);
@@ -143,7 +163,7 @@ static void or_bwd_head(or_job *J, int bh) {
     memcpy(seg, ck + SS * c, sizeof(double) * SS);
     for (int t = t0; t < t1; ++t) {
       memcpy(seg + SS * (t - t0 + 1), seg + SS * (t - t0), sizeof(double) * SS);
-      or_step(seg + SS * (t - t0 + 1), J->la + qo + (size_t)t * dk,
+      or_step(seg + SS * (t - t0 + 1), J->la + qo + (size_t)t * dk, or_lb(J, vo, t),
               J->k + qo + (size_t)t * dk, J->v + vo + (size_t)t * dv, dk, dv);
     }
     for (int t = t1 - 1; t >= t0; --t) {
@@ -173,11 +193,28 @@ static void or_bwd_head(or_job *J, int bh) {
       for (int j = 0; j < dv; ++j) dvt[j] = 0.0;
       for (int i = 0; i < dk; ++i)
         for (int j = 0; j < dv; ++j) dvt[j] += dS[(size_t)i * dv + j] * kt[i];
-      for (int i = 0; i < dk; ++i) {
-        double g = exp(at[i]), s = 0.0;
-        for (int j = 0; j < dv; ++j) s += dS[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];
-        dat[i] = g * s;
-        for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= g;
+      const double *bt = or_lb(J, vo, t);
+      if (!bt) {
+        for (int i = 0; i < dk; ++i) {
+          double g = exp(at[i]), s = 0.0;
+          for (int j = 0; j < dv; ++j) s += dS[(size_t)i * dv + j] * Sp[(size_t)i * dv + j];
+          dat[i] = g * s;
+          for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= g;
+        }
+      } else {
+        double *dbt = J->dlb + vo + (size_t)t * dv;
+        for (int j = 0; j < dv; ++j) dbt[j] = 0.0;
+        for (int i = 0; i < dk; ++i) {
+          double g = exp(at[i]), s = 0.0;
+          for (int j = 0; j < dv; ++j) {
+            double G = g * exp(bt[j]);
+            double c = dS[(size_t)i * dv + j] * G * Sp[(size_t)i * dv + j];
+            s += c;
+            dbt[j] += c;
+            dS[(size_t)i * dv + j] *= G;
+          }
+          dat[i] = s;
+        }
       }
     }
   }
@@ -246,5 +283,40 @@ int gla_oracle_bwd(int B, int H, int L, int dk, int dv,
   J.q = q; J.k = k; J.v = v; J.la = log_alpha; J.h0 = h0;
   J.dout = dout; J.dhT = dhT;
   J.dq = dq; J.dkk = dkk; J.dvv = dvv; J.dla = dlog_alpha; J.dh0 = dh0;
+  return or_run(&J, or_bwd_worker, nthreads);
+}
+
+int ggla_oracle_fwd(int B, int H, int L, int dk, int dv,
+                    const double *q, const double *k, const double *v,
+                    const double *log_alpha, const double *log_beta, const double *h0,
+                    double *o, double *hT, int nthreads) {
+  if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
+  if (B * H == 0) return 0;
+  if ((L > 0) && (!q || !k || !v || !log_alpha || !log_beta || !o)) return -1;
+  or_job J;
+  memset(&J, 0, sizeof(J));
+  J.B = B; J.H = H; J.L = L; J.dk = dk; J.dv = dv;
+  J.q = q; J.k = k; J.v = v; J.la = log_alpha; J.lb = log_beta; J.h0 = h0;
+  J.o = o; J.hT = hT;
+  return or_run(&J, or_fwd_worker, nthreads);
+}
+
+int ggla_oracle_bwd(int B, int H, int L, int dk, int dv,
+                    const double *q, const double *k, const double *v,
+                    const double *log_alpha, const double *log_beta, const double *h0,
+                    const double *dout, const double *dhT,
+                    double *dq, double *dkk, double *dvv, double *dlog_alpha,
+                    double *dlog_beta, double *dh0, int nthreads) {
+  if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
+  if (B * H == 0) return 0;
+  if ((L > 0) && (!q || !k || !v || !log_alpha || !log_beta || !dout || !dq || !dkk ||
+                  !dvv || !dlog_alpha || !dlog_beta))
+    return -1;
+  or_job J;
+  memset(&J, 0, sizeof(J));
+  J.B = B; J.H = H; J.L = L; J.dk = dk; J.dv = dv;
+  J.q = q; J.k = k; J.v = v; J.la = log_alpha; J.lb = log_beta; J.h0 = h0;
+  J.dout = dout; J.dhT = dhT;
+  J.dq = dq; J.dkk = dkk; J.dvv = dvv; J.dla = dlog_alpha; J.dlb = dlog_beta; J.dh0 = dh0;
   return or_run(&J, or_bwd_worker, nthreads);
 }
