@@ -24,8 +24,9 @@ count 2*L*C*(dk+dv) + 4*L*dk*dv per head, the dominant kernel's roofline
 launch stream, in a second pass of the same K steps: the events add a few
 microseconds per launch, so the step time is taken in a pass without them),
 the fp64 oracle timed on the host cores, a fwd+bwd figure, a one-token decode
-figure and the op-level layer (projections and gates in torch around these
-kernels) at d = 1024 with 4 heads.
+figure, the general gate G = alpha^T beta (forward, forward + backward and
+its kernels) at the same head shape, and the op-level layer (projections and
+gates in torch around these kernels) at d = 1024 with 4 heads.
 Progress goes to stderr.
 """
 from __future__ import annotations
@@ -164,6 +165,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the fwd+bwd figure")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step figure")
     ap.add_argument("--no-layer", action="store_true", help="skip the op-level layer figure")
+    ap.add_argument("--no-general", action="store_true", help="skip the general-gate figure")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -421,6 +423,82 @@ def main():
             decode = {"error": f"{type(e).__name__}: {e}"}
             log(f"[bench] decode failed: {e}")
 
+    # ---- the general gate G = alpha^T beta (ggla_fwd / ggla_bwd) at the same
+    # head shape, with a column gate drawn like the row gate
+    general = None
+    if not args.no_general:
+        try:
+            from chunkwise_linear_rnn_gla_amd.inputs import make_log_beta
+            lbg = make_log_beta(w.B, w.H, w.L, w.dv, seed=w.seed).to(dev)
+            gws = torch.empty(gla.ggla_bwd_workspace_size(dims, code), dtype=torch.uint8,
+                              device=dev)
+            og = torch.empty_like(x.v)
+            hg = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+            gouts = [torch.empty_like(x.q), torch.empty_like(x.k), torch.empty_like(x.v),
+                     torch.empty_like(x.log_alpha), torch.empty_like(lbg)]
+            dog = torch.randn(w.B, w.H, w.L, w.dv, generator=torch.Generator().manual_seed(6)
+                              ).to(x.q.dtype).to(dev)
+
+            def gf():
+                st = gla.ggla_fwd(dims, code, x.q, x.k, x.v, x.log_alpha, lbg, None, og, hg,
+                                  gws, gws.numel(), stream)
+                if st:
+                    raise gla.GlaError(st, "ggla_fwd")
+
+            def gfb():
+                gf()
+                st = gla.ggla_bwd(dims, code, x.q, x.k, x.v, x.log_alpha, lbg, None, dog, None,
+                                  *gouts, None, gws, gws.numel(), stream)
+                if st:
+                    raise gla.GlaError(st, "ggla_bwd")
+
+            res = {}
+            for name, fn, kk in (("fwd", gf, max(20, args.steps // 2)),
+                                 ("fwd_bwd", gfb, max(5, args.steps // 10))):
+                for _ in range(5):
+                    fn()
+                torch.cuda.synchronize()
+                tg = time.perf_counter()
+                for _ in range(kk):
+                    fn()
+                torch.cuda.synchronize()
+                res[name] = (time.perf_counter() - tg) * 1e3 / kk
+            # per-kernel durations of the forward from events on the launch stream
+            kf = max(20, args.steps // 2)
+            _abi.gla_profile_begin(2 * kf)
+            for _ in range(kf):
+                gf()
+            torch.cuda.synchronize()
+            _abi.gla_profile_end()
+            per = {}
+            for i in range(_abi.gla_profile_count()):
+                nm, ms = _abi.gla_profile_get(i)
+                per.setdefault(nm, []).append(ms)
+            nc16 = -(-w.L // 16)
+            rb = 32 * w.dk * esize + 4 * 272 + 4 * w.dk   # one 16-token record
+            BHg = w.B * w.H
+            gbytes = {"gg_prep": BHg * w.L * (2 * w.dk * esize + 4 * w.dk) + BHg * nc16 * rb,
+                      "gg_recur": BHg * nc16 * rb + BHg * w.L * w.dv * (2 * esize + 4)
+                      + BHg * w.dk * w.dv * 4}
+            gk = {}
+            for nm, lst in per.items():
+                avg = sum(lst) / len(lst) * 1e-3
+                gk[nm] = {"avg_us": round(avg * 1e6, 2),
+                          "algorithmic_bytes": gbytes.get(nm),
+                          "achieved_gbps": round(gbytes[nm] / avg / 1e9, 1) if nm in gbytes else None}
+            general = {"workload": f"general gate B{w.B} H{w.H} L{w.L} dk{w.dk} dv{w.dv} {w.dtype}",
+                       "fwd_ms": round(res["fwd"], 4),
+                       "fwd_tokens_per_s": round(tokens / (res["fwd"] * 1e-3), 1),
+                       "fwd_bwd_ms": round(res["fwd_bwd"], 4),
+                       "fwd_bwd_tokens_per_s": round(tokens / (res["fwd_bwd"] * 1e-3), 1),
+                       "kernels": gk}
+            del gws, og, hg, gouts, dog, lbg
+            log(f"[bench] general gate fwd {res['fwd'] * 1e3:.1f} us, fwd+bwd "
+                f"{res['fwd_bwd'] * 1e3:.1f} us; {gk}")
+        except Exception as e:  # reported, not hidden
+            general = {"error": f"{type(e).__name__}: {e}"}
+            log(f"[bench] general gate failed: {e}")
+
     # ---- the op-level layer (projections, gate, norm and output gate in
     # torch, the recurrence in the kernels) at d = 1024, 4 heads, which gives
     # this head shape; seeded random weights
@@ -498,7 +576,7 @@ def main():
         "warm": {"ms_per_step": round(warm_ms, 5),
                  "tokens_per_s": round(tokens / (warm_ms * 1e-3), 1)},
         "roofline": roofline, "step_roofline": step_roofline, "kernels": kernels, "copy_gbps": round(copy_gbps, 1),
-        "decode": decode, "layer": layer,
+        "decode": decode, "layer": layer, "general": general,
         "fwd_bwd": fwd_bwd, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -10,11 +10,14 @@ library; ``_abi`` exposes the raw C entry points under their C names.
 from __future__ import annotations
 
 from . import _abi
-from ._abi import (GLA_BF16, GLA_FP32, GlaDims, GlaError, gla_abi_version, gla_bwd,  # noqa: F401
-                   gla_bwd_workspace_size, gla_decode, gla_fwd, gla_fwd_workspace_size,
+from ._abi import (GLA_BF16, GLA_FP32, GlaDims, GlaError, ggla_bwd,  # noqa: F401
+                   ggla_bwd_workspace_size, ggla_fwd, ggla_fwd_workspace_size, gla_abi_version,
+                   gla_bwd, gla_bwd_workspace_size, gla_decode, gla_fwd, gla_fwd_workspace_size,
                    gla_status_string)
 
-__all__ = ["fwd", "bwd", "decode", "dims_for", "gla_fwd", "gla_bwd", "gla_decode",
+__all__ = ["fwd", "bwd", "decode", "fwd_general", "bwd_general", "dims_for", "gla_fwd",
+           "gla_bwd", "gla_decode", "ggla_fwd", "ggla_bwd", "ggla_fwd_workspace_size",
+           "ggla_bwd_workspace_size",
            "gla_fwd_workspace_size", "gla_bwd_workspace_size", "gla_abi_version",
            "gla_status_string", "GlaDims", "GlaError", "GLA_FP32", "GLA_BF16"]
 
@@ -133,3 +136,62 @@ def decode(q, k, v, log_alpha, state, out=None):
     if st != 0:
         raise GlaError(st, "gla_decode")
     return o
+
+
+def fwd_general(q, k, v, log_alpha, log_beta, h0=None, final_state=True, workspace=None,
+                out=None):
+    """Forward with the general gate G_t = alpha_t^T beta_t.  As ``fwd``, plus
+    log_beta [B,H,L,dv] fp32 (the column gate).  Returns (o, hT or None)."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    _check(q, "q", io)
+    _check(k, "k", io, q.shape)
+    _check(v, "v", io, (B, H, L, dv))
+    _check(log_alpha, "log_alpha", torch.float32, q.shape)
+    _check(log_beta, "log_beta", torch.float32, (B, H, L, dv))
+    _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    dims = GlaDims(B, H, L, dk, dv, 16, 16)
+    code = _dtype_code(q)
+    o = out if out is not None else torch.empty(B, H, L, dv, dtype=io, device=q.device)
+    hT = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if final_state else None
+    n = ggla_fwd_workspace_size(dims, code)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = ggla_fwd(dims, code, q, k, v, log_alpha, log_beta, h0, o, hT, workspace,
+                  workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise GlaError(st, "ggla_fwd")
+    return o, hT
+
+
+def bwd_general(q, k, v, log_alpha, log_beta, h0, dout, dhT=None, want_dh0=True,
+                workspace=None):
+    """Backward of ``fwd_general``.  Returns (dq, dk, dv, dlog_alpha, dlog_beta,
+    dh0 or None)."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    io = q.dtype
+    _check(q, "q", io)
+    _check(k, "k", io, q.shape)
+    _check(v, "v", io, (B, H, L, dv))
+    _check(log_alpha, "log_alpha", torch.float32, q.shape)
+    _check(log_beta, "log_beta", torch.float32, (B, H, L, dv))
+    _check(h0, "h0", torch.float32, (B, H, dk, dv))
+    _check(dout, "dout", io, (B, H, L, dv))
+    _check(dhT, "dhT", torch.float32, (B, H, dk, dv))
+    dims = GlaDims(B, H, L, dk, dv, 16, 16)
+    code = _dtype_code(q)
+    dq, dkk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dla, dlb = torch.empty_like(log_alpha), torch.empty_like(log_beta)
+    dh0 = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if want_dh0 else None
+    n = ggla_bwd_workspace_size(dims, code)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = ggla_bwd(dims, code, q, k, v, log_alpha, log_beta, h0, dout, dhT, dq, dkk, dvv, dla,
+                  dlb, dh0, workspace, workspace.numel(), _stream(q.device))
+    if st != 0:
+        raise GlaError(st, "ggla_bwd")
+    return dq, dkk, dvv, dla, dlb, dh0

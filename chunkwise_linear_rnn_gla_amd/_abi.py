@@ -19,7 +19,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_NULL", 2: "GLA_ERR_SHAPE", 3: "GLA_ERR_DTYPE"
 
 # Every symbol include/gla.h declares.
 EXPORTS = ("gla_abi_version", "gla_status_string", "gla_fwd_workspace_size",
-           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_decode", "gla_profile_begin",
+           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_decode", "ggla_fwd_workspace_size",
+           "ggla_bwd_workspace_size", "ggla_fwd", "ggla_bwd", "gla_profile_begin",
            "gla_profile_end", "gla_profile_count", "gla_profile_get")
 
 
@@ -62,6 +63,13 @@ def load():
     lib.gla_bwd.restype = i32
     lib.gla_decode.argtypes = [dims_p, i32] + [vp] * 6 + [vp]
     lib.gla_decode.restype = i32
+    for f in (lib.ggla_fwd_workspace_size, lib.ggla_bwd_workspace_size):
+        f.argtypes = [dims_p, i32, ctypes.POINTER(sz)]
+        f.restype = i32
+    lib.ggla_fwd.argtypes = [dims_p, i32] + [vp] * 8 + [vp, sz, vp]
+    lib.ggla_fwd.restype = i32
+    lib.ggla_bwd.argtypes = [dims_p, i32] + [vp] * 14 + [vp, sz, vp]
+    lib.ggla_bwd.restype = i32
     lib.gla_profile_begin.argtypes = [i32]
     lib.gla_profile_begin.restype = i32
     lib.gla_profile_end.argtypes = []
@@ -122,6 +130,39 @@ def gla_bwd(dims, dtype, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv, dlog_alp
     return load().gla_bwd(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                           _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
                           _ptr(dlog_alpha), _ptr(dh0), _ptr(workspace), workspace_bytes, stream)
+
+
+def ggla_fwd_workspace_size(dims: GlaDims, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().ggla_fwd_workspace_size(ctypes.byref(dims), dtype, ctypes.byref(n))
+    if st != 0:
+        raise GlaError(st, "ggla_fwd_workspace_size")
+    return n.value
+
+
+def ggla_bwd_workspace_size(dims: GlaDims, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().ggla_bwd_workspace_size(ctypes.byref(dims), dtype, ctypes.byref(n))
+    if st != 0:
+        raise GlaError(st, "ggla_bwd_workspace_size")
+    return n.value
+
+
+def ggla_fwd(dims, dtype, q, k, v, log_alpha, log_beta, h0, o, hT, workspace, workspace_bytes,
+             stream):
+    """Raw call; pointer arguments are tensors, ints or None.  Returns the status."""
+    return load().ggla_fwd(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(log_alpha), _ptr(log_beta), _ptr(h0), _ptr(o), _ptr(hT),
+                           _ptr(workspace), workspace_bytes, stream)
+
+
+def ggla_bwd(dims, dtype, q, k, v, log_alpha, log_beta, h0, dout, dhT, dq, dk, dv, dlog_alpha,
+             dlog_beta, dh0, workspace, workspace_bytes, stream):
+    """Raw call; pointer arguments are tensors, ints or None.  Returns the status."""
+    return load().ggla_bwd(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(log_alpha), _ptr(log_beta), _ptr(h0), _ptr(dout), _ptr(dhT),
+                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dlog_alpha), _ptr(dlog_beta),
+                           _ptr(dh0), _ptr(workspace), workspace_bytes, stream)
 
 
 def gla_decode(dims, dtype, q, k, v, log_alpha, state, o, stream):

@@ -381,6 +381,171 @@ gla_status gla_decode(const gla_dims* dims, int dtype, const void* q, const void
   return GLA_OK;
 }
 
+// ---- general gate G = alpha^T beta
+static gla_status gg_validate(const gla_dims* d, int dtype) {
+  if (!d) return GLA_ERR_NULL;
+  if (dtype != GLA_FP32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
+  const int q = dtype == GLA_BF16 ? 32 : 16;
+  if (d->B < 0 || d->H < 0 || d->L < 0 || d->L > (1 << 24)) return GLA_ERR_SHAPE;
+  if ((int64_t)d->B * d->H > 65535) return GLA_ERR_SHAPE;
+  if (d->dk < 16 || d->dk > 256 || d->dv < 16 || d->dv > 256) return GLA_ERR_SHAPE;
+  if (d->dk % q || d->dv % q) return GLA_ERR_SHAPE;
+  return GLA_OK;
+}
+
+namespace {
+// Workspace of the general gate.  Forward: the pass records.  Backward: the
+// records of fp32 passes, fp32 copies of bf16 inputs, the recomputed output
+// without its same-token term (o_off) and hT, and dq, dk, dv in full and
+// without their same-token terms, all fp32; gate-gradient partial sums.
+struct GgWs {
+  size_t q32, k32, v32, do32, ooff, hT32, fq, fk, fv, oq, ok, ov, tot, hs, end;
+};
+GgWs gg_layout(const gla_dims* d, int bf16, int bwd) {
+  const size_t BH = (size_t)d->B * d->H, L = (size_t)d->L;
+  GgWs w{};
+  size_t off;
+  if (!bwd) {
+    off = align_up(gg_pass_rec_bytes(bf16, (int)BH, d->L, d->dk));
+  } else {
+    size_t r = gg_pass_rec_bytes(0, (int)BH, d->L, d->dk);
+    const size_t r2 = gg_pass_rec_bytes(0, (int)BH, d->L, d->dv);
+    off = align_up(r > r2 ? r : r2);
+    const size_t nk = align_up(BH * L * d->dk * 4), nv = align_up(BH * L * d->dv * 4);
+    if (bf16) {
+      w.q32 = off; off += nk;
+      w.k32 = off; off += nk;
+      w.v32 = off; off += nv;
+      w.do32 = off; off += nv;
+    }
+    w.ooff = off; off += nv;
+    w.hT32 = off; off += align_up(BH * d->dk * d->dv * 4);
+    w.fq = off; off += nk;
+    w.fk = off; off += nk;
+    w.fv = off; off += nv;
+    w.oq = off; off += nk;
+    w.ok = off; off += nk;
+    w.ov = off; off += nv;
+    w.tot = off; off += align_up(BH * gg_gate_groups(d->L) * (d->dk + d->dv) * 4);
+    w.hs = off; off += align_up(BH * (d->dk + d->dv) * 4);
+  }
+  w.end = off;
+  return w;
+}
+Plan gg_state_plan(const gla_dims* d) {
+  Plan p{};
+  p.B = d->B; p.H = d->H; p.BH = d->B * d->H; p.dk = d->dk; p.dv = d->dv;
+  return p;
+}
+}  // namespace
+
+gla_status ggla_fwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes) {
+  if (!bytes) return GLA_ERR_NULL;
+  gla_status st = gg_validate(dims, dtype);
+  if (st != GLA_OK) return st;
+  *bytes = gg_layout(dims, dtype == GLA_BF16, 0).end;
+  return GLA_OK;
+}
+
+gla_status ggla_bwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes) {
+  if (!bytes) return GLA_ERR_NULL;
+  gla_status st = gg_validate(dims, dtype);
+  if (st != GLA_OK) return st;
+  *bytes = gg_layout(dims, dtype == GLA_BF16, 1).end;
+  return GLA_OK;
+}
+
+gla_status ggla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k,
+                    const void* v, const float* log_alpha, const float* log_beta,
+                    const float* h0, void* o, float* hT, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  gla_status st = gg_validate(dims, dtype);
+  if (st != GLA_OK) return st;
+  const int bf16 = dtype == GLA_BF16, BH = dims->B * dims->H, L = dims->L;
+  if (BH == 0) return GLA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (L == 0) {
+    if ((st = check_ptrs({}, {h0, hT})) != GLA_OK) return st;
+    if (hT) GLA_LAUNCH("copy_state", launch_copy_state(gg_state_plan(dims), h0, hT, s));
+    return GLA_OK;
+  }
+  if ((st = check_ptrs({q, k, v, log_alpha, log_beta, o}, {h0, hT})) != GLA_OK) return st;
+  const GgWs w = gg_layout(dims, bf16, 0);
+  if (!workspace || workspace_bytes < w.end) return GLA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GLA_ERR_ALIGN;
+  const GgPass ps{q, k, v, log_alpha, log_beta, dims->dk, dims->dv, 0, h0, 0, o, 0, nullptr,
+                  hT, nullptr, nullptr};
+  GLA_LAUNCH("gg_prep", launch_gg_pass(ps, 0, bf16, BH, L, workspace, s));
+  GLA_LAUNCH("gg_recur", launch_gg_pass(ps, 1, bf16, BH, L, workspace, s));
+  return GLA_OK;
+}
+
+gla_status ggla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k,
+                    const void* v, const float* log_alpha, const float* log_beta,
+                    const float* h0, const void* dout, const float* dhT, void* dq, void* dk,
+                    void* dv, float* dlog_alpha, float* dlog_beta, float* dh0, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  gla_status st = gg_validate(dims, dtype);
+  if (st != GLA_OK) return st;
+  const int bf16 = dtype == GLA_BF16, BH = dims->B * dims->H, L = dims->L;
+  const int DK = dims->dk, DV = dims->dv;
+  if (BH == 0) return GLA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (L == 0) {
+    if ((st = check_ptrs({}, {dhT, dh0})) != GLA_OK) return st;
+    if (dh0) GLA_LAUNCH("copy_state", launch_copy_state(gg_state_plan(dims), dhT, dh0, s));
+    return GLA_OK;
+  }
+  if ((st = check_ptrs({q, k, v, log_alpha, log_beta, dout, dq, dk, dv, dlog_alpha, dlog_beta},
+                       {h0, dhT, dh0})) != GLA_OK)
+    return st;
+  const GgWs w = gg_layout(dims, bf16, 1);
+  if (!workspace || workspace_bytes < w.end) return GLA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GLA_ERR_ALIGN;
+  char* ws = (char*)workspace;
+  // The passes run in fp32 arithmetic: the closed-form gate gradients subtract
+  // terms tens of times larger than their result, which bf16 operands in the
+  // passes would not resolve.
+  const void *xq = q, *xk = k, *xv = v, *xdo = dout;
+  if (bf16) {
+    const size_t nk = (size_t)BH * L * DK, nv = (size_t)BH * L * DV;
+    GLA_LAUNCH("gg_widen", launch_gg_widen(q, (float*)(ws + w.q32), nk, s));
+    GLA_LAUNCH("gg_widen", launch_gg_widen(k, (float*)(ws + w.k32), nk, s));
+    GLA_LAUNCH("gg_widen", launch_gg_widen(v, (float*)(ws + w.v32), nv, s));
+    GLA_LAUNCH("gg_widen", launch_gg_widen(dout, (float*)(ws + w.do32), nv, s));
+    xq = ws + w.q32; xk = ws + w.k32; xv = ws + w.v32; xdo = ws + w.do32;
+  }
+  float* ooff = (float*)(ws + w.ooff);
+  float* hT32 = (float*)(ws + w.hT32);
+  float *fq = (float*)(ws + w.fq), *fk = (float*)(ws + w.fk), *fv = (float*)(ws + w.fv);
+  float *oq = (float*)(ws + w.oq), *ok = (float*)(ws + w.ok), *ov = (float*)(ws + w.ov);
+  // the forward again, for o and hT (closed-form gate gradients)
+  const GgPass p0{xq, xk, xv, log_alpha, log_beta, DK, DV, 0, h0, 0, nullptr, 0, ooff,
+                  dhT ? hT32 : nullptr, nullptr, nullptr};
+  // dq_t = S_t do_t: the transposed state, q <- do, k <- v, v <- k, gates swapped
+  const GgPass p1{xdo, xv, xk, log_beta, log_alpha, DV, DK, 0, h0, 1, fq, 0, oq, nullptr,
+                  nullptr, nullptr};
+  // dv_s = k_s dS_s, dS_s = G_{s+1} ⊙ dS_{s+1} + q_s^T do_s from dS = dhT: the
+  // reversed sequence with q <- k, k <- q, v <- do; its final state dS_0 times
+  // token 0's gate is dh0
+  const GgPass p2{xk, xq, xdo, log_alpha, log_beta, DK, DV, 1, dhT, 0, fv, 0, ov, dh0, log_alpha,
+                  log_beta};
+  // dk_s = dS_s v_s: the same, transposed: q <- v, k <- do, v <- q, gates swapped
+  const GgPass p3{xv, xdo, xq, log_beta, log_alpha, DV, DK, 1, dhT, 1, fk, 0, ok, nullptr,
+                  nullptr, nullptr};
+  const GgPass* passes[4] = {&p0, &p1, &p2, &p3};
+  static const char* names[4][2] = {{"gg_prep", "gg_recur"}, {"gg_prep_dq", "gg_recur_dq"},
+                                    {"gg_prep_dv", "gg_recur_dv"}, {"gg_prep_dk", "gg_recur_dk"}};
+  for (int i = 0; i < 4; ++i) {
+    GLA_LAUNCH(names[i][0], launch_gg_pass(*passes[i], 0, 0, BH, L, ws, s));
+    GLA_LAUNCH(names[i][1], launch_gg_pass(*passes[i], 1, 0, BH, L, ws, s));
+  }
+  GLA_LAUNCH("gg_gates", launch_gg_gates(bf16, BH, L, DK, DV, q, k, oq, ok, ooff, dout, v, ov,
+                                         hT32, dhT, (float*)(ws + w.tot), (float*)(ws + w.hs),
+                                         fq, fk, fv, dlog_alpha, dlog_beta, dq, dk, dv, s));
+  return GLA_OK;
+}
+
 gla_status gla_profile_begin(int capacity) {
   if (capacity < 1) return GLA_ERR_SHAPE;
   if (capacity != g_cap) {

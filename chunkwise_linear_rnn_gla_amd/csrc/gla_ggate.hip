@@ -1,0 +1,605 @@
+// gla_ggate.hip -- the general gate G_t = alpha_t^T beta_t (gfx950).
+//
+// Recurrence (papercache.org notes on GLA, App. C, general form; the row gate
+// alpha acts on the d_k rows of the state, the column gate beta on its d_v
+// columns):
+//     S_t = (alpha_t^T beta_t) ⊙ S_{t-1} + k_t^T v_t,     o_t = q_t S_t.
+// App. C.2 states that the chunkwise form carries over with both gates.  For
+// a chunk of C = 16 tokens with chunk-local inclusive cumsums A (of log alpha,
+// C x d_k) and Bt (of log beta, C x d_v) and chunk totals a, b:
+//     O   = e^{Bt} ⊙ ((Q ⊙ e^{A}) S)                          (inter-chunk)
+//         + e^{Bt - b} ⊙ (P (V ⊙ e^{b - Bt}))                 (intra-chunk)
+//     S  <- diag(e^{a}) S diag(e^{b}) + (K ⊙ e^{a - A})^T (V ⊙ e^{b - Bt})
+// with P[t][s] = sum_i q_t[i] k_s[i] e^{A_t[i] - A_s[i]} for s <= t, formed
+// in log space (the notes' §4.3 secondary chunking keeps the diagonal blocks
+// in full precision for the same reason).  Every factor is <= 1 except
+// e^{Bt - b}, which is at most e^{-b}: the intra term takes the product form
+// while a column's decay over the chunk stays under e^{60}, and a log-space
+// sum per (t, s) pair for columns that decay faster (sharp beta gates).  The
+// same-token term P[t][t] v_t (factor 1) is added separately in fp32: its
+// operands need no rounding, and the backward's closed-form gate gradients
+// are formed from outputs without it (the same-token parts of q ⊙ dq and
+// k ⊙ dk, and of o ⊙ do and v ⊙ dv, are equal and cancel exactly).
+//
+// Two kernels per pass, as for the row-gated forward:
+//   k_gg_prep  (chunk, batch-head): cumsum of log alpha, Q~ = Q e^{A},
+//              K~ = K e^{a - A}, e^{a} and P, stored as MFMA fragments;
+//   k_gg_recur (16-column tile, batch-head), one wave: the state tile stays in
+//              MFMA accumulators across the chunks; per chunk the inter term
+//              (Q~ S), the intra term (P V~), the output, the decay and the
+//              update (K~^T V~), with the beta cumsum formed across lanes.
+// A pass can read its sequence backwards with the gates shifted by one token
+// and take its initial state transposed; the backward is built from such
+// passes (gla_api.hip).  Gate gradients come from the closed form of App. C
+// (k_gg_gate_tot / k_gg_gate_fin).
+#include "gla_common.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
+
+constexpr int kGC = 16;            // tokens per chunk
+constexpr float kSafeDecay = 60.f;  // product form while -b <= this
+
+__device__ inline floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Sequence position read by pass token u (-1: past the end).
+__device__ inline int data_row(int u, int L, int rev) {
+  if (u >= L) return -1;
+  return rev ? L - 1 - u : u;
+}
+// Row of the gate applied at pass token u (-1: gate 1).  A reversed pass
+// applies at token u the gate of original token L - u, and none at u = 0.
+__device__ inline int gate_row(int u, int L, int rev) {
+  if (u >= L) return -1;
+  if (!rev) return u;
+  return u == 0 ? -1 : L - u;
+}
+
+// Index of Q~[t][i] in the chunk's Q fragment record.  bf16 (16x16x32 A
+// operand): [DKP/32][64 lanes][8]; lane t + 16 g, slot e < 4 holds channel
+// 32 p + 4 g + e and slot e >= 4 channel 32 p + 16 + 4 g + e - 4, matching a B
+// operand built from two accumulator tiles of the state.  fp32 (16x16x4, four
+// steps per 16-row tile): [DKP/16][64][4], lane t + 16 g, slot s = channel
+// 16 m + 4 g + s.
+template <typename T> __device__ inline int qf_index(int t, int i);
+template <> __device__ inline int qf_index<bf16>(int t, int i) {
+  const int p = i >> 5, r = i & 31, hi = r >> 4, rr = r & 15;
+  return ((p * 64 + t + 16 * (rr >> 2)) << 3) + 4 * hi + (rr & 3);
+}
+template <> __device__ inline int qf_index<float>(int t, int i) {
+  const int m = i >> 4, r = i & 15;
+  return ((m * 64 + t + 16 * (r >> 2)) << 2) + (r & 3);
+}
+// K~[t][i] as the A operand of the state update (rows i, K = tokens):
+// [DKP/16][64][4], lane (i % 16) + 16 (t / 4), slot t % 4.
+__device__ inline int kf_index(int t, int i) {
+  return (((i >> 4) * 64 + (i & 15) + 16 * (t >> 2)) << 2) + (t & 3);
+}
+// s + err = a + b exactly (Knuth's two-sum).  The chunk-local cumsums are kept
+// as hi + lo pairs so that a difference B_t - B_s, the exponent of a decay
+// between two tokens, is accurate relative to its own size rather than to
+// |B_t|, which sharp gates make hundreds of times larger.
+__device__ inline float two_sum(float a, float b, float& err) {
+  const float s = a + b, bp = s - a;
+  err = (a - (s - bp)) + (b - bp);
+  return s;
+}
+
+// P[t][s] for s < t (zero on and above the diagonal): [64][4] fp32, lane
+// t + 16 (s / 4), slot s % 4; then P[t][t], 16 fp32; then e^{a}, DKP fp32.
+__device__ inline int pf_index(int t, int s) { return ((t + 16 * (s >> 2)) << 2) + (s & 3); }
+
+}  // namespace
+
+constexpr int kPfFloats = 256 + 16;  // P below the diagonal, then its diagonal
+
+size_t gg_rec_bytes(int is_bf16, int dkp) {
+  return (size_t)32 * dkp * (is_bf16 ? 2 : 4) + 4 * kPfFloats + (size_t)4 * dkp;
+}
+
+int gg_padded_dim(int is_bf16, int d) {
+  for (int p = is_bf16 ? 32 : 16; p <= 256; p *= 2)
+    if (d <= p) return p;
+  return -1;
+}
+
+// grid (NC, BH), 256 threads.  dk: channels of the pass's q and k; dkp: the
+// record's (padded) channel count.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_gg_prep(const T* __restrict__ q,
+                                                      const T* __restrict__ k,
+                                                      const float* __restrict__ la,
+                                                      uint8_t* __restrict__ rec, size_t rec_bytes,
+                                                      int L, int dk, int dkp, int NC, int rev) {
+  extern __shared__ float sm[];
+  const int ld = dkp + 1;  // odd row stride: the P loop reads 16 rows at one column
+  float* qs = sm;
+  float* ks = qs + kGC * ld;
+  float* cs = ks + kGC * ld;  // cumsum, hi part
+  float* cl = cs + kGC * ld;  // lo part
+  const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  for (int x = tid; x < kGC * dkp; x += kThreads) {
+    const int t = x / dkp, i = x - t * dkp, u = n * kGC + t;
+    const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
+    const bool in = i < dk;
+    qs[t * ld + i] = (in && dr >= 0) ? to_f32(q[((size_t)bh * L + dr) * dk + i]) : 0.f;
+    ks[t * ld + i] = (in && dr >= 0) ? to_f32(k[((size_t)bh * L + dr) * dk + i]) : 0.f;
+    cs[t * ld + i] = (in && gr >= 0) ? la[((size_t)bh * L + gr) * dk + i] : 0.f;
+  }
+  __syncthreads();
+  uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
+  T* qf = reinterpret_cast<T*>(r);
+  T* kf = qf + kGC * dkp;
+  float* pf = reinterpret_cast<float*>(kf + kGC * dkp);
+  float* ga = pf + kPfFloats;
+  for (int i = tid; i < dkp; i += kThreads) {
+    float c = 0.f, e = 0.f;
+#pragma unroll
+    for (int t = 0; t < kGC; ++t) {
+      float err;
+      c = two_sum(c, cs[t * ld + i], err);
+      e += err;
+      cs[t * ld + i] = c;
+      cl[t * ld + i] = e;
+    }
+    ga[i] = gexp<T>(c + e);
+#pragma unroll
+    for (int t = 0; t < kGC; ++t) {
+      const float at = cs[t * ld + i], al = cl[t * ld + i];
+      qf[qf_index<T>(t, i)] = from_f32<T>(qs[t * ld + i] * gexp<T>(at + al));
+      kf[kf_index(t, i)] = from_f32<T>(ks[t * ld + i] * gexp<T>((c - at) + (e - al)));
+    }
+  }
+  __syncthreads();
+  // P, one (t, s) pair per thread; the diagonal goes to its own slots, and
+  // the fragment holds zero on and above it
+  const int t = tid >> 4, s = tid & 15;
+  float acc = 0.f;
+  if (s <= t) {
+    const float* qt = qs + t * ld;
+    const float* ksr = ks + s * ld;
+    const float* ct = cs + t * ld;
+    const float* csr = cs + s * ld;
+    const float* lt = cl + t * ld;
+    const float* lsr = cl + s * ld;
+    for (int i = 0; i < dk; ++i)
+      acc += qt[i] * ksr[i] * gexp<T>((ct[i] - csr[i]) + (lt[i] - lsr[i]));
+  }
+  pf[pf_index(t, s)] = s < t ? acc : 0.f;
+  if (s == t) pf[256 + t] = acc;
+}
+
+// Fragments of one chunk's records for one lane.
+template <typename T, int MT> struct GgFrag;
+template <int MT> struct GgFrag<bf16, MT> {
+  bf16x8 q[MT / 2];
+  bf16x4 k[MT];
+};
+template <int MT> struct GgFrag<float, MT> {
+  f4 q[MT];
+  f4 k[MT];
+};
+
+template <int MT>
+__device__ inline void load_qk(GgFrag<bf16, MT>& f, const bf16* qf, const bf16* kf, int l) {
+#pragma unroll
+  for (int p = 0; p < MT / 2; ++p) f.q[p] = *reinterpret_cast<const bf16x8*>(qf + ((p * 64 + l) << 3));
+#pragma unroll
+  for (int m = 0; m < MT; ++m) f.k[m] = *reinterpret_cast<const bf16x4*>(kf + ((m * 64 + l) << 2));
+}
+template <int MT>
+__device__ inline void load_qk(GgFrag<float, MT>& f, const float* qf, const float* kf, int l) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m) f.q[m] = *reinterpret_cast<const f4*>(qf + ((m * 64 + l) << 2));
+#pragma unroll
+  for (int m = 0; m < MT; ++m) f.k[m] = *reinterpret_cast<const f4*>(kf + ((m * 64 + l) << 2));
+}
+
+// acc += Q~ S (16 tokens x 16 columns), S in accumulator layout.
+template <int MT>
+__device__ inline floatx4 inter(const GgFrag<bf16, MT>& f, const floatx4 (&S)[MT]) {
+  floatx4 acc = zero4();
+#pragma unroll
+  for (int p = 0; p < MT / 2; ++p) {
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      b[e] = static_cast<bf16>(S[2 * p][e]);
+      b[4 + e] = static_cast<bf16>(S[2 * p + 1][e]);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.q[p], b, acc, 0, 0, 0);
+  }
+  return acc;
+}
+template <int MT>
+__device__ inline floatx4 inter(const GgFrag<float, MT>& f, const floatx4 (&S)[MT]) {
+  floatx4 acc = zero4();
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma4(f.q[m][s], S[m][s], acc);
+  return acc;
+}
+
+// P V~ (16 x 16): P in fp32 (hi + lo for bf16 operands), V~ in accumulator
+// layout (lane (j, g) holds tokens 4 g .. 4 g + 3 of column j).
+__device__ inline floatx4 intra(const f4& p, const floatx4& vt, bf16) {
+  bf16x4 hi, lo, vb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = static_cast<bf16>(p[e]);
+    lo[e] = static_cast<bf16>(p[e] - static_cast<float>(hi[e]));
+    vb[e] = static_cast<bf16>(vt[e]);
+  }
+  return mfma16(lo, vb, mfma16(hi, vb, zero4()));
+}
+__device__ inline floatx4 intra(const f4& p, const floatx4& vt, float) {
+  floatx4 acc = zero4();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma4(p[s], vt[s], acc);
+  return acc;
+}
+
+// S += K~^T V~
+template <int MT>
+__device__ inline void update(floatx4 (&S)[MT], const GgFrag<bf16, MT>& f, const floatx4& vt) {
+  bf16x4 vb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) vb[e] = static_cast<bf16>(vt[e]);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) S[m] = mfma16(f.k[m], vb, S[m]);
+}
+template <int MT>
+__device__ inline void update(floatx4 (&S)[MT], const GgFrag<float, MT>& f, const floatx4& vt) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) S[m] = mfma4(f.k[m][s], vt[s], S[m]);
+}
+
+// grid (dv / 16, BH), one wave.  Lane (j, g) = (l % 16, l / 16) owns state
+// column j of the tile and, in every 16 x 16 accumulator tile, rows 4 g + e.
+// init: [BH][dk][dv] ([BH][dv][dk] when init_t), or null for zeros.  o (if
+// not null) receives the output, ooff (if not null) the output without the
+// same-token term, in fp32.  fin (if not null) receives the final state
+// [BH][dk][dv], first multiplied by the gate of sequence token 0 when
+// fin_la / fin_lb are given.
+template <typename T, typename TO, int MT>
+__global__ __launch_bounds__(kWave) void k_gg_recur(
+    const uint8_t* __restrict__ rec, size_t rec_bytes, const T* __restrict__ v,
+    const float* __restrict__ lb, const float* __restrict__ init, int init_t,
+    TO* __restrict__ o, float* __restrict__ ooff, float* __restrict__ fin,
+    const float* __restrict__ fin_la,
+    const float* __restrict__ fin_lb, int L, int dk, int dv, int NC, int rev) {
+  constexpr int DKP = MT * 16;
+  const int l = threadIdx.x, j = l & 15, g = l >> 4;
+  const int jc = blockIdx.x * 16 + j, bh = blockIdx.y;
+  floatx4 S[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * m + 4 * g + e;
+      float x = 0.f;
+      if (init && row < dk)
+        x = init_t ? init[((size_t)bh * dv + jc) * dk + row] : init[((size_t)bh * dk + row) * dv + jc];
+      S[m][e] = x;
+    }
+  const T* vb = v + (size_t)bh * L * dv + jc;
+  const float* lbb = lb + (size_t)bh * L * dv + jc;
+
+  for (int n = 0; n < NC; ++n) {
+    const uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
+    const T* qf = reinterpret_cast<const T*>(r);
+    const T* kf = qf + kGC * DKP;
+    const float* pf = reinterpret_cast<const float*>(kf + kGC * DKP);
+    const float* ga = pf + kPfFloats;
+    GgFrag<T, MT> f;
+    load_qk(f, qf, kf, l);
+    const f4 p = *reinterpret_cast<const f4*>(pf + 4 * l);
+    const f4 pd = *reinterpret_cast<const f4*>(pf + 256 + 4 * g);  // P[4g + e][4g + e]
+    float vv[4], c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int u = n * kGC + 4 * g + e;
+      const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
+      vv[e] = dr >= 0 ? to_f32(vb[(size_t)dr * dv]) : 0.f;
+      c[e] = gr >= 0 ? lbb[(size_t)gr * dv] : 0.f;
+    }
+    // chunk-local inclusive cumsum of log beta down the 16 rows of column j,
+    // as hi (c) + lo (cl) pairs: within the lane's 4 rows, then the totals of
+    // the lanes above it (row groups g' < g) added in front
+    float cl[4], err;
+    cl[0] = 0.f;
+#pragma unroll
+    for (int e = 1; e < 4; ++e) {
+      c[e] = two_sum(c[e - 1], c[e], err);
+      cl[e] = cl[e - 1] + err;
+    }
+    float th[4], tl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      th[r] = __shfl(c[3], j + 16 * r);
+      tl[r] = __shfl(cl[3], j + 16 * r);
+    }
+    float eh = 0.f, el = 0.f;  // sum of the totals of row groups before g
+    float bh_ = 0.f, bl_ = 0.f;  // chunk total
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < g) {
+        eh = two_sum(eh, th[r], err);
+        el += tl[r] + err;
+      }
+      bh_ = two_sum(bh_, th[r], err);
+      bl_ += tl[r] + err;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = two_sum(eh, c[e], err);
+      cl[e] += el + err;
+    }
+    const float bt = bh_ + bl_;  // chunk total (rounded)
+    floatx4 vt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vt[e] = vv[e] * gexp<T>((bh_ - c[e]) + (bl_ - cl[e]));
+    const floatx4 a1 = inter(f, S);
+    const floatx4 a2 = intra(p, vt, T());
+    float res[4];
+    const bool safe = bt >= -kSafeDecay;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      res[e] = gexp<T>(c[e] + cl[e]) * a1[e] + gexp<T>((c[e] - bh_) + (cl[e] - bl_)) * a2[e];
+    if (__any(!safe)) {
+      // log-space intra term: sum_{s < t} P[t][s] v_s e^{Bt_t - Bt_s}
+      float sl[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kGC; ++s) {
+        const int src = j + 16 * (s >> 2);
+        const float cs = __shfl(c[s & 3], src), ls = __shfl(cl[s & 3], src);
+        const float vs = __shfl(vv[s & 3], src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * g + e;
+          if (s < t) sl[e] += pf[pf_index(t, s)] * vs * gexp<T>((c[e] - cs) + (cl[e] - ls));
+        }
+      }
+      if (!safe)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = gexp<T>(c[e] + cl[e]) * a1[e] + sl[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int dr = data_row(n * kGC + 4 * g + e, L, rev);
+      if (dr < 0) continue;
+      const size_t x = ((size_t)bh * L + dr) * dv + jc;
+      if (ooff) ooff[x] = res[e];
+      if (o) o[x] = from_f32<TO>(res[e] + pd[e] * vv[e]);
+    }
+    // decay and update
+    const float gb = gexp<T>(bt);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const f4 gm = *reinterpret_cast<const f4*>(ga + 16 * m + 4 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[m][e] *= gm[e] * gb;
+    }
+    update(S, f, vt);
+  }
+  if (fin) {
+    const float gb = fin_lb ? gexp<T>(fin_lb[(size_t)bh * L * dv + jc]) : 1.f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * m + 4 * g + e;
+        if (row < dk) {
+          const float gr = fin_la ? gexp<T>(fin_la[(size_t)bh * L * dk + row]) * gb : 1.f;
+          fin[((size_t)bh * dk + row) * dv + jc] = S[m][e] * gr;
+        }
+      }
+  }
+}
+
+// Closed-form gate gradients (App. C): per token,
+//   dlog b_t = q_t ⊙ dq_t - k_t ⊙ dk_t       (d_k channels, alpha)
+//   dlog d_t = o_t ⊙ do_t - v_t ⊙ dv_t       (d_v channels, beta)
+// and each dlog gate is the sum over later tokens, plus the row / column sums
+// of hT ⊙ dhT.  dq, dk, dv and o enter without their same-token terms, whose
+// contributions to the two differences are equal and cancel exactly; what is
+// left is the part that the gates decay.  Chunks of kGT tokens: totals first,
+// then the carry-in.
+constexpr int kGT = 64;
+
+template <typename T>
+__device__ inline float gg_term(int c, size_t row, int dk, int dv, const T* q, const T* k,
+                                const float* dq, const float* dkk, const float* o32,
+                                const T* dout, const T* v, const float* dvv) {
+  if (c < dk) {
+    const size_t x = row * dk + c;
+    return to_f32(q[x]) * dq[x] - to_f32(k[x]) * dkk[x];
+  }
+  const size_t x = row * dv + (c - dk);
+  return o32[x] * to_f32(dout[x]) - to_f32(v[x]) * dvv[x];
+}
+
+// grid (ceil(L / kGT), BH); tot [BH][NG][dk + dv]
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_gg_gate_tot(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ dq,
+    const float* __restrict__ dkk, const float* __restrict__ o32, const T* __restrict__ dout,
+    const T* __restrict__ v, const float* __restrict__ dvv, float* __restrict__ tot, int L,
+    int dk, int dv) {
+  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, D = dk + dv;
+  const int t0 = cg * kGT, t1 = min(L, t0 + kGT);
+  for (int c = threadIdx.x; c < D; c += kThreads) {
+    float s = 0.f;
+    for (int t = t0; t < t1; ++t)
+      s += gg_term(c, (size_t)bh * L + t, dk, dv, q, k, dq, dkk, o32, dout, v, dvv);
+    tot[((size_t)bh * NG + cg) * D + c] = s;
+  }
+}
+
+// grid (BH); hs [BH][dk + dv] = row sums, then column sums, of hT ⊙ dhT
+__global__ __launch_bounds__(kThreads) void k_gg_hsum(const float* __restrict__ hT,
+                                                      const float* __restrict__ dhT,
+                                                      float* __restrict__ hs, int dk, int dv) {
+  const int bh = blockIdx.x;
+  const float* h = hT + (size_t)bh * dk * dv;
+  const float* d = dhT + (size_t)bh * dk * dv;
+  for (int c = threadIdx.x; c < dk + dv; c += kThreads) {
+    float s = 0.f;
+    if (c < dk)
+      for (int j = 0; j < dv; ++j) s += h[(size_t)c * dv + j] * d[(size_t)c * dv + j];
+    else
+      for (int i = 0; i < dk; ++i) s += h[(size_t)i * dv + c - dk] * d[(size_t)i * dv + c - dk];
+    hs[(size_t)bh * (dk + dv) + c] = s;
+  }
+}
+
+// grid (ceil(L / kGT), BH): dlog alpha, dlog beta, and dq, dk, dv in the I/O
+// dtype from their full fp32 values (fq, fk, fv).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_gg_gate_fin(
+    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ dq,
+    const float* __restrict__ dkk, const float* __restrict__ o32, const T* __restrict__ dout,
+    const T* __restrict__ v, const float* __restrict__ dvv, const float* __restrict__ tot,
+    const float* __restrict__ hs, const float* __restrict__ fq, const float* __restrict__ fk,
+    const float* __restrict__ fv, float* __restrict__ dla, float* __restrict__ dlb,
+    T* __restrict__ dq_out, T* __restrict__ dk_out, T* __restrict__ dv_out, int L, int dk,
+    int dv) {
+  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, D = dk + dv;
+  const int t0 = cg * kGT, t1 = min(L, t0 + kGT);
+  for (int c = threadIdx.x; c < D; c += kThreads) {
+    float run = hs ? hs[(size_t)bh * D + c] : 0.f;
+    for (int g2 = cg + 1; g2 < NG; ++g2) run += tot[((size_t)bh * NG + g2) * D + c];
+    for (int t = t1 - 1; t >= t0; --t) {
+      const size_t row = (size_t)bh * L + t;
+      run += gg_term(c, row, dk, dv, q, k, dq, dkk, o32, dout, v, dvv);
+      if (c < dk) {
+        dla[row * dk + c] = run;
+        dq_out[row * dk + c] = from_f32<T>(fq[row * dk + c]);
+        dk_out[row * dk + c] = from_f32<T>(fk[row * dk + c]);
+      } else {
+        dlb[row * dv + c - dk] = run;
+        dv_out[row * dv + c - dk] = from_f32<T>(fv[row * dv + c - dk]);
+      }
+    }
+  }
+}
+
+// bf16 -> fp32 copy (the backward's passes run in fp32 arithmetic)
+__global__ __launch_bounds__(kThreads) void k_gg_widen(const bf16* __restrict__ x,
+                                                       float* __restrict__ y, size_t n) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) y[i] = static_cast<float>(x[i]);
+}
+
+// ---- launchers ----
+
+hipError_t launch_gg_widen(const void* x, float* y, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gg_widen, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, (const bf16*)x, y, n);
+  return hipGetLastError();
+}
+
+template <typename T, typename TO>
+static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t* r, size_t rb,
+                            int L, int NC, hipStream_t s) {
+#define GG_RECUR(MT)                                                                          \
+  hipLaunchKernelGGL((k_gg_recur<T, TO, MT>), grid, dim3(kWave), 0, s, r, rb, (const T*)ps.v, \
+                     ps.lb, ps.init, ps.init_t, (TO*)ps.o, ps.o_off, ps.fin, ps.fin_la,       \
+                     ps.fin_lb, L,                                                            \
+                     ps.dk, ps.dv, NC, ps.rev)
+  if constexpr (sizeof(T) == 4) {
+    if (dkp == 16) { GG_RECUR(1); return; }
+  }
+  if (dkp == 32) GG_RECUR(2);
+  else if (dkp == 64) GG_RECUR(4);
+  else if (dkp == 128) GG_RECUR(8);
+  else GG_RECUR(16);
+#undef GG_RECUR
+}
+
+// part 0: k_gg_prep, part 1: k_gg_recur (separate so that each launch can be
+// timed on its own)
+hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int BH, int L, void* rec,
+                          hipStream_t s) {
+  const int NC = (L + kGC - 1) / kGC;
+  const int dkp = gg_padded_dim(is_bf16, ps.dk);
+  if (dkp < 0 || ps.dv % 16 || BH <= 0 || NC <= 0) return hipErrorInvalidValue;
+  const size_t rb = gg_rec_bytes(is_bf16, dkp);
+  uint8_t* r = static_cast<uint8_t*>(rec);
+  if (part == 0) {
+    const size_t lds = sizeof(float) * 4 * kGC * (dkp + 1);  // 65.8 KB at 256 channels
+    const dim3 pg(NC, BH);
+    if (lds > 65536) {
+      const hipError_t e =
+          is_bf16 ? hipFuncSetAttribute((const void*)k_gg_prep<bf16>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                  : hipFuncSetAttribute((const void*)k_gg_prep<float>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    if (is_bf16)
+      hipLaunchKernelGGL((k_gg_prep<bf16>), pg, dim3(kThreads), lds, s, (const bf16*)ps.q,
+                         (const bf16*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
+    else
+      hipLaunchKernelGGL((k_gg_prep<float>), pg, dim3(kThreads), lds, s, (const float*)ps.q,
+                         (const float*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
+  } else {
+    const dim3 rg(ps.dv / 16, BH);
+    if (!is_bf16) launch_gg_recur<float, float>(ps, dkp, rg, r, rb, L, NC, s);
+    else if (ps.o_f32) launch_gg_recur<bf16, float>(ps, dkp, rg, r, rb, L, NC, s);
+    else launch_gg_recur<bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
+  }
+  return hipGetLastError();
+}
+
+size_t gg_pass_rec_bytes(int is_bf16, int BH, int L, int d) {
+  const int dkp = gg_padded_dim(is_bf16, d);
+  if (dkp < 0) return 0;
+  return gg_rec_bytes(is_bf16, dkp) * (size_t)BH * ((L + kGC - 1) / kGC);
+}
+
+int gg_gate_groups(int L) { return (L + kGT - 1) / kGT; }
+
+hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const void* q,
+                           const void* k, const float* dq32, const float* dk32, const float* o32,
+                           const void* dout, const void* v, const float* dv32, const float* hT,
+                           const float* dhT, float* tot, float* hs, const float* fq,
+                           const float* fk, const float* fv, float* dla, float* dlb, void* dq,
+                           void* dkk, void* dvv, hipStream_t s) {
+  const dim3 grid(gg_gate_groups(L), BH);
+  if (dhT) hipLaunchKernelGGL(k_gg_hsum, dim3(BH), dim3(kThreads), 0, s, hT, dhT, hs, dk, dv);
+  const float* hsp = dhT ? hs : nullptr;
+  if (is_bf16) {
+    hipLaunchKernelGGL((k_gg_gate_tot<bf16>), grid, dim3(kThreads), 0, s, (const bf16*)q,
+                       (const bf16*)k, dq32, dk32, o32, (const bf16*)dout, (const bf16*)v, dv32,
+                       tot, L, dk, dv);
+    hipLaunchKernelGGL((k_gg_gate_fin<bf16>), grid, dim3(kThreads), 0, s, (const bf16*)q,
+                       (const bf16*)k, dq32, dk32, o32, (const bf16*)dout, (const bf16*)v, dv32,
+                       tot, hsp, fq, fk, fv, dla, dlb, (bf16*)dq, (bf16*)dkk, (bf16*)dvv, L, dk,
+                       dv);
+  } else {
+    hipLaunchKernelGGL((k_gg_gate_tot<float>), grid, dim3(kThreads), 0, s, (const float*)q,
+                       (const float*)k, dq32, dk32, o32, (const float*)dout, (const float*)v,
+                       dv32, tot, L, dk, dv);
+    hipLaunchKernelGGL((k_gg_gate_fin<float>), grid, dim3(kThreads), 0, s, (const float*)q,
+                       (const float*)k, dq32, dk32, o32, (const float*)dout, (const float*)v,
+                       dv32, tot, hsp, fq, fk, fv, dla, dlb, (float*)dq, (float*)dkk, (float*)dvv,
+                       L, dk, dv);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gla

@@ -154,6 +154,54 @@ hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT,
 hipError_t launch_decode(const Plan& p, const void* q, const void* k, const void* v,
                          const float* la, float* state, void* o, hipStream_t s);
 
+// ---- general gate G = alpha^T beta (gla_ggate.hip) ----
+// One pass of the general-gate recurrence over [BH][L] rows: state rows = the
+// channels of q and k (dk), columns = those of v (dv); la [BH][L][dk] and
+// lb [BH][L][dv] are the log row and column gates.  rev: the pass runs the
+// sequence backwards, applying at its token u the gates of token L - u (none
+// at u = 0).  init: [BH][dk][dv] (transposed, [BH][dv][dk], when init_t) or
+// null; o [BH][L][dv] (or null) in the I/O dtype or fp32 (o_f32, bf16 passes
+// only); o_off (or null) fp32, the output without its same-token term; fin
+// (or null) receives the final state, multiplied by the gate of sequence
+// token 0 (fin_la, fin_lb) when those are given.
+struct GgPass {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* la;
+  const float* lb;
+  int dk, dv, rev;
+  const float* init;
+  int init_t;
+  void* o;
+  int o_f32;
+  float* o_off;
+  float* fin;
+  const float* fin_la;
+  const float* fin_lb;
+};
+// State rows are padded to the next of 16 (fp32 only), 32, 64, 128, 256;
+// -1 past 256.
+int gg_padded_dim(int is_bf16, int d);
+// Record bytes of one pass over [BH][L] with d state rows.
+size_t gg_pass_rec_bytes(int is_bf16, int BH, int L, int d);
+// part 0 launches the per-chunk prep (records into rec), part 1 the recurrence.
+hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int BH, int L, void* rec,
+                          hipStream_t s);
+// Token groups of the gate-gradient kernels (their totals are [BH][groups][dk + dv]).
+int gg_gate_groups(int L);
+// dlog alpha, dlog beta by the closed form from dq32, dk32, dv32, o32 (fp32,
+// without their same-token terms), and dq, dk, dv converted from the full
+// fp32 values fq, fk, fv.  hs: [BH][dk + dv] scratch (used when dhT is given).
+hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const void* q,
+                           const void* k, const float* dq32, const float* dk32, const float* o32,
+                           const void* dout, const void* v, const float* dv32, const float* hT,
+                           const float* dhT, float* tot, float* hs, const float* fq,
+                           const float* fk, const float* fv, float* dla, float* dlb, void* dq,
+                           void* dkk, void* dvv, hipStream_t s);
+// y[i] = x[i] for n bf16 values x, fp32 y.
+hipError_t launch_gg_widen(const void* x, float* y, size_t n, hipStream_t s);
+
 // dla += rs + the dlog b totals of all later chunks (dlt [BH][NC][dk]).
 hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,
                             hipStream_t s);

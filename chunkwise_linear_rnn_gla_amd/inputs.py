@@ -115,6 +115,29 @@ def make_inputs(B, H, L, dk, dv, dtype="bf16", seed=0, gate="sigmoid16", h0_std=
     return Inputs(q, k, v, a, h0, do, dhT)
 
 
+def make_log_beta(B, H, L, dv, seed=0, gate="sigmoid16", gate_value=-0.05):
+    """Seeded column gate log beta [B, H, L, dv] (fp32) for the general gate
+    G = alpha^T beta, drawn from its own generator (seed + 7919) so that the
+    draws of make_inputs with the same seed are unchanged.  Same modes as the
+    row gate: logsigmoid(z) / 16, zero, constant, per-channel constant and
+    "extreme" (-U(0, 20))."""
+    g = torch.Generator().manual_seed(int(seed) + 7919)
+    z = torch.randn(B, H, L, dv, generator=g)
+    if gate == "sigmoid16":
+        b = F.logsigmoid(z) / 16.0
+    elif gate == "zero":
+        b = torch.zeros_like(z)
+    elif gate == "const":
+        b = torch.full_like(z, float(gate_value))
+    elif gate == "channel_const":
+        b = (F.logsigmoid(z[:, :, :1, :]) / 16.0).expand_as(z).contiguous()
+    elif gate == "extreme":
+        b = -20.0 * torch.rand(B, H, L, dv, generator=g)
+    else:
+        raise ValueError(f"unknown gate mode {gate!r}")
+    return b.to(torch.float32).contiguous()
+
+
 def workload_inputs(w: Workload) -> Inputs:
     return make_inputs(w.B, w.H, w.L, w.dk, w.dv, w.dtype, w.seed, h0_std=w.h0_std,
                        with_do=w.backward)

@@ -137,6 +137,46 @@ gla_status gla_decode(const gla_dims *dims, int dtype,
                       const void *q, const void *k, const void *v,
                       const float *log_alpha, float *state, void *o, void *stream);
 
+/* ---- general gate G_t = alpha_t^T beta_t (papercache.org notes, App. C) ----
+ * The recurrence with an outer-product gate: log_alpha gates the d_k rows of
+ * the state and log_beta its d_v columns,
+ *     S_t = (alpha_t^T beta_t) ⊙ S_{t-1} + k_t^T v_t,     o_t = q_t S_t
+ * (App. C.1 parallel form O = (((Q ⊙ B)(K / B)^T ⊙ M)(V / D)) ⊙ D with B, D
+ * the cumulative products of alpha, beta; log_beta = 0 gives gla_fwd).  It is
+ * computed chunkwise (App. C.2) in 16-token chunks; the chunk and subchunk
+ * fields of dims are not used.
+ *   dims: dk and dv multiples of 16 (GLA_FP32) or 32 (GLA_BF16), each in
+ *         [16, 256]; B * H <= 65535; otherwise GLA_ERR_SHAPE.
+ *   in : q, k [B,H,L,dk], v [B,H,L,dv] in `dtype`; log_alpha [B,H,L,dk] and
+ *        log_beta [B,H,L,dv] fp32 (entries <= 0 expected; not checked);
+ *        h0 [B,H,dk,dv] fp32 or NULL for zeros.
+ *   out: o [B,H,L,dv] in `dtype`; hT [B,H,dk,dv] fp32 or NULL to skip.
+ *   workspace: at least ggla_fwd_workspace_size bytes, 16-byte aligned,
+ *   clobbered.  Errors as for gla_fwd. */
+gla_status ggla_fwd_workspace_size(const gla_dims *dims, int dtype, size_t *bytes);
+gla_status ggla_bwd_workspace_size(const gla_dims *dims, int dtype, size_t *bytes);
+gla_status ggla_fwd(const gla_dims *dims, int dtype,
+                    const void *q, const void *k, const void *v,
+                    const float *log_alpha, const float *log_beta, const float *h0,
+                    void *o, float *hT,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward of ggla_fwd for dout = dL/do and dhT = dL/dhT (NULL for zeros).
+ * dq, dk and dv are each a pass of the same recurrence with the roles of the
+ * operands exchanged (dk and dv on the reversed sequence, gates shifted by
+ * one token).  The gate gradients use App. C's closed form:
+ *     dlog_alpha_t = sum_{i >= t} (q_i ⊙ dq_i - k_i ⊙ dk_i) + rowsum(hT ⊙ dhT)
+ *     dlog_beta_t  = sum_{i >= t} (o_i ⊙ do_i - v_i ⊙ dv_i) + colsum(hT ⊙ dhT)
+ *   out: dq, dk [B,H,L,dk], dv [B,H,L,dv] in `dtype`; dlog_alpha [B,H,L,dk],
+ *        dlog_beta [B,H,L,dv] fp32; dh0 [B,H,dk,dv] fp32 or NULL to skip.
+ *   workspace: at least ggla_bwd_workspace_size bytes, as for ggla_fwd. */
+gla_status ggla_bwd(const gla_dims *dims, int dtype,
+                    const void *q, const void *k, const void *v,
+                    const float *log_alpha, const float *log_beta, const float *h0,
+                    const void *dout, const float *dhT,
+                    void *dq, void *dk, void *dv, float *dlog_alpha, float *dlog_beta,
+                    float *dh0, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- launch profiling (measurement support; not part of the computation) ----
  * While enabled, every kernel launch made by gla_fwd / gla_bwd is bracketed by
  * two HIP events recorded on the launch stream, so per-kernel GPU durations can

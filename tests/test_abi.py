@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gla_[a-z0-9_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(g?gla_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -146,3 +146,29 @@ def test_decode_errors():
     assert _abi.gla_decode(d, GLA_BF16, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == 1
     assert _abi.gla_decode(d, GLA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None) == 4
     assert _abi.gla_decode(good_dims(B=0), GLA_BF16, *([None] * 6), None) == 0
+
+
+def test_general_gate_errors():
+    # ggla_*: validation happens before any launch; chunk fields are not used
+    d = good_dims(L=64, chunk=0, subchunk=0)
+    n_fwd = _abi.ggla_fwd_workspace_size(d, GLA_BF16)
+    n_bwd = _abi.ggla_bwd_workspace_size(d, GLA_BF16)
+    assert 0 < n_fwd < n_bwd
+    args = [FAKE] * 5 + [None, FAKE, None]
+    assert _abi.ggla_fwd(d, 2, *args, FAKE, n_fwd, None) == 3
+    assert _abi.load().ggla_fwd(None, GLA_BF16, *([FAKE] * 8), FAKE, n_fwd, None) == 1
+    assert _abi.ggla_fwd(good_dims(dv=512), GLA_BF16, *args, FAKE, n_fwd, None) == 2
+    assert _abi.ggla_fwd(good_dims(dk=48), GLA_BF16, *args, FAKE, n_fwd, None) == 2
+    assert _abi.ggla_fwd(good_dims(B=300, H=300), GLA_BF16, *args, FAKE, n_fwd, None) == 2
+    assert _abi.ggla_fwd(d, GLA_BF16, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE,
+                         n_fwd, None) == 1
+    assert _abi.ggla_fwd(d, GLA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None, FAKE, None, FAKE,
+                         n_fwd, None) == 4
+    assert _abi.ggla_fwd(d, GLA_BF16, *args, FAKE, n_fwd - 1, None) == 5
+    bargs = [FAKE] * 5 + [None, FAKE, None] + [FAKE] * 5 + [None]
+    assert _abi.ggla_bwd(d, GLA_BF16, *bargs, FAKE, n_bwd - 1, None) == 5
+    bad = list(bargs)
+    bad[12] = None  # dlog_beta
+    assert _abi.ggla_bwd(d, GLA_BF16, *bad, FAKE, n_bwd, None) == 1
+    assert _abi.ggla_fwd(good_dims(B=0), GLA_BF16, *([None] * 8), None, 0, None) == 0
+    assert _abi.ggla_bwd(good_dims(B=0), GLA_BF16, *([None] * 14), None, 0, None) == 0
