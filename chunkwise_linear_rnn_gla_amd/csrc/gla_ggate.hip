@@ -34,6 +34,7 @@
 // (k_gg_gate_tot / k_gg_gate_fin).
 #include "gla_common.h"
 #include "gla_internal.h"
+#include "gla_pblock.h"  // xcd_logical
 
 namespace gla {
 
@@ -190,16 +191,22 @@ template <int MT> struct GgFrag<float, MT> {
 };
 
 template <int MT>
-__device__ inline void load_qk(GgFrag<bf16, MT>& f, const bf16* qf, const bf16* kf, int l) {
+__device__ inline void load_q(GgFrag<bf16, MT>& f, const bf16* qf, int l) {
 #pragma unroll
   for (int p = 0; p < MT / 2; ++p) f.q[p] = *reinterpret_cast<const bf16x8*>(qf + ((p * 64 + l) << 3));
+}
+template <int MT>
+__device__ inline void load_q(GgFrag<float, MT>& f, const float* qf, int l) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m) f.q[m] = *reinterpret_cast<const f4*>(qf + ((m * 64 + l) << 2));
+}
+template <int MT>
+__device__ inline void load_k(GgFrag<bf16, MT>& f, const bf16* kf, int l) {
 #pragma unroll
   for (int m = 0; m < MT; ++m) f.k[m] = *reinterpret_cast<const bf16x4*>(kf + ((m * 64 + l) << 2));
 }
 template <int MT>
-__device__ inline void load_qk(GgFrag<float, MT>& f, const float* qf, const float* kf, int l) {
-#pragma unroll
-  for (int m = 0; m < MT; ++m) f.q[m] = *reinterpret_cast<const f4*>(qf + ((m * 64 + l) << 2));
+__device__ inline void load_k(GgFrag<float, MT>& f, const float* kf, int l) {
 #pragma unroll
   for (int m = 0; m < MT; ++m) f.k[m] = *reinterpret_cast<const f4*>(kf + ((m * 64 + l) << 2));
 }
@@ -266,7 +273,65 @@ __device__ inline void update(floatx4 (&S)[MT], const GgFrag<float, MT>& f, cons
     for (int s = 0; s < 4; ++s) S[m] = mfma4(f.k[m][s], vt[s], S[m]);
 }
 
-// grid (dv / 16, BH), one wave.  Lane (j, g) = (l % 16, l / 16) owns state
+// Everything one lane reads for one chunk; the recurrence loads chunk n + 1
+// into a second set while it computes chunk n.  From 128 state rows on the
+// second set would not fit in registers: with 128 rows of bf16 operands only
+// the operands needed first (Q~, P, v, log beta) are loaded ahead, and K~ and
+// e^{a}, needed last, at the start of their own chunk; past that nothing is
+// loaded ahead (values parked in accumulator registers would cost a wait on
+// every load in flight), and each chunk's loads are issued together.
+template <typename T, int MT> struct GgIn {
+  GgFrag<T, MT> f;
+  f4 p, pd;     // P below the diagonal (A fragment), P[4g + e][4g + e]
+  f4 ga[MT];    // e^{a} at the lane's state rows
+  float v[4], lb[4];
+};
+
+// 2: all of chunk n + 1 loaded ahead; 1: the early operands; 0: nothing
+template <typename T, int MT> constexpr int gg_ahead() {
+  return MT <= 4 ? 2 : (MT == 8 && sizeof(T) == 2 ? 1 : 0);
+}
+
+template <typename T, int MT>
+__device__ inline void gg_load_late(GgIn<T, MT>& in, const uint8_t* __restrict__ rec,
+                                    size_t rec_bytes, int bh, int n, int NC, int l, int g) {
+  constexpr int DKP = MT * 16;
+  const T* kf = reinterpret_cast<const T*>(rec + ((size_t)bh * NC + n) * rec_bytes) + kGC * DKP;
+  const float* pf = reinterpret_cast<const float*>(kf + kGC * DKP);
+  load_k(in.f, kf, l);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) in.ga[m] = *reinterpret_cast<const f4*>(pf + kPfFloats + 16 * m + 4 * g);
+}
+
+template <typename T, int MT>
+__device__ inline void gg_load(GgIn<T, MT>& in, const uint8_t* __restrict__ rec, size_t rec_bytes,
+                               const T* __restrict__ vb, const float* __restrict__ lbb, int bh,
+                               int n, int NC, int L, int dv, int rev, int l, int g) {
+  constexpr int DKP = MT * 16;
+  const uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
+  const T* qf = reinterpret_cast<const T*>(r);
+  const float* pf = reinterpret_cast<const float*>(qf + 2 * kGC * DKP);
+  load_q(in.f, qf, l);
+  in.p = *reinterpret_cast<const f4*>(pf + 4 * l);
+  in.pd = *reinterpret_cast<const f4*>(pf + 256 + 4 * g);
+  if constexpr (gg_ahead<T, MT>() == 2) gg_load_late(in, rec, rec_bytes, bh, n, NC, l, g);
+  // unconditional loads (a clamped row, then a select): a load under a branch
+  // would make the compiler wait for every load in flight, the next chunk's too
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int u = n * kGC + 4 * g + e;
+    const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
+    const float x = to_f32(vb[(size_t)(dr > 0 ? dr : 0) * dv]);
+    const float y = lbb[(size_t)(gr > 0 ? gr : 0) * dv];
+    in.v[e] = dr >= 0 ? x : 0.f;
+    in.lb[e] = gr >= 0 ? y : 0.f;
+  }
+}
+
+// grid (dv / 16 * BH), one wave per workgroup; the dv / 16 column tiles of a
+// (batch, head), which read the same chunk records, take consecutive logical
+// ids placed on one XCD so that its L2 serves their repeated reads.  Lane
+// (j, g) = (l % 16, l / 16) owns state
 // column j of the tile and, in every 16 x 16 accumulator tile, rows 4 g + e.
 // init: [BH][dk][dv] ([BH][dv][dk] when init_t), or null for zeros.  o (if
 // not null) receives the output, ooff (if not null) the output without the
@@ -282,7 +347,8 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
     const float* __restrict__ fin_lb, int L, int dk, int dv, int NC, int rev) {
   constexpr int DKP = MT * 16;
   const int l = threadIdx.x, j = l & 15, g = l >> 4;
-  const int jc = blockIdx.x * 16 + j, bh = blockIdx.y;
+  const int nt = dv / 16, lid = xcd_logical(blockIdx.x, gridDim.x);
+  const int bh = lid / nt, jc = (lid - bh * nt) * 16 + j;
   floatx4 S[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m)
@@ -297,23 +363,23 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
   const T* vb = v + (size_t)bh * L * dv + jc;
   const float* lbb = lb + (size_t)bh * L * dv + jc;
 
+  constexpr int AHEAD = gg_ahead<T, MT>();
+  GgIn<T, MT> cur, nxt;
+  if constexpr (AHEAD > 0) gg_load(cur, rec, rec_bytes, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
   for (int n = 0; n < NC; ++n) {
-    const uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
-    const T* qf = reinterpret_cast<const T*>(r);
-    const T* kf = qf + kGC * DKP;
-    const float* pf = reinterpret_cast<const float*>(kf + kGC * DKP);
-    const float* ga = pf + kPfFloats;
-    GgFrag<T, MT> f;
-    load_qk(f, qf, kf, l);
-    const f4 p = *reinterpret_cast<const f4*>(pf + 4 * l);
-    const f4 pd = *reinterpret_cast<const f4*>(pf + 256 + 4 * g);  // P[4g + e][4g + e]
+    if constexpr (AHEAD == 0) gg_load(cur, rec, rec_bytes, vb, lbb, bh, n, NC, L, dv, rev, l, g);
+    if constexpr (AHEAD < 2) gg_load_late(cur, rec, rec_bytes, bh, n, NC, l, g);
+    if constexpr (AHEAD > 0)
+      if (n + 1 < NC) gg_load(nxt, rec, rec_bytes, vb, lbb, bh, n + 1, NC, L, dv, rev, l, g);
+    const GgFrag<T, MT>& f = cur.f;
+    const f4 p = cur.p, pd = cur.pd;
+    const float* pf = reinterpret_cast<const float*>(
+        rec + ((size_t)bh * NC + n) * rec_bytes + (size_t)32 * DKP * sizeof(T));
     float vv[4], c[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int u = n * kGC + 4 * g + e;
-      const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
-      vv[e] = dr >= 0 ? to_f32(vb[(size_t)dr * dv]) : 0.f;
-      c[e] = gr >= 0 ? lbb[(size_t)gr * dv] : 0.f;
+      vv[e] = cur.v[e];
+      c[e] = cur.lb[e];
     }
     // chunk-local inclusive cumsum of log beta down the 16 rows of column j,
     // as hi (c) + lo (cl) pairs: within the lane's 4 rows, then the totals of
@@ -387,12 +453,12 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
     // decay and update
     const float gb = gexp<T>(bt);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const f4 gm = *reinterpret_cast<const f4*>(ga + 16 * m + 4 * g);
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][e] *= gm[e] * gb;
-    }
+      for (int e = 0; e < 4; ++e) S[m][e] *= cur.ga[m][e] * gb;
     update(S, f, vt);
+    if constexpr (AHEAD > 0)
+      if (n + 1 < NC) cur = nxt;
   }
   if (fin) {
     const float gb = fin_lb ? gexp<T>(fin_lb[(size_t)bh * L * dv + jc]) : 1.f;
@@ -557,7 +623,7 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int BH, int L
       hipLaunchKernelGGL((k_gg_prep<float>), pg, dim3(kThreads), lds, s, (const float*)ps.q,
                          (const float*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
   } else {
-    const dim3 rg(ps.dv / 16, BH);
+    const dim3 rg((ps.dv / 16) * BH);
     if (!is_bf16) launch_gg_recur<float, float>(ps, dkp, rg, r, rb, L, NC, s);
     else if (ps.o_f32) launch_gg_recur<bf16, float>(ps, dkp, rg, r, rb, L, NC, s);
     else launch_gg_recur<bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
