@@ -44,6 +44,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f4;
 
 constexpr int kGC = 16;            // tokens per chunk
 constexpr float kSafeDecay = 60.f;  // product form while -b <= this
+constexpr float kSafeP = 8.f;       // P on MFMA for channels decaying less than this
 
 __device__ inline floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -127,7 +128,10 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const T* __restrict__ q,
   float* ks = qs + kGC * ld;
   float* cs = ks + kGC * ld;  // cumsum, hi part
   float* cl = cs + kGC * ld;  // lo part
+  float* part = cl + kGC * ld;  // the four waves' partial P tiles
+  uint32_t* umask = reinterpret_cast<uint32_t*>(part + 1024);  // channels left to the log-space sum
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  if (tid < 8) umask[tid] = 0u;
   for (int x = tid; x < kGC * dkp; x += kThreads) {
     const int t = x / dkp, i = x - t * dkp, u = n * kGC + t;
     const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
@@ -153,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const T* __restrict__ q,
       cl[t * ld + i] = e;
     }
     ga[i] = gexp<T>(c + e);
+    if (cs[i] - c > kSafeP) atomicOr(&umask[i >> 5], 1u << (i & 31));
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
       const float at = cs[t * ld + i], al = cl[t * ld + i];
@@ -161,19 +166,47 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const T* __restrict__ q,
     }
   }
   __syncthreads();
-  // P, one (t, s) pair per thread; the diagonal goes to its own slots, and
-  // the fragment holds zero on and above it
+  // P[t][s] = sum_i q_t[i] k_s[i] e^{A_t[i] - A_s[i]}.  Channels whose decay
+  // over the chunk stays under e^{kSafeP} take one fp32 MFMA tile with the
+  // chunk's first row as reference, (q_t e^{A_t - A_0}) (k_s e^{A_0 - A_s}),
+  // both exponents under kSafeP so that the product keeps fp32 accuracy;
+  // each wave covers a quarter of the channels.  Faster-decaying channels
+  // (sharp gates) take the per-pair log-space sum.
+  {
+    const int w = tid >> 6, l = tid & 63, r16 = l & 15, kk = l >> 4;
+    const int span = dkp >> 2;
+    floatx4 acc = zero4();
+    for (int i0 = w * span; i0 < (w + 1) * span; i0 += 4) {
+      const int i = i0 + kk;
+      const bool sf = !((umask[i >> 5] >> (i & 31)) & 1u);
+      const float c0 = cs[i], l0 = cl[i];
+      const float a = sf ? qs[r16 * ld + i] *
+                               gexp<T>((cs[r16 * ld + i] - c0) + (cl[r16 * ld + i] - l0))
+                         : 0.f;
+      const float b = sf ? ks[r16 * ld + i] *
+                               gexp<T>((c0 - cs[r16 * ld + i]) + (l0 - cl[r16 * ld + i]))
+                         : 0.f;
+      acc = mfma4(a, b, acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[w * 256 + (4 * kk + e) * 16 + r16] = acc[e];
+  }
+  __syncthreads();
   const int t = tid >> 4, s = tid & 15;
   float acc = 0.f;
   if (s <= t) {
+    acc = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
     const float* qt = qs + t * ld;
     const float* ksr = ks + s * ld;
     const float* ct = cs + t * ld;
     const float* csr = cs + s * ld;
     const float* lt = cl + t * ld;
     const float* lsr = cl + s * ld;
-    for (int i = 0; i < dk; ++i)
-      acc += qt[i] * ksr[i] * gexp<T>((ct[i] - csr[i]) + (lt[i] - lsr[i]));
+    for (int wd = 0; wd < ((dkp + 31) >> 5); ++wd)
+      for (uint32_t m = umask[wd]; m; m &= m - 1) {
+        const int i = wd * 32 + __builtin_ctz(m);
+        acc += qt[i] * ksr[i] * gexp<T>((ct[i] - csr[i]) + (lt[i] - lsr[i]));
+      }
   }
   pf[pf_index(t, s)] = s < t ? acc : 0.f;
   if (s == t) pf[256 + t] = acc;
@@ -606,7 +639,8 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int BH, int L
   const size_t rb = gg_rec_bytes(is_bf16, dkp);
   uint8_t* r = static_cast<uint8_t*>(rec);
   if (part == 0) {
-    const size_t lds = sizeof(float) * 4 * kGC * (dkp + 1);  // 65.8 KB at 256 channels
+    // 4 arrays of 16 padded rows, 4 partial P tiles, 8 mask words: 69.9 KB at 256 channels
+    const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + 8);
     const dim3 pg(NC, BH);
     if (lds > 65536) {
       const hipError_t e =
