@@ -36,6 +36,9 @@ EXTRA_FLAGS = {
     # the ILP-oriented scheduler interleaves them far better than the default
     # occupancy-oriented one (one wave per SIMD runs there anyway)
     "gla_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    # the general gate's recurrence rescales and converts its state every
+    # chunk: in accumulator registers each such access costs a move
+    "gla_ggate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
