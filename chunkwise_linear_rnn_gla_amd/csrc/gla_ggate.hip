@@ -95,6 +95,14 @@ __device__ inline float two_sum(float a, float b, float& err) {
   err = (a - (s - bp)) + (b - bp);
   return s;
 }
+// The compensation serves fp32 operands (the backward's passes, whose gate
+// gradients cancel); with bf16 operands it is below their rounding, and the
+// lo parts fold away as zeros.
+template <typename T> __device__ inline float csum(float a, float b, float& err) {
+  if constexpr (sizeof(T) == 4) return two_sum(a, b, err);
+  err = 0.f;
+  return a + b;
+}
 
 // P[t][s] for s < t (zero on and above the diagonal): [64][4] fp32, lane
 // t + 16 (s / 4), slot s % 4; then P[t][t], 16 fp32; then e^{a}, DKP fp32.
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const T* __restrict__ q,
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
       float err;
-      c = two_sum(c, cs[t * ld + i], err);
+      c = csum<T>(c, cs[t * ld + i], err);
       e += err;
       cs[t * ld + i] = c;
       cl[t * ld + i] = e;
@@ -421,29 +429,29 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
     cl[0] = 0.f;
 #pragma unroll
     for (int e = 1; e < 4; ++e) {
-      c[e] = two_sum(c[e - 1], c[e], err);
+      c[e] = csum<T>(c[e - 1], c[e], err);
       cl[e] = cl[e - 1] + err;
     }
     float th[4], tl[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       th[r] = __shfl(c[3], j + 16 * r);
-      tl[r] = __shfl(cl[3], j + 16 * r);
+      tl[r] = sizeof(T) == 4 ? __shfl(cl[3], j + 16 * r) : 0.f;
     }
     float eh = 0.f, el = 0.f;  // sum of the totals of row groups before g
     float bh_ = 0.f, bl_ = 0.f;  // chunk total
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r < g) {
-        eh = two_sum(eh, th[r], err);
+        eh = csum<T>(eh, th[r], err);
         el += tl[r] + err;
       }
-      bh_ = two_sum(bh_, th[r], err);
+      bh_ = csum<T>(bh_, th[r], err);
       bl_ += tl[r] + err;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      c[e] = two_sum(eh, c[e], err);
+      c[e] = csum<T>(eh, c[e], err);
       cl[e] += el + err;
     }
     const float bt = bh_ + bl_;  // chunk total (rounded)
@@ -463,7 +471,8 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
 #pragma unroll
       for (int s = 0; s < kGC; ++s) {
         const int src = j + 16 * (s >> 2);
-        const float cs = __shfl(c[s & 3], src), ls = __shfl(cl[s & 3], src);
+        const float cs = __shfl(c[s & 3], src);
+        const float ls = sizeof(T) == 4 ? __shfl(cl[s & 3], src) : 0.f;
         const float vs = __shfl(vv[s & 3], src);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
