@@ -134,6 +134,22 @@ def test_general_bench_shape_forward_and_backward():
         assert e <= TOL["bf16"], name
 
 
+def test_general_long_sequence():
+    # 1,024 chunks in sequence with an initial state: no drift over a long run
+    x, lb = _inputs("bf16", 1, 4, 16384, 128, 256, "sigmoid16", "sigmoid16", 0.1, seed=1004)
+    say("[ggla] long sequence B1 H4 L16384 dk128 dv256 bf16, h0 std 0.1")
+    d, lbd = _dev(x, lb)
+    o, hT = fwd_general(d.q, d.k, d.v, d.log_alpha, lbd, d.h0)
+    torch.cuda.synchronize()
+    ro, rhT = oracle.ggla_fwd(as_f64(x.q), as_f64(x.k), as_f64(x.v), as_f64(x.log_alpha),
+                              as_f64(lb), as_f64(x.h0))
+    eo, eh = rel_l2(as_f64(o), ro), rel_l2(as_f64(hT), rhT)
+    # the last 512 tokens on their own as well: a late drift would show there
+    el = rel_l2(as_f64(o)[:, :, -512:], ro[:, :, -512:])
+    say(f"      rel_l2 o={eo:.3e} (last 512: {el:.3e}) hT={eh:.3e}")
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 def test_general_empty_sequence_and_batch():
     q = torch.empty(1, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
     v = torch.empty(1, 2, 0, 96, device="cuda", dtype=torch.bfloat16)
