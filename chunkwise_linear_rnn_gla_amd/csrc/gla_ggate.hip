@@ -333,29 +333,31 @@ template <typename T, int MT> constexpr int gg_ahead() {
   return MT <= 4 ? 2 : (MT == 8 && sizeof(T) == 2 ? 1 : 0);
 }
 
+// MT: the wave's tiles; DKP: the record's channels; m0: the wave's first tile
 template <typename T, int MT>
 __device__ inline void gg_load_late(GgIn<T, MT>& in, const uint8_t* __restrict__ rec,
-                                    size_t rec_bytes, int bh, int n, int NC, int l, int g) {
-  constexpr int DKP = MT * 16;
+                                    size_t rec_bytes, int DKP, int m0, int bh, int n, int NC,
+                                    int l, int g) {
   const T* kf = reinterpret_cast<const T*>(rec + ((size_t)bh * NC + n) * rec_bytes) + kGC * DKP;
   const float* pf = reinterpret_cast<const float*>(kf + kGC * DKP);
-  load_k(in.f, kf, l);
+  load_k(in.f, kf + 256 * m0, l);
 #pragma unroll
-  for (int m = 0; m < MT; ++m) in.ga[m] = *reinterpret_cast<const f4*>(pf + kPfFloats + 16 * m + 4 * g);
+  for (int m = 0; m < MT; ++m)
+    in.ga[m] = *reinterpret_cast<const f4*>(pf + kPfFloats + 16 * (m0 + m) + 4 * g);
 }
 
 template <typename T, int MT>
 __device__ inline void gg_load(GgIn<T, MT>& in, const uint8_t* __restrict__ rec, size_t rec_bytes,
-                               const T* __restrict__ vb, const float* __restrict__ lbb, int bh,
-                               int n, int NC, int L, int dv, int rev, int l, int g) {
-  constexpr int DKP = MT * 16;
+                               int DKP, int m0, const T* __restrict__ vb,
+                               const float* __restrict__ lbb, int bh, int n, int NC, int L,
+                               int dv, int rev, int l, int g) {
   const uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
   const T* qf = reinterpret_cast<const T*>(r);
   const float* pf = reinterpret_cast<const float*>(qf + 2 * kGC * DKP);
-  load_q(in.f, qf, l);
+  load_q(in.f, qf + 256 * m0, l);  // 256 elements per 16-channel tile in both layouts
   in.p = *reinterpret_cast<const f4*>(pf + 4 * l);
   in.pd = *reinterpret_cast<const f4*>(pf + 256 + 4 * g);
-  if constexpr (gg_ahead<T, MT>() == 2) gg_load_late(in, rec, rec_bytes, bh, n, NC, l, g);
+  if constexpr (gg_ahead<T, MT>() == 2) gg_load_late(in, rec, rec_bytes, DKP, m0, bh, n, NC, l, g);
   // unconditional loads (a clamped row, then a select): a load under a branch
   // would make the compiler wait for every load in flight, the next chunk's too
 #pragma unroll
@@ -369,33 +371,40 @@ __device__ inline void gg_load(GgIn<T, MT>& in, const uint8_t* __restrict__ rec,
   }
 }
 
-// grid (dv / 16 * BH), one wave per workgroup; the dv / 16 column tiles of a
+// grid (dv / 16 * BH), NWR waves per workgroup; the dv / 16 column tiles of a
 // (batch, head), which read the same chunk records, take consecutive logical
-// ids placed on one XCD so that its L2 serves their repeated reads.  Lane
-// (j, g) = (l % 16, l / 16) owns state
-// column j of the tile and, in every 16 x 16 accumulator tile, rows 4 g + e.
+// ids placed on one XCD so that its L2 serves their repeated reads.  The NWR
+// waves split the state tile's MT 16-row blocks between them (twice the waves
+// of one per tile, half the per-chunk work each): each forms its share of the
+// inter term Q~ S, the others hand theirs to wave 0 through LDS, and wave 0
+// adds the intra term and writes the output; each wave decays and updates its
+// own rows.  Lane (j, g) = (l % 16, l / 16) owns state column j of the tile
+// and, in every 16 x 16 accumulator tile, rows 4 g + e.
 // init: [BH][dk][dv] ([BH][dv][dk] when init_t), or null for zeros.  o (if
 // not null) receives the output, ooff (if not null) the output without the
 // same-token term, in fp32.  fin (if not null) receives the final state
 // [BH][dk][dv], first multiplied by the gate of sequence token 0 when
 // fin_la / fin_lb are given.
-template <typename T, typename TO, int MT>
-__global__ __launch_bounds__(kWave) void k_gg_recur(
+template <typename T, typename TO, int MT, int NWR>
+__global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
     const uint8_t* __restrict__ rec, size_t rec_bytes, const T* __restrict__ v,
     const float* __restrict__ lb, const float* __restrict__ init, int init_t,
     TO* __restrict__ o, float* __restrict__ ooff, float* __restrict__ fin,
     const float* __restrict__ fin_la,
     const float* __restrict__ fin_lb, int L, int dk, int dv, int NC, int rev) {
-  constexpr int DKP = MT * 16;
-  const int l = threadIdx.x, j = l & 15, g = l >> 4;
+  constexpr int DKP = MT * 16, MTW = MT / NWR;
+  static_assert(MT % NWR == 0 && (sizeof(T) == 4 || MTW % 2 == 0), "row split");
+  __shared__ f4 red[2][NWR > 1 ? NWR - 1 : 1][kWave];  // partial inter terms
+  const int w = threadIdx.x / kWave, l = threadIdx.x & (kWave - 1), j = l & 15, g = l >> 4;
+  const int m0 = w * MTW;
   const int nt = dv / 16, lid = xcd_logical(blockIdx.x, gridDim.x);
   const int bh = lid / nt, jc = (lid - bh * nt) * 16 + j;
-  floatx4 S[MT];
+  floatx4 S[MTW];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MTW; ++m)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int row = 16 * m + 4 * g + e;
+      const int row = 16 * (m0 + m) + 4 * g + e;
       float x = 0.f;
       if (init && row < dk)
         x = init_t ? init[((size_t)bh * dv + jc) * dk + row] : init[((size_t)bh * dk + row) * dv + jc];
@@ -404,15 +413,18 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
   const T* vb = v + (size_t)bh * L * dv + jc;
   const float* lbb = lb + (size_t)bh * L * dv + jc;
 
-  constexpr int AHEAD = gg_ahead<T, MT>();
-  GgIn<T, MT> cur, nxt;
-  if constexpr (AHEAD > 0) gg_load(cur, rec, rec_bytes, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
+  constexpr int AHEAD = gg_ahead<T, MTW>();
+  GgIn<T, MTW> cur, nxt;
+  if constexpr (AHEAD > 0)
+    gg_load(cur, rec, rec_bytes, DKP, m0, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
   for (int n = 0; n < NC; ++n) {
-    if constexpr (AHEAD == 0) gg_load(cur, rec, rec_bytes, vb, lbb, bh, n, NC, L, dv, rev, l, g);
-    if constexpr (AHEAD < 2) gg_load_late(cur, rec, rec_bytes, bh, n, NC, l, g);
+    if constexpr (AHEAD == 0)
+      gg_load(cur, rec, rec_bytes, DKP, m0, vb, lbb, bh, n, NC, L, dv, rev, l, g);
+    if constexpr (AHEAD < 2) gg_load_late(cur, rec, rec_bytes, DKP, m0, bh, n, NC, l, g);
     if constexpr (AHEAD > 0)
-      if (n + 1 < NC) gg_load(nxt, rec, rec_bytes, vb, lbb, bh, n + 1, NC, L, dv, rev, l, g);
-    const GgFrag<T, MT>& f = cur.f;
+      if (n + 1 < NC)
+        gg_load(nxt, rec, rec_bytes, DKP, m0, vb, lbb, bh, n + 1, NC, L, dv, rev, l, g);
+    const GgFrag<T, MTW>& f = cur.f;
     const f4 p = cur.p, pd = cur.pd;
     const float* pf = reinterpret_cast<const float*>(
         rec + ((size_t)bh * NC + n) * rec_bytes + (size_t)32 * DKP * sizeof(T));
@@ -458,44 +470,58 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
     floatx4 vt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vt[e] = vv[e] * gexp<T>((bh_ - c[e]) + (bl_ - cl[e]));
-    const floatx4 a1 = inter(f, S);
-    const floatx4 a2 = intra(p, vt, T());
-    float res[4];
-    const bool safe = bt >= -kSafeDecay;
+    floatx4 a1 = inter(f, S);
+    if constexpr (NWR > 1) {
+      if (w > 0) red[n & 1][w - 1][l] = a1;
+      __syncthreads();  // one per chunk: the buffers alternate, and the next
+                        // write to this one comes after the next barrier
+      if (w == 0)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      res[e] = gexp<T>(c[e] + cl[e]) * a1[e] + gexp<T>((c[e] - bh_) + (cl[e] - bl_)) * a2[e];
-    if (__any(!safe)) {
-      // log-space intra term: sum_{s < t} P[t][s] v_s e^{Bt_t - Bt_s}
-      float sl[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < NWR - 1; ++r) {
+          const f4 x = red[n & 1][r][l];
 #pragma unroll
-      for (int s = 0; s < kGC; ++s) {
-        const int src = j + 16 * (s >> 2);
-        const float cs = __shfl(c[s & 3], src);
-        const float ls = sizeof(T) == 4 ? __shfl(cl[s & 3], src) : 0.f;
-        const float vs = __shfl(vv[s & 3], src);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 4 * g + e;
-          if (s < t) sl[e] += pf[pf_index(t, s)] * vs * gexp<T>((c[e] - cs) + (cl[e] - ls));
+          for (int e = 0; e < 4; ++e) a1[e] += x[e];
         }
-      }
-      if (!safe)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) res[e] = gexp<T>(c[e] + cl[e]) * a1[e] + sl[e];
     }
+    if (w == 0) {  // wave 0: intra term and output
+      const floatx4 a2 = intra(p, vt, T());
+      float res[4];
+      const bool safe = bt >= -kSafeDecay;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int dr = data_row(n * kGC + 4 * g + e, L, rev);
-      if (dr < 0) continue;
-      const size_t x = ((size_t)bh * L + dr) * dv + jc;
-      if (ooff) ooff[x] = res[e];
-      if (o) o[x] = from_f32<TO>(res[e] + pd[e] * vv[e]);
+      for (int e = 0; e < 4; ++e)
+        res[e] = gexp<T>(c[e] + cl[e]) * a1[e] + gexp<T>((c[e] - bh_) + (cl[e] - bl_)) * a2[e];
+      if (__any(!safe)) {
+        // log-space intra term: sum_{s < t} P[t][s] v_s e^{Bt_t - Bt_s}
+        float sl[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kGC; ++s) {
+          const int src = j + 16 * (s >> 2);
+          const float cs = __shfl(c[s & 3], src);
+          const float ls = sizeof(T) == 4 ? __shfl(cl[s & 3], src) : 0.f;
+          const float vs = __shfl(vv[s & 3], src);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 4 * g + e;
+            if (s < t) sl[e] += pf[pf_index(t, s)] * vs * gexp<T>((c[e] - cs) + (cl[e] - ls));
+          }
+        }
+        if (!safe)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) res[e] = gexp<T>(c[e] + cl[e]) * a1[e] + sl[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int dr = data_row(n * kGC + 4 * g + e, L, rev);
+        if (dr < 0) continue;
+        const size_t x = ((size_t)bh * L + dr) * dv + jc;
+        if (ooff) ooff[x] = res[e];
+        if (o) o[x] = from_f32<TO>(res[e] + pd[e] * vv[e]);
+      }
     }
     // decay and update
     const float gb = gexp<T>(bt);
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTW; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[m][e] *= cur.ga[m][e] * gb;
     update(S, f, vt);
@@ -505,10 +531,10 @@ __global__ __launch_bounds__(kWave) void k_gg_recur(
   if (fin) {
     const float gb = fin_lb ? gexp<T>(fin_lb[(size_t)bh * L * dv + jc]) : 1.f;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTW; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = 16 * m + 4 * g + e;
+        const int row = 16 * (m0 + m) + 4 * g + e;
         if (row < dk) {
           const float gr = fin_la ? gexp<T>(fin_la[(size_t)bh * L * dk + row]) * gb : 1.f;
           fin[((size_t)bh * dk + row) * dv + jc] = S[m][e] * gr;
@@ -620,11 +646,15 @@ hipError_t launch_gg_widen(const void* x, float* y, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Waves per state tile: two from 64 state rows on (32 for fp32), one below.
+template <typename T> constexpr int gg_row_split(int MT) { return MT >= (sizeof(T) == 2 ? 4 : 2) ? 2 : 1; }
+
 template <typename T, typename TO>
 static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t* r, size_t rb,
                             int L, int NC, hipStream_t s) {
 #define GG_RECUR(MT)                                                                          \
-  hipLaunchKernelGGL((k_gg_recur<T, TO, MT>), grid, dim3(kWave), 0, s, r, rb, (const T*)ps.v, \
+  hipLaunchKernelGGL((k_gg_recur<T, TO, MT, gg_row_split<T>(MT)>), grid,                        \
+                     dim3(kWave * gg_row_split<T>(MT)), 0, s, r, rb, (const T*)ps.v,           \
                      ps.lb, ps.init, ps.init_t, (TO*)ps.o, ps.o_off, ps.fin, ps.fin_la,       \
                      ps.fin_lb, L,                                                            \
                      ps.dk, ps.dv, NC, ps.rev)
