@@ -332,6 +332,12 @@ template <typename T, int MT> struct GgIn {
 template <typename T, int MT> constexpr int gg_ahead() {
   return MT <= 4 ? 2 : (MT == 8 && sizeof(T) == 2 ? 1 : 0);
 }
+// Chunks loaded ahead when everything is (gg_ahead == 2): two for bf16 state
+// slices of up to 64 rows (a chunk step is shorter than the memory latency),
+// else one.
+template <typename T, int MT> constexpr int gg_depth() {
+  return (sizeof(T) == 2 && MT <= 4) ? 2 : 1;
+}
 
 // MT: the wave's tiles; DKP: the record's channels; m0: the wave's first tile
 template <typename T, int MT>
@@ -358,16 +364,29 @@ __device__ inline void gg_load(GgIn<T, MT>& in, const uint8_t* __restrict__ rec,
   in.p = *reinterpret_cast<const f4*>(pf + 4 * l);
   in.pd = *reinterpret_cast<const f4*>(pf + 256 + 4 * g);
   if constexpr (gg_ahead<T, MT>() == 2) gg_load_late(in, rec, rec_bytes, DKP, m0, bh, n, NC, l, g);
-  // unconditional loads (a clamped row, then a select): a load under a branch
-  // would make the compiler wait for every load in flight, the next chunk's too
+  // unconditional loads of a clamped row, kept raw: a load under a branch, or
+  // a select on its value here, would wait for it at once; the rows past the
+  // sequence are zeroed where the values are used (gg_valid)
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int u = n * kGC + 4 * g + e;
     const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
-    const float x = to_f32(vb[(size_t)(dr > 0 ? dr : 0) * dv]);
-    const float y = lbb[(size_t)(gr > 0 ? gr : 0) * dv];
-    in.v[e] = dr >= 0 ? x : 0.f;
-    in.lb[e] = gr >= 0 ? y : 0.f;
+    in.v[e] = to_f32(vb[(size_t)(dr > 0 ? dr : 0) * dv]);
+    in.lb[e] = lbb[(size_t)(gr > 0 ? gr : 0) * dv];
+  }
+}
+
+// v and log beta of chunk n as loaded by gg_load, with the rows that have no
+// value (past the sequence) or no gate (the first row of a reversed pass)
+// set to zero.
+template <typename T, int MT>
+__device__ inline void gg_valid(const GgIn<T, MT>& in, int n, int L, int rev, int g, float* v,
+                                float* lb) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int u = n * kGC + 4 * g + e;
+    v[e] = data_row(u, L, rev) >= 0 ? in.v[e] : 0.f;
+    lb[e] = gate_row(u, L, rev) >= 0 ? in.lb[e] : 0.f;
   }
 }
 
@@ -413,27 +432,23 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   const T* vb = v + (size_t)bh * L * dv + jc;
   const float* lbb = lb + (size_t)bh * L * dv + jc;
 
-  constexpr int AHEAD = gg_ahead<T, MTW>();
-  GgIn<T, MTW> cur, nxt;
-  if constexpr (AHEAD > 0)
-    gg_load(cur, rec, rec_bytes, DKP, m0, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
-  for (int n = 0; n < NC; ++n) {
+  constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW>() : 1;
+  // One chunk step: chunk n from `cur`; first the loads of chunk `nl` (if in
+  // range) go into `ld`.  The loop below is unrolled by the number of register
+  // sets so that the sets change roles without copies: a copy of a register
+  // whose load is in flight would wait for that load.
+  auto step = [&](int n, GgIn<T, MTW>& cur, GgIn<T, MTW>& ld, int nl) {
     if constexpr (AHEAD == 0)
       gg_load(cur, rec, rec_bytes, DKP, m0, vb, lbb, bh, n, NC, L, dv, rev, l, g);
     if constexpr (AHEAD < 2) gg_load_late(cur, rec, rec_bytes, DKP, m0, bh, n, NC, l, g);
     if constexpr (AHEAD > 0)
-      if (n + 1 < NC)
-        gg_load(nxt, rec, rec_bytes, DKP, m0, vb, lbb, bh, n + 1, NC, L, dv, rev, l, g);
+      if (nl < NC) gg_load(ld, rec, rec_bytes, DKP, m0, vb, lbb, bh, nl, NC, L, dv, rev, l, g);
     const GgFrag<T, MTW>& f = cur.f;
     const f4 p = cur.p, pd = cur.pd;
     const float* pf = reinterpret_cast<const float*>(
         rec + ((size_t)bh * NC + n) * rec_bytes + (size_t)32 * DKP * sizeof(T));
     float vv[4], c[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vv[e] = cur.v[e];
-      c[e] = cur.lb[e];
-    }
+    gg_valid(cur, n, L, rev, g, vv, c);
     // chunk-local inclusive cumsum of log beta down the 16 rows of column j,
     // as hi (c) + lo (cl) pairs: within the lane's 4 rows, then the totals of
     // the lanes above it (row groups g' < g) added in front
@@ -525,8 +540,24 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[m][e] *= cur.ga[m][e] * gb;
     update(S, f, vt);
-    if constexpr (AHEAD > 0)
-      if (n + 1 < NC) cur = nxt;
+  };
+  GgIn<T, MTW> ra, rb, rc;
+  if constexpr (AHEAD == 0) {
+    for (int n = 0; n < NC; ++n) step(n, ra, ra, NC);
+  } else if constexpr (DEPTH == 1) {
+    gg_load(ra, rec, rec_bytes, DKP, m0, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
+    for (int n = 0; n < NC; n += 2) {
+      step(n, ra, rb, n + 1);
+      if (n + 1 < NC) step(n + 1, rb, ra, n + 2);
+    }
+  } else {
+    gg_load(ra, rec, rec_bytes, DKP, m0, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
+    if (NC > 1) gg_load(rb, rec, rec_bytes, DKP, m0, vb, lbb, bh, 1, NC, L, dv, rev, l, g);
+    for (int n = 0; n < NC; n += 3) {
+      step(n, ra, rc, n + 2);
+      if (n + 1 < NC) step(n + 1, rb, ra, n + 3);
+      if (n + 2 < NC) step(n + 2, rc, rb, n + 4);
+    }
   }
   if (fin) {
     const float gb = fin_lb ? gexp<T>(fin_lb[(size_t)bh * L * dv + jc]) : 1.f;
