@@ -441,8 +441,11 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
     if constexpr (AHEAD == 0)
       gg_load(cur, rec, rec_bytes, DKP, m0, vb, lbb, bh, n, NC, L, dv, rev, l, g);
     if constexpr (AHEAD < 2) gg_load_late(cur, rec, rec_bytes, DKP, m0, bh, n, NC, l, g);
+    // the prefetch is unconditional (past the end it reloads the last chunk,
+    // unused): under a branch, the wait counts at its join would force waits
+    // on the current set's loads as well
     if constexpr (AHEAD > 0)
-      if (nl < NC) gg_load(ld, rec, rec_bytes, DKP, m0, vb, lbb, bh, nl, NC, L, dv, rev, l, g);
+      gg_load(ld, rec, rec_bytes, DKP, m0, vb, lbb, bh, nl < NC ? nl : NC - 1, NC, L, dv, rev, l, g);
     const GgFrag<T, MTW>& f = cur.f;
     const f4 p = cur.p, pd = cur.pd;
     const float* pf = reinterpret_cast<const float*>(
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
     }
   } else {
     gg_load(ra, rec, rec_bytes, DKP, m0, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
-    if (NC > 1) gg_load(rb, rec, rec_bytes, DKP, m0, vb, lbb, bh, 1, NC, L, dv, rev, l, g);
+    gg_load(rb, rec, rec_bytes, DKP, m0, vb, lbb, bh, NC > 1 ? 1 : 0, NC, L, dv, rev, l, g);
     for (int n = 0; n < NC; n += 3) {
       step(n, ra, rc, n + 2);
       if (n + 1 < NC) step(n + 1, rb, ra, n + 3);
