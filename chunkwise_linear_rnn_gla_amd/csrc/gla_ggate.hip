@@ -330,7 +330,7 @@ template <typename T, int MT> struct GgIn {
 
 // 2: all of chunk n + 1 loaded ahead; 1: the early operands; 0: nothing
 template <typename T, int MT> constexpr int gg_ahead() {
-  return MT <= 4 ? 2 : (MT == 8 && sizeof(T) == 2 ? 1 : 0);
+  return MT <= 4 ? 2 : (MT == 8 ? 1 : 0);
 }
 // Chunks loaded ahead when everything is (gg_ahead == 2): two for bf16 state
 // slices of up to 64 rows (a chunk step is shorter than the memory latency),
