@@ -24,10 +24,12 @@
 // Two kernels per pass, as for the row-gated forward:
 //   k_gg_prep  (chunk, batch-head): cumsum of log alpha, Q~ = Q e^{A},
 //              K~ = K e^{a - A}, e^{a} and P, stored as MFMA fragments;
-//   k_gg_recur (16-column tile, batch-head), one wave: the state tile stays in
-//              MFMA accumulators across the chunks; per chunk the inter term
-//              (Q~ S), the intra term (P V~), the output, the decay and the
-//              update (K~^T V~), with the beta cumsum formed across lanes.
+//   k_gg_recur (16-column tile, batch-head), one or two waves: the state
+//              tile stays in MFMA accumulators across the chunks (its rows
+//              split over two waves from 64 rows on); per chunk the inter
+//              term (Q~ S), the intra term (P V~), the output, the decay and
+//              the update (K~^T V~), with the beta cumsum formed across lanes
+//              and the next chunks' operands loaded ahead.
 // A pass can read its sequence backwards with the gates shifted by one token
 // and take its initial state transposed; the backward is built from such
 // passes (gla_api.hip).  Gate gradients come from the closed form of App. C
