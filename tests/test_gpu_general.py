@@ -101,6 +101,23 @@ def test_general_backward_matches_oracle(dtype, B, H, L, dk, dv, ga, gb, h0):
         assert e <= tol[name], f"{name} rel_l2 {e}"
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_general_backward_without_dhT(dtype):
+    # dhT absent: the dv pass starts from a zero state; dh0 is still its
+    # final state times token 0's gate, and hT enters no gate gradient
+    x, lb = _inputs(dtype, 2, 2, 77, 64, 96, "sigmoid16", "sigmoid16", 0.5, seed=91)
+    say(f"[ggla bwd] {dtype} without dhT, B2 H2 L77 dk64 dv96")
+    d, lbd = _dev(x, lb)
+    g = bwd_general(d.q, d.k, d.v, d.log_alpha, lbd, d.h0, d.do, None)
+    torch.cuda.synchronize()
+    ref = oracle.ggla_bwd(as_f64(x.q), as_f64(x.k), as_f64(x.v), as_f64(x.log_alpha),
+                          as_f64(lb), as_f64(x.h0), as_f64(x.do), None)
+    for name, got, want in zip(("dq", "dk", "dv", "dlog_alpha", "dlog_beta", "dh0"), g, ref):
+        e = rel_l2(as_f64(got), want)
+        say(f"      {name}: rel_l2 {e:.3e}")
+        assert e <= TOL[dtype], f"{name} rel_l2 {e}"
+
+
 def test_unit_column_gate_matches_row_gated_path():
     # log beta = 0: the general path and gla_fwd compute the same o and hT
     x = make_inputs(2, 2, 200, 128, 256, "bf16", seed=21, h0_std=0.5)
