@@ -473,8 +473,8 @@ gla_status ggla_fwd(const gla_dims* dims, int dtype, const void* q, const void* 
   const GgWs w = gg_layout(dims, bf16, 0);
   if (!workspace || workspace_bytes < w.end) return GLA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GLA_ERR_ALIGN;
-  const GgPass ps{q, k, v, log_alpha, log_beta, dims->dk, dims->dv, 0, h0, 0, o, 0, nullptr,
-                  hT, nullptr, nullptr};
+  const GgPass ps{q, k, v, log_alpha, log_beta, dims->dk, dims->dv, 0, h0, 0, o, nullptr, hT,
+                  nullptr, nullptr};
   GLA_LAUNCH("gg_prep", launch_gg_pass(ps, 0, bf16, BH, L, workspace, s));
   GLA_LAUNCH("gg_recur", launch_gg_pass(ps, 1, bf16, BH, L, workspace, s));
   return GLA_OK;
@@ -520,19 +520,19 @@ gla_status ggla_bwd(const gla_dims* dims, int dtype, const void* q, const void* 
   float *fq = (float*)(ws + w.fq), *fk = (float*)(ws + w.fk), *fv = (float*)(ws + w.fv);
   float *oq = (float*)(ws + w.oq), *ok = (float*)(ws + w.ok), *ov = (float*)(ws + w.ov);
   // the forward again, for o and hT (closed-form gate gradients)
-  const GgPass p0{xq, xk, xv, log_alpha, log_beta, DK, DV, 0, h0, 0, nullptr, 0, ooff,
+  const GgPass p0{xq, xk, xv, log_alpha, log_beta, DK, DV, 0, h0, 0, nullptr, ooff,
                   dhT ? hT32 : nullptr, nullptr, nullptr};
   // dq_t = S_t do_t: the transposed state, q <- do, k <- v, v <- k, gates swapped
-  const GgPass p1{xdo, xv, xk, log_beta, log_alpha, DV, DK, 0, h0, 1, fq, 0, oq, nullptr,
-                  nullptr, nullptr};
+  const GgPass p1{xdo, xv, xk, log_beta, log_alpha, DV, DK, 0, h0, 1, fq, oq, nullptr, nullptr,
+                  nullptr};
   // dv_s = k_s dS_s, dS_s = G_{s+1} ⊙ dS_{s+1} + q_s^T do_s from dS = dhT: the
   // reversed sequence with q <- k, k <- q, v <- do; its final state dS_0 times
   // token 0's gate is dh0
-  const GgPass p2{xk, xq, xdo, log_alpha, log_beta, DK, DV, 1, dhT, 0, fv, 0, ov, dh0, log_alpha,
+  const GgPass p2{xk, xq, xdo, log_alpha, log_beta, DK, DV, 1, dhT, 0, fv, ov, dh0, log_alpha,
                   log_beta};
   // dk_s = dS_s v_s: the same, transposed: q <- v, k <- do, v <- q, gates swapped
-  const GgPass p3{xv, xdo, xq, log_beta, log_alpha, DV, DK, 1, dhT, 1, fk, 0, ok, nullptr,
-                  nullptr, nullptr};
+  const GgPass p3{xv, xdo, xq, log_beta, log_alpha, DV, DK, 1, dhT, 1, fk, ok, nullptr, nullptr,
+                  nullptr};
   const GgPass* passes[4] = {&p0, &p1, &p2, &p3};
   static const char* names[4][2] = {{"gg_prep", "gg_recur"}, {"gg_prep_dq", "gg_recur_dq"},
                                     {"gg_prep_dv", "gg_recur_dv"}, {"gg_prep_dk", "gg_recur_dk"}};

@@ -733,9 +733,8 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int BH, int L
                          (const float*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
   } else {
     const dim3 rg((ps.dv / 16) * BH);
-    if (!is_bf16) launch_gg_recur<float, float>(ps, dkp, rg, r, rb, L, NC, s);
-    else if (ps.o_f32) launch_gg_recur<bf16, float>(ps, dkp, rg, r, rb, L, NC, s);
-    else launch_gg_recur<bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
+    if (is_bf16) launch_gg_recur<bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
+    else launch_gg_recur<float, float>(ps, dkp, rg, r, rb, L, NC, s);
   }
   return hipGetLastError();
 }

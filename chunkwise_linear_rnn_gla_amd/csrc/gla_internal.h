@@ -160,8 +160,8 @@ hipError_t launch_decode(const Plan& p, const void* q, const void* k, const void
 // lb [BH][L][dv] are the log row and column gates.  rev: the pass runs the
 // sequence backwards, applying at its token u the gates of token L - u (none
 // at u = 0).  init: [BH][dk][dv] (transposed, [BH][dv][dk], when init_t) or
-// null; o [BH][L][dv] (or null) in the I/O dtype or fp32 (o_f32, bf16 passes
-// only); o_off (or null) fp32, the output without its same-token term; fin
+// null; o [BH][L][dv] (or null) in the pass's dtype; o_off (or null) fp32, the
+// output without its same-token term; fin
 // (or null) receives the final state, multiplied by the gate of sequence
 // token 0 (fin_la, fin_lb) when those are given.
 struct GgPass {
@@ -174,7 +174,6 @@ struct GgPass {
   const float* init;
   int init_t;
   void* o;
-  int o_f32;
   float* o_off;
   float* fin;
   const float* fin_la;
