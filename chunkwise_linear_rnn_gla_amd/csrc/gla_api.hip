@@ -395,11 +395,11 @@ static gla_status gg_validate(const gla_dims* d, int dtype) {
 
 namespace {
 // Workspace of the general gate.  Forward: the pass records.  Backward: the
-// records of fp32 passes, fp32 copies of bf16 inputs, the recomputed output
-// without its same-token term (o_off) and hT, and dq, dk, dv in full and
-// without their same-token terms, all fp32; gate-gradient partial sums.
+// records of fp32 passes, the recomputed output without its same-token term
+// (o_off) and hT, and dq, dk, dv in full and without their same-token terms,
+// all fp32; gate-gradient partial sums.
 struct GgWs {
-  size_t q32, k32, v32, do32, ooff, hT32, fq, fk, fv, oq, ok, ov, tot, hs, end;
+  size_t ooff, hT32, fq, fk, fv, oq, ok, ov, tot, hs, end;
 };
 GgWs gg_layout(const gla_dims* d, int bf16, int bwd) {
   const size_t BH = (size_t)d->B * d->H, L = (size_t)d->L;
@@ -412,12 +412,6 @@ GgWs gg_layout(const gla_dims* d, int bf16, int bwd) {
     const size_t r2 = gg_pass_rec_bytes(0, (int)BH, d->L, d->dv);
     off = align_up(r > r2 ? r : r2);
     const size_t nk = align_up(BH * L * d->dk * 4), nv = align_up(BH * L * d->dv * 4);
-    if (bf16) {
-      w.q32 = off; off += nk;
-      w.k32 = off; off += nk;
-      w.v32 = off; off += nv;
-      w.do32 = off; off += nv;
-    }
     w.ooff = off; off += nv;
     w.hT32 = off; off += align_up(BH * d->dk * d->dv * 4);
     w.fq = off; off += nk;
@@ -475,8 +469,8 @@ gla_status ggla_fwd(const gla_dims* dims, int dtype, const void* q, const void* 
   if (misaligned(workspace)) return GLA_ERR_ALIGN;
   const GgPass ps{q, k, v, log_alpha, log_beta, dims->dk, dims->dv, 0, h0, 0, o, nullptr, hT,
                   nullptr, nullptr};
-  GLA_LAUNCH("gg_prep", launch_gg_pass(ps, 0, bf16, BH, L, workspace, s));
-  GLA_LAUNCH("gg_recur", launch_gg_pass(ps, 1, bf16, BH, L, workspace, s));
+  GLA_LAUNCH("gg_prep", launch_gg_pass(ps, 0, bf16, bf16, BH, L, workspace, s));
+  GLA_LAUNCH("gg_recur", launch_gg_pass(ps, 1, bf16, bf16, BH, L, workspace, s));
   return GLA_OK;
 }
 
@@ -503,42 +497,33 @@ gla_status ggla_bwd(const gla_dims* dims, int dtype, const void* q, const void* 
   if (!workspace || workspace_bytes < w.end) return GLA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GLA_ERR_ALIGN;
   char* ws = (char*)workspace;
-  // The passes run in fp32 arithmetic: the closed-form gate gradients subtract
-  // terms tens of times larger than their result, which bf16 operands in the
-  // passes would not resolve.
-  const void *xq = q, *xk = k, *xv = v, *xdo = dout;
-  if (bf16) {
-    const size_t nk = (size_t)BH * L * DK, nv = (size_t)BH * L * DV;
-    GLA_LAUNCH("gg_widen", launch_gg_widen(q, (float*)(ws + w.q32), nk, s));
-    GLA_LAUNCH("gg_widen", launch_gg_widen(k, (float*)(ws + w.k32), nk, s));
-    GLA_LAUNCH("gg_widen", launch_gg_widen(v, (float*)(ws + w.v32), nv, s));
-    GLA_LAUNCH("gg_widen", launch_gg_widen(dout, (float*)(ws + w.do32), nv, s));
-    xq = ws + w.q32; xk = ws + w.k32; xv = ws + w.v32; xdo = ws + w.do32;
-  }
+  // The passes run in fp32 arithmetic (bf16 inputs are converted as they are
+  // read): the closed-form gate gradients subtract terms tens of times larger
+  // than their result, which bf16 operands in the passes would not resolve.
   float* ooff = (float*)(ws + w.ooff);
   float* hT32 = (float*)(ws + w.hT32);
   float *fq = (float*)(ws + w.fq), *fk = (float*)(ws + w.fk), *fv = (float*)(ws + w.fv);
   float *oq = (float*)(ws + w.oq), *ok = (float*)(ws + w.ok), *ov = (float*)(ws + w.ov);
   // the forward again, for o and hT (closed-form gate gradients)
-  const GgPass p0{xq, xk, xv, log_alpha, log_beta, DK, DV, 0, h0, 0, nullptr, ooff,
+  const GgPass p0{q, k, v, log_alpha, log_beta, DK, DV, 0, h0, 0, nullptr, ooff,
                   dhT ? hT32 : nullptr, nullptr, nullptr};
   // dq_t = S_t do_t: the transposed state, q <- do, k <- v, v <- k, gates swapped
-  const GgPass p1{xdo, xv, xk, log_beta, log_alpha, DV, DK, 0, h0, 1, fq, oq, nullptr, nullptr,
+  const GgPass p1{dout, v, k, log_beta, log_alpha, DV, DK, 0, h0, 1, fq, oq, nullptr, nullptr,
                   nullptr};
   // dv_s = k_s dS_s, dS_s = G_{s+1} ⊙ dS_{s+1} + q_s^T do_s from dS = dhT: the
   // reversed sequence with q <- k, k <- q, v <- do; its final state dS_0 times
   // token 0's gate is dh0
-  const GgPass p2{xk, xq, xdo, log_alpha, log_beta, DK, DV, 1, dhT, 0, fv, ov, dh0, log_alpha,
+  const GgPass p2{k, q, dout, log_alpha, log_beta, DK, DV, 1, dhT, 0, fv, ov, dh0, log_alpha,
                   log_beta};
   // dk_s = dS_s v_s: the same, transposed: q <- v, k <- do, v <- q, gates swapped
-  const GgPass p3{xv, xdo, xq, log_beta, log_alpha, DV, DK, 1, dhT, 1, fk, ok, nullptr, nullptr,
+  const GgPass p3{v, dout, q, log_beta, log_alpha, DV, DK, 1, dhT, 1, fk, ok, nullptr, nullptr,
                   nullptr};
   const GgPass* passes[4] = {&p0, &p1, &p2, &p3};
   static const char* names[4][2] = {{"gg_prep", "gg_recur"}, {"gg_prep_dq", "gg_recur_dq"},
                                     {"gg_prep_dv", "gg_recur_dv"}, {"gg_prep_dk", "gg_recur_dk"}};
   for (int i = 0; i < 4; ++i) {
-    GLA_LAUNCH(names[i][0], launch_gg_pass(*passes[i], 0, 0, BH, L, ws, s));
-    GLA_LAUNCH(names[i][1], launch_gg_pass(*passes[i], 1, 0, BH, L, ws, s));
+    GLA_LAUNCH(names[i][0], launch_gg_pass(*passes[i], 0, 0, bf16, BH, L, ws, s));
+    GLA_LAUNCH(names[i][1], launch_gg_pass(*passes[i], 1, 0, bf16, BH, L, ws, s));
   }
   GLA_LAUNCH("gg_gates", launch_gg_gates(bf16, BH, L, DK, DV, q, k, oq, ok, ooff, dout, v, ov,
                                          hT32, dhT, (float*)(ws + w.tot), (float*)(ws + w.hs),

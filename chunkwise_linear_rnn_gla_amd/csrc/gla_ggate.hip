@@ -126,9 +126,11 @@ int gg_padded_dim(int is_bf16, int d) {
 
 // grid (NC, BH), 256 threads.  dk: channels of the pass's q and k; dkp: the
 // record's (padded) channel count.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_gg_prep(const T* __restrict__ q,
-                                                      const T* __restrict__ k,
+// T: the record and arithmetic type; TI: the element type of q and k (bf16
+// inputs of an fp32 pass are converted as they are read)
+template <typename T, typename TI>
+__global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
+                                                      const TI* __restrict__ k,
                                                       const float* __restrict__ la,
                                                       uint8_t* __restrict__ rec, size_t rec_bytes,
                                                       int L, int dk, int dkp, int NC, int rev) {
@@ -354,9 +356,9 @@ __device__ inline void gg_load_late(GgIn<T, MT>& in, const uint8_t* __restrict__
     in.ga[m] = *reinterpret_cast<const f4*>(pf + kPfFloats + 16 * (m0 + m) + 4 * g);
 }
 
-template <typename T, int MT>
+template <typename T, int MT, typename TI>
 __device__ inline void gg_load(GgIn<T, MT>& in, const uint8_t* __restrict__ rec, size_t rec_bytes,
-                               int DKP, int m0, const T* __restrict__ vb,
+                               int DKP, int m0, const TI* __restrict__ vb,
                                const float* __restrict__ lbb, int bh, int n, int NC, int L,
                                int dv, int rev, int l, int g) {
   const uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
@@ -406,9 +408,9 @@ __device__ inline void gg_valid(const GgIn<T, MT>& in, int n, int L, int rev, in
 // same-token term, in fp32.  fin (if not null) receives the final state
 // [BH][dk][dv], first multiplied by the gate of sequence token 0 when
 // fin_la / fin_lb are given.
-template <typename T, typename TO, int MT, int NWR>
+template <typename T, typename TO, int MT, int NWR, typename TI>
 __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
-    const uint8_t* __restrict__ rec, size_t rec_bytes, const T* __restrict__ v,
+    const uint8_t* __restrict__ rec, size_t rec_bytes, const TI* __restrict__ v,
     const float* __restrict__ lb, const float* __restrict__ init, int init_t,
     TO* __restrict__ o, float* __restrict__ ooff, float* __restrict__ fin,
     const float* __restrict__ fin_la,
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
         x = init_t ? init[((size_t)bh * dv + jc) * dk + row] : init[((size_t)bh * dk + row) * dv + jc];
       S[m][e] = x;
     }
-  const T* vb = v + (size_t)bh * L * dv + jc;
+  const TI* vb = v + (size_t)bh * L * dv + jc;
   const float* lbb = lb + (size_t)bh * L * dv + jc;
 
   constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW>() : 1;
@@ -666,31 +668,17 @@ __global__ __launch_bounds__(kThreads) void k_gg_gate_fin(
   }
 }
 
-// bf16 -> fp32 copy (the backward's passes run in fp32 arithmetic)
-__global__ __launch_bounds__(kThreads) void k_gg_widen(const bf16* __restrict__ x,
-                                                       float* __restrict__ y, size_t n) {
-  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i < n) y[i] = static_cast<float>(x[i]);
-}
-
 // ---- launchers ----
-
-hipError_t launch_gg_widen(const void* x, float* y, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gg_widen, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, (const bf16*)x, y, n);
-  return hipGetLastError();
-}
 
 // Waves per state tile: two from 64 state rows on (32 for fp32), one below.
 template <typename T> constexpr int gg_row_split(int MT) { return MT >= (sizeof(T) == 2 ? 4 : 2) ? 2 : 1; }
 
-template <typename T, typename TO>
+template <typename T, typename TO, typename TI>
 static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t* r, size_t rb,
                             int L, int NC, hipStream_t s) {
 #define GG_RECUR(MT)                                                                          \
-  hipLaunchKernelGGL((k_gg_recur<T, TO, MT, gg_row_split<T>(MT)>), grid,                        \
-                     dim3(kWave * gg_row_split<T>(MT)), 0, s, r, rb, (const T*)ps.v,           \
+  hipLaunchKernelGGL((k_gg_recur<T, TO, MT, gg_row_split<T>(MT), TI>), grid,                    \
+                     dim3(kWave * gg_row_split<T>(MT)), 0, s, r, rb, (const TI*)ps.v,          \
                      ps.lb, ps.init, ps.init_t, (TO*)ps.o, ps.o_off, ps.fin, ps.fin_la,       \
                      ps.fin_lb, L,                                                            \
                      ps.dk, ps.dv, NC, ps.rev)
@@ -705,36 +693,50 @@ static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t*
 }
 
 // part 0: k_gg_prep, part 1: k_gg_recur (separate so that each launch can be
-// timed on its own)
-hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int BH, int L, void* rec,
-                          hipStream_t s) {
+// timed on its own).  is_bf16: the pass's records and arithmetic; in_bf16: the
+// element type of its q, k and v (bf16 inputs may feed an fp32 pass).
+template <typename T, typename TI>
+static void launch_gg_prep(const GgPass& ps, dim3 pg, size_t lds, uint8_t* r, size_t rb, int L,
+                           int dkp, int NC, hipStream_t s) {
+  hipLaunchKernelGGL((k_gg_prep<T, TI>), pg, dim3(kThreads), lds, s, (const TI*)ps.q,
+                     (const TI*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
+}
+
+template <typename T, typename TI>
+static hipError_t gg_prep_lds(size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute((const void*)k_gg_prep<T, TI>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, int BH, int L,
+                          void* rec, hipStream_t s) {
   const int NC = (L + kGC - 1) / kGC;
   const int dkp = gg_padded_dim(is_bf16, ps.dk);
-  if (dkp < 0 || ps.dv % 16 || BH <= 0 || NC <= 0) return hipErrorInvalidValue;
+  if (dkp < 0 || ps.dv % 16 || BH <= 0 || NC <= 0 || (is_bf16 && !in_bf16))
+    return hipErrorInvalidValue;
   const size_t rb = gg_rec_bytes(is_bf16, dkp);
   uint8_t* r = static_cast<uint8_t*>(rec);
   if (part == 0) {
     // 4 arrays of 16 padded rows, 4 partial P tiles, 8 mask words: 69.9 KB at 256 channels
     const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + 8);
     const dim3 pg(NC, BH);
-    if (lds > 65536) {
-      const hipError_t e =
-          is_bf16 ? hipFuncSetAttribute((const void*)k_gg_prep<bf16>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
-                  : hipFuncSetAttribute((const void*)k_gg_prep<float>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
+    hipError_t e;
+    if (is_bf16) {
+      if ((e = gg_prep_lds<bf16, bf16>(lds)) != hipSuccess) return e;
+      launch_gg_prep<bf16, bf16>(ps, pg, lds, r, rb, L, dkp, NC, s);
+    } else if (in_bf16) {
+      if ((e = gg_prep_lds<float, bf16>(lds)) != hipSuccess) return e;
+      launch_gg_prep<float, bf16>(ps, pg, lds, r, rb, L, dkp, NC, s);
+    } else {
+      if ((e = gg_prep_lds<float, float>(lds)) != hipSuccess) return e;
+      launch_gg_prep<float, float>(ps, pg, lds, r, rb, L, dkp, NC, s);
     }
-    if (is_bf16)
-      hipLaunchKernelGGL((k_gg_prep<bf16>), pg, dim3(kThreads), lds, s, (const bf16*)ps.q,
-                         (const bf16*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
-    else
-      hipLaunchKernelGGL((k_gg_prep<float>), pg, dim3(kThreads), lds, s, (const float*)ps.q,
-                         (const float*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
   } else {
     const dim3 rg((ps.dv / 16) * BH);
-    if (is_bf16) launch_gg_recur<bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
-    else launch_gg_recur<float, float>(ps, dkp, rg, r, rb, L, NC, s);
+    if (is_bf16) launch_gg_recur<bf16, bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
+    else if (in_bf16) launch_gg_recur<float, float, bf16>(ps, dkp, rg, r, rb, L, NC, s);
+    else launch_gg_recur<float, float, float>(ps, dkp, rg, r, rb, L, NC, s);
   }
   return hipGetLastError();
 }

@@ -185,8 +185,10 @@ int gg_padded_dim(int is_bf16, int d);
 // Record bytes of one pass over [BH][L] with d state rows.
 size_t gg_pass_rec_bytes(int is_bf16, int BH, int L, int d);
 // part 0 launches the per-chunk prep (records into rec), part 1 the recurrence.
-hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int BH, int L, void* rec,
-                          hipStream_t s);
+// is_bf16: the records and arithmetic; in_bf16: the element type of q, k, v
+// (bf16 inputs may feed an fp32 pass, not the reverse).
+hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, int BH, int L,
+                          void* rec, hipStream_t s);
 // Token groups of the gate-gradient kernels (their totals are [BH][groups][dk + dv]).
 int gg_gate_groups(int L);
 // dlog alpha, dlog beta by the closed form from dq32, dk32, dv32, o32 (fp32,
@@ -198,8 +200,6 @@ hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const voi
                            const float* dhT, float* tot, float* hs, const float* fq,
                            const float* fk, const float* fv, float* dla, float* dlb, void* dq,
                            void* dkk, void* dvv, hipStream_t s);
-// y[i] = x[i] for n bf16 values x, fp32 y.
-hipError_t launch_gg_widen(const void* x, float* y, size_t n, hipStream_t s);
 
 // dla += rs + the dlog b totals of all later chunks (dlt [BH][NC][dk]).
 hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,
