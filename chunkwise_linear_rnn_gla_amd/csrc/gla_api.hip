@@ -396,10 +396,11 @@ static gla_status gg_validate(const gla_dims* d, int dtype) {
 namespace {
 // Workspace of the general gate.  Forward: the pass records.  Backward: the
 // records of fp32 passes, the recomputed output without its same-token term
-// (o_off) and hT, and dq, dk, dv in full and without their same-token terms,
-// all fp32; gate-gradient partial sums.
+// (o_off) and hT, and dq, dk, dv without their same-token terms, all fp32;
+// gate-gradient partial sums.  The passes write dq, dk, dv in the I/O dtype
+// to the caller's buffers.
 struct GgWs {
-  size_t ooff, hT32, fq, fk, fv, oq, ok, ov, tot, hs, end;
+  size_t ooff, hT32, oq, ok, ov, tot, hs, end;
 };
 GgWs gg_layout(const gla_dims* d, int bf16, int bwd) {
   const size_t BH = (size_t)d->B * d->H, L = (size_t)d->L;
@@ -414,9 +415,6 @@ GgWs gg_layout(const gla_dims* d, int bf16, int bwd) {
     const size_t nk = align_up(BH * L * d->dk * 4), nv = align_up(BH * L * d->dv * 4);
     w.ooff = off; off += nv;
     w.hT32 = off; off += align_up(BH * d->dk * d->dv * 4);
-    w.fq = off; off += nk;
-    w.fk = off; off += nk;
-    w.fv = off; off += nv;
     w.oq = off; off += nk;
     w.ok = off; off += nk;
     w.ov = off; off += nv;
@@ -502,21 +500,20 @@ gla_status ggla_bwd(const gla_dims* dims, int dtype, const void* q, const void* 
   // than their result, which bf16 operands in the passes would not resolve.
   float* ooff = (float*)(ws + w.ooff);
   float* hT32 = (float*)(ws + w.hT32);
-  float *fq = (float*)(ws + w.fq), *fk = (float*)(ws + w.fk), *fv = (float*)(ws + w.fv);
   float *oq = (float*)(ws + w.oq), *ok = (float*)(ws + w.ok), *ov = (float*)(ws + w.ov);
   // the forward again, for o and hT (closed-form gate gradients)
   const GgPass p0{q, k, v, log_alpha, log_beta, DK, DV, 0, h0, 0, nullptr, ooff,
                   dhT ? hT32 : nullptr, nullptr, nullptr};
   // dq_t = S_t do_t: the transposed state, q <- do, k <- v, v <- k, gates swapped
-  const GgPass p1{dout, v, k, log_beta, log_alpha, DV, DK, 0, h0, 1, fq, oq, nullptr, nullptr,
+  const GgPass p1{dout, v, k, log_beta, log_alpha, DV, DK, 0, h0, 1, dq, oq, nullptr, nullptr,
                   nullptr};
   // dv_s = k_s dS_s, dS_s = G_{s+1} ⊙ dS_{s+1} + q_s^T do_s from dS = dhT: the
   // reversed sequence with q <- k, k <- q, v <- do; its final state dS_0 times
   // token 0's gate is dh0
-  const GgPass p2{k, q, dout, log_alpha, log_beta, DK, DV, 1, dhT, 0, fv, ov, dh0, log_alpha,
+  const GgPass p2{k, q, dout, log_alpha, log_beta, DK, DV, 1, dhT, 0, dv, ov, dh0, log_alpha,
                   log_beta};
   // dk_s = dS_s v_s: the same, transposed: q <- v, k <- do, v <- q, gates swapped
-  const GgPass p3{v, dout, q, log_beta, log_alpha, DV, DK, 1, dhT, 1, fk, ok, nullptr, nullptr,
+  const GgPass p3{v, dout, q, log_beta, log_alpha, DV, DK, 1, dhT, 1, dk, ok, nullptr, nullptr,
                   nullptr};
   const GgPass* passes[4] = {&p0, &p1, &p2, &p3};
   static const char* names[4][2] = {{"gg_prep", "gg_recur"}, {"gg_prep_dq", "gg_recur_dq"},
@@ -527,7 +524,7 @@ gla_status ggla_bwd(const gla_dims* dims, int dtype, const void* q, const void* 
   }
   GLA_LAUNCH("gg_gates", launch_gg_gates(bf16, BH, L, DK, DV, q, k, oq, ok, ooff, dout, v, ov,
                                          hT32, dhT, (float*)(ws + w.tot), (float*)(ws + w.hs),
-                                         fq, fk, fv, dlog_alpha, dlog_beta, dq, dk, dv, s));
+                                         dlog_alpha, dlog_beta, s));
   return GLA_OK;
 }
 

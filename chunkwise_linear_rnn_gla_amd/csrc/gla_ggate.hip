@@ -637,17 +637,14 @@ __global__ __launch_bounds__(kThreads) void k_gg_hsum(const float* __restrict__ 
   }
 }
 
-// grid (ceil(L / kGT), BH): dlog alpha, dlog beta, and dq, dk, dv in the I/O
-// dtype from their full fp32 values (fq, fk, fv).
+// grid (ceil(L / kGT), BH): dlog alpha and dlog beta
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_gg_gate_fin(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ dq,
     const float* __restrict__ dkk, const float* __restrict__ o32, const T* __restrict__ dout,
     const T* __restrict__ v, const float* __restrict__ dvv, const float* __restrict__ tot,
-    const float* __restrict__ hs, const float* __restrict__ fq, const float* __restrict__ fk,
-    const float* __restrict__ fv, float* __restrict__ dla, float* __restrict__ dlb,
-    T* __restrict__ dq_out, T* __restrict__ dk_out, T* __restrict__ dv_out, int L, int dk,
-    int dv) {
+    const float* __restrict__ hs, float* __restrict__ dla, float* __restrict__ dlb, int L,
+    int dk, int dv) {
   const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, D = dk + dv;
   const int t0 = cg * kGT, t1 = min(L, t0 + kGT);
   for (int c = threadIdx.x; c < D; c += kThreads) {
@@ -656,14 +653,8 @@ __global__ __launch_bounds__(kThreads) void k_gg_gate_fin(
     for (int t = t1 - 1; t >= t0; --t) {
       const size_t row = (size_t)bh * L + t;
       run += gg_term(c, row, dk, dv, q, k, dq, dkk, o32, dout, v, dvv);
-      if (c < dk) {
-        dla[row * dk + c] = run;
-        dq_out[row * dk + c] = from_f32<T>(fq[row * dk + c]);
-        dk_out[row * dk + c] = from_f32<T>(fk[row * dk + c]);
-      } else {
-        dlb[row * dv + c - dk] = run;
-        dv_out[row * dv + c - dk] = from_f32<T>(fv[row * dv + c - dk]);
-      }
+      if (c < dk) dla[row * dk + c] = run;
+      else dlb[row * dv + c - dk] = run;
     }
   }
 }
@@ -734,8 +725,10 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
     }
   } else {
     const dim3 rg((ps.dv / 16) * BH);
+    // o is written in the element type of the inputs (o_off, when asked
+    // for, in fp32)
     if (is_bf16) launch_gg_recur<bf16, bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
-    else if (in_bf16) launch_gg_recur<float, float, bf16>(ps, dkp, rg, r, rb, L, NC, s);
+    else if (in_bf16) launch_gg_recur<float, bf16, bf16>(ps, dkp, rg, r, rb, L, NC, s);
     else launch_gg_recur<float, float, float>(ps, dkp, rg, r, rb, L, NC, s);
   }
   return hipGetLastError();
@@ -752,9 +745,8 @@ int gg_gate_groups(int L) { return (L + kGT - 1) / kGT; }
 hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const void* q,
                            const void* k, const float* dq32, const float* dk32, const float* o32,
                            const void* dout, const void* v, const float* dv32, const float* hT,
-                           const float* dhT, float* tot, float* hs, const float* fq,
-                           const float* fk, const float* fv, float* dla, float* dlb, void* dq,
-                           void* dkk, void* dvv, hipStream_t s) {
+                           const float* dhT, float* tot, float* hs, float* dla, float* dlb,
+                           hipStream_t s) {
   const dim3 grid(gg_gate_groups(L), BH);
   if (dhT) hipLaunchKernelGGL(k_gg_hsum, dim3(BH), dim3(kThreads), 0, s, hT, dhT, hs, dk, dv);
   const float* hsp = dhT ? hs : nullptr;
@@ -764,16 +756,14 @@ hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const voi
                        tot, L, dk, dv);
     hipLaunchKernelGGL((k_gg_gate_fin<bf16>), grid, dim3(kThreads), 0, s, (const bf16*)q,
                        (const bf16*)k, dq32, dk32, o32, (const bf16*)dout, (const bf16*)v, dv32,
-                       tot, hsp, fq, fk, fv, dla, dlb, (bf16*)dq, (bf16*)dkk, (bf16*)dvv, L, dk,
-                       dv);
+                       tot, hsp, dla, dlb, L, dk, dv);
   } else {
     hipLaunchKernelGGL((k_gg_gate_tot<float>), grid, dim3(kThreads), 0, s, (const float*)q,
                        (const float*)k, dq32, dk32, o32, (const float*)dout, (const float*)v,
                        dv32, tot, L, dk, dv);
     hipLaunchKernelGGL((k_gg_gate_fin<float>), grid, dim3(kThreads), 0, s, (const float*)q,
                        (const float*)k, dq32, dk32, o32, (const float*)dout, (const float*)v,
-                       dv32, tot, hsp, fq, fk, fv, dla, dlb, (float*)dq, (float*)dkk, (float*)dvv,
-                       L, dk, dv);
+                       dv32, tot, hsp, dla, dlb, L, dk, dv);
   }
   return hipGetLastError();
 }

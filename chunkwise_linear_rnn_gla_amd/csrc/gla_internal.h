@@ -192,14 +192,13 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
 // Token groups of the gate-gradient kernels (their totals are [BH][groups][dk + dv]).
 int gg_gate_groups(int L);
 // dlog alpha, dlog beta by the closed form from dq32, dk32, dv32, o32 (fp32,
-// without their same-token terms), and dq, dk, dv converted from the full
-// fp32 values fq, fk, fv.  hs: [BH][dk + dv] scratch (used when dhT is given).
+// without their same-token terms).  hs: [BH][dk + dv] scratch (used when dhT
+// is given).
 hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const void* q,
                            const void* k, const float* dq32, const float* dk32, const float* o32,
                            const void* dout, const void* v, const float* dv32, const float* hT,
-                           const float* dhT, float* tot, float* hs, const float* fq,
-                           const float* fk, const float* fv, float* dla, float* dlb, void* dq,
-                           void* dkk, void* dvv, hipStream_t s);
+                           const float* dhT, float* tot, float* hs, float* dla, float* dlb,
+                           hipStream_t s);
 
 // dla += rs + the dlog b totals of all later chunks (dlt [BH][NC][dk]).
 hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,
