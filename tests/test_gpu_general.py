@@ -118,6 +118,27 @@ def test_general_backward_without_dhT(dtype):
         assert e <= TOL[dtype], f"{name} rel_l2 {e}"
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("L", [1, 16, 17])
+def test_general_chunk_edges(dtype, L):
+    # one token, exactly one 16-token chunk, one token past it; h0 and dhT set
+    x, lb = _inputs(dtype, 1, 2, L, 32, 64, "sigmoid16", "sigmoid16", 0.5, seed=200 + L)
+    say(f"[ggla] chunk edges {dtype} L={L}")
+    d, lbd = _dev(x, lb)
+    o, hT = fwd_general(d.q, d.k, d.v, d.log_alpha, lbd, d.h0)
+    g = bwd_general(d.q, d.k, d.v, d.log_alpha, lbd, d.h0, d.do, d.dhT)
+    torch.cuda.synchronize()
+    f = [as_f64(t) for t in (x.q, x.k, x.v, x.log_alpha)]
+    ro, rhT = oracle.ggla_fwd(*f, as_f64(lb), as_f64(x.h0))
+    ref = oracle.ggla_bwd(*f, as_f64(lb), as_f64(x.h0), as_f64(x.do), as_f64(x.dhT))
+    pairs = [("o", o, ro), ("hT", hT, rhT)]
+    pairs += list(zip(("dq", "dk", "dv", "dlog_alpha", "dlog_beta", "dh0"), g, ref))
+    for name, got, want in pairs:
+        e = rel_l2(as_f64(got), want)
+        say(f"      {name}: rel_l2 {e:.3e}")
+        assert e <= TOL[dtype], f"{name} rel_l2 {e}"
+
+
 def test_unit_column_gate_matches_row_gated_path():
     # log beta = 0: the general path and gla_fwd compute the same o and hT
     x = make_inputs(2, 2, 200, 128, 256, "bf16", seed=21, h0_std=0.5)
