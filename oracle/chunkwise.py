@@ -2,65 +2,60 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-This is a second, independent statement of what the layer computes: the
-chunkwise-parallel form of "Gated Linear Attention Transformers with
-Hardware-Efficient Training" (papercache.org notes, §4.2 chunkwise form and
-§4.3 / Figure 3 secondary chunking; App. B, the PyTorch-style listing of the
-secondary-chunking forward).  It is used only to pin the token-by-token
-recurrence in ``gla_oracle.c``: the two must agree for every chunk size C
-(notes §2.2: C = L is the parallel form, C = 1 the recurrent form).
+A second, independent statement of what the layer computes, used only to pin
+the token-by-token recurrence in ``gla_oracle.c``: the two must agree for
+every chunk size C (papercache.org notes on "Gated Linear Attention
+Transformers with Hardware-Efficient Training", §2.2: C = L is the parallel
+form, C = 1 the recurrent form).  It is written from the matrix equations of
+the chunkwise form (notes §4.2) and the block split of secondary chunking
+(notes §4.3, Figure 3), one whole-chunk or whole-block array operation per
+equation:
 
-Per head, with a = log alpha and chunk size C, sub-chunk size c:
-
-* B = inclusive cumsum of a *within each chunk* (the listing's cumsum; its
-  printed loop body indexes a[i] / B[i] where the chunk-local position
-  i*C + j is meant -- taken that way here, which is the only reading under
-  which the listing reproduces the recurrence).
-* Inter-chunk: O_n += (Q ⊙ e^B) S_{n-1};  S_n = diag(e^{b}) S_{n-1} +
-  (K ⊙ e^{b - B})^T V, with b = B at the chunk's last row.
-* Intra-chunk, per sub-chunk j:
-    - diagonal block in full precision log space:
-      P[m, r] = sum_k q_mk k_rk exp(B_mk - B_rk) for r <= m;
-    - earlier sub-chunks u < j via the reference row z = B at sub-chunk j's
-      first row: (Q_j ⊙ e^{B_j - z}) (K_u ⊙ e^{z - B_u})^T, both factors <= 1.
-* h0 / hT: S_0 = h0 (the chunk state may come from a previous segment,
-  notes §2.2); hT = S_{L/C}.  The listing itself starts from zeros and does
-  not return the final state; adding both is the plain extension.
-
-Nothing here is blocked, fused or reordered beyond those steps.
+* Per chunk, B is the cumulative sum of a = log alpha from the chunk's first
+  row (inclusive), so Lambda = e^B is the decay from the chunk start, b = B
+  at the last row is the chunk's total log decay, gamma = e^b and
+  Gamma = e^{b - B} the decay from a row to the chunk end.
+* Output:  O = (Q ⊙ Lambda) S_prev + P V, with the chunk's causal gated
+  score matrix P[m, r] = sum_k q_mk k_rk exp(B_mk - B_rk) for r <= m.
+* State:   S = diag(gamma) S_prev + (K ⊙ Gamma)^T V.
+* P by sub-chunks of c rows (Figure 3): blocks on the diagonal in log space
+  (the pairwise differences B_m - B_r masked to r <= m before the
+  exponential); blocks below the diagonal as one matrix product per query
+  sub-chunk j through the reference row z = B at its first row,
+  (Q_j ⊙ e^{B_j - z}) (K_{<j} ⊙ e^{z - B_{<j}})^T, where both factors are <= 1.
+* S_0 = h0 (a previous segment's state, notes §2.2, or zeros); hT = the state
+  after the last chunk.
 """
 from __future__ import annotations
 
 import numpy as np
 
 
+def chunk_scores(q, k, B, c):
+    """The causal gated score matrix P (C x C) of one chunk, by sub-chunks of
+    c rows: log space on the diagonal blocks, reference-row products below."""
+    C = q.shape[0]
+    t = np.arange(C)
+    on_diag_block = (t[:, None] // c == t[None, :] // c) & (t[:, None] >= t[None, :])
+    diff = np.where(on_diag_block[:, :, None], B[:, None, :] - B[None, :, :], -np.inf)
+    P = np.einsum("mk,rk,mrk->mr", q, k, np.exp(diff))
+    for j in range(1, C // c):
+        rows, z = slice(j * c, (j + 1) * c), B[j * c]
+        P[rows, : j * c] = (q[rows] * np.exp(B[rows] - z)) @ (k[: j * c] * np.exp(z - B[: j * c])).T
+    return P
+
+
 def _head(q, k, v, a, h0, C, c):
     L, dk = q.shape
-    dv = v.shape[1]
-    S = np.zeros((dk, dv)) if h0 is None else np.array(h0, dtype=np.float64)
-    o = np.zeros((L, dv))
-    for n in range(L // C):
-        rows = slice(n * C, (n + 1) * C)
-        bq, bk, bv, ba = q[rows], k[rows], v[rows], a[rows]
-        Bc = np.cumsum(ba, axis=0)            # chunk-local inclusive cumsum
-        b_last = Bc[-1]
-        oc = (bq * np.exp(Bc)) @ S            # inter-chunk contribution
-        S = np.exp(b_last)[:, None] * S + (bk * np.exp(b_last - Bc)).T @ bv
-        for j in range(C // c):
-            t = slice(j * c, (j + 1) * c)
-            qj, kj, vj, Bj = bq[t], bk[t], bv[t], Bc[t]
-            P = np.zeros((c, c))
-            for m in range(c):
-                for r in range(m + 1):
-                    P[m, r] = np.sum(qj[m] * kj[r] * np.exp(Bj[m] - Bj[r]))
-            oc[t] += P @ vj
-            z = Bj[0]
-            qs = qj * np.exp(Bj - z)
-            for u in range(j):
-                y = slice(u * c, (u + 1) * c)
-                ks = bk[y] * np.exp(z - Bc[y])
-                oc[t] += (qs @ ks.T) @ bv[y]
-        o[rows] = oc
+    S = np.zeros((dk, v.shape[1])) if h0 is None else np.array(h0, dtype=np.float64)
+    o = np.empty((L, v.shape[1]))
+    for n0 in range(0, L, C):
+        rows = slice(n0, n0 + C)
+        Q, K, V = q[rows], k[rows], v[rows]
+        B = np.cumsum(a[rows], axis=0)
+        b = B[-1]
+        o[rows] = (Q * np.exp(B)) @ S + chunk_scores(Q, K, B, c) @ V
+        S = np.exp(b)[:, None] * S + (K * np.exp(b - B)).T @ V
     return o, S
 
 

@@ -9,8 +9,9 @@ operand, a decay applied at the wrong step) fails at least one of them:
   diagonal (papercache.org notes §2.1, "Eq. 1" and the parallel form).
 * Brute force with explicit per-pair gate products b_t / b_i (notes §4.1,
   parallel form via b_t = prod alpha_j), no logs and no cumsum, tiny inputs.
-* The chunkwise form with secondary chunking (notes §4.2, §4.3 / Fig. 3, App. B
-  listing), independent code, equal for C in {1, 16, 64, L} (notes §2.2).
+* The chunkwise form with secondary chunking (notes §4.2 equations, §4.3 /
+  Figure 3 block split), independent code, equal for C in {1, 16, 64, L}
+  (notes §2.2).
 * A data-independent decay gamma (RetNet-style, notes §4 intro; Table 1) gives
   ((Q K^T) ⊙ D) V with D_ti = gamma^(t-i); a channel-shared scalar gate
   (Mamba-2 style, notes §4.1) gives D_ti = prod_{s=i+1..t} gamma_s.
