@@ -19,7 +19,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_NULL", 2: "GLA_ERR_SHAPE", 3: "GLA_ERR_DTYPE"
 
 # Every symbol include/gla.h declares.
 EXPORTS = ("gla_abi_version", "gla_status_string", "gla_fwd_workspace_size",
-           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_decode", "ggla_fwd_workspace_size",
+           "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_fwd_ex_workspace_size",
+           "gla_fwd_ex", "gla_decode", "ggla_fwd_workspace_size",
            "ggla_bwd_workspace_size", "ggla_fwd", "ggla_bwd", "gla_profile_begin",
            "gla_profile_end", "gla_profile_count", "gla_profile_get")
 
@@ -28,6 +29,17 @@ class GlaDims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("subchunk", ctypes.c_int32)]
+
+
+# gla_fwd_algo
+GLA_FWD_AUTO, GLA_FWD_TWO_PASS, GLA_FWD_FUSED, GLA_FWD_MATERIALIZED = 0, 1, 2, 3
+FWD_ALGOS = {"auto": GLA_FWD_AUTO, "two_pass": GLA_FWD_TWO_PASS, "fused": GLA_FWD_FUSED,
+             "materialized": GLA_FWD_MATERIALIZED}
+
+
+class GlaFwdConfig(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32), ("recur_waves", ctypes.c_int32),
+                ("recur_segments", ctypes.c_int32)]
 
 
 class GlaError(RuntimeError):
@@ -61,6 +73,11 @@ def load():
     lib.gla_fwd.restype = i32
     lib.gla_bwd.argtypes = [dims_p, i32] + [vp] * 12 + [vp, sz, vp]
     lib.gla_bwd.restype = i32
+    cfg_p = ctypes.POINTER(GlaFwdConfig)
+    lib.gla_fwd_ex_workspace_size.argtypes = [dims_p, i32, cfg_p, ctypes.POINTER(sz)]
+    lib.gla_fwd_ex_workspace_size.restype = i32
+    lib.gla_fwd_ex.argtypes = [dims_p, i32, cfg_p] + [vp] * 7 + [vp, sz, vp]
+    lib.gla_fwd_ex.restype = i32
     lib.gla_decode.argtypes = [dims_p, i32] + [vp] * 6 + [vp]
     lib.gla_decode.restype = i32
     for f in (lib.ggla_fwd_workspace_size, lib.ggla_bwd_workspace_size):
@@ -122,6 +139,26 @@ def gla_fwd(dims, dtype, q, k, v, log_alpha, h0, o, hT, workspace, workspace_byt
     return load().gla_fwd(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v),
                           _ptr(log_alpha), _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
                           workspace_bytes, stream)
+
+
+def _cfg(cfg):
+    return None if cfg is None else ctypes.byref(cfg)
+
+
+def gla_fwd_ex_workspace_size(dims: GlaDims, dtype: int, cfg) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().gla_fwd_ex_workspace_size(ctypes.byref(dims), dtype, _cfg(cfg), ctypes.byref(n))
+    if st != 0:
+        raise GlaError(st, "gla_fwd_ex_workspace_size")
+    return n.value
+
+
+def gla_fwd_ex(dims, dtype, cfg, q, k, v, log_alpha, h0, o, hT, workspace, workspace_bytes,
+               stream):
+    """Raw call with a GlaFwdConfig (or None); returns the status."""
+    return load().gla_fwd_ex(ctypes.byref(dims), dtype, _cfg(cfg), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(log_alpha), _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
+                             workspace_bytes, stream)
 
 
 def gla_bwd(dims, dtype, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv, dlog_alpha, dh0,

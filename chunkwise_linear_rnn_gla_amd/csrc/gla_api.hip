@@ -4,6 +4,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/gla.h"
 #include "gla_internal.h"
 
@@ -11,7 +14,8 @@ namespace gla {
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan* p) {
+bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan* p,
+               const FwdOptions& opt) {
   if (B < 0 || H < 0 || L < 0) return false;
   if (c != 16) return false;
   if (bf16) {
@@ -23,6 +27,8 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   }
   if (dk < 16 || dk > 256 || dv < 16 || dv > 512) return false;
   if ((int64_t)B * H > (1 << 20) || L > (1 << 24)) return false;
+  if (opt.algo < FWD_AUTO || opt.algo > FWD_MATERIALIZED) return false;
+  if (opt.recur_waves < 0 || opt.recur_segments < 0) return false;
   Plan& P = *p;
   P.B = B; P.H = H; P.L = L; P.dk = dk; P.dv = dv; P.C = C; P.c = c; P.bf16 = bf16;
   P.BH = B * H;
@@ -44,16 +50,31 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     P.seg_chunks = (int)((P.NC + want - 1) / want);
     P.NSEG = (P.NC + P.seg_chunks - 1) / P.seg_chunks;
   }
+  // Forward path: the two-pass forward (chunk prep + recurrence) wherever its
+  // kernels are instantiated, unless the caller asks for another one; an
+  // explicitly requested path that the shape does not support is an error,
+  // not a silent substitution.
+  const bool can_recur = recur_supported(bf16, C, dk, dv, L);
+  const bool can_fused = fused_supported(bf16, C, dk, dv);
+  switch (opt.algo) {
+    case FWD_TWO_PASS:
+      if (!can_recur) return false;
+      P.recur = 1; P.fused = 0;
+      break;
+    case FWD_FUSED:
+      if (!can_fused) return false;
+      P.recur = 0; P.fused = 1;
+      break;
+    case FWD_MATERIALIZED:
+      P.recur = 0; P.fused = 0;
+      break;
+    default:
+      P.recur = can_recur;
+      P.fused = !can_recur && can_fused;
+      break;
+  }
   // Fused forward: one workgroup per (batch-head, segment, d_v tile); enough
   // segments to give every compute unit a workgroup.
-  // Forward path: the two-pass forward (chunk prep + recurrence) wherever its
-  // kernels are instantiated; GLA_FORWARD=fused | materialized selects the
-  // single-pass fused segment kernel or the materialised-state kernels.
-  const char* env = getenv("GLA_FORWARD");
-  const bool want_fused = env && strcmp(env, "fused") == 0;
-  const bool want_mat = env && strcmp(env, "materialized") == 0;
-  P.recur = !want_fused && !want_mat && recur_supported(bf16, C, dk, dv, L);
-  P.fused = !P.recur && !want_mat && fused_supported(bf16, C, dk, dv);
   P.DVTF = fused_dv_tile(bf16, dk, dv);
   P.NSEGF = 1;
   P.segf_chunks = P.NC > 0 ? P.NC : 1;
@@ -66,7 +87,9 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   }
   // Recurrence: 16 state columns per wave; the largest workgroup that still
   // gives 256 workgroups, and sequence segments when even one wave per
-  // workgroup leaves the chip mostly idle.
+  // workgroup leaves the chip mostly idle.  Explicit wave and segment counts
+  // apply to the two-pass forward only.
+  if (!P.recur && (opt.recur_waves || opt.recur_segments)) return false;
   const int wmin = recur_min_waves(bf16, dk), wmax = recur_max_waves(bf16, dk);
   P.NWVR = wmin;
   for (int w = wmax; w >= wmin; w /= 2) {
@@ -74,9 +97,10 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     P.NWVR = w;
     if ((int64_t)P.BH * (dv / (16 * w)) >= 256) break;
   }
-  if (const char* e = getenv("GLA_RECUR_WAVES")) {
-    const int w = atoi(e);
-    if ((w == 1 || w == 2 || w == 4) && w >= wmin && w <= wmax && dv % (16 * w) == 0) P.NWVR = w;
+  if (opt.recur_waves) {
+    const int w = opt.recur_waves;
+    if ((w != 1 && w != 2 && w != 4) || w < wmin || w > wmax || dv % (16 * w)) return false;
+    P.NWVR = w;
   }
   P.NSEGR = 1;
   P.segr_chunks = P.NC > 0 ? P.NC : 1;
@@ -84,10 +108,7 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     const int64_t units = (int64_t)P.BH * (dv / (16 * P.NWVR));
     int64_t want = 1;
     if (units < 128) want = (256 + units - 1) / units;
-    if (const char* e = getenv("GLA_RECUR_SEGMENTS")) {
-      const int v = atoi(e);
-      if (v >= 1) want = v;
-    }
+    if (opt.recur_segments) want = opt.recur_segments;
     if (want > P.NC) want = P.NC;
     if (want > 1) {
       P.segr_chunks = (int)((P.NC + want - 1) / want);
@@ -101,12 +122,14 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   P.off_st = off; off = align_up(off + BH * P.NC * S * P.esize);
   P.off_seg_u = off; off = align_up(off + (P.NSEG > 1 ? BH * P.NSEG * S * 4 : 0));
   P.off_seg_in = off; off = align_up(off + (P.NSEG > 1 ? BH * P.NSEG * S * 4 : 0));
+  // the materialised forward's layout (also the start of the backward's)
+  const size_t ws_mat = off;
   {
     // the fused forward reuses the cumsum region and needs its own segment states
     size_t f = P.off_st;
     P.off_fu = f; f = align_up(f + (P.NSEGF > 1 ? BH * P.NSEGF * S * 4 : 0));
     P.off_fi = f; f = align_up(f + (P.NSEGF > 1 ? BH * P.NSEGF * S * 4 : 0));
-    P.ws_fwd = off > f ? off : f;
+    P.ws_fused = f;
   }
   {
     // the two-pass forward's buffers (its own region from the start)
@@ -120,9 +143,10 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     P.off_ru = f; f = align_up(f + (P.NSEGR > 1 ? BH * P.NSEGR * S * 4 : 0));
     P.off_ri = f; f = align_up(f + (P.NSEGR > 1 ? BH * P.NSEGR * S * 4 : 0));
     P.off_rg = f; f = align_up(f + (P.NSEGR > 1 ? BH * P.NSEGR * dk * 4 : 0));
-    if (P.recur && f > P.ws_fwd) P.ws_fwd = f;
+    P.ws_recur = f;
   }
-  off = P.ws_fwd;
+  P.ws_fwd = P.recur ? P.ws_recur : (P.fused ? P.ws_fused : ws_mat);
+  off = ws_mat > P.ws_fused ? ws_mat : P.ws_fused;
   // backward extras: dS per chunk in two layouts, hT, chunk totals of
   // dlog b, rowsum(hT * dhT)
   P.off_st2 = off; off = align_up(off + 2 * BH * P.NC * S * P.esize);
@@ -144,10 +168,22 @@ using namespace gla;
 
 static bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15) != 0; }
 
-static gla_status validate(const gla_dims* d, int dtype, Plan* p) {
+static FwdOptions fwd_options(const gla_fwd_config* cfg) {
+  FwdOptions o;
+  if (cfg) {
+    o.algo = cfg->algo;
+    o.recur_waves = cfg->recur_waves;
+    o.recur_segments = cfg->recur_segments;
+  }
+  return o;
+}
+
+static gla_status validate(const gla_dims* d, int dtype, Plan* p,
+                           const gla_fwd_config* cfg = nullptr) {
   if (!d) return GLA_ERR_NULL;
   if (dtype != GLA_FP32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
-  if (!make_plan(d->B, d->H, d->L, d->dk, d->dv, d->chunk, d->subchunk, dtype == GLA_BF16, p))
+  if (!make_plan(d->B, d->H, d->L, d->dk, d->dv, d->chunk, d->subchunk, dtype == GLA_BF16, p,
+                 fwd_options(cfg)))
     return GLA_ERR_SHAPE;
   return GLA_OK;
 }
@@ -163,26 +199,37 @@ static gla_status check_ptrs(std::initializer_list<const void*> required,
   return GLA_OK;
 }
 
-// ---- launch profiling: HIP events around each launch on its stream
+// ---- launch profiling: HIP events around each launch on its stream.  A
+// mutex guards the record table; the slot a launch reserved before it was
+// enqueued is remembered per thread until its closing event is recorded.
 namespace {
 struct ProfRec {
-  const char* name;
+  const char* name;  // null: the opening event could not be recorded
   hipEvent_t a, b;
+  int done;          // closing event recorded
 };
+std::mutex g_prof_mu;
 ProfRec* g_recs = nullptr;
-int g_cap = 0, g_n = 0, g_on = 0, g_pending = -1;
+int g_cap = 0, g_n = 0;
+std::atomic<int> g_on{0};
+thread_local int t_pending = -1;
 
 void prof_before(const char* name, hipStream_t s) {
-  g_pending = -1;
-  if (!g_on || g_n >= g_cap) return;
-  if (hipEventRecord(g_recs[g_n].a, s) != hipSuccess) return;
-  g_recs[g_n].name = name;
-  g_pending = g_n;
+  t_pending = -1;
+  if (!g_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_on.load(std::memory_order_relaxed) || g_n >= g_cap) return;
+  const int i = g_n++;
+  g_recs[i].done = 0;
+  g_recs[i].name = hipEventRecord(g_recs[i].a, s) == hipSuccess ? name : nullptr;
+  if (g_recs[i].name) t_pending = i;
 }
 void prof_after(hipStream_t s) {
-  if (g_pending < 0) return;
-  if (hipEventRecord(g_recs[g_pending].b, s) == hipSuccess) g_n = g_pending + 1;
-  g_pending = -1;
+  if (t_pending < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (t_pending < g_cap && hipEventRecord(g_recs[t_pending].b, s) == hipSuccess)
+    g_recs[t_pending].done = 1;
+  t_pending = -1;
 }
 }  // namespace
 
@@ -211,13 +258,18 @@ const char* gla_status_string(int status) {
   }
 }
 
-gla_status gla_fwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes) {
+gla_status gla_fwd_ex_workspace_size(const gla_dims* dims, int dtype, const gla_fwd_config* cfg,
+                                     size_t* bytes) {
   if (!bytes) return GLA_ERR_NULL;
   Plan p;
-  gla_status st = validate(dims, dtype, &p);
+  gla_status st = validate(dims, dtype, &p, cfg);
   if (st != GLA_OK) return st;
   *bytes = p.ws_fwd;
   return GLA_OK;
+}
+
+gla_status gla_fwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes) {
+  return gla_fwd_ex_workspace_size(dims, dtype, nullptr, bytes);
 }
 
 gla_status gla_bwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes) {
@@ -232,8 +284,16 @@ gla_status gla_bwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes
 gla_status gla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k, const void* v,
                    const float* log_alpha, const float* h0, void* o, float* hT,
                    void* workspace, size_t workspace_bytes, void* stream) {
+  return gla_fwd_ex(dims, dtype, nullptr, q, k, v, log_alpha, h0, o, hT, workspace,
+                    workspace_bytes, stream);
+}
+
+gla_status gla_fwd_ex(const gla_dims* dims, int dtype, const gla_fwd_config* cfg, const void* q,
+                      const void* k, const void* v, const float* log_alpha, const float* h0,
+                      void* o, float* hT, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   Plan p;
-  gla_status st = validate(dims, dtype, &p);
+  gla_status st = validate(dims, dtype, &p, cfg);
   if (st != GLA_OK) return st;
   if (p.BH == 0) return GLA_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -530,6 +590,8 @@ gla_status ggla_bwd(const gla_dims* dims, int dtype, const void* q, const void* 
 
 gla_status gla_profile_begin(int capacity) {
   if (capacity < 1) return GLA_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_on.store(0);
   if (capacity != g_cap) {
     for (int i = 0; i < g_cap; ++i) {
       (void)hipEventDestroy(g_recs[i].a);
@@ -537,10 +599,16 @@ gla_status gla_profile_begin(int capacity) {
     }
     free(g_recs);
     g_cap = 0;
+    g_n = 0;
     g_recs = (ProfRec*)calloc((size_t)capacity, sizeof(ProfRec));
     if (!g_recs) return GLA_ERR_HIP;
     for (int i = 0; i < capacity; ++i) {
-      if (hipEventCreate(&g_recs[i].a) != hipSuccess || hipEventCreate(&g_recs[i].b) != hipSuccess) {
+      if (hipEventCreate(&g_recs[i].a) != hipSuccess) {
+        g_cap = i;
+        return GLA_ERR_HIP;
+      }
+      if (hipEventCreate(&g_recs[i].b) != hipSuccess) {
+        (void)hipEventDestroy(g_recs[i].a);
         g_cap = i;
         return GLA_ERR_HIP;
       }
@@ -548,20 +616,25 @@ gla_status gla_profile_begin(int capacity) {
     }
   }
   g_n = 0;
-  g_pending = -1;
-  g_on = 1;
+  g_on.store(1);
   return GLA_OK;
 }
 
-void gla_profile_end(void) { g_on = 0; }
+void gla_profile_end(void) { g_on.store(0); }
 
-int gla_profile_count(void) { return g_n; }
+int gla_profile_count(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  return g_n;
+}
 
 gla_status gla_profile_get(int index, const char** kernel, float* ms) {
   if (!kernel || !ms) return GLA_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   if (index < 0 || index >= g_n) return GLA_ERR_SHAPE;
-  if (hipEventElapsedTime(ms, g_recs[index].a, g_recs[index].b) != hipSuccess) return GLA_ERR_HIP;
-  *kernel = g_recs[index].name;
+  const ProfRec& r = g_recs[index];
+  if (!r.name || !r.done) return GLA_ERR_HIP;
+  if (hipEventElapsedTime(ms, r.a, r.b) != hipSuccess) return GLA_ERR_HIP;
+  *kernel = r.name;
   return GLA_OK;
 }
 

@@ -36,11 +36,23 @@ struct Plan {
   // diagonal blocks [BH][NC][C][16], chunk log decays [BH][NC][dk], segment
   // local states / entry states [BH][NSEGR][dk][dv], segment log decays
   size_t off_qg, off_kg, off_ph, off_pl, off_gl, off_ru, off_ri, off_rg;
-  size_t ws_fwd, ws_bwd;
+  size_t ws_fwd, ws_bwd;    // workspace of the chosen forward path; of the backward
+  size_t ws_recur, ws_fused;  // workspace of the two-pass and of the fused forward
 };
 
-// Fills everything but the status; returns false if the sizes are unsupported.
-bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan* p);
+// Forward path and its tuning, as the caller chose them (gla_fwd_config in
+// include/gla.h); zeros mean "automatic".
+enum FwdAlgo { FWD_AUTO = 0, FWD_TWO_PASS = 1, FWD_FUSED = 2, FWD_MATERIALIZED = 3 };
+struct FwdOptions {
+  int algo = FWD_AUTO;
+  int recur_waves = 0;
+  int recur_segments = 0;
+};
+
+// Fills everything but the status; returns false if the sizes (or the
+// requested forward path) are unsupported.
+bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan* p,
+               const FwdOptions& opt = FwdOptions());
 
 // ---- forward kernels (gla_fwd.hip) ----
 hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t s);

@@ -68,9 +68,11 @@ __device__ inline void touch_lines(const void* base, int bytes, int l, unsigned 
   r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
   r[2] = __builtin_amdgcn_readfirstlane(bytes);
   r[3] = 0x00020000;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+  // M0 (the LDS address) is an operand the compiler loads ("{m0}"), not a
+  // register the statement sets behind its back
+  asm volatile("buffer_load_dword %1, %2, %3 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_dummy)), "v"((unsigned)l * 128u), "s"(r),
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds_dummy)), "v"((unsigned)l * 128u), "s"(r),
                  "s"(0u)
                : "memory");
 }

@@ -41,12 +41,14 @@ __device__ inline i32x4 make_rsrc(const void* base) {
   r[3] = 0x00020000;
   return r;
 }
-// lds_wave_base: LDS byte address (wave-uniform).  M0 carries it; no other
-// code in the kernels that use this sets or reads M0.
+// lds_wave_base: LDS byte address (wave-uniform).  The instruction takes it
+// in M0, which the "{m0}" operand asks the compiler to load: the compiler
+// then knows M0's contents at this point and keeps any value of its own
+// there safe, so the statement has no hidden effect on registers.
 __device__ inline void dma16b(const i32x4& r, unsigned voff, unsigned soff, unsigned lds_wave_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(voff), "s"(r),
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(voff), "s"(r),
                  "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory");
 }

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 1
+#define GLA_ABI_VERSION 2
 
 typedef enum { GLA_FP32 = 0, GLA_BF16 = 1 } gla_dtype;
 
@@ -103,6 +103,48 @@ gla_status gla_fwd(const gla_dims *dims, int dtype,
                    const float *log_alpha, const float *h0,
                    void *o, float *hT,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward path selection and tuning for gla_fwd_ex (zeros: automatic).  The
+ * paths compute the same function (papercache.org notes §4.2-4.3) and differ
+ * in where the chunk states live (notes §3.3 / Figure 1: materialised in
+ * memory, or kept on chip):
+ *   GLA_FWD_AUTO          the two-pass forward wherever it supports the shape
+ *                         (gla_fwd's choice), else the fused one, else the
+ *                         materialised one;
+ *   GLA_FWD_TWO_PASS      per-chunk prep pass over all chunks in parallel, then
+ *                         a recurrence pass with the state on chip;
+ *   GLA_FWD_FUSED         one pass per sequence segment with the state on chip
+ *                         (C = 64, dk in {64, 128, 256} (fp32: 64, 128),
+ *                         dv % 128 == 0);
+ *   GLA_FWD_MATERIALIZED  chunk states S_{n-1} written to the workspace, then
+ *                         one output pass over all chunks in parallel.
+ * recur_waves (1, 2 or 4 computing waves of 16 state columns per recurrence
+ * workgroup) and recur_segments (>= 1 sequence segments of the recurrence)
+ * apply to the two-pass forward only.  A path or setting the shape does not
+ * support gives GLA_ERR_SHAPE (no silent substitution). */
+typedef enum {
+  GLA_FWD_AUTO = 0,
+  GLA_FWD_TWO_PASS = 1,
+  GLA_FWD_FUSED = 2,
+  GLA_FWD_MATERIALIZED = 3
+} gla_fwd_algo;
+
+typedef struct {
+  int32_t algo;            /* gla_fwd_algo */
+  int32_t recur_waves;     /* 0 = automatic */
+  int32_t recur_segments;  /* 0 = automatic */
+} gla_fwd_config;
+
+/* gla_fwd with an explicit path and tuning; cfg == NULL is gla_fwd itself.
+ * The workspace depends on the configuration: size it with
+ * gla_fwd_ex_workspace_size for the same cfg. */
+gla_status gla_fwd_ex_workspace_size(const gla_dims *dims, int dtype, const gla_fwd_config *cfg,
+                                     size_t *bytes);
+gla_status gla_fwd_ex(const gla_dims *dims, int dtype, const gla_fwd_config *cfg,
+                      const void *q, const void *k, const void *v,
+                      const float *log_alpha, const float *h0,
+                      void *o, float *hT,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Backward of gla_fwd for the loss gradients dout = dL/do and dhT = dL/dhT
  * (NULL for zeros).  States are recomputed, not read from a forward call
@@ -178,12 +220,13 @@ gla_status ggla_bwd(const gla_dims *dims, int dtype,
                     float *dh0, void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- launch profiling (measurement support; not part of the computation) ----
- * While enabled, every kernel launch made by gla_fwd / gla_bwd is bracketed by
- * two HIP events recorded on the launch stream, so per-kernel GPU durations can
- * be read back after the caller synchronises.  Records beyond `capacity` are
- * dropped (and counted).  Enabling creates the events (host-side HIP calls);
- * it must not be done inside a captured stream.  Not thread-safe: one
- * profiling session per process at a time.
+ * While enabled, every kernel launch made by the entry points above is
+ * bracketed by two HIP events recorded on the launch stream, so per-kernel GPU
+ * durations can be read back after the caller synchronises.  Records beyond
+ * `capacity` are dropped.  Enabling creates the events (host-side HIP calls);
+ * it must not be done inside a captured stream.  The record table is guarded
+ * by a mutex, so launches from several threads may be profiled together (one
+ * table per process; a begin while others launch restarts it).
  *   gla_profile_begin : enable and clear; capacity >= 1 records.
  *                       GLA_ERR_SHAPE if capacity < 1, GLA_ERR_HIP if the
  *                       events cannot be created.
@@ -191,8 +234,9 @@ gla_status ggla_bwd(const gla_dims *dims, int dtype,
  *   gla_profile_count : number of records kept so far (dropped ones excluded).
  *   gla_profile_get   : name of the i-th record's kernel (static string) and its
  *                       duration in ms; GLA_ERR_SHAPE for a bad index,
- *                       GLA_ERR_NULL for NULL outputs, GLA_ERR_HIP if the
- *                       events have not completed (caller did not sync). */
+ *                       GLA_ERR_NULL for NULL outputs, GLA_ERR_HIP if one of
+ *                       its events could not be recorded or has not completed
+ *                       (caller did not sync). */
 gla_status gla_profile_begin(int capacity);
 void gla_profile_end(void);
 int gla_profile_count(void);

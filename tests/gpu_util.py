@@ -4,8 +4,10 @@ import numpy as np
 import torch
 
 import oracle
+from chunkwise_linear_rnn_gla_amd import GLA_BF16, GLA_FP32, GlaDims, GlaError, _abi
 from chunkwise_linear_rnn_gla_amd import bwd as gla_bwd_t
 from chunkwise_linear_rnn_gla_amd import fwd as gla_fwd_t
+from chunkwise_linear_rnn_gla_amd import fwd_config, gla_fwd_ex_workspace_size
 from chunkwise_linear_rnn_gla_amd.inputs import as_f64
 
 # Tolerances (relative L2 per output tensor): the required bar for fp32 I/O and
@@ -24,11 +26,38 @@ def dtype_name(x):
     return "bf16" if x.q.dtype == torch.bfloat16 else "fp32"
 
 
-def run_fwd(x, chunk=64, subchunk=16, dev="cuda"):
+# The kernel that marks each forward path in the launch records.
+PATH_KERNEL = {"two_pass": "chunk_prep", "fused": "seg_output", "materialized": "chunk_output"}
+
+
+def fwd_path_supported(x, chunk, algo, **cfg):
+    """Whether the library accepts `algo` (and cfg) for this shape: the
+    workspace query validates exactly as the call does."""
+    if algo == "auto" and not cfg:
+        return True
+    B, H, L, dk = x.q.shape
+    dims = GlaDims(B, H, L, dk, x.v.shape[-1], chunk, 16)
+    code = GLA_BF16 if x.q.dtype == torch.bfloat16 else GLA_FP32
+    try:
+        gla_fwd_ex_workspace_size(dims, code, fwd_config(algo, **cfg))
+    except GlaError as e:
+        if e.status == 2:
+            return False
+        raise
+    return True
+
+
+def run_fwd(x, chunk=64, subchunk=16, dev="cuda", algo="auto", **cfg):
+    """The forward through the C ABI; returns (o, hT, names of the launched
+    kernels)."""
     d = x.to(dev)
-    o, hT = gla_fwd_t(d.q, d.k, d.v, d.log_alpha, d.h0, chunk=chunk, subchunk=subchunk)
+    _abi.gla_profile_begin(64)
+    o, hT = gla_fwd_t(d.q, d.k, d.v, d.log_alpha, d.h0, chunk=chunk, subchunk=subchunk,
+                      algo=algo, **cfg)
     torch.cuda.synchronize()
-    return as_f64(o), as_f64(hT)
+    _abi.gla_profile_end()
+    names = [_abi.gla_profile_get(i)[0] for i in range(_abi.gla_profile_count())]
+    return as_f64(o), as_f64(hT), names
 
 
 def oracle_fwd(x):

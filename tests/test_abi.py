@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert _abi.gla_abi_version() == 1
+    assert _abi.gla_abi_version() == 2
     for s in range(7):
         assert _abi.status_string(s) and _abi.status_string(s) != "unknown status"
     assert _abi.status_string(99) == "unknown status"
@@ -172,3 +172,73 @@ def test_general_gate_errors():
     assert _abi.ggla_bwd(d, GLA_BF16, *bad, FAKE, n_bwd, None) == 1
     assert _abi.ggla_fwd(good_dims(B=0), GLA_BF16, *([None] * 8), None, 0, None) == 0
     assert _abi.ggla_bwd(good_dims(B=0), GLA_BF16, *([None] * 14), None, 0, None) == 0
+
+
+def cfg_status(d, dtype, algo, waves=0, segs=0):
+    n = ctypes.c_size_t(0)
+    c = _abi.GlaFwdConfig(algo, waves, segs)
+    return _abi.load().gla_fwd_ex_workspace_size(ctypes.byref(d), dtype, ctypes.byref(c),
+                                                 ctypes.byref(n)), n.value
+
+
+def test_forward_config_validation():
+    d = good_dims()
+    st_auto, n_auto = cfg_status(d, GLA_BF16, _abi.GLA_FWD_AUTO)
+    st_two, n_two = cfg_status(d, GLA_BF16, _abi.GLA_FWD_TWO_PASS)
+    st_mat, n_mat = cfg_status(d, GLA_BF16, _abi.GLA_FWD_MATERIALIZED)
+    st_fus, n_fus = cfg_status(d, GLA_BF16, _abi.GLA_FWD_FUSED)
+    assert st_auto == st_two == st_mat == st_fus == 0
+    # the automatic choice is the two-pass forward here, and gla_fwd's query
+    # agrees with gla_fwd_ex's for a NULL config
+    assert n_auto == n_two == _abi.gla_fwd_workspace_size(d, GLA_BF16)
+    n = ctypes.c_size_t(0)
+    assert _abi.load().gla_fwd_ex_workspace_size(ctypes.byref(d), GLA_BF16, None,
+                                                 ctypes.byref(n)) == 0 and n.value == n_auto
+    # the materialised states need more workspace than the two-pass records
+    assert n_mat > n_two > 0 and n_fus > 0
+    # requested paths and settings the shape does not support are refused
+    assert cfg_status(good_dims(dk=32), GLA_BF16, _abi.GLA_FWD_FUSED)[0] == 2   # fused: dk 64+
+    assert cfg_status(good_dims(chunk=32), GLA_BF16, _abi.GLA_FWD_FUSED)[0] == 2
+    assert cfg_status(d, GLA_BF16, 7)[0] == 2
+    assert cfg_status(d, GLA_BF16, -1)[0] == 2
+    assert cfg_status(d, GLA_BF16, _abi.GLA_FWD_TWO_PASS, waves=3)[0] == 2
+    assert cfg_status(good_dims(dk=256), GLA_BF16, _abi.GLA_FWD_TWO_PASS, waves=1)[0] == 2
+    assert cfg_status(d, GLA_BF16, _abi.GLA_FWD_MATERIALIZED, waves=2)[0] == 2
+    assert cfg_status(d, GLA_BF16, _abi.GLA_FWD_FUSED, segs=2)[0] == 2
+    assert cfg_status(d, GLA_BF16, _abi.GLA_FWD_TWO_PASS, segs=-1)[0] == 2
+    for w in (1, 2, 4):
+        assert cfg_status(d, GLA_BF16, _abi.GLA_FWD_TWO_PASS, waves=w)[0] == 0
+    # more recurrence segments need more workspace (segment states)
+    st1, n1 = cfg_status(d, GLA_BF16, _abi.GLA_FWD_TWO_PASS, segs=1)
+    st4, n4 = cfg_status(d, GLA_BF16, _abi.GLA_FWD_TWO_PASS, segs=4)
+    assert st1 == st4 == 0 and n4 > n1
+    # gla_fwd_ex validates like the query, before anything is launched
+    c = _abi.GlaFwdConfig(_abi.GLA_FWD_FUSED, 0, 0)
+    assert _abi.gla_fwd_ex(good_dims(dk=32), GLA_BF16, c, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                           None, FAKE, 1 << 40, None) == 2
+    assert _abi.gla_fwd_ex(d, GLA_BF16, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                           n_auto - 1, None) == 5
+
+
+def test_python_argument_checks_before_any_call():
+    """The binding rejects buffers the kernels would misuse (the C side sees
+    only pointers): wrong dtype, shape, layout or device of an output."""
+    import torch
+    from chunkwise_linear_rnn_gla_amd import _check, fwd_config
+    o = torch.empty(2, 3, 5, 8, dtype=torch.bfloat16)
+    _check(o, "out", torch.bfloat16, (2, 3, 5, 8), o.device, require_device=False)
+    with pytest.raises(TypeError):
+        _check(o, "out", torch.float32, (2, 3, 5, 8), o.device, require_device=False)
+    with pytest.raises(ValueError):
+        _check(o, "out", torch.bfloat16, (2, 3, 5, 16), o.device, require_device=False)
+    with pytest.raises(ValueError):
+        _check(o.transpose(2, 3), "out", torch.bfloat16, None, o.device, require_device=False)
+    with pytest.raises(ValueError):
+        _check(o, "out", torch.bfloat16, (2, 3, 5, 8), torch.device("meta"),
+               require_device=False)
+    with pytest.raises(ValueError):
+        _check(o, "out", torch.bfloat16, (2, 3, 5, 8))   # not a device tensor
+    with pytest.raises(ValueError):
+        fwd_config("bogus")
+    c = fwd_config("two_pass", recur_waves=2, recur_segments=3)
+    assert (c.algo, c.recur_waves, c.recur_segments) == (_abi.GLA_FWD_TWO_PASS, 2, 3)

@@ -1,35 +1,49 @@
 """GPU parity of the forward: the HIP path (through the C ABI) against the fp64
 oracle on the same seeded inputs, element by element (relative L2 per output
 tensor: <= 1e-5 for fp32 I/O, <= 5e-3 for bf16 I/O)."""
-import os
-
 import numpy as np
 import pytest
 import torch
 
 from chunkwise_linear_rnn_gla_amd.inputs import WORKLOADS, make_inputs, workload_inputs
-from gpu_util import TOL, dtype_name, oracle_fwd, rel_l2, run_fwd, say
+from gpu_util import (PATH_KERNEL, TOL, dtype_name, fwd_path_supported, oracle_fwd, rel_l2,
+                      run_fwd, say)
 
 pytestmark = pytest.mark.gpu
 
+# The forward path of the running test (set by the autouse fixture below).
+_PATH = {"algo": "auto"}
+
 
 @pytest.fixture(params=["auto", "fused", "materialized"], autouse=True)
-def forward_path(request, monkeypatch):
-    """Run every forward case through each forward path: the default (the
-    two-pass chunk prep + recurrence wherever it applies), the single-pass
-    fused segment kernel (GLA_FORWARD=fused, where it applies) and the
-    materialised-state kernels (GLA_FORWARD=materialized)."""
-    if request.param == "auto":
-        monkeypatch.delenv("GLA_FORWARD", raising=False)
-    else:
-        monkeypatch.setenv("GLA_FORWARD", request.param)
-    return request.param
+def forward_path(request):
+    """Run every forward case through each forward path, requested explicitly
+    through gla_fwd_ex: the default (the two-pass chunk prep + recurrence
+    wherever it applies), the single-pass fused segment kernel and the
+    materialised-state kernels.  A case whose shape a path does not support
+    is skipped for that path (the library refuses it rather than running
+    another one)."""
+    _PATH["algo"] = request.param
+    yield request.param
+    _PATH["algo"] = "auto"
 
 
-def check_fwd(x, chunk, tag=""):
+def skip_unsupported(x, chunk, **cfg):
+    algo = _PATH["algo"]
+    if not fwd_path_supported(x, chunk, algo, **cfg):
+        pytest.skip(f"the {algo} forward does not support dk={x.q.shape[-1]} "
+                    f"dv={x.v.shape[-1]} C={chunk} {dtype_name(x)} {cfg or ''}")
+    return algo
+
+
+def check_fwd(x, chunk, tag="", **cfg):
     dt = dtype_name(x)
-    say(f"[fwd] {tag} dtype={dt} shape={tuple(x.q.shape)} dv={x.v.shape[-1]} C={chunk}")
-    o, hT = run_fwd(x, chunk)
+    algo = skip_unsupported(x, chunk, **cfg)
+    say(f"[fwd] {tag} path={algo} dtype={dt} shape={tuple(x.q.shape)} dv={x.v.shape[-1]} "
+        f"C={chunk} {cfg or ''}")
+    o, hT, names = run_fwd(x, chunk, algo=algo, **cfg)
+    if algo in PATH_KERNEL and x.q.shape[2] > 0 and x.q.shape[0] * x.q.shape[1] > 0:
+        assert PATH_KERNEL[algo] in names, (algo, names)
     ro, rh = oracle_fwd(x)
     eo, eh = rel_l2(o, ro), rel_l2(hT, rh)
     say(f"      rel_l2 o={eo:.3e} hT={eh:.3e}")
@@ -91,12 +105,13 @@ def test_fused_segments(dt, dk, dv, L):
 
 @pytest.mark.parametrize("waves", [1, 2, 4])
 @pytest.mark.parametrize("dt,dk", [("fp32", 64), ("bf16", 128)])
-def test_recurrence_workgroup_shapes(waves, dt, dk, monkeypatch):
+def test_recurrence_workgroup_shapes(waves, dt, dk, forward_path):
     # 32 (batch, head) pairs: one segment per sequence, 16 state columns per
-    # wave and 1, 2 or 4 waves per workgroup
-    monkeypatch.setenv("GLA_RECUR_WAVES", str(waves))
+    # wave and 1, 2 or 4 waves per workgroup (a two-pass setting)
+    if forward_path != "auto":
+        pytest.skip("recurrence workgroup shapes are a setting of the two-pass forward")
     x = make_inputs(4, 8, 300, dk, 128, dt, seed=320 + waves + dk, h0_std=0.3)
-    check_fwd(x, 64, f"recur-waves{waves}")
+    check_fwd(x, 64, f"recur-waves{waves}", recur_waves=waves)
 
 
 def test_single_chunk_and_single_token():
@@ -107,24 +122,25 @@ def test_single_chunk_and_single_token():
 
 def test_empty_sequence_copies_h0():
     x = make_inputs(2, 2, 0, 32, 64, "fp32", seed=307, h0_std=1.0)
-    o, hT = run_fwd(x, 64)
+    o, hT, _ = run_fwd(x, 64, algo=skip_unsupported(x, 64))
     assert o.shape == (2, 2, 0, 64)
     assert np.array_equal(hT, x.h0.double().numpy())
     x = make_inputs(1, 1, 0, 32, 64, "bf16", seed=308)
-    _, hT = run_fwd(x, 64)
+    _, hT, _ = run_fwd(x, 64, algo=skip_unsupported(x, 64))
     assert not hT.any()
 
 
 def test_zero_batch():
     x = make_inputs(0, 2, 64, 32, 64, "bf16", seed=309)
-    o, hT = run_fwd(x, 64)
+    o, hT, _ = run_fwd(x, 64, algo=skip_unsupported(x, 64))
     assert o.shape == (0, 2, 64, 64) and hT.shape == (0, 2, 32, 64)
 
 
 def test_deterministic():
     x = make_inputs(2, 2, 256, 64, 128, "bf16", seed=310, h0_std=0.2)
-    a = run_fwd(x, 64)
-    b = run_fwd(x, 64)
+    algo = skip_unsupported(x, 64)
+    a = run_fwd(x, 64, algo=algo)
+    b = run_fwd(x, 64, algo=algo)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
@@ -133,3 +149,15 @@ def test_deterministic():
 def test_full_size_workloads(name):
     w = WORKLOADS[name]
     check_fwd(workload_inputs(w), w.chunk, name)
+
+
+def test_wrong_out_buffer_is_rejected():
+    # a caller-supplied output of the wrong dtype or shape never reaches the
+    # kernels (they would write past it)
+    from chunkwise_linear_rnn_gla_amd import fwd
+    d = make_inputs(1, 2, 64, 32, 64, "bf16", seed=312).to("cuda")
+    with pytest.raises(TypeError):
+        fwd(d.q, d.k, d.v, d.log_alpha, out=torch.empty(1, 2, 64, 64, device="cuda"))
+    with pytest.raises(ValueError):
+        fwd(d.q, d.k, d.v, d.log_alpha,
+            out=torch.empty(1, 2, 32, 64, dtype=torch.bfloat16, device="cuda"))
