@@ -20,7 +20,7 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_NULL", 2: "GLA_ERR_SHAPE", 3: "GLA_ERR_DTYPE"
 # Every symbol include/gla.h declares.
 EXPORTS = ("gla_abi_version", "gla_status_string", "gla_fwd_workspace_size",
            "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_fwd_ex_workspace_size",
-           "gla_fwd_ex", "gla_decode", "ggla_fwd_workspace_size",
+           "gla_fwd_ex", "gla_fwd_noalloc", "gla_decode", "ggla_fwd_workspace_size",
            "ggla_bwd_workspace_size", "ggla_fwd", "ggla_bwd", "gla_profile_begin",
            "gla_profile_end", "gla_profile_count", "gla_profile_get")
 
@@ -78,6 +78,8 @@ def load():
     lib.gla_fwd_ex_workspace_size.restype = i32
     lib.gla_fwd_ex.argtypes = [dims_p, i32, cfg_p] + [vp] * 7 + [vp, sz, vp]
     lib.gla_fwd_ex.restype = i32
+    lib.gla_fwd_noalloc.argtypes = [dims_p, i32] + [vp] * 7 + [vp]
+    lib.gla_fwd_noalloc.restype = i32
     lib.gla_decode.argtypes = [dims_p, i32] + [vp] * 6 + [vp]
     lib.gla_decode.restype = i32
     for f in (lib.ggla_fwd_workspace_size, lib.ggla_bwd_workspace_size):
@@ -159,6 +161,13 @@ def gla_fwd_ex(dims, dtype, cfg, q, k, v, log_alpha, h0, o, hT, workspace, works
     return load().gla_fwd_ex(ctypes.byref(dims), dtype, _cfg(cfg), _ptr(q), _ptr(k), _ptr(v),
                              _ptr(log_alpha), _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
                              workspace_bytes, stream)
+
+
+def gla_fwd_noalloc(dims, dtype, q, k, v, log_alpha, h0, o, hT, stream):
+    """Raw call of the allocation-free forward (scratch in the library's
+    static device array); returns the status."""
+    return load().gla_fwd_noalloc(ctypes.byref(dims), dtype, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(log_alpha), _ptr(h0), _ptr(o), _ptr(hT), stream)
 
 
 def gla_bwd(dims, dtype, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv, dlog_alpha, dh0,

@@ -241,6 +241,64 @@ void prof_after(hipStream_t s) {
     prof_after(s);                                   \
   } while (0)
 
+// The two-pass forward on workspace ws (the chunk records of pass 1, and the
+// segment states when the recurrence is split into sequence segments).
+static gla_status run_two_pass(const Plan& p, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* h0, void* o, float* hT,
+                               char* ws, hipStream_t s) {
+  // pass 1: per-chunk operands and score matrices; pass 2: the recurrence
+  // (segment local states and a scan over segments first when segmented)
+  void* qg = ws + p.off_qg;
+  void* kg = ws + p.off_kg;
+  void* ph = ws + p.off_ph;
+  void* pl = ws + p.off_pl;
+  float* gl = (float*)(ws + p.off_gl);
+  float* ru = (float*)(ws + p.off_ru);
+  float* ri = (float*)(ws + p.off_ri);
+  float* rg = (float*)(ws + p.off_rg);
+  GLA_LAUNCH("chunk_prep", launch_chunk_prep(p, q, k, log_alpha, v, qg, kg, gl, ph, pl, s));
+  if (p.NSEGR > 1) {
+    GLA_LAUNCH("recur_local", launch_chunk_recur(p, 0, qg, kg, ph, pl, gl, v, nullptr, nullptr, ru, rg, s));
+    Plan ps = p;
+    ps.NSEG = p.NSEGR;
+    GLA_LAUNCH("segment_scan", launch_segment_scan(ps, 0, rg, h0, ru, ri, hT, s));
+    GLA_LAUNCH("chunk_recur", launch_chunk_recur(p, 1, qg, kg, ph, pl, gl, v, ri, o, nullptr, nullptr, s));
+  } else {
+    GLA_LAUNCH("chunk_recur", launch_chunk_recur(p, 1, qg, kg, ph, pl, gl, v, h0, o, hT, nullptr, s));
+  }
+  return GLA_OK;
+}
+
+// ---- scratch of the allocation-free forward (gla_fwd_noalloc)
+// The two-pass forward's records live in this array of the library instead
+// of a caller's workspace.  Each GPU the library runs on holds its own copy
+// (GLA_NOALLOC_SCRATCH_BYTES, as .bss of the code object) until the process
+// ends.  On the host, `scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device with that device
+// current (hipGetSymbolAddress), and only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[GLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch copy (looked up on the
+// first call on that device).
+gla_status scratch_address(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GLA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GLA_ERR_HIP;
+    g_scratch_addr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return GLA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int gla_abi_version(void) { return GLA_ABI_VERSION; }
@@ -313,29 +371,7 @@ gla_status gla_fwd_ex(const gla_dims* dims, int dtype, const gla_fwd_config* cfg
   float* seg_u = (float*)(ws + p.off_seg_u);
   float* seg_in = (float*)(ws + p.off_seg_in);
 
-  if (p.recur) {
-    // pass 1: per-chunk operands and score matrices; pass 2: the recurrence
-    // (segment local states and a scan over segments first when segmented)
-    void* qg = ws + p.off_qg;
-    void* kg = ws + p.off_kg;
-    void* ph = ws + p.off_ph;
-    void* pl = ws + p.off_pl;
-    float* gl = (float*)(ws + p.off_gl);
-    float* ru = (float*)(ws + p.off_ru);
-    float* ri = (float*)(ws + p.off_ri);
-    float* rg = (float*)(ws + p.off_rg);
-    GLA_LAUNCH("chunk_prep", launch_chunk_prep(p, q, k, log_alpha, v, qg, kg, gl, ph, pl, s));
-    if (p.NSEGR > 1) {
-      GLA_LAUNCH("recur_local", launch_chunk_recur(p, 0, qg, kg, ph, pl, gl, v, nullptr, nullptr, ru, rg, s));
-      Plan ps = p;
-      ps.NSEG = p.NSEGR;
-      GLA_LAUNCH("segment_scan", launch_segment_scan(ps, 0, rg, h0, ru, ri, hT, s));
-      GLA_LAUNCH("chunk_recur", launch_chunk_recur(p, 1, qg, kg, ph, pl, gl, v, ri, o, nullptr, nullptr, s));
-    } else {
-      GLA_LAUNCH("chunk_recur", launch_chunk_recur(p, 1, qg, kg, ph, pl, gl, v, h0, o, hT, nullptr, s));
-    }
-    return GLA_OK;
-  }
+  if (p.recur) return run_two_pass(p, q, k, v, log_alpha, h0, o, hT, ws, s);
   GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
   if (p.fused) {
     // segment entry states from the segments' local states, then one fused
@@ -361,6 +397,27 @@ gla_status gla_fwd_ex(const gla_dims* dims, int dtype, const gla_fwd_config* cfg
   }
   GLA_LAUNCH("chunk_output", launch_chunk_output(p, q, k, v, cum, states, o, s));
   return GLA_OK;
+}
+
+gla_status gla_fwd_noalloc(const gla_dims* dims, int dtype, const void* q, const void* k,
+                           const void* v, const float* log_alpha, const float* h0, void* o,
+                           float* hT, void* stream) {
+  const gla_fwd_config cfg{GLA_FWD_TWO_PASS, 0, 0};
+  Plan p;
+  gla_status st = validate(dims, dtype, &p, &cfg);
+  if (st != GLA_OK) return st;
+  if (p.ws_fwd > (size_t)GLA_NOALLOC_SCRATCH_BYTES) return GLA_ERR_WORKSPACE;
+  if (p.BH == 0) return GLA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.L == 0) {
+    if ((st = check_ptrs({}, {h0, hT})) != GLA_OK) return st;
+    if (hT) GLA_LAUNCH("copy_state", launch_copy_state(p, h0, hT, s));
+    return GLA_OK;
+  }
+  if ((st = check_ptrs({q, k, v, log_alpha, o}, {h0, hT})) != GLA_OK) return st;
+  char* ws = nullptr;
+  if ((st = scratch_address(&ws)) != GLA_OK) return st;
+  return run_two_pass(p, q, k, v, log_alpha, h0, o, hT, ws, s);
 }
 
 gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k, const void* v,

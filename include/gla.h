@@ -146,6 +146,34 @@ gla_status gla_fwd_ex(const gla_dims *dims, int dtype, const gla_fwd_config *cfg
                       void *o, float *hT,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- allocation-free forward ----
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): gla_fwd's
+ * two-pass path (GLA_FWD_TWO_PASS) with its scratch, the per-chunk records of
+ * the prep pass (and the recurrence's segment states), in a static device
+ * array of the library instead of a workspace argument.  The array holds
+ * GLA_NOALLOC_SCRATCH_BYTES; each GPU the library runs on keeps its own copy
+ * until the process ends.  The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine); on its first call on a device it looks up
+ * that device's copy (hipGetSymbolAddress).
+ *   Arguments, layouts, results and errors as gla_fwd, on the current device
+ *   (the stream must belong to it).  Shapes outside the two-pass forward's
+ *   (gla_fwd_ex_workspace_size with GLA_FWD_TWO_PASS refuses them) give
+ *   GLA_ERR_SHAPE; shapes whose records exceed the array
+ *   (gla_fwd_ex_workspace_size with GLA_FWD_TWO_PASS > GLA_NOALLOC_SCRATCH_BYTES;
+ *   the GLA-340M layer shape B8 H4 L2048 dk128 dv256 bf16 needs 41 MiB, twice
+ *   that batch 82 MiB) give GLA_ERR_WORKSPACE, both before anything is
+ *   enqueued.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (different streams or threads, without ordering between them) race
+ *   and give wrong results.  The kernels need no particular initial contents,
+ *   so nothing is cleared between calls. */
+#define GLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+gla_status gla_fwd_noalloc(const gla_dims *dims, int dtype,
+                           const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *h0,
+                           void *o, float *hT, void *stream);
+
 /* Backward of gla_fwd for the loss gradients dout = dL/do and dhT = dL/dhT
  * (NULL for zeros).  States are recomputed, not read from a forward call
  * (zako-mio report ch. 2.2: materialise in the forward, recompute in the

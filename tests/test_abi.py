@@ -242,3 +242,22 @@ def test_python_argument_checks_before_any_call():
         fwd_config("bogus")
     c = fwd_config("two_pass", recur_waves=2, recur_segments=3)
     assert (c.algo, c.recur_waves, c.recur_segments) == (_abi.GLA_FWD_TWO_PASS, 2, 3)
+
+
+def test_noalloc_forward_rejects_before_any_device_call():
+    # sizes are validated before the entry point touches the device: shapes
+    # outside the two-pass forward, and records beyond the static scratch
+    text = open(HEADER).read()
+    limit = int(re.search(r"#define GLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+                .group(1)) << int(re.search(r"<< (\d+)\)", text).group(1))
+    big = good_dims(B=16)
+    assert _abi.gla_fwd_ex_workspace_size(big, GLA_BF16, _abi.GlaFwdConfig(1, 0, 0)) > limit
+    assert _abi.gla_fwd_ex_workspace_size(good_dims(B=8), GLA_BF16,
+                                          _abi.GlaFwdConfig(1, 0, 0)) <= limit
+    assert _abi.gla_fwd_noalloc(big, GLA_BF16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                None) == 5
+    assert _abi.gla_fwd_noalloc(good_dims(dk=256), GLA_FP32, FAKE, FAKE, FAKE, FAKE, None,
+                                FAKE, None, None) == 2
+    assert _abi.gla_fwd_noalloc(good_dims(), 9, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                None) == 3
+    assert _abi.load().gla_fwd_noalloc(None, GLA_BF16, *([FAKE] * 7), None) == 1
