@@ -116,18 +116,20 @@ def measured_traffic(kernel, workload):
 def recur_plan(w, nc):
     """(waves per workgroup, sequence segments) of the two-pass forward's
     recurrence as the library plans them: 16 state columns per wave, the
-    largest workgroup that still gives 256 workgroups, segments only when
-    fewer than 128 workgroups remain."""
+    largest workgroup that still gives 256 workgroups, or, when even one-wave
+    workgroups give fewer than 128, the largest workgroup and enough sequence
+    segments to fill the chip."""
     bf16 = w.dtype == "bf16"
     wmin = 2 if (w.dk >= 256 if bf16 else w.dk >= 128) else 1
     wmax = 2 if (bf16 and w.dk >= 256) else 4
     bh = w.B * w.H
+    starved = bh * (w.dv // (16 * wmin)) < 128
     nwv = wmin
     for cand in (4, 2, 1):
         if cand < wmin or cand > wmax or w.dv % (16 * cand):
             continue
         nwv = cand
-        if bh * (w.dv // (16 * cand)) >= 256:
+        if starved or bh * (w.dv // (16 * cand)) >= 256:
             break
     units = bh * (w.dv // (16 * nwv))
     nseg = 1

@@ -10,14 +10,15 @@ library; ``_abi`` exposes the raw C entry points under their C names.
 from __future__ import annotations
 
 from . import _abi
-from ._abi import (FWD_ALGOS, GLA_BF16, GLA_FP32, GlaDims, GlaError,  # noqa: F401
-                   GlaFwdConfig, ggla_bwd, ggla_bwd_workspace_size, ggla_fwd,
-                   ggla_fwd_workspace_size, gla_abi_version, gla_bwd, gla_bwd_workspace_size,
-                   gla_decode, gla_fwd, gla_fwd_ex, gla_fwd_ex_workspace_size,
-                   gla_fwd_workspace_size, gla_status_string)
+from ._abi import (BWD_ALGOS, FWD_ALGOS, GLA_BF16, GLA_FP32, GlaBwdConfig,  # noqa: F401
+                   GlaDims, GlaError, GlaFwdConfig, ggla_bwd, ggla_bwd_workspace_size, ggla_fwd,
+                   ggla_fwd_workspace_size, gla_abi_version, gla_bwd, gla_bwd_ex,
+                   gla_bwd_ex_workspace_size, gla_bwd_workspace_size, gla_decode, gla_fwd,
+                   gla_fwd_ex, gla_fwd_ex_workspace_size, gla_fwd_workspace_size,
+                   gla_status_string)
 
 __all__ = ["fwd", "bwd", "decode", "fwd_general", "bwd_general", "dims_for", "fwd_config",
-           "gla_fwd", "gla_fwd_ex", "gla_bwd", "gla_decode", "ggla_fwd", "ggla_bwd",
+           "bwd_config", "gla_fwd", "gla_fwd_ex", "gla_bwd", "gla_bwd_ex", "gla_decode", "ggla_fwd", "ggla_bwd",
            "ggla_fwd_workspace_size", "ggla_bwd_workspace_size", "gla_fwd_workspace_size",
            "gla_fwd_ex_workspace_size", "gla_bwd_workspace_size", "gla_abi_version",
            "gla_status_string", "GlaDims", "GlaFwdConfig", "GlaError", "GLA_FP32", "GLA_BF16"]
@@ -72,6 +73,13 @@ def _stream(device):
     return _torch().cuda.current_stream(device).cuda_stream
 
 
+def bwd_config(algo="auto"):
+    """A GlaBwdConfig for gla_bwd_ex: algo in "auto", "materialized", "recurrent"."""
+    if algo not in BWD_ALGOS:
+        raise ValueError(f"unknown backward algo {algo!r}; one of {sorted(BWD_ALGOS)}")
+    return GlaBwdConfig(BWD_ALGOS[algo])
+
+
 def fwd(q, k, v, log_alpha, h0=None, chunk=64, subchunk=16, final_state=True, workspace=None,
         out=None, algo="auto", recur_waves=0, recur_segments=0):
     """GLA forward.  q, k [B,H,L,dk], v [B,H,L,dv] (fp32 or bf16), log_alpha
@@ -106,8 +114,9 @@ def fwd(q, k, v, log_alpha, h0=None, chunk=64, subchunk=16, final_state=True, wo
 
 
 def bwd(q, k, v, log_alpha, h0, dout, dhT=None, chunk=64, subchunk=16, want_dh0=True,
-        workspace=None):
-    """GLA backward.  Returns (dq, dk, dv, dlog_alpha, dh0 or None)."""
+        workspace=None, algo="auto"):
+    """GLA backward.  algo selects the path (see bwd_config; the default is
+    gla_bwd's automatic choice).  Returns (dq, dk, dv, dlog_alpha, dh0 or None)."""
     torch = _torch()
     B, H, L, dk = q.shape
     dv = v.shape[-1]
@@ -127,13 +136,14 @@ def bwd(q, k, v, log_alpha, h0, dout, dhT=None, chunk=64, subchunk=16, want_dh0=
     dvv = torch.empty_like(v)
     dla = torch.empty_like(log_alpha)
     dh0 = torch.empty(B, H, dk, dv, dtype=torch.float32, device=q.device) if want_dh0 else None
-    n = gla_bwd_workspace_size(dims, code)
+    cfg = bwd_config(algo)
+    n = gla_bwd_ex_workspace_size(dims, code, cfg)
     if workspace is None or workspace.numel() < n:
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
-    st = gla_bwd(dims, code, q, k, v, log_alpha, h0, dout, dhT, dq, dkk, dvv, dla, dh0,
-                 workspace, workspace.numel(), _stream(q.device))
+    st = gla_bwd_ex(dims, code, cfg, q, k, v, log_alpha, h0, dout, dhT, dq, dkk, dvv, dla, dh0,
+                    workspace, workspace.numel(), _stream(q.device))
     if st != 0:
-        raise GlaError(st, "gla_bwd")
+        raise GlaError(st, "gla_bwd_ex")
     return dq, dkk, dvv, dla, dh0
 
 

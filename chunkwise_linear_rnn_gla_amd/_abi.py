@@ -20,7 +20,8 @@ STATUS = {0: "GLA_OK", 1: "GLA_ERR_NULL", 2: "GLA_ERR_SHAPE", 3: "GLA_ERR_DTYPE"
 # Every symbol include/gla.h declares.
 EXPORTS = ("gla_abi_version", "gla_status_string", "gla_fwd_workspace_size",
            "gla_bwd_workspace_size", "gla_fwd", "gla_bwd", "gla_fwd_ex_workspace_size",
-           "gla_fwd_ex", "gla_fwd_noalloc", "gla_decode", "ggla_fwd_workspace_size",
+           "gla_fwd_ex", "gla_fwd_noalloc", "gla_bwd_ex_workspace_size", "gla_bwd_ex",
+           "gla_decode", "ggla_fwd_workspace_size",
            "ggla_bwd_workspace_size", "ggla_fwd", "ggla_bwd", "gla_profile_begin",
            "gla_profile_end", "gla_profile_count", "gla_profile_get")
 
@@ -40,6 +41,16 @@ FWD_ALGOS = {"auto": GLA_FWD_AUTO, "two_pass": GLA_FWD_TWO_PASS, "fused": GLA_FW
 class GlaFwdConfig(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int32), ("recur_waves", ctypes.c_int32),
                 ("recur_segments", ctypes.c_int32)]
+
+
+# gla_bwd_algo
+GLA_BWD_AUTO, GLA_BWD_MATERIALIZED, GLA_BWD_RECURRENT = 0, 1, 2
+BWD_ALGOS = {"auto": GLA_BWD_AUTO, "materialized": GLA_BWD_MATERIALIZED,
+             "recurrent": GLA_BWD_RECURRENT}
+
+
+class GlaBwdConfig(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32)]
 
 
 class GlaError(RuntimeError):
@@ -78,6 +89,11 @@ def load():
     lib.gla_fwd_ex_workspace_size.restype = i32
     lib.gla_fwd_ex.argtypes = [dims_p, i32, cfg_p] + [vp] * 7 + [vp, sz, vp]
     lib.gla_fwd_ex.restype = i32
+    bcfg_p = ctypes.POINTER(GlaBwdConfig)
+    lib.gla_bwd_ex_workspace_size.argtypes = [dims_p, i32, bcfg_p, ctypes.POINTER(sz)]
+    lib.gla_bwd_ex_workspace_size.restype = i32
+    lib.gla_bwd_ex.argtypes = [dims_p, i32, bcfg_p] + [vp] * 12 + [vp, sz, vp]
+    lib.gla_bwd_ex.restype = i32
     lib.gla_fwd_noalloc.argtypes = [dims_p, i32] + [vp] * 7 + [vp]
     lib.gla_fwd_noalloc.restype = i32
     lib.gla_decode.argtypes = [dims_p, i32] + [vp] * 6 + [vp]
@@ -160,6 +176,23 @@ def gla_fwd_ex(dims, dtype, cfg, q, k, v, log_alpha, h0, o, hT, workspace, works
     """Raw call with a GlaFwdConfig (or None); returns the status."""
     return load().gla_fwd_ex(ctypes.byref(dims), dtype, _cfg(cfg), _ptr(q), _ptr(k), _ptr(v),
                              _ptr(log_alpha), _ptr(h0), _ptr(o), _ptr(hT), _ptr(workspace),
+                             workspace_bytes, stream)
+
+
+def gla_bwd_ex_workspace_size(dims: GlaDims, dtype: int, cfg) -> int:
+    n = ctypes.c_size_t(0)
+    st = load().gla_bwd_ex_workspace_size(ctypes.byref(dims), dtype, _cfg(cfg), ctypes.byref(n))
+    if st != 0:
+        raise GlaError(st, "gla_bwd_ex_workspace_size")
+    return n.value
+
+
+def gla_bwd_ex(dims, dtype, cfg, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv, dlog_alpha, dh0,
+               workspace, workspace_bytes, stream):
+    """Raw call with a GlaBwdConfig (or None); returns the status."""
+    return load().gla_bwd_ex(ctypes.byref(dims), dtype, _cfg(cfg), _ptr(q), _ptr(k), _ptr(v),
+                             _ptr(log_alpha), _ptr(h0), _ptr(dout), _ptr(dhT), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(dlog_alpha), _ptr(dh0), _ptr(workspace),
                              workspace_bytes, stream)
 
 

@@ -39,6 +39,8 @@ EXTRA_FLAGS = {
     # the general gate's recurrence rescales and converts its state every
     # chunk: in accumulator registers each such access costs a move
     "gla_ggate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the backward's state recurrences: accumulators read as operands every chunk
+    "gla_bwd_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -28,6 +28,7 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   if (dk < 16 || dk > 256 || dv < 16 || dv > 512) return false;
   if ((int64_t)B * H > (1 << 20) || L > (1 << 24)) return false;
   if (opt.algo < FWD_AUTO || opt.algo > FWD_MATERIALIZED) return false;
+  if (opt.bwd_algo < BWD_AUTO || opt.bwd_algo > BWD_RECURRENT) return false;
   if (opt.recur_waves < 0 || opt.recur_segments < 0) return false;
   Plan& P = *p;
   P.B = B; P.H = H; P.L = L; P.dk = dk; P.dv = dv; P.C = C; P.c = c; P.bf16 = bf16;
@@ -90,12 +91,19 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   // workgroup leaves the chip mostly idle.  Explicit wave and segment counts
   // apply to the two-pass forward only.
   if (!P.recur && (opt.recur_waves || opt.recur_segments)) return false;
+  // When even the narrowest workgroups leave the chip under-filled, the
+  // sequence is split into segments anyway: then the widest workgroup is
+  // best, since every workgroup of a (batch, head) streams all of its chunk
+  // records (16 segments of four-wave workgroups run the long-sequence
+  // workload, B1 H4 L16384, in 85 us against 119 us for 4 segments of
+  // one-wave workgroups).
   const int wmin = recur_min_waves(bf16, dk), wmax = recur_max_waves(bf16, dk);
+  const bool starved = (int64_t)P.BH * (dv / (16 * wmin)) < 128;
   P.NWVR = wmin;
   for (int w = wmax; w >= wmin; w /= 2) {
     if (dv % (16 * w)) continue;
     P.NWVR = w;
-    if ((int64_t)P.BH * (dv / (16 * w)) >= 256) break;
+    if (starved || (int64_t)P.BH * (dv / (16 * w)) >= 256) break;
   }
   if (opt.recur_waves) {
     const int w = opt.recur_waves;
@@ -158,7 +166,24 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   // low halves of the recomputed states and state gradients (bf16 split)
   P.off_stlo = off; off = align_up(off + (bf16 ? BH * P.NC * S * 2 : 0));
   P.off_dstlo = off; off = align_up(off + (bf16 ? BH * P.NC * S * 2 : 0));
-  P.ws_bwd = off;
+  const size_t ws_bwd_mat = off;
+  // the backward with the states on chip, where its kernels exist for the
+  // shape (the dv pass reuses the two-pass forward's kernels and plan)
+  const bool can_rec = bwd_inter_supported(bf16, C, dk, dv, L) && recur_supported(bf16, C, dk, dv, L);
+  if (opt.bwd_algo == BWD_RECURRENT && !can_rec) return false;
+  P.bwd_rec = opt.bwd_algo == BWD_RECURRENT || (opt.bwd_algo == BWD_AUTO && can_rec);
+  {
+    const size_t LD = BH * (size_t)L * dk * 4;
+    size_t f = 0;
+    P.off_bcum = f; f = align_up(f + LD);
+    P.off_bdA = f; f = align_up(f + BH * P.NC * C * C * 4);
+    P.off_bdqi = f; f = align_up(f + LD);
+    P.off_bdki = f; f = align_up(f + LD);
+    P.off_bdlt = f; f = align_up(f + BH * P.NC * dk * 4);
+    P.off_brs = f; f = align_up(f + BH * dk * 4);
+    P.off_bvrec = f; f = align_up(f + P.ws_recur);
+    P.ws_bwd = P.bwd_rec ? f : ws_bwd_mat;
+  }
   return true;
 }
 
@@ -168,22 +193,24 @@ using namespace gla;
 
 static bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15) != 0; }
 
-static FwdOptions fwd_options(const gla_fwd_config* cfg) {
+static FwdOptions options(const gla_fwd_config* cfg, const gla_bwd_config* bcfg) {
   FwdOptions o;
   if (cfg) {
     o.algo = cfg->algo;
     o.recur_waves = cfg->recur_waves;
     o.recur_segments = cfg->recur_segments;
   }
+  if (bcfg) o.bwd_algo = bcfg->algo;
   return o;
 }
 
 static gla_status validate(const gla_dims* d, int dtype, Plan* p,
-                           const gla_fwd_config* cfg = nullptr) {
+                           const gla_fwd_config* cfg = nullptr,
+                           const gla_bwd_config* bcfg = nullptr) {
   if (!d) return GLA_ERR_NULL;
   if (dtype != GLA_FP32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
   if (!make_plan(d->B, d->H, d->L, d->dk, d->dv, d->chunk, d->subchunk, dtype == GLA_BF16, p,
-                 fwd_options(cfg)))
+                 options(cfg, bcfg)))
     return GLA_ERR_SHAPE;
   return GLA_OK;
 }
@@ -269,6 +296,60 @@ static gla_status run_two_pass(const Plan& p, const void* q, const void* k, cons
   return GLA_OK;
 }
 
+// The backward with the states kept on chip (bf16, C = 64):
+//  * the chunk-local cumsum B of log alpha and dA = (dO V^T) masked, per chunk;
+//  * one launch of two recurrences over the chunks with the transposed state
+//    (k_bwd_inter): the inter-chunk terms of dq (S, chunks in order) and of dk
+//    (dS, chunks backwards), rowsum(hT ⊙ dhT) and dh0;
+//  * the intra-chunk terms of dq and dk added per chunk, with the closed-form
+//    dlog b = q ⊙ dq - k ⊙ dk and its reverse cumsum inside the chunk, then
+//    the carry over later chunks (zako-mio report ch. 3.4);
+//  * dv: the gradient of v is the forward of the time-reversed sequence with
+//    queries k, keys q, values dout, the gates shifted by one token and dhT
+//    as the initial state, so the two-pass forward's kernels compute it in
+//    their reversed mode.
+static gla_status run_bwd_recurrent(const Plan& p, const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const float* h0, const void* dout,
+                                    const float* dhT, void* dq, void* dk, void* dv,
+                                    float* dlog_alpha, float* dh0, char* ws, hipStream_t s) {
+  float* cum = (float*)(ws + p.off_bcum);
+  float* dA = (float*)(ws + p.off_bdA);
+  float* dqi = (float*)(ws + p.off_bdqi);
+  float* dki = (float*)(ws + p.off_bdki);
+  float* dlt = (float*)(ws + p.off_bdlt);
+  float* rs = (float*)(ws + p.off_brs);
+  char* vr = ws + p.off_bvrec;
+  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
+  GLA_LAUNCH("chunk_attn", launch_chunk_attn(p, q, k, v, dout, cum, nullptr, dA, s));
+  const BwdInterJob jq{dout, v, k, h0, dqi, rs, dhT, nullptr, 0};
+  const BwdInterJob jk{v, dout, q, dhT, dki, nullptr, nullptr, dh0, 1};
+  GLA_LAUNCH("bwd_inter", launch_bwd_inter(p, jq, jk, cum, s));
+  GLA_LAUNCH("chunk_dqdk", launch_chunk_dqdk_inter(p, q, k, cum, dA, dqi, dki, dq, dk,
+                                                   dlog_alpha, dlt, s));
+  GLA_LAUNCH("dla_carry", launch_dla_carry(p, dlt, rs, dlog_alpha, s));
+  // dv: the forward's passes over the reversed sequence (q <- k, k <- q,
+  // v <- dout, h0 <- dhT); its final state is not needed (dh0 came above)
+  void* qg = vr + p.off_qg;
+  void* kg = vr + p.off_kg;
+  void* ph = vr + p.off_ph;
+  void* pl = vr + p.off_pl;
+  float* gl = (float*)(vr + p.off_gl);
+  GLA_LAUNCH("chunk_prep_rev", launch_chunk_prep_rev(p, k, q, log_alpha, dout, qg, kg, gl, ph, pl, s));
+  if (p.NSEGR > 1) {
+    float* ru = (float*)(vr + p.off_ru);
+    float* ri = (float*)(vr + p.off_ri);
+    float* rg = (float*)(vr + p.off_rg);
+    GLA_LAUNCH("recur_local_rev", launch_chunk_recur_rev(p, 0, qg, kg, ph, pl, gl, dout, nullptr, nullptr, ru, rg, s));
+    Plan ps = p;
+    ps.NSEG = p.NSEGR;
+    GLA_LAUNCH("segment_scan_rev", launch_segment_scan(ps, 0, rg, dhT, ru, ri, nullptr, s));
+    GLA_LAUNCH("chunk_recur_rev", launch_chunk_recur_rev(p, 1, qg, kg, ph, pl, gl, dout, ri, dv, nullptr, nullptr, s));
+  } else {
+    GLA_LAUNCH("chunk_recur_rev", launch_chunk_recur_rev(p, 1, qg, kg, ph, pl, gl, dout, dhT, dv, nullptr, nullptr, s));
+  }
+  return GLA_OK;
+}
+
 // ---- scratch of the allocation-free forward (gla_fwd_noalloc)
 // The two-pass forward's records live in this array of the library instead
 // of a caller's workspace.  Each GPU the library runs on holds its own copy
@@ -330,13 +411,18 @@ gla_status gla_fwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes
   return gla_fwd_ex_workspace_size(dims, dtype, nullptr, bytes);
 }
 
-gla_status gla_bwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes) {
+gla_status gla_bwd_ex_workspace_size(const gla_dims* dims, int dtype, const gla_bwd_config* cfg,
+                                     size_t* bytes) {
   if (!bytes) return GLA_ERR_NULL;
   Plan p;
-  gla_status st = validate(dims, dtype, &p);
+  gla_status st = validate(dims, dtype, &p, nullptr, cfg);
   if (st != GLA_OK) return st;
   *bytes = p.ws_bwd;
   return GLA_OK;
+}
+
+gla_status gla_bwd_workspace_size(const gla_dims* dims, int dtype, size_t* bytes) {
+  return gla_bwd_ex_workspace_size(dims, dtype, nullptr, bytes);
 }
 
 gla_status gla_fwd(const gla_dims* dims, int dtype, const void* q, const void* k, const void* v,
@@ -424,8 +510,17 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
                    const float* log_alpha, const float* h0, const void* dout, const float* dhT,
                    void* dq, void* dk, void* dv, float* dlog_alpha, float* dh0,
                    void* workspace, size_t workspace_bytes, void* stream) {
+  return gla_bwd_ex(dims, dtype, nullptr, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv,
+                    dlog_alpha, dh0, workspace, workspace_bytes, stream);
+}
+
+gla_status gla_bwd_ex(const gla_dims* dims, int dtype, const gla_bwd_config* cfg, const void* q,
+                      const void* k, const void* v, const float* log_alpha, const float* h0,
+                      const void* dout, const float* dhT, void* dq, void* dk, void* dv,
+                      float* dlog_alpha, float* dh0, void* workspace, size_t workspace_bytes,
+                      void* stream) {
   Plan p;
-  gla_status st = validate(dims, dtype, &p);
+  gla_status st = validate(dims, dtype, &p, nullptr, cfg);
   if (st != GLA_OK) return st;
   if (p.BH == 0) return GLA_OK;
   hipStream_t s = (hipStream_t)stream;
@@ -441,6 +536,8 @@ gla_status gla_bwd(const gla_dims* dims, int dtype, const void* q, const void* k
   if (misaligned(workspace)) return GLA_ERR_ALIGN;
 
   char* ws = (char*)workspace;
+  if (p.bwd_rec) return run_bwd_recurrent(p, q, k, v, log_alpha, h0, dout, dhT, dq, dk, dv,
+                                          dlog_alpha, dh0, ws, s);
   float* cum = (float*)(ws + p.off_cum);
   float* sg = (float*)(ws + p.off_sg);
   void* st_n = ws + p.off_st;                       // S_{n-1}, [dk][dv]

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_attn(
   const int w = wave_id(), l = lane_id(), tid = threadIdx.x;
   const int r0 = n * C, rv = min(C, L - r0);
   const size_t qo = (size_t)bh * L * dk, vo = (size_t)bh * L * dv;
-  float* Ab = Aw + ((size_t)bh * NC + n) * C * C;
+  float* Ab = Aw ? Aw + ((size_t)bh * NC + n) * C * C : nullptr;
   float* dAb = dAw + ((size_t)bh * NC + n) * C * C;
 
   // dA on MFMA over d_v: lower block triangle tiles (ti >= tj)
@@ -86,9 +86,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_attn(
   // zeros above the block diagonal
   for (int it = tid; it < C * C; it += kThreads) {
     const int row = it / C, col = it % C;
-    if ((col >> 4) > (row >> 4)) { dAb[it] = 0.f; Ab[it] = 0.f; }
-    else if (col > row) Ab[it] = 0.f;
+    if ((col >> 4) > (row >> 4)) dAb[it] = 0.f;
+    if (Aw && col > row) Ab[it] = 0.f;
   }
+  if (!Aw) return;  // dA only (the score matrix A is formed elsewhere)
 
   PB pb;
   pb.init();
@@ -133,13 +134,16 @@ struct OffCols {
 };
 
 // One workgroup per (batch-head, chunk, d_k tile of TK channels).
-template <typename T, int C, int TK>
+// IB: the inter-chunk terms (already scaled by Lambda and Gamma) come in fp32
+// from dqi / dki (k_bwd_inter) instead of products with materialised states.
+template <typename T, int C, int TK, bool IB>
 __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ cum, const T* __restrict__ st_n,
     const T* __restrict__ st_lo, const T* __restrict__ dst_n, const T* __restrict__ dst_lo,
-    const float* __restrict__ dAw, T* __restrict__ dq, T* __restrict__ dkk,
-    float* __restrict__ dla, float* __restrict__ dlt, int L, int dk, int dv, int NC) {
+    const float* __restrict__ dAw, const float* __restrict__ dqi, const float* __restrict__ dki,
+    T* __restrict__ dq, T* __restrict__ dkk, float* __restrict__ dla, float* __restrict__ dlt,
+    int L, int dk, int dv, int NC) {
   using M = Mma<T>;
   constexpr bool BF = sizeof(T) == 2;
   constexpr int PT = 16 / (int)sizeof(T);
@@ -255,7 +259,30 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     raw_load(tb_, cum + tgi);
   }
   InterFrags f0;
-  inter_load(f0, 0);
+  if constexpr (!IB) {
+    inter_load(f0, 0);
+  } else {
+    // the inter terms of this wave's rows and channels (rows past the end of
+    // the sequence are never read; their terms stay 0)
+#pragma unroll
+    for (int rt = 0; rt < NRW; ++rt) {
+      const int rti = wr + WR * rt;
+      if (rti >= NRT) continue;
+#pragma unroll
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int c = (wc + WC * ct) * 16 + (l & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = rti * 16 + (l >> 4) * 4 + r;
+          if (row < rv) {
+            const size_t gi = qo + (size_t)(r0 + row) * dk + c0 + c;
+            aq[rt][ct][r] = dqi[gi];
+            ak[rt][ct][r] = dki[gi];
+          }
+        }
+      }
+    }
+  }
 
   // dA rows of the block as 4-element vectors (hi / lo split, the diagonal
   // blocks zeroed and kept in fp32 apart); with transpose, its columns
@@ -315,30 +342,34 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   // inter-chunk terms: dO S_{n-1}^T and V dS_n^T, reduction over d_v, in
   // groups of KG K steps whose operands are loaded before their products are
   // issued.  The first group's loads were issued at the start of the kernel.
-#pragma unroll
-  for (int gk = 0; gk < KG; ++gk)
-    if (gk * M::K < dv) inter_mma(f0, gk);
-  for (int kk0 = KG * M::K; kk0 < dv; kk0 += KG * M::K) {
-    InterFrags f;
-    inter_load(f, kk0);
+  if constexpr (!IB) {
 #pragma unroll
     for (int gk = 0; gk < KG; ++gk)
-      if (kk0 + gk * M::K < dv) inter_mma(f, gk);
+      if (gk * M::K < dv) inter_mma(f0, gk);
+    for (int kk0 = KG * M::K; kk0 < dv; kk0 += KG * M::K) {
+      InterFrags f;
+      inter_load(f, kk0);
+#pragma unroll
+      for (int gk = 0; gk < KG; ++gk)
+        if (kk0 + gk * M::K < dv) inter_mma(f, gk);
+    }
   }
   lds_barrier();  // al ready
+  if constexpr (!IB) {
 #pragma unroll
-  for (int rt = 0; rt < NRW; ++rt) {
-    const int rti = wr + WR * rt;
-    if (rti >= NRT) continue;
+    for (int rt = 0; rt < NRW; ++rt) {
+      const int rti = wr + WR * rt;
+      if (rti >= NRT) continue;
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct) {
-      const int c = (wc + WC * ct) * 16 + (l & 15);
-      const float blast = bt[C - 1][c];
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int c = (wc + WC * ct) * 16 + (l & 15);
+        const float blast = bt[C - 1][c];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rti * 16 + (l >> 4) * 4 + r;
-        aq[rt][ct][r] *= gexp<T>(bt[row][c]);
-        ak[rt][ct][r] *= gexp<T>(blast - bt[row][c]);
+        for (int r = 0; r < 4; ++r) {
+          const int row = rti * 16 + (l >> 4) * 4 + r;
+          aq[rt][ct][r] *= gexp<T>(bt[row][c]);
+          ak[rt][ct][r] *= gexp<T>(blast - bt[row][c]);
+        }
       }
     }
   }
@@ -777,9 +808,20 @@ static hipError_t launch_dqdk_t(const Plan& p, const void* q, const void* k, con
                                 const void* st_lo, const void* dst_n, const void* dst_lo,
                                 const float* dAw, void* dq, void* dk, float* dla, float* dlt,
                                 hipStream_t s) {
-  hipLaunchKernelGGL((k_chunk_dqdk<T, C, TK>), dim3(p.NC, p.dk / TK, p.BH), dim3(kThreads), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)dout, cum, (const T*)st_n,
-                     (const T*)st_lo, (const T*)dst_n, (const T*)dst_lo, dAw, (T*)dq, (T*)dk, dla,
+  hipLaunchKernelGGL((k_chunk_dqdk<T, C, TK, false>), dim3(p.NC, p.dk / TK, p.BH), dim3(kThreads),
+                     0, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, cum,
+                     (const T*)st_n, (const T*)st_lo, (const T*)dst_n, (const T*)dst_lo, dAw,
+                     nullptr, nullptr, (T*)dq, (T*)dk, dla, dlt, p.L, p.dk, p.dv, p.NC);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_dqdk_inter(const Plan& p, const void* q, const void* k, const float* cum,
+                                   const float* dAw, const float* dqi, const float* dki, void* dq,
+                                   void* dk, float* dla, float* dlt, hipStream_t s) {
+  if (!p.bf16 || p.C != 64 || p.dk % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_chunk_dqdk<bf16, 64, 32, true>), dim3(p.NC, p.dk / 32, p.BH),
+                     dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k, nullptr, nullptr, cum,
+                     nullptr, nullptr, nullptr, nullptr, dAw, dqi, dki, (bf16*)dq, (bf16*)dk, dla,
                      dlt, p.L, p.dk, p.dv, p.NC);
   return hipGetLastError();
 }

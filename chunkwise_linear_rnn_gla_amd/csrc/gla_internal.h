@@ -38,15 +38,22 @@ struct Plan {
   size_t off_qg, off_kg, off_ph, off_pl, off_gl, off_ru, off_ri, off_rg;
   size_t ws_fwd, ws_bwd;    // workspace of the chosen forward path; of the backward
   size_t ws_recur, ws_fused;  // workspace of the two-pass and of the fused forward
+  // backward with the states on chip (bwd_rec): cumsum, dA, the inter terms of
+  // dq and dk (fp32), chunk totals of dlog b, rowsum(hT * dhT), and the
+  // two-pass records of the reversed-sequence dv pass (at off_bvrec)
+  int bwd_rec;
+  size_t off_bcum, off_bdA, off_bdqi, off_bdki, off_bdlt, off_brs, off_bvrec;
 };
 
 // Forward path and its tuning, as the caller chose them (gla_fwd_config in
 // include/gla.h); zeros mean "automatic".
 enum FwdAlgo { FWD_AUTO = 0, FWD_TWO_PASS = 1, FWD_FUSED = 2, FWD_MATERIALIZED = 3 };
+enum BwdAlgo { BWD_AUTO = 0, BWD_MATERIALIZED = 1, BWD_RECURRENT = 2 };
 struct FwdOptions {
   int algo = FWD_AUTO;
   int recur_waves = 0;
   int recur_segments = 0;
+  int bwd_algo = BWD_AUTO;  // the backward's path (gla_bwd_config)
 };
 
 // Fills everything but the status; returns false if the sizes (or the
@@ -144,8 +151,21 @@ hipError_t launch_chunk_recur(const Plan& p, int out, const void* qg, const void
                               const float* init, void* o, float* fin, float* seg_g,
                               hipStream_t s);
 
+// The two passes over the time-reversed sequence (bf16, C = 64): row p is
+// row L - 1 - p of q, k, v and o in memory and takes the log gate of row
+// L - p (0 at p = 0).  Given (q, k, v) = (k, q, dout) and init = dhT, the
+// output is dv (papercache.org notes §4.2 chunkwise form, run backwards).
+hipError_t launch_chunk_prep_rev(const Plan& p, const void* q, const void* k, const float* la,
+                                 const void* v, void* qg, void* kg, float* grec, void* ph,
+                                 void* pl, hipStream_t s);
+hipError_t launch_chunk_recur_rev(const Plan& p, int out, const void* qg, const void* kg,
+                                  const void* ph, const void* pl, const float* grec,
+                                  const void* v, const float* init, void* o, float* fin,
+                                  float* seg_g, hipStream_t s);
+
 // ---- backward kernels (gla_bwd.hip) ----
-// A (chunk score matrix) and dA = (dO V^T) ⊙ M per chunk, fp32 C x C blocks.
+// A (chunk score matrix) and dA = (dO V^T) ⊙ M per chunk, fp32 C x C blocks
+// (Aw null: dA only).
 hipError_t launch_chunk_attn(const Plan& p, const void* q, const void* k, const void* v,
                              const void* dout, const float* cum, float* Aw, float* dAw,
                              hipStream_t s);
@@ -156,6 +176,11 @@ hipError_t launch_chunk_dqdk(const Plan& p, const void* q, const void* k, const 
                              const void* st_lo, const void* dst_n, const void* dst_lo,
                              const float* dAw, void* dq, void* dk, float* dla, float* dlt,
                              hipStream_t s);
+// The same with the inter-chunk terms (scaled) from dqi / dki [BH][L][dk]
+// fp32 (bf16 I/O, C = 64, dk % 32 == 0).
+hipError_t launch_chunk_dqdk_inter(const Plan& p, const void* q, const void* k, const float* cum,
+                                   const float* dAw, const float* dqi, const float* dki, void* dq,
+                                   void* dk, float* dla, float* dlt, hipStream_t s);
 hipError_t launch_chunk_dv(const Plan& p, const void* k, const void* dout, const float* cum,
                            const void* dst_t, const float* Aw, void* dv, hipStream_t s);
 hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT, float* rs,
@@ -211,6 +236,29 @@ hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const voi
                            const void* dout, const void* v, const float* dv32, const float* hT,
                            const float* dhT, float* tot, float* hs, float* dla, float* dlb,
                            hipStream_t s);
+
+// ---- the backward's inter-chunk terms with the states on chip (gla_bwd_recur.hip) ----
+// One job of k_bwd_inter (bf16 rows): the output product X_y U scaled by
+// Lambda (dq job, rev = 0, U = S^T, chunks in order) or Gamma (dk job,
+// rev = 1, U = dS^T, chunks backwards), in fp32 to `out` [BH][L][dk]; U is
+// updated with X_u^T (z ⊙ Gamma) (dq) or X_u^T (z ⊙ Lambda) (dk).  init:
+// entering state [BH][dk][dv] (h0 or dhT) or null.  fin_rs (dq job):
+// rowsum(hT ⊙ fin_with) [BH][dk] (zeros when fin_with is null).  fin_state
+// (dk job): dh0 [BH][dk][dv].
+struct BwdInterJob {
+  const void* xy;
+  const void* xu;
+  const void* z;
+  const float* init;
+  float* out;
+  float* fin_rs;
+  const float* fin_with;
+  float* fin_state;
+  int rev;
+};
+bool bwd_inter_supported(int bf16, int C, int dk, int dv, int L);
+hipError_t launch_bwd_inter(const Plan& p, const BwdInterJob& jq, const BwdInterJob& jk,
+                            const float* cum, hipStream_t s);
 
 // dla += rs + the dlog b totals of all later chunks (dlt [BH][NC][dk]).
 hipError_t launch_dla_carry(const Plan& p, const float* dlt, const float* rs, float* dla,

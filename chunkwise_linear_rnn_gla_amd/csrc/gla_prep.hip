@@ -84,8 +84,15 @@ __device__ inline void touch_lines(const void* base, int bytes, int l, unsigned 
 // under 128 per lane, so that four workgroups (one wave per SIMD each) are
 // resident per CU: the usual grid (one workgroup per chunk, a few per CU) then
 // runs in a single round.
-template <typename T, int C>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_chunk_prep(
+//
+// REV: the time-reversed sequence, the dv pass of the backward.  Row p of the
+// reversed sequence is original row L - 1 - p of q, k and v, and its log gate
+// is the next original token's, log alpha[L - p] (0 at p = 0): the gradient
+// flows from a token to the tokens before it, decayed by the gates after
+// them.  Everything else (records, chunk numbering) refers to the reversed
+// sequence.
+template <typename T, int C, bool REV>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(REV ? 3 : 4))) void k_chunk_prep(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ la,
     const T* __restrict__ v, unsigned char* __restrict__ qrec, unsigned char* __restrict__ krec,
     unsigned char* __restrict__ prec, unsigned char* __restrict__ lrec,
@@ -136,7 +143,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // and waited for at the end of the slice loop.
   auto touch_v = [&]() __attribute__((always_inline)) {
     const int vbytes = rv * dv * (int)sizeof(T);
-    const unsigned char* vrow = reinterpret_cast<const unsigned char*>(v + ((size_t)bh * L + r0) * dv);
+    const size_t vr0 = REV ? (size_t)(L - r0 - rv) : (size_t)r0;  // first row in memory
+    const unsigned char* vrow = reinterpret_cast<const unsigned char*>(v + ((size_t)bh * L + vr0) * dv);
     const unsigned dmy = (unsigned)(size_t)(__attribute__((address_space(3))) void*)vtouch;
     for (int p0 = wave_id() * 8192; p0 < vbytes; p0 += (kThreads / kWave) * 8192)
       touch_lines(vrow + p0, min(8192, vbytes - p0), lane_id(), dmy);
@@ -154,12 +162,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const bool uld = tid < NU && urow < rv;
   // chunk-uniform bases and 32-bit per-thread offsets (one address register
   // per lane instead of a 64-bit pointer per load)
-  const size_t cbase = io + (size_t)r0 * dk;
+  // The chunk's rows in memory start at row r0, or (reversed sequence) at
+  // row L - r0 - rv, whose rows then run backwards: chunk row p is memory row
+  // rv - 1 - p from there, and its log gate memory row rv - p.
+  const size_t cbase = io + (size_t)(REV ? L - r0 - rv : r0) * dk;
   const T* qc = q + cbase;
   const T* kc = k + cbase;
   const float* lc = la + cbase;
-  const unsigned uoff = (unsigned)(urow * dk + uc8);
-  const unsigned aoff = (unsigned)(rg * RPT * dk + ch);
+  const unsigned uoff = (unsigned)((REV ? rv - 1 - urow : urow) * dk + uc8);
+  const unsigned aoff = (unsigned)((REV ? rv - rg * RPT : rg * RPT) * dk + ch);
   Raw8<T> rq, rk;
   float ra[RPT];
   auto fetch = [&](int grp) __attribute__((always_inline)) {
@@ -174,7 +185,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = rg * RPT + i;
-      ra[i] = row < rv ? lc[aoff + (unsigned)(i * dk) + s0] : 0.f;
+      if constexpr (REV)  // the first row of the reversed sequence has no gate
+        ra[i] = (row < rv && r0 + row > 0) ? lc[aoff - (unsigned)(i * dk) + s0] : 0.f;
+      else
+        ra[i] = row < rv ? lc[aoff + (unsigned)(i * dk) + s0] : 0.f;
     }
   };
   fetch(0);
@@ -285,14 +299,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // =========================================================== launcher
-template <typename T, int C>
+template <typename T, int C, bool REV = false>
 static hipError_t launch_prep_t(const Plan& p, const void* q, const void* k, const float* la,
                                 const void* v, void* qg, void* kg, float* grec, void* ph,
                                 void* pl, hipStream_t s) {
-  hipLaunchKernelGGL((k_chunk_prep<T, C>), dim3(p.NC, p.BH), dim3(kThreads), 0, s, (const T*)q,
-                     (const T*)k, la, (const T*)v, (unsigned char*)qg, (unsigned char*)kg,
-                     (unsigned char*)ph, (unsigned char*)pl, grec, p.L, p.dk, p.dv, p.NC);
+  hipLaunchKernelGGL((k_chunk_prep<T, C, REV>), dim3(p.NC, p.BH), dim3(kThreads), 0, s,
+                     (const T*)q, (const T*)k, la, (const T*)v, (unsigned char*)qg,
+                     (unsigned char*)kg, (unsigned char*)ph, (unsigned char*)pl, grec, p.L, p.dk,
+                     p.dv, p.NC);
   return hipGetLastError();
+}
+
+hipError_t launch_chunk_prep_rev(const Plan& p, const void* q, const void* k, const float* la,
+                                 const void* v, void* qg, void* kg, float* grec, void* ph,
+                                 void* pl, hipStream_t s) {
+  if (!p.bf16 || p.C != 64) return hipErrorInvalidValue;
+  return launch_prep_t<bf16, 64, true>(p, q, k, la, v, qg, kg, grec, ph, pl, s);
 }
 
 hipError_t launch_chunk_prep(const Plan& p, const void* q, const void* k, const float* la,

@@ -13,6 +13,7 @@
 // (no output) the same walk starts from zero and leaves each segment's own
 // state contribution and total log decay for the segment scan.
 #include "gla_common.h"
+#include "gla_dma.h"
 #include "gla_internal.h"
 #include "gla_pblock.h"
 #include "gla_records.h"
@@ -20,50 +21,6 @@
 namespace gla {
 
 namespace {
-
-// Asynchronous global -> LDS copy through a buffer resource: 16 bytes at
-// rsrc base + soff + voff (voff per lane, soff wave-uniform) into LDS at
-// lds_wave_base + 16 * lane.
-// The copy is issued from inline assembly: the instruction writes no
-// register, and the compiler, which cannot tell which LDS bytes a copy
-// writes, would otherwise wait for every outstanding copy (including the
-// prefetch of a later chunk) before the next LDS read.  Completion is waited
-// for explicitly (wait_vm) before a staged buffer is read.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-__device__ inline i32x4 make_rsrc(const void* base) {
-  // raw buffer: stride 0, range 2 GiB, 32-bit data format
-  const unsigned long long a = (unsigned long long)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
-  r[2] = 0x7fffffff;
-  r[3] = 0x00020000;
-  return r;
-}
-// lds_wave_base: LDS byte address (wave-uniform).  The instruction takes it
-// in M0, which the "{m0}" operand asks the compiler to load: the compiler
-// then knows M0's contents at this point and keeps any value of its own
-// there safe, so the statement has no hidden effect on registers.
-__device__ inline void dma16b(const i32x4& r, unsigned voff, unsigned soff, unsigned lds_wave_base) {
-  asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "{m0}"(__builtin_amdgcn_readfirstlane(lds_wave_base)), "v"(voff), "s"(r),
-                 "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory");
-}
-// LDS byte address of a __shared__ object.
-template <typename P>
-__device__ inline unsigned lds_addr(P* p) {
-  return (unsigned)(size_t)(__attribute__((address_space(3))) void*)p;
-}
-// Wait until at most N of this wave's global memory operations are
-// outstanding.  Loads complete in issue order, so in a wave that issues only
-// loads this waits for all but the last N.
-template <int N>
-__device__ inline void wait_vm_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory"); }
-// Wait for this wave's outstanding global memory operations (LDS copies too).
-__device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Loading wave li of NLD issues copies li, li + NLD, ... of a contiguous tile
 // of NCOPY copies (all NLD waves issue a one-copy tile); copy c moves the
@@ -151,7 +108,11 @@ struct RecurLayout {
 // only issue the LDS copies and wait for them, so that their memory counters
 // hold nothing but loads (a partial wait is exact) and the computing waves,
 // which store the output, never wait on memory.
-template <typename T, int C, int DK, int NWV, int OUT>
+//
+// REV: the time-reversed sequence (the dv pass of the backward): row p of a
+// chunk's V and of the output is row L - 1 - p in memory; the records, built
+// by the prep pass in its reversed mode, need no change.
+template <typename T, int C, int DK, int NWV, int OUT, bool REV = false>
 __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) void k_chunk_recur(
     const unsigned char* __restrict__ qrec, const unsigned char* __restrict__ krec,
     const unsigned char* __restrict__ prec, const unsigned char* __restrict__ lrec,
@@ -238,7 +199,7 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
     // V rows past the end of the sequence repeat the last row (their K~ rows
     // and P columns are zero)
     const int r0 = n * C;
-    const i32x4 vr = make_rsrc(v + ((size_t)bh * L + r0) * dv + j0);
+    const i32x4 vr = make_rsrc(REV ? v + (size_t)bh * L * dv + j0 : v + ((size_t)bh * L + r0) * dv + j0);
     const bool full = r0 + C <= L;
     constexpr int NVC = Lay::VB / 1024;
 #pragma unroll
@@ -247,7 +208,8 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
       int rho, u;
       vslot(c, rho, u);
       if (!full) rho = min(rho, L - 1 - r0);
-      dma16b(vr, (unsigned)(rho * dv * ES + u * 16), 0u, base + (unsigned)(c * 1024));
+      const int prow = REV ? L - 1 - r0 - rho : rho;  // row in memory (from r0 unless REV)
+      dma16b(vr, (unsigned)(prow * dv * ES + u * 16), 0u, base + (unsigned)(c * 1024));
     }
   };
 
@@ -276,12 +238,14 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
   // hardware, so the stores need no branch.
   const __amdgpu_buffer_rsrc_t orsrc =
       __builtin_amdgcn_make_buffer_rsrc(OUT ? o + (size_t)bh * L * dv : o, 0, L * dv * ES, 0x00020000);
+  // (REV: rows past the end of the sequence map to negative rows, whose
+  // offsets, read unsigned, fall outside the resource as well)
   auto store_out = [&](int n, const floatx4 (&ot)[NRT]) __attribute__((always_inline)) {
     if constexpr (OUT) {
-      const int off0 = ((n * C + ln) * dv + j0 + vc + 4 * g) * ES;
 #pragma unroll
       for (int jt = 0; jt < NRT; ++jt) {
-        const int off = off0 + 16 * jt * dv * ES;
+        const int row = n * C + 16 * jt + ln;
+        const int off = ((REV ? L - 1 - row : row) * dv + j0 + vc + 4 * g) * ES;
         if constexpr (BF) {
           bf16x4 h;
 #pragma unroll
@@ -544,7 +508,7 @@ __global__ __launch_bounds__((RecurLayout<T, C, DK, NWV, OUT>::NWAVES * kWave)) 
 }
 
 // =========================================================== launchers
-template <typename T, int C, int DK, int NWV>
+template <typename T, int C, int DK, int NWV, bool REV>
 static hipError_t launch_recur_w(const Plan& p, int out, const void* qg, const void* kg,
                                  const void* ph, const void* pl, const float* grec,
                                  const void* v, const float* init, void* o, float* fin,
@@ -553,30 +517,30 @@ static hipError_t launch_recur_w(const Plan& p, int out, const void* qg, const v
   const unsigned char *q8 = (const unsigned char*)qg, *k8 = (const unsigned char*)kg,
                       *p8 = (const unsigned char*)ph, *l8 = (const unsigned char*)pl;
   if (out)
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1>), grid,
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 1, REV>), grid,
                        dim3(RecurLayout<T, C, DK, NWV, 1>::NWAVES * kWave), 0, s, q8, k8,
                        p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
                        p.NSEGR, p.segr_chunks);
   else
-    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0>), grid,
+    hipLaunchKernelGGL((k_chunk_recur<T, C, DK, NWV, 0, REV>), grid,
                        dim3(RecurLayout<T, C, DK, NWV, 0>::NWAVES * kWave), 0, s, q8, k8,
                        p8, l8, grec, (const T*)v, init, (T*)o, fin, seg_g, p.L, p.dv, p.NC,
                        p.NSEGR, p.segr_chunks);
   return hipGetLastError();
 }
 
-template <typename T, int C, int DK>
+template <typename T, int C, int DK, bool REV = false>
 static hipError_t launch_recur_d(const Plan& p, int out, const void* qg, const void* kg,
                                  const void* ph, const void* pl, const float* grec,
                                  const void* v, const float* init, void* o, float* fin,
                                  float* seg_g, hipStream_t s) {
   if constexpr (recur_max_waves(sizeof(T) == 2, DK) == 4)
     if (p.NWVR == 4)
-      return launch_recur_w<T, C, DK, 4>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
+      return launch_recur_w<T, C, DK, 4, REV>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   if (p.NWVR == 2)
-    return launch_recur_w<T, C, DK, 2>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
+    return launch_recur_w<T, C, DK, 2, REV>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   if constexpr (recur_min_waves(sizeof(T) == 2, DK) == 1)
-    return launch_recur_w<T, C, DK, 1>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
+    return launch_recur_w<T, C, DK, 1, REV>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s);
   return hipErrorInvalidValue;
 }
 
@@ -599,6 +563,22 @@ static hipError_t launch_recur_c(const Plan& p, int out, const void* qg, const v
     GLA_RECUR_DK(128);
   }
 #undef GLA_RECUR_DK
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_recur_rev(const Plan& p, int out, const void* qg, const void* kg,
+                                  const void* ph, const void* pl, const float* grec,
+                                  const void* v, const float* init, void* o, float* fin,
+                                  float* seg_g, hipStream_t s) {
+  if (!p.bf16 || p.C != 64) return hipErrorInvalidValue;
+#define GLA_RECUR_REV_DK(D)                                                                      \
+  if (p.dk == D)                                                                                 \
+  return launch_recur_d<bf16, 64, D, true>(p, out, qg, kg, ph, pl, grec, v, init, o, fin, seg_g, s)
+  GLA_RECUR_REV_DK(32);
+  GLA_RECUR_REV_DK(64);
+  GLA_RECUR_REV_DK(128);
+  GLA_RECUR_REV_DK(256);
+#undef GLA_RECUR_REV_DK
   return hipErrorInvalidValue;
 }
 

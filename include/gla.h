@@ -191,6 +191,42 @@ gla_status gla_bwd(const gla_dims *dims, int dtype,
                    void *dq, void *dk, void *dv, float *dlog_alpha, float *dh0,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* Backward path selection for gla_bwd_ex (zeros: automatic).  Both paths
+ * recompute the states rather than reading them from a forward call:
+ *   GLA_BWD_AUTO          the recurrent path wherever it supports the shape
+ *                         (gla_bwd's choice), else the materialised one;
+ *   GLA_BWD_MATERIALIZED  the chunk states S_{n-1} and state gradients dS_n
+ *                         are written to the workspace (bf16 high and low
+ *                         parts) and read back per chunk;
+ *   GLA_BWD_RECURRENT     no state leaves the chip: one launch walks the
+ *                         chunks with the transposed state S^T (in order) and
+ *                         dS^T (backwards) and emits the inter-chunk parts of
+ *                         dq and dk; dv is the forward of the time-reversed
+ *                         sequence (queries k, keys q, values dout, gates
+ *                         shifted by one token, initial state dhT).  bf16 I/O,
+ *                         chunk 64, dk % 32 == 0, dv in {128, 256}.
+ * A path the shape does not support gives GLA_ERR_SHAPE. */
+typedef enum {
+  GLA_BWD_AUTO = 0,
+  GLA_BWD_MATERIALIZED = 1,
+  GLA_BWD_RECURRENT = 2
+} gla_bwd_algo;
+
+typedef struct {
+  int32_t algo;  /* gla_bwd_algo */
+} gla_bwd_config;
+
+/* gla_bwd with an explicit path; cfg == NULL is gla_bwd itself.  Size the
+ * workspace with gla_bwd_ex_workspace_size for the same cfg. */
+gla_status gla_bwd_ex_workspace_size(const gla_dims *dims, int dtype, const gla_bwd_config *cfg,
+                                     size_t *bytes);
+gla_status gla_bwd_ex(const gla_dims *dims, int dtype, const gla_bwd_config *cfg,
+                      const void *q, const void *k, const void *v,
+                      const float *log_alpha, const float *h0,
+                      const void *dout, const float *dhT,
+                      void *dq, void *dk, void *dv, float *dlog_alpha, float *dh0,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* One token of the recurrent form, in place on the state (papercache.org
  * notes §2.1 and §4.1, recurrent form: the constant-memory inference step).
  * Per (batch, head), with a = log_alpha of the token:

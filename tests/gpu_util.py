@@ -7,7 +7,8 @@ import oracle
 from chunkwise_linear_rnn_gla_amd import GLA_BF16, GLA_FP32, GlaDims, GlaError, _abi
 from chunkwise_linear_rnn_gla_amd import bwd as gla_bwd_t
 from chunkwise_linear_rnn_gla_amd import fwd as gla_fwd_t
-from chunkwise_linear_rnn_gla_amd import fwd_config, gla_fwd_ex_workspace_size
+from chunkwise_linear_rnn_gla_amd import (bwd_config, fwd_config, gla_bwd_ex_workspace_size,
+                                          gla_fwd_ex_workspace_size)
 from chunkwise_linear_rnn_gla_amd.inputs import as_f64
 
 # Tolerances (relative L2 per output tensor): the required bar for fp32 I/O and
@@ -64,10 +65,33 @@ def oracle_fwd(x):
     return oracle.fwd(as_f64(x.q), as_f64(x.k), as_f64(x.v), as_f64(x.log_alpha), as_f64(x.h0))
 
 
-def run_bwd(x, chunk=64, subchunk=16, dev="cuda"):
+def bwd_path_supported(x, chunk, algo):
+    """Whether the library accepts the backward path `algo` for this shape."""
+    if algo == "auto":
+        return True
+    B, H, L, dk = x.q.shape
+    dims = GlaDims(B, H, L, dk, x.v.shape[-1], chunk, 16)
+    code = GLA_BF16 if x.q.dtype == torch.bfloat16 else GLA_FP32
+    try:
+        gla_bwd_ex_workspace_size(dims, code, bwd_config(algo))
+    except GlaError as e:
+        if e.status == 2:
+            return False
+        raise
+    return True
+
+
+def run_bwd(x, chunk=64, subchunk=16, dev="cuda", algo="auto", names=None):
+    """The backward through the C ABI; the launched kernels' names are
+    appended to `names` when a list is given."""
     d = x.to(dev)
-    g = gla_bwd_t(d.q, d.k, d.v, d.log_alpha, d.h0, d.do, d.dhT, chunk=chunk, subchunk=subchunk)
+    _abi.gla_profile_begin(64)
+    g = gla_bwd_t(d.q, d.k, d.v, d.log_alpha, d.h0, d.do, d.dhT, chunk=chunk, subchunk=subchunk,
+                  algo=algo)
     torch.cuda.synchronize()
+    _abi.gla_profile_end()
+    if names is not None:
+        names.extend(_abi.gla_profile_get(i)[0] for i in range(_abi.gla_profile_count()))
     return tuple(as_f64(t) for t in g)
 
 

@@ -6,18 +6,42 @@ import numpy as np
 import pytest
 
 from chunkwise_linear_rnn_gla_amd.inputs import WORKLOADS, make_inputs, workload_inputs
-from gpu_util import TOL, dtype_name, oracle_bwd, rel_l2, run_bwd, say
+from gpu_util import (TOL, bwd_path_supported, dtype_name, oracle_bwd, rel_l2, run_bwd, say)
 
 pytestmark = pytest.mark.gpu
 
 NAMES = ("dq", "dk", "dv", "dlog_alpha", "dh0")
 
+# The backward path of the running test (set by the autouse fixture below).
+_PATH = {"algo": "auto"}
+# The kernel that marks the recurrent backward in the launch records.
+RECURRENT_KERNEL = "bwd_inter"
 
-def check_bwd(x, chunk, tag="", tol=None):
+
+@pytest.fixture(params=["auto", "materialized"], autouse=True)
+def backward_path(request):
+    """Run every backward case through the automatic choice (the recurrent
+    path, states on chip, wherever it supports the shape) and through the
+    materialised-state path, requested explicitly through gla_bwd_ex."""
+    _PATH["algo"] = request.param
+    yield request.param
+    _PATH["algo"] = "auto"
+
+
+def check_bwd(x, chunk, tag="", tol=None, algo=None):
     dt = dtype_name(x)
-    say(f"[bwd] {tag} dtype={dt} shape={tuple(x.q.shape)} dv={x.v.shape[-1]} C={chunk} "
-        f"h0={'y' if x.h0 is not None else 'n'} dhT={'y' if x.dhT is not None else 'n'}")
-    got = run_bwd(x, chunk)
+    algo = algo or _PATH["algo"]
+    if not bwd_path_supported(x, chunk, algo):
+        pytest.skip(f"the {algo} backward does not support dk={x.q.shape[-1]} "
+                    f"dv={x.v.shape[-1]} C={chunk} {dt}")
+    names = []
+    got = run_bwd(x, chunk, algo=algo, names=names)
+    ran = "recurrent" if RECURRENT_KERNEL in names else "materialized"
+    say(f"[bwd] {tag} path={algo}->{ran} dtype={dt} shape={tuple(x.q.shape)} "
+        f"dv={x.v.shape[-1]} C={chunk} h0={'y' if x.h0 is not None else 'n'} "
+        f"dhT={'y' if x.dhT is not None else 'n'}")
+    if algo != "auto" and x.q.shape[2] > 0 and x.q.shape[0] * x.q.shape[1] > 0:
+        assert ran == algo, (algo, names)
     ref = oracle_bwd(x)
     errs = {n: rel_l2(g, r) for n, g, r in zip(NAMES, got, ref)}
     say("      " + " ".join(f"{n}={e:.3e}" for n, e in errs.items()))
@@ -85,6 +109,36 @@ def test_single_token_and_single_chunk():
     check_bwd(make_inputs(1, 2, 1, 32, 64, "fp32", seed=604, h0_std=1.0, with_do=True,
                           dhT_std=1.0), 64, "L=1")
     check_bwd(make_inputs(1, 2, 64, 32, 64, "fp32", seed=605, with_do=True), 64, "L=C")
+
+
+@pytest.mark.parametrize("dk", [32, 64, 128, 256])
+@pytest.mark.parametrize("dv", [128, 256])
+def test_recurrent_backward_shapes(dk, dv, backward_path):
+    # the recurrent path's own shape table: every dk tile count, both dv,
+    # a ragged last chunk, h0 and dhT given
+    if backward_path != "auto":
+        pytest.skip("recurrent-path shapes (covered once)")
+    x = make_inputs(2, 2, 300, dk, dv, "bf16", seed=620 + dk + dv, h0_std=0.3, with_do=True,
+                    dhT_std=0.2)
+    check_bwd(x, 64, "recurrent-shapes", algo="recurrent")
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 2048])
+def test_recurrent_backward_chunk_edges(L, backward_path):
+    if backward_path != "auto":
+        pytest.skip("recurrent-path chunk edges (covered once)")
+    x = make_inputs(1, 4, L, 128, 256, "bf16", seed=640 + L, h0_std=0.2, with_do=True,
+                    dhT_std=0.3)
+    check_bwd(x, 64, f"recurrent-L{L}", algo="recurrent")
+
+
+@pytest.mark.parametrize("gate", ["zero", "extreme", "const", "channel_const"])
+def test_recurrent_backward_gates(gate, backward_path):
+    if backward_path != "auto":
+        pytest.skip("recurrent-path gate modes (covered once)")
+    x = make_inputs(2, 2, 200, 64, 128, "bf16", seed=650, gate=gate, h0_std=0.2, with_do=True,
+                    dhT_std=0.2, gate_value=-0.3)
+    check_bwd(x, 64, f"recurrent-gate-{gate}", algo="recurrent")
 
 
 def test_empty_sequence_passes_dhT():
