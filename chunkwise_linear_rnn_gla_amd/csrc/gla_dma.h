@@ -50,4 +50,25 @@ __device__ inline void wait_vm_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N
 // Wait for this wave's outstanding global memory operations (LDS copies too).
 __device__ inline void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Prefetch into the caches: a 4-byte asynchronous LDS copy per lane from byte
+// 128 l of [base, base + bytes) (lanes past the end read nothing), one per
+// 128-byte line of an 8 KB piece.  The LDS bytes written at lds_dummy +
+// 4 * lane are never read.
+__device__ inline void touch_lines(const void* base, int bytes, int l, unsigned lds_dummy) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const unsigned long long a = (unsigned long long)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  // M0 (the LDS address) is an operand the compiler loads ("{m0}"), not a
+  // register the statement sets behind its back
+  asm volatile("buffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "{m0}"(__builtin_amdgcn_readfirstlane(lds_dummy)), "v"((unsigned)l * 128u), "s"(r),
+                 "s"(0u)
+               : "memory");
+}
+
 }  // namespace gla

@@ -15,6 +15,7 @@
 // part of its diagonal 16 x 16 blocks.  The records' layouts are those of
 // gla_records.h; pass 2 is gla_recur.hip.
 #include "gla_common.h"
+#include "gla_dma.h"
 #include "gla_internal.h"
 #include "gla_pblock.h"
 #include "gla_records.h"
@@ -54,27 +55,6 @@ __device__ inline void store_masked(unsigned char* dst, const T* src, int last) 
     }
   }
   *reinterpret_cast<f32x4*>(dst) = val;
-}
-
-// Prefetch into the caches: a 4-byte asynchronous LDS copy per lane from byte
-// 128 l of [base, base + bytes) (lanes past the end read nothing), one per
-// 128-byte line of an 8 KB piece.  The LDS bytes written at lds_dummy +
-// 4 * lane are never read.
-__device__ inline void touch_lines(const void* base, int bytes, int l, unsigned lds_dummy) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  const unsigned long long a = (unsigned long long)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000;
-  // M0 (the LDS address) is an operand the compiler loads ("{m0}"), not a
-  // register the statement sets behind its back
-  asm volatile("buffer_load_dword %1, %2, %3 offen lds"
-               :
-               : "{m0}"(__builtin_amdgcn_readfirstlane(lds_dummy)), "v"((unsigned)l * 128u), "s"(r),
-                 "s"(0u)
-               : "memory");
 }
 
 }  // namespace
