@@ -114,6 +114,76 @@ def test_recurrence_workgroup_shapes(waves, dt, dk, forward_path):
     check_fwd(x, 64, f"recur-waves{waves}", recur_waves=waves)
 
 
+@pytest.mark.parametrize("dt,dk", [("fp32", 64), ("bf16", 128)])
+def test_recurrence_workgroup_shapes_bitwise(dt, dk, forward_path):
+    # Each wave of the recurrence owns 16 state columns and runs the same
+    # instructions on them whatever the number of waves per workgroup, so with
+    # the sequence split the same way (one segment) the outputs are identical
+    # to the bit.  (Other settings change the arithmetic: segments re-associate
+    # the state sum over chunks, and the fused and materialised forwards order
+    # their products differently; those are compared with the oracle.)
+    if forward_path != "auto":
+        pytest.skip("recurrence workgroup shapes are a setting of the two-pass forward")
+    x = make_inputs(2, 4, 300, dk, 128, dt, seed=330 + dk, h0_std=0.3)
+    runs = {}
+    for waves in (1, 2, 4):
+        if not fwd_path_supported(x, 64, "two_pass", recur_waves=waves, recur_segments=1):
+            continue
+        say(f"[fwd] bitwise recur_waves={waves} dtype={dt} dk={dk}")
+        o, hT, names = run_fwd(x, 64, algo="two_pass", recur_waves=waves, recur_segments=1)
+        assert "chunk_recur" in names, names
+        runs[waves] = (o, hT)
+    assert len(runs) >= 2, "fewer than two workgroup shapes to compare"
+    (w0, (o0, h0)), *rest = sorted(runs.items())
+    for w, (o, h) in rest:
+        assert np.array_equal(o, o0), f"o differs between {w0} and {w} waves"
+        assert np.array_equal(h, h0), f"hT differs between {w0} and {w} waves"
+
+
+def _slice(x, a, b, h0):
+    """Tokens [a, b) of every sequence, entering with state h0."""
+    from chunkwise_linear_rnn_gla_amd.inputs import Inputs
+    t = lambda z: z[:, :, a:b].contiguous()
+    return Inputs(t(x.q), t(x.k), t(x.v), t(x.log_alpha), h0, None, None)
+
+
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+@pytest.mark.parametrize("split", [256, 200])
+def test_segment_split_carries_the_state(dt, split, forward_path):
+    # A sequence run as two calls, the second entering with the first's final
+    # state (papercache.org notes §2.2: the recurrence only needs the previous
+    # state; the zako-mio report ch. 4.5 trains this way across segments),
+    # against one call and against the oracle.
+    x = make_inputs(2, 3, 512, 64, 128, dt, seed=340 + split, h0_std=0.3)
+    algo = skip_unsupported(x, 64)
+
+    def split_run(**cfg):
+        o1, h1, _ = run_fwd(_slice(x, 0, split, x.h0), 64, algo=algo, **cfg)
+        o2, h2, _ = run_fwd(_slice(x, split, 512, torch.from_numpy(h1).float()), 64, algo=algo,
+                            **cfg)
+        return np.concatenate([o1, o2], axis=2), h2
+
+    say(f"[fwd] segment split at {split} path={algo} dtype={dt}")
+    o, hT, _ = run_fwd(x, 64, algo=algo)
+    os_, hs = split_run()
+    ro, rh = oracle_fwd(x)
+    eo, eh = rel_l2(os_, ro), rel_l2(hs, rh)
+    say(f"      rel_l2 vs oracle o={eo:.3e} hT={eh:.3e}; vs one call "
+        f"o={rel_l2(os_, o):.3e} hT={rel_l2(hs, hT):.3e}")
+    assert eo <= TOL[dt] and eh <= TOL[dt]
+    assert rel_l2(os_, o) <= TOL[dt] and rel_l2(hs, hT) <= TOL[dt]
+    if algo == "two_pass" or (algo == "auto" and fwd_path_supported(x, 64, "two_pass")):
+        if split % 64 == 0:
+            # On a chunk boundary, with the sequence in one recurrence segment
+            # in every call, each chunk sees the same tokens and the same fp32
+            # entering state (held in the accumulators, or loaded from h0), so
+            # the two-pass forward matches one call to the bit.
+            algo = "two_pass"
+            o, hT, _ = run_fwd(x, 64, algo=algo, recur_segments=1)
+            os_, hs = split_run(recur_segments=1)
+            assert np.array_equal(os_, o) and np.array_equal(hs, hT)
+
+
 def test_single_chunk_and_single_token():
     check_fwd(make_inputs(1, 2, 64, 32, 64, "fp32", seed=304, h0_std=1.0), 64, "L=C")
     check_fwd(make_inputs(1, 2, 1, 32, 64, "fp32", seed=305, h0_std=1.0), 64, "L=1")
