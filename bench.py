@@ -71,14 +71,46 @@ KERNEL_SOURCES = [
     "chunkwise_linear_rnn_gla_amd/csrc/gla_api.hip",
     "chunkwise_linear_rnn_gla_amd/csrc/gla_fwd.hip",
     "chunkwise_linear_rnn_gla_amd/csrc/gla_bwd.hip",
+    "chunkwise_linear_rnn_gla_amd/csrc/gla_bwd_recur.hip",
+    "chunkwise_linear_rnn_gla_amd/csrc/gla_dma.h",
     "chunkwise_linear_rnn_gla_amd/build.py",
 ]
-# rocprofv3 kernel names -> the library's launch names
-KERNEL_NAMES = [("k_chunk_prep", "chunk_prep"), ("k_chunk_recur", "chunk_recur"),
-                ("k_segment_scan", "segment_scan"), ("k_cumsum", "chunk_cumsum"),
-                ("k_chunk_state", "chunk_state"), ("k_chunk_attn", "chunk_attn"),
-                ("k_chunk_dqdk", "chunk_dqdk"), ("k_chunk_dv", "chunk_dv"),
-                ("k_rowsum_state", "rowsum_state"), ("k_dla_carry", "dla_carry")]
+# rocprofv3 kernel names (mangled or demangled) -> the library's launch names
+KERNEL_NAMES = {"chunk_prep": "chunk_prep", "chunk_recur": "chunk_recur",
+                "segment_scan": "segment_scan", "cumsum": "chunk_cumsum",
+                "chunk_state": "chunk_state", "chunk_attn": "chunk_attn",
+                "chunk_dqdk": "chunk_dqdk", "chunk_dv": "chunk_dv",
+                "rowsum_state": "rowsum_state", "dla_carry": "dla_carry",
+                "bwd_inter": "bwd_inter", "seg_output": "seg_output", "decode": "decode"}
+
+
+def launch_name(kname):
+    """The launch name of a kernel as rocprofv3 reports it, or None.  The
+    prep and recurrence kernels' last template argument is the time-reversed
+    mode of the backward's dv pass (..., true> / ...Lb1EEEv); the
+    recurrence's one before it is 1 for the output pass and 0 for the
+    segments' local-state pass."""
+    import re
+    m = re.search(r"k_([a-z_]+[a-z])", kname)
+    if not m or m.group(1) not in KERNEL_NAMES:
+        return None
+    name = KERNEL_NAMES[m.group(1)]
+    if name in ("chunk_prep", "chunk_recur"):
+        tail = re.search(r"L[ib](\d)ELb([01])EEEv", kname)      # mangled
+        dtail = re.search(r",\s*(\d+),\s*(true|false)\s*>", kname)  # demangled
+        if name == "chunk_prep":
+            rev = bool(re.search(r"Lb1EEEv", kname) or re.search(r",\s*true\s*>", kname))
+        else:
+            out, rev = True, False
+            if tail:
+                out, rev = tail.group(1) == "1", tail.group(2) == "1"
+            elif dtail:
+                out, rev = dtail.group(1) == "1", dtail.group(2) == "true"
+            if not out:
+                name = "recur_local"
+        if rev:
+            name += "_rev"
+    return name
 
 
 def log(*a):
@@ -368,8 +400,14 @@ def backward_leg(w, args, torch, gla, _abi, dev, stream):
     comp = compulsory_bwd(w, esize)
     fl = flops_bwd(w)
     gbps = comp / (bwd_ms * 1e-3) / 1e9
-    kernels = {n: {"launches": len(l), "avg_us": round(sum(l) / len(l) * 1e3, 2)}
-               for n, l in per.items()}
+    kernels = {}
+    for n, l in per.items():
+        kernels[n] = {"launches": len(l), "avg_us": round(sum(l) / len(l) * 1e3, 2)}
+        tr = measured_traffic(n, w.name)
+        if tr:
+            kernels[n]["traffic"] = tr["bytes_per_launch"]
+            kernels[n]["traffic_read"] = tr["read_bytes_per_launch"]
+            kernels[n]["traffic_write"] = tr["write_bytes_per_launch"]
     log(f"[bench] {w.name}: bwd {bwd_ms * 1e3:.1f} us, fwd+bwd {fb_ms * 1e3:.1f} us; {kernels}")
     del fws, bws, outs
     return {"workload": w.name, "steps": kb,
@@ -588,7 +626,6 @@ def cpu_baseline(w):
 def _counter_sums(d):
     """{launch name: (dispatches, mean counter value)} from a rocprofv3 --pmc
     run's counter_collection.csv files under directory d."""
-    import re
     acc = {}
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -597,18 +634,7 @@ def _counter_sums(d):
         with open(fn) as f:
             per_dispatch = {}
             for row in csv.DictReader(f):
-                kname = row.get("Kernel_Name", "")
-                name = None
-                for key, nm in KERNEL_NAMES:
-                    if key in kname:
-                        name = nm
-                        # the recurrence's last template argument is 1 for the
-                        # output pass and 0 for the local-state pass (mangled:
-                        # ...Li0EEEv, demangled: ..., 0>)
-                        if key == "k_chunk_recur" and (re.search(r"Li0EEEv", kname) or
-                                                       re.search(r",\s*0\s*>", kname)):
-                            name = "recur_local"
-                        break
+                name = launch_name(row.get("Kernel_Name", ""))
                 if name is None:
                     continue
                 did = row.get("Dispatch_Id")
