@@ -153,22 +153,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   constexpr int WC = NCT < 4 ? NCT : 4, WR = 4 / WC;
   constexpr int NCW = NCT / WC, NRW = (NRT + WR - 1) / WR;
   __shared__ float dad[C][17];                              // diagonal blocks, fp32
-  __shared__ float qf[C][LDK], kf[C][LDK], bt[C][LDK], al[C][LDK];
-  // One region serves, in turn, the dq blocks' dA (diagonal blocks zeroed)
-  // and operand, the dk blocks' dA^T ([r][m]) and operand, and the diagonal
-  // blocks' terms of dq and dk (dgo).  Operands are [ch][column] (OffCols),
-  // each with its low part for bf16.
+  __shared__ float qf[C][LDK], kf[C][LDK], bt[C][LDK];
+  // One region serves, in turn, dA with its diagonal blocks zeroed (rows for
+  // the dq blocks, transposed reads for the dk blocks; with its low part for
+  // bf16), the diagonal blocks' terms of dq and dk (dgo), and dlog b.
   using OC = OffCols<M::K, C>;
-  constexpr int LDO = (OC::WQ > OC::WK ? OC::WQ : OC::WK) + PT;
   constexpr int DA_BYTES = C * LDA * (int)sizeof(T), DAL_BYTES = BF ? DA_BYTES : 0;
-  constexpr int OP_BYTES = TK * LDO * (int)sizeof(T), OPL_BYTES = BF ? OP_BYTES : 0;
-  constexpr int OFF_BYTES = DA_BYTES + DAL_BYTES + OP_BYTES + OPL_BYTES;
+  constexpr int OFF_BYTES = DA_BYTES + DAL_BYTES;
   constexpr int DGO_BYTES = 2 * C * (TK + 4) * 4;
+  static_assert(C * LDK * 4 <= DGO_BYTES, "dlog b fits the region");
   __shared__ __attribute__((aligned(16))) unsigned char ubuf[OFF_BYTES > DGO_BYTES ? OFF_BYTES : DGO_BYTES];
   auto da = reinterpret_cast<T(*)[LDA]>(ubuf);
   auto dal = reinterpret_cast<T(*)[LDA]>(ubuf + DA_BYTES);
-  auto op = reinterpret_cast<T(*)[LDO]>(ubuf + DA_BYTES + DAL_BYTES);
-  auto opl = reinterpret_cast<T(*)[LDO]>(ubuf + DA_BYTES + DAL_BYTES + OP_BYTES);
   auto dgo = reinterpret_cast<float(*)[C][TK + 4]>(ubuf);
 
   const int n = blockIdx.x, c0 = blockIdx.y * TK, bh = blockIdx.z;
@@ -285,8 +281,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   }
 
   // dA rows of the block as 4-element vectors (hi / lo split, the diagonal
-  // blocks zeroed and kept in fp32 apart); with transpose, its columns
-  auto stage_da = [&](bool transpose) __attribute__((always_inline)) {
+  // blocks zeroed and kept in fp32 apart)
+  auto stage_da = [&]() __attribute__((always_inline)) {
     if (!has_da) return;
     const bool dgb = (m0 >> 4) == (c4 >> 4);  // inside a diagonal 16 x 16 block
     floatx4 hi[4], lo[4];
@@ -294,32 +290,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (dgb && !transpose) dad[m0 + i][(c4 + e) & 15] = xda[i][e];
+        if (dgb) dad[m0 + i][(c4 + e) & 15] = xda[i][e];
         const float xo = dgb ? 0.f : xda[i][e];
         hi[i][e] = to_f32(from_f32<T>(xo));
         lo[i][e] = xo - hi[i][e];
       }
-    if (!transpose) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        store4(&da[m0 + i][c4], hi[i]);
-        if constexpr (BF) store4(&dal[m0 + i][c4], lo[i]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        floatx4 th, tl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          th[i] = hi[i][e];
-          tl[i] = lo[i][e];
-        }
-        store4(&da[c4 + e][m0], th);
-        if constexpr (BF) store4(&dal[c4 + e][m0], tl);
-      }
+    for (int i = 0; i < 4; ++i) {
+      store4(&da[m0 + i][c4], hi[i]);
+      if constexpr (BF) store4(&dal[m0 + i][c4], lo[i]);
     }
   };
-  stage_da(false);
+  stage_da();
   // q, k (0 past the end of the sequence) and the cumsum of the tile
   if (has_tile) {
     float x[8];
@@ -334,10 +316,6 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     store8(&bt[trow][tc], x);
   }
   lds_barrier();
-  for (int it = tid; it < C * TK; it += kThreads) {
-    const int row = it / TK, c = it % TK;
-    al[row][c] = (row & 15) ? gexp<T>(bt[row][c] - bt[row - 1][c]) : 1.f;
-  }
 
   // inter-chunk terms: dO S_{n-1}^T and V dS_n^T, reduction over d_v, in
   // groups of KG K steps whose operands are loaded before their products are
@@ -354,7 +332,6 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         if (kk0 + gk * M::K < dv) inter_mma(f, gk);
     }
   }
-  lds_barrier();  // al ready
   if constexpr (!IB) {
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
@@ -378,28 +355,29 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   // of each block (both factors <= 1):
   //   dq rows of sub-chunk j:  e^{B_m - z_j} ⊙ [dA_off (K ⊙ e^{z_j - B})]
   //   dk rows of sub-chunk u:  e^{z'_u - B_r} ⊙ [dA_off^T (Q ⊙ e^{B - z'_u})]
-  // First the dq blocks, then the dk blocks in the same LDS: each operand is
-  // formed in one pass, then every wave handles the blocks of its row tiles.
-  if constexpr (NRT > 1) {
-    // 8 consecutive columns (rows of the chunk) of one channel per unit; the
-    // block boundaries of the column layout are multiples of 8
-    static_assert(OC::WQ % 8 == 0 && OC::WK % 8 == 0, "8-column units");
-    for (int it = tid; it < TK * (OC::WQ / 8); it += kThreads) {
-      const int c = it % TK, col = (it / TK) * 8;
-      int j = 1;
-      while (j + 1 < NRT && col >= OC::OQ(j + 1)) ++j;
-      const int r = col - OC::OQ(j);
-      const float z = bt[16 * j][c];
-      float x[8], lo[8];
+  // Each lane forms its own B operand (its output channel, the K rows its
+  // fragment holds) from the staged k or q and the cumsum, with the low part
+  // for bf16; the A operand is dA's rows (dq) or, read transposed, its
+  // columns (dk).  Nothing is written to LDS here.
+  // x = src[tok][c] e^{+-(B_tok - z)} for tok in [t0, t1), else 0
+  auto gated = [&](const float (*src)[LDK], int c, int kc, int t0, int t1, float z, bool up,
+                   typename M::frag& fh, typename M::frag& fl) __attribute__((always_inline)) {
+    if constexpr (BF) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[e] = r + e < 16 * j ? kf[r + e][c] * gexp<T>(z - bt[r + e][c]) : 0.f;
-        lo[e] = x[e] - to_f32(from_f32<T>(x[e]));
+        const int tok = kc + e;
+        const float g = up ? bt[tok][c] - z : z - bt[tok][c];
+        const float x = (tok >= t0 && tok < t1) ? src[tok][c] * gexp<T>(g) : 0.f;
+        fh[e] = static_cast<bf16>(x);
+        fl[e] = static_cast<bf16>(x - static_cast<float>(fh[e]));
       }
-      store8(&op[c][col], x);
-      if constexpr (BF) store8(&opl[c][col], lo);
+    } else {
+      const float g = up ? bt[kc][c] - z : z - bt[kc][c];
+      fh = (kc >= t0 && kc < t1) ? src[kc][c] * gexp<T>(g) : 0.f;
+      fl = 0.f;
     }
-    lds_barrier();
+  };
+  if constexpr (NRT > 1) {
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
       const int j = wr + WR * rt;
@@ -407,42 +385,26 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
+        const float z = bt[16 * j][c];
         floatx4 t4 = zero4();
         for (int kk = 0; kk < OC::KQ(j); kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
-          auto b = load_frag<T>(&op[c][OC::OQ(j) + kc]);
-          auto ah = load_frag<T>(&da[j * 16 + (l & 15)][kc]);
-          t4 = M::run(ah, b, t4);
+          typename M::frag bh, bl;
+          gated(kf, c, kc, 0, 16 * j, z, false, bh, bl);
+          const auto ah = load_frag<T>(&da[j * 16 + (l & 15)][kc]);
+          t4 = M::run(ah, bh, t4);
           if constexpr (BF) {
-            t4 = M::run(load_frag<T>(&dal[j * 16 + (l & 15)][kc]), b, t4);
-            t4 = M::run(ah, load_frag<T>(&opl[c][OC::OQ(j) + kc]), t4);
+            t4 = M::run(load_frag<T>(&dal[j * 16 + (l & 15)][kc]), bh, t4);
+            t4 = M::run(ah, bl, t4);
           }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = j * 16 + (l >> 4) * 4 + r;
-          aq[rt][ct][r] += gexp<T>(bt[row][c] - bt[16 * j][c]) * t4[r];
+          aq[rt][ct][r] += gexp<T>(bt[row][c] - z) * t4[r];
         }
       }
     }
-    lds_barrier();  // done with dA and the dq operand
-    stage_da(true);
-    for (int it = tid; it < TK * (OC::WK / 8); it += kThreads) {
-      const int c = it % TK, col = (it / TK) * 8;
-      int u = 0;
-      while (u + 2 < NRT && col >= OC::OK(u + 1)) ++u;
-      const int m = OC::MLO(u) + col - OC::OK(u);
-      const float z = bt[16 * u + 15][c];
-      float x[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = m + e >= 16 * (u + 1) ? qf[m + e][c] * gexp<T>(bt[m + e][c] - z) : 0.f;
-        lo[e] = x[e] - to_f32(from_f32<T>(x[e]));
-      }
-      store8(&op[c][col], x);
-      if constexpr (BF) store8(&opl[c][col], lo);
-    }
-    lds_barrier();
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
       const int u = wr + WR * rt;
@@ -450,22 +412,29 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
+        const float z = bt[16 * u + 15][c];
         floatx4 t4 = zero4();
         for (int kk = OC::MLO(u); kk < C; kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
-          const int oc = OC::OK(u) + kc - OC::MLO(u);
-          auto b = load_frag<T>(&op[c][oc]);
-          auto ah = load_frag<T>(&da[u * 16 + (l & 15)][kc]);
-          t4 = M::run(ah, b, t4);
+          typename M::frag bh, bl, ah, alo;
+          gated(qf, c, kc, 16 * (u + 1), C, z, true, bh, bl);
+          // A[r][m] = dA[m][r] for r in sub-chunk u (the lane's row), m at kc
           if constexpr (BF) {
-            t4 = M::run(load_frag<T>(&dal[u * 16 + (l & 15)][kc]), b, t4);
-            t4 = M::run(ah, load_frag<T>(&opl[c][oc]), t4);
+            ah = col_frag_tr(&da[0][0], LDA, kk, 16 * u, l);
+            alo = col_frag_tr(&dal[0][0], LDA, kk, 16 * u, l);
+          } else {
+            ah = da[kc][16 * u + (l & 15)];
+          }
+          t4 = M::run(ah, bh, t4);
+          if constexpr (BF) {
+            t4 = M::run(alo, bh, t4);
+            t4 = M::run(ah, bl, t4);
           }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = u * 16 + (l >> 4) * 4 + r;
-          ak[rt][ct][r] += gexp<T>(bt[16 * u + 15][c] - bt[row][c]) * t4[r];
+          ak[rt][ct][r] += gexp<T>(z - bt[row][c]) * t4[r];
         }
       }
     }
@@ -481,7 +450,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     float a[16], x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      a[i] = al[16 * b + i][c];
+      // the per-row gate alpha of row i in the block (row 0's is not used)
+      a[i] = i ? gexp<T>(bt[16 * b + i][c] - bt[16 * b + i - 1][c]) : 1.f;
       x[i] = which ? qf[16 * b + i][c] : kf[16 * b + i][c];
     }
     const float* dd = &dad[16 * b][0];  // [16][17]: dA[16 b + m][16 b + s]
@@ -528,7 +498,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     }
   }
   lds_barrier();  // everyone is done with bt / al / the operands
-  float* dlb = &al[0][0];  // reuse: dlog b of the tile, [C][LDK]
+  float* dlb = reinterpret_cast<float*>(ubuf);  // reuse: dlog b of the tile, [C][LDK]
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
     const int rti = wr + WR * rt;
