@@ -36,7 +36,7 @@
 // (k_gg_gate_tot / k_gg_gate_fin).
 #include "gla_common.h"
 #include "gla_internal.h"
-#include "gla_pblock.h"  // xcd_logical
+#include "gla_pblock.h"  // xcd_logical, load8
 
 namespace gla {
 
@@ -142,21 +142,43 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   float* cl = cs + kGC * ld;  // lo part
   float* part = cl + kGC * ld;  // the four waves' partial P tiles
   uint32_t* umask = reinterpret_cast<uint32_t*>(part + 1024);  // channels left to the log-space sum
+  // Q~ and K~ in record order, written out in 16-byte units (16-byte
+  // aligned: the arrays above are 4 (16 (dkp + 1)) + 1032 floats)
+  T* stg = reinterpret_cast<T*>(umask + 8);
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   if (tid < 8) umask[tid] = 0u;
-  for (int x = tid; x < kGC * dkp; x += kThreads) {
-    const int t = x / dkp, i = x - t * dkp, u = n * kGC + t;
+  // q, k and log alpha of the chunk, 8 channels per load (dk is a multiple of
+  // 16 and the padded channels are zero)
+  for (int x = tid; x < kGC * (dkp / 8); x += kThreads) {
+    const int t = x / (dkp / 8), i = (x - t * (dkp / 8)) * 8, u = n * kGC + t;
     const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
-    const bool in = i < dk;
-    qs[t * ld + i] = (in && dr >= 0) ? to_f32(q[((size_t)bh * L + dr) * dk + i]) : 0.f;
-    ks[t * ld + i] = (in && dr >= 0) ? to_f32(k[((size_t)bh * L + dr) * dk + i]) : 0.f;
-    cs[t * ld + i] = (in && gr >= 0) ? la[((size_t)bh * L + gr) * dk + i] : 0.f;
+    float qv[8], kv[8], av[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = kv[e] = av[e] = 0.f;
+    if (i < dk && dr >= 0) {
+      const size_t o = ((size_t)bh * L + dr) * dk + i;
+      load8(q + o, qv);
+      load8(k + o, kv);
+    }
+    if (i < dk && gr >= 0) {
+      const f32x4* a4 = reinterpret_cast<const f32x4*>(la + ((size_t)bh * L + gr) * dk + i);
+      const f32x4 a0 = a4[0], a1 = a4[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        av[e] = a0[e];
+        av[e + 4] = a1[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qs[t * ld + i + e] = qv[e];
+      ks[t * ld + i + e] = kv[e];
+      cs[t * ld + i + e] = av[e];
+    }
   }
   __syncthreads();
   uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
-  T* qf = reinterpret_cast<T*>(r);
-  T* kf = qf + kGC * dkp;
-  float* pf = reinterpret_cast<float*>(kf + kGC * dkp);
+  float* pf = reinterpret_cast<float*>(r + (size_t)2 * kGC * dkp * sizeof(T));
   float* ga = pf + kPfFloats;
   for (int i = tid; i < dkp; i += kThreads) {
     float c = 0.f, e = 0.f;
@@ -173,11 +195,18 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
       const float at = cs[t * ld + i], al = cl[t * ld + i];
-      qf[qf_index<T>(t, i)] = from_f32<T>(qs[t * ld + i] * gexp<T>(at + al));
-      kf[kf_index(t, i)] = from_f32<T>(ks[t * ld + i] * gexp<T>((c - at) + (e - al)));
+      stg[qf_index<T>(t, i)] = from_f32<T>(qs[t * ld + i] * gexp<T>(at + al));
+      stg[kGC * dkp + kf_index(t, i)] = from_f32<T>(ks[t * ld + i] * gexp<T>((c - at) + (e - al)));
     }
   }
   __syncthreads();
+  // the Q~ and K~ records (contiguous at the record's start)
+  {
+    const int units = 2 * kGC * dkp * (int)sizeof(T) / 16;
+    const f32x4* src = reinterpret_cast<const f32x4*>(stg);
+    f32x4* dst = reinterpret_cast<f32x4*>(r);
+    for (int x = tid; x < units; x += kThreads) dst[x] = src[x];
+  }
   // P[t][s] = sum_i q_t[i] k_s[i] e^{A_t[i] - A_s[i]}.  Channels whose decay
   // over the chunk stays under e^{kSafeP} take one fp32 MFMA tile with the
   // chunk's first row as reference, (q_t e^{A_t - A_0}) (k_s e^{A_0 - A_s}),
@@ -709,8 +738,10 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
   const size_t rb = gg_rec_bytes(is_bf16, dkp);
   uint8_t* r = static_cast<uint8_t*>(rec);
   if (part == 0) {
-    // 4 arrays of 16 padded rows, 4 partial P tiles, 8 mask words: 69.9 KB at 256 channels
-    const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + 8);
+    // 4 arrays of 16 padded rows, 4 partial P tiles, 8 mask words, and the
+    // staged Q~ and K~: 101.9 KB at 256 fp32 channels
+    const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + 8) +
+                       (size_t)2 * kGC * dkp * (is_bf16 ? 2 : 4);
     const dim3 pg(NC, BH);
     hipError_t e;
     if (is_bf16) {
