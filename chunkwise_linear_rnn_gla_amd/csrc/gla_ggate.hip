@@ -142,9 +142,13 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   float* cl = cs + kGC * ld;  // lo part
   float* part = cl + kGC * ld;  // the four waves' partial P tiles
   uint32_t* umask = reinterpret_cast<uint32_t*>(part + 1024);  // channels left to the log-space sum
-  // Q~ and K~ in record order, written out in 16-byte units (16-byte
-  // aligned: the arrays above are 4 (16 (dkp + 1)) + 1032 floats)
-  T* stg = reinterpret_cast<T*>(umask + 8);
+  // bf16: Q~ and K~ in record order, written out in 16-byte units (16-byte
+  // aligned: the arrays above are 4 (16 (dkp + 1)) + 1032 floats).  fp32
+  // stores its elements directly: staging would take the 256-channel
+  // passes' LDS past what lets two workgroups share a CU.
+  constexpr bool STAGE = sizeof(T) == 2;
+  uint8_t* r = rec + ((size_t)blockIdx.y * NC + blockIdx.x) * rec_bytes;
+  T* stg = STAGE ? reinterpret_cast<T*>(umask + 8) : reinterpret_cast<T*>(r);
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   if (tid < 8) umask[tid] = 0u;
   // q, k and log alpha of the chunk, 8 channels per load (dk is a multiple of
@@ -177,7 +181,6 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
     }
   }
   __syncthreads();
-  uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
   float* pf = reinterpret_cast<float*>(r + (size_t)2 * kGC * dkp * sizeof(T));
   float* ga = pf + kPfFloats;
   for (int i = tid; i < dkp; i += kThreads) {
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   }
   __syncthreads();
   // the Q~ and K~ records (contiguous at the record's start)
-  {
+  if constexpr (STAGE) {
     const int units = 2 * kGC * dkp * (int)sizeof(T) / 16;
     const f32x4* src = reinterpret_cast<const f32x4*>(stg);
     f32x4* dst = reinterpret_cast<f32x4*>(r);
@@ -738,10 +741,10 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
   const size_t rb = gg_rec_bytes(is_bf16, dkp);
   uint8_t* r = static_cast<uint8_t*>(rec);
   if (part == 0) {
-    // 4 arrays of 16 padded rows, 4 partial P tiles, 8 mask words, and the
-    // staged Q~ and K~: 101.9 KB at 256 fp32 channels
+    // 4 arrays of 16 padded rows, 4 partial P tiles, 8 mask words (69.9 KB at
+    // 256 fp32 channels), and for bf16 the staged Q~ and K~
     const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + 8) +
-                       (size_t)2 * kGC * dkp * (is_bf16 ? 2 : 4);
+                       (is_bf16 ? (size_t)2 * kGC * dkp * 2 : 0);
     const dim3 pg(NC, BH);
     hipError_t e;
     if (is_bf16) {
