@@ -33,7 +33,7 @@
 // A pass can read its sequence backwards with the gates shifted by one token
 // and take its initial state transposed; the backward is built from such
 // passes (gla_api.hip).  Gate gradients come from the closed form of App. C
-// (k_gg_gate_tot / k_gg_gate_fin).
+// (k_gg_gate_scan, k_gg_gate_carry, k_gg_gate_add).
 #include "gla_common.h"
 #include "gla_internal.h"
 #include "gla_pblock.h"  // xcd_logical, load8
@@ -619,75 +619,126 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
 // and each dlog gate is the sum over later tokens, plus the row / column sums
 // of hT ⊙ dhT.  dq, dk, dv and o enter without their same-token terms, whose
 // contributions to the two differences are equal and cancel exactly; what is
-// left is the part that the gates decay.  Chunks of kGT tokens: totals first,
-// then the carry-in.
+// left is the part that the gates decay.  The suffix sums run in groups of kGT
+// tokens: each group's own suffix sums and its total (k_gg_gate_scan), the
+// carry into each group from the totals after it (k_gg_gate_carry), then the
+// carry added to the group's rows (k_gg_gate_add).  Every operand is read
+// once, four channels per lane.
 constexpr int kGT = 64;
 
-template <typename T>
-__device__ inline float gg_term(int c, size_t row, int dk, int dv, const T* q, const T* k,
-                                const float* dq, const float* dkk, const float* o32,
-                                const T* dout, const T* v, const float* dvv) {
-  if (c < dk) {
-    const size_t x = row * dk + c;
-    return to_f32(q[x]) * dq[x] - to_f32(k[x]) * dkk[x];
-  }
-  const size_t x = row * dv + (c - dk);
-  return o32[x] * to_f32(dout[x]) - to_f32(v[x]) * dvv[x];
+// Four consecutive elements as fp32 (8- or 16-byte loads).
+template <typename T> __device__ inline f4 ld4(const T* p);
+template <> __device__ inline f4 ld4<float>(const float* p) {
+  return *reinterpret_cast<const f4*>(p);
+}
+template <> __device__ inline f4 ld4<bf16>(const bf16* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  f4 r;
+  r[0] = __uint_as_float(u.x << 16);
+  r[1] = __uint_as_float(u.x & 0xffff0000u);
+  r[2] = __uint_as_float(u.y << 16);
+  r[3] = __uint_as_float(u.y & 0xffff0000u);
+  return r;
 }
 
-// grid (ceil(L / kGT), BH); tot [BH][NG][dk + dv]
+// grid (ceil(L / kGT), BH, 2), one wave; z = 0: the d_k channels (q ⊙ dq -
+// k ⊙ dk into dla), z = 1: the d_v channels (do ⊙ o - v ⊙ dv into dlb).  Lane
+// l owns channels 4 l .. 4 l + 3.  Writes the group's suffix sums to dla /
+// dlb and its totals to tot [BH][NG][dk + dv].
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_gg_gate_tot(
+__global__ __launch_bounds__(kWave) void k_gg_gate_scan(
     const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ dq,
     const float* __restrict__ dkk, const float* __restrict__ o32, const T* __restrict__ dout,
-    const T* __restrict__ v, const float* __restrict__ dvv, float* __restrict__ tot, int L,
-    int dk, int dv) {
-  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, D = dk + dv;
+    const T* __restrict__ v, const float* __restrict__ dvv, float* __restrict__ tot,
+    float* __restrict__ dla, float* __restrict__ dlb, int L, int dk, int dv) {
+  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, half = blockIdx.z;
+  const int d = half ? dv : dk, c = 4 * threadIdx.x;
+  if (c >= d) return;
+  const T* a = half ? dout : q;
+  const float* b = half ? o32 : dq;
+  const T* x2 = half ? v : k;
+  const float* y2 = half ? dvv : dkk;
+  float* out = half ? dlb : dla;
   const int t0 = cg * kGT, t1 = min(L, t0 + kGT);
-  for (int c = threadIdx.x; c < D; c += kThreads) {
-    float s = 0.f;
-    for (int t = t0; t < t1; ++t)
-      s += gg_term(c, (size_t)bh * L + t, dk, dv, q, k, dq, dkk, o32, dout, v, dvv);
-    tot[((size_t)bh * NG + cg) * D + c] = s;
+  f4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int t = t1 - 1; t >= t0; --t) {
+    const size_t x = ((size_t)bh * L + t) * d + c;
+    const f4 av = ld4(a + x), bv = ld4(b + x), cv = ld4(x2 + x), ev = ld4(y2 + x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) run[e] += av[e] * bv[e] - cv[e] * ev[e];
+    *reinterpret_cast<f4*>(out + x) = run;
+  }
+  *reinterpret_cast<f4*>(tot + ((size_t)bh * NG + cg) * (dk + dv) + (half ? dk : 0) + c) = run;
+}
+
+// grid (BH, ceil((dk + dv) / kWave)), one wave: tot[bh][g][c] <- hs[bh][c] +
+// the totals of the groups after g (hs: null for zeros).  The totals are read
+// in batches ahead of the stores that overwrite them.
+__global__ __launch_bounds__(kWave) void k_gg_gate_carry(float* __restrict__ tot,
+                                                         const float* __restrict__ hs, int NG,
+                                                         int D) {
+  const int bh = blockIdx.x, c = blockIdx.y * kWave + threadIdx.x;
+  if (c >= D) return;
+  float run = hs ? hs[(size_t)bh * D + c] : 0.f;
+  float* p = tot + (size_t)bh * NG * D + c;
+  constexpr int kB = 16;
+  for (int g1 = NG; g1 > 0; g1 -= kB) {
+    float x[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) x[i] = g1 - 1 - i >= 0 ? p[(size_t)(g1 - 1 - i) * D] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kB; ++i)
+      if (g1 - 1 - i >= 0) {
+        p[(size_t)(g1 - 1 - i) * D] = run;
+        run += x[i];
+      }
   }
 }
 
-// grid (BH); hs [BH][dk + dv] = row sums, then column sums, of hT ⊙ dhT
+// grid (ceil(L / kGT), BH, 2), one wave: the carry of k_gg_gate_carry added
+// to the group's rows of dla / dlb.
+__global__ __launch_bounds__(kWave) void k_gg_gate_add(const float* __restrict__ tot,
+                                                       float* __restrict__ dla,
+                                                       float* __restrict__ dlb, int L, int dk,
+                                                       int dv) {
+  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, half = blockIdx.z;
+  const int d = half ? dv : dk, c = 4 * threadIdx.x;
+  if (c >= d) return;
+  float* out = half ? dlb : dla;
+  const f4 cy =
+      *reinterpret_cast<const f4*>(tot + ((size_t)bh * NG + cg) * (dk + dv) + (half ? dk : 0) + c);
+  const int t0 = cg * kGT, t1 = min(L, t0 + kGT);
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) {
+    f4* o = reinterpret_cast<f4*>(out + ((size_t)bh * L + t) * d + c);
+    f4 x = *o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] += cy[e];
+    *o = x;
+  }
+}
+
+// grid (BH), kThreads; hs [BH][dk + dv] = row sums, then column sums, of
+// hT ⊙ dhT: a wave per row for the row sums, a lane per column for the
+// column sums (both read along the rows).
 __global__ __launch_bounds__(kThreads) void k_gg_hsum(const float* __restrict__ hT,
                                                       const float* __restrict__ dhT,
                                                       float* __restrict__ hs, int dk, int dv) {
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x, w = threadIdx.x / kWave, l = threadIdx.x & (kWave - 1);
   const float* h = hT + (size_t)bh * dk * dv;
   const float* d = dhT + (size_t)bh * dk * dv;
-  for (int c = threadIdx.x; c < dk + dv; c += kThreads) {
+  for (int i = w; i < dk; i += kThreads / kWave) {
     float s = 0.f;
-    if (c < dk)
-      for (int j = 0; j < dv; ++j) s += h[(size_t)c * dv + j] * d[(size_t)c * dv + j];
-    else
-      for (int i = 0; i < dk; ++i) s += h[(size_t)i * dv + c - dk] * d[(size_t)i * dv + c - dk];
-    hs[(size_t)bh * (dk + dv) + c] = s;
+    for (int j = l; j < dv; j += kWave) s += h[(size_t)i * dv + j] * d[(size_t)i * dv + j];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (l == 0) hs[(size_t)bh * (dk + dv) + i] = s;
   }
-}
-
-// grid (ceil(L / kGT), BH): dlog alpha and dlog beta
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_gg_gate_fin(
-    const T* __restrict__ q, const T* __restrict__ k, const float* __restrict__ dq,
-    const float* __restrict__ dkk, const float* __restrict__ o32, const T* __restrict__ dout,
-    const T* __restrict__ v, const float* __restrict__ dvv, const float* __restrict__ tot,
-    const float* __restrict__ hs, float* __restrict__ dla, float* __restrict__ dlb, int L,
-    int dk, int dv) {
-  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, D = dk + dv;
-  const int t0 = cg * kGT, t1 = min(L, t0 + kGT);
-  for (int c = threadIdx.x; c < D; c += kThreads) {
-    float run = hs ? hs[(size_t)bh * D + c] : 0.f;
-    for (int g2 = cg + 1; g2 < NG; ++g2) run += tot[((size_t)bh * NG + g2) * D + c];
-    for (int t = t1 - 1; t >= t0; --t) {
-      const size_t row = (size_t)bh * L + t;
-      run += gg_term(c, row, dk, dv, q, k, dq, dkk, o32, dout, v, dvv);
-      if (c < dk) dla[row * dk + c] = run;
-      else dlb[row * dv + c - dk] = run;
-    }
+  for (int j = threadIdx.x; j < dv; j += kThreads) {
+    float s = 0.f;
+    for (int i = 0; i < dk; ++i) s += h[(size_t)i * dv + j] * d[(size_t)i * dv + j];
+    hs[(size_t)bh * (dk + dv) + dk + j] = s;
   }
 }
 
@@ -781,24 +832,20 @@ hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const voi
                            const void* dout, const void* v, const float* dv32, const float* hT,
                            const float* dhT, float* tot, float* hs, float* dla, float* dlb,
                            hipStream_t s) {
-  const dim3 grid(gg_gate_groups(L), BH);
+  const int NG = gg_gate_groups(L), D = dk + dv;
+  const dim3 grid(NG, BH, 2);
   if (dhT) hipLaunchKernelGGL(k_gg_hsum, dim3(BH), dim3(kThreads), 0, s, hT, dhT, hs, dk, dv);
-  const float* hsp = dhT ? hs : nullptr;
-  if (is_bf16) {
-    hipLaunchKernelGGL((k_gg_gate_tot<bf16>), grid, dim3(kThreads), 0, s, (const bf16*)q,
+  if (is_bf16)
+    hipLaunchKernelGGL((k_gg_gate_scan<bf16>), grid, dim3(kWave), 0, s, (const bf16*)q,
                        (const bf16*)k, dq32, dk32, o32, (const bf16*)dout, (const bf16*)v, dv32,
-                       tot, L, dk, dv);
-    hipLaunchKernelGGL((k_gg_gate_fin<bf16>), grid, dim3(kThreads), 0, s, (const bf16*)q,
-                       (const bf16*)k, dq32, dk32, o32, (const bf16*)dout, (const bf16*)v, dv32,
-                       tot, hsp, dla, dlb, L, dk, dv);
-  } else {
-    hipLaunchKernelGGL((k_gg_gate_tot<float>), grid, dim3(kThreads), 0, s, (const float*)q,
+                       tot, dla, dlb, L, dk, dv);
+  else
+    hipLaunchKernelGGL((k_gg_gate_scan<float>), grid, dim3(kWave), 0, s, (const float*)q,
                        (const float*)k, dq32, dk32, o32, (const float*)dout, (const float*)v,
-                       dv32, tot, L, dk, dv);
-    hipLaunchKernelGGL((k_gg_gate_fin<float>), grid, dim3(kThreads), 0, s, (const float*)q,
-                       (const float*)k, dq32, dk32, o32, (const float*)dout, (const float*)v,
-                       dv32, tot, hsp, dla, dlb, L, dk, dv);
-  }
+                       dv32, tot, dla, dlb, L, dk, dv);
+  hipLaunchKernelGGL(k_gg_gate_carry, dim3(BH, (D + kWave - 1) / kWave), dim3(kWave), 0, s, tot,
+                     dhT ? hs : nullptr, NG, D);
+  hipLaunchKernelGGL(k_gg_gate_add, grid, dim3(kWave), 0, s, tot, dla, dlb, L, dk, dv);
   return hipGetLastError();
 }
 
