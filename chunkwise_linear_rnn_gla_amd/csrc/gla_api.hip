@@ -602,7 +602,7 @@ static gla_status gg_validate(const gla_dims* d, int dtype) {
   const int q = dtype == GLA_BF16 ? 32 : 16;
   if (d->B < 0 || d->H < 0 || d->L < 0 || d->L > (1 << 24)) return GLA_ERR_SHAPE;
   if ((int64_t)d->B * d->H > 65535) return GLA_ERR_SHAPE;
-  if (d->dk < 16 || d->dk > 256 || d->dv < 16 || d->dv > 256) return GLA_ERR_SHAPE;
+  if (d->dk < 16 || d->dk > 256 || d->dv < 16 || d->dv > 512) return GLA_ERR_SHAPE;
   if (d->dk % q || d->dv % q) return GLA_ERR_SHAPE;
   return GLA_OK;
 }

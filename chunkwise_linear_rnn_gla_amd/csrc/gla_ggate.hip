@@ -113,13 +113,16 @@ __device__ inline int pf_index(int t, int s) { return ((t + 16 * (s >> 2)) << 2)
 }  // namespace
 
 constexpr int kPfFloats = 256 + 16;  // P below the diagonal, then its diagonal
+// State rows of a pass: up to 256 with bf16 records; the fp32 passes of the
+// backward whose rows are the d_v channels take up to 512.
+constexpr int kMaxRowsF32 = 512, kMaskWords = kMaxRowsF32 / 32;
 
 size_t gg_rec_bytes(int is_bf16, int dkp) {
   return (size_t)32 * dkp * (is_bf16 ? 2 : 4) + 4 * kPfFloats + (size_t)4 * dkp;
 }
 
 int gg_padded_dim(int is_bf16, int d) {
-  for (int p = is_bf16 ? 32 : 16; p <= 256; p *= 2)
+  for (int p = is_bf16 ? 32 : 16; p <= (is_bf16 ? 256 : kMaxRowsF32); p *= 2)
     if (d <= p) return p;
   return -1;
 }
@@ -143,14 +146,15 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   float* part = cl + kGC * ld;  // the four waves' partial P tiles
   uint32_t* umask = reinterpret_cast<uint32_t*>(part + 1024);  // channels left to the log-space sum
   // bf16: Q~ and K~ in record order, written out in 16-byte units (16-byte
-  // aligned: the arrays above are 4 (16 (dkp + 1)) + 1032 floats).  fp32
+  // aligned: the arrays above are 4 (16 (dkp + 1)) + 1024 + kMaskWords
+  // floats).  fp32
   // stores its elements directly: staging would take the 256-channel
   // passes' LDS past what lets two workgroups share a CU.
   constexpr bool STAGE = sizeof(T) == 2;
   uint8_t* r = rec + ((size_t)blockIdx.y * NC + blockIdx.x) * rec_bytes;
-  T* stg = STAGE ? reinterpret_cast<T*>(umask + 8) : reinterpret_cast<T*>(r);
+  T* stg = STAGE ? reinterpret_cast<T*>(umask + kMaskWords) : reinterpret_cast<T*>(r);
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  if (tid < 8) umask[tid] = 0u;
+  if (tid < kMaskWords) umask[tid] = 0u;
   // q, k and log alpha of the chunk, 8 channels per load (dk is a multiple of
   // 16 and the padded channels are zero)
   for (int x = tid; x < kGC * (dkp / 8); x += kThreads) {
@@ -641,9 +645,18 @@ template <> __device__ inline f4 ld4<bf16>(const bf16* p) {
   return r;
 }
 
-// grid (ceil(L / kGT), BH, 2), one wave; z = 0: the d_k channels (q ⊙ dq -
-// k ⊙ dk into dla), z = 1: the d_v channels (do ⊙ o - v ⊙ dv into dlb).  Lane
-// l owns channels 4 l .. 4 l + 3.  Writes the group's suffix sums to dla /
+// The channel blocks of the gate kernels: 256 channels (four per lane) each,
+// the d_k blocks first, then the d_v blocks (grid z).
+constexpr int kGQ = 4 * kWave;
+__device__ inline void gg_gate_block(int z, int dk, int dv, int& half, int& c) {
+  const int nzk = (dk + kGQ - 1) / kGQ;
+  half = z >= nzk;
+  c = 4 * (int)threadIdx.x + kGQ * (half ? z - nzk : z);
+}
+int gg_gate_zblocks(int dk, int dv) { return (dk + kGQ - 1) / kGQ + (dv + kGQ - 1) / kGQ; }
+
+// grid (ceil(L / kGT), BH, gg_gate_zblocks), one wave; the d_k channels take
+// q ⊙ dq - k ⊙ dk into dla, the d_v channels do ⊙ o - v ⊙ dv into dlb.  Writes the group's suffix sums to dla /
 // dlb and its totals to tot [BH][NG][dk + dv].
 template <typename T>
 __global__ __launch_bounds__(kWave) void k_gg_gate_scan(
@@ -651,8 +664,10 @@ __global__ __launch_bounds__(kWave) void k_gg_gate_scan(
     const float* __restrict__ dkk, const float* __restrict__ o32, const T* __restrict__ dout,
     const T* __restrict__ v, const float* __restrict__ dvv, float* __restrict__ tot,
     float* __restrict__ dla, float* __restrict__ dlb, int L, int dk, int dv) {
-  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, half = blockIdx.z;
-  const int d = half ? dv : dk, c = 4 * threadIdx.x;
+  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x;
+  int half, c;
+  gg_gate_block(blockIdx.z, dk, dv, half, c);
+  const int d = half ? dv : dk;
   if (c >= d) return;
   const T* a = half ? dout : q;
   const float* b = half ? o32 : dq;
@@ -696,14 +711,16 @@ __global__ __launch_bounds__(kWave) void k_gg_gate_carry(float* __restrict__ tot
   }
 }
 
-// grid (ceil(L / kGT), BH, 2), one wave: the carry of k_gg_gate_carry added
-// to the group's rows of dla / dlb.
+// grid as k_gg_gate_scan: the carry of k_gg_gate_carry added to the group's
+// rows of dla / dlb.
 __global__ __launch_bounds__(kWave) void k_gg_gate_add(const float* __restrict__ tot,
                                                        float* __restrict__ dla,
                                                        float* __restrict__ dlb, int L, int dk,
                                                        int dv) {
-  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x, half = blockIdx.z;
-  const int d = half ? dv : dk, c = 4 * threadIdx.x;
+  const int cg = blockIdx.x, bh = blockIdx.y, NG = gridDim.x;
+  int half, c;
+  gg_gate_block(blockIdx.z, dk, dv, half, c);
+  const int d = half ? dv : dk;
   if (c >= d) return;
   float* out = half ? dlb : dla;
   const f4 cy =
@@ -744,8 +761,11 @@ __global__ __launch_bounds__(kThreads) void k_gg_hsum(const float* __restrict__ 
 
 // ---- launchers ----
 
-// Waves per state tile: two from 64 state rows on (32 for fp32), one below.
-template <typename T> constexpr int gg_row_split(int MT) { return MT >= (sizeof(T) == 2 ? 4 : 2) ? 2 : 1; }
+// Waves per state tile: two from 64 state rows on (32 for fp32), one below;
+// four for the 512 rows of an fp32 pass.
+template <typename T> constexpr int gg_row_split(int MT) {
+  return MT >= 32 ? 4 : (MT >= (sizeof(T) == 2 ? 4 : 2) ? 2 : 1);
+}
 
 template <typename T, typename TO, typename TI>
 static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t* r, size_t rb,
@@ -758,6 +778,7 @@ static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t*
                      ps.dk, ps.dv, NC, ps.rev)
   if constexpr (sizeof(T) == 4) {
     if (dkp == 16) { GG_RECUR(1); return; }
+    if (dkp == 512) { GG_RECUR(32); return; }
   }
   if (dkp == 32) GG_RECUR(2);
   else if (dkp == 64) GG_RECUR(4);
@@ -792,9 +813,9 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
   const size_t rb = gg_rec_bytes(is_bf16, dkp);
   uint8_t* r = static_cast<uint8_t*>(rec);
   if (part == 0) {
-    // 4 arrays of 16 padded rows, 4 partial P tiles, 8 mask words (69.9 KB at
-    // 256 fp32 channels), and for bf16 the staged Q~ and K~
-    const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + 8) +
+    // 4 arrays of 16 padded rows, 4 partial P tiles, the mask words (69.9 KB
+    // at 256 fp32 channels, 135.5 KB at 512), and for bf16 the staged Q~ and K~
+    const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + kMaskWords) +
                        (is_bf16 ? (size_t)2 * kGC * dkp * 2 : 0);
     const dim3 pg(NC, BH);
     hipError_t e;
@@ -833,7 +854,7 @@ hipError_t launch_gg_gates(int is_bf16, int BH, int L, int dk, int dv, const voi
                            const float* dhT, float* tot, float* hs, float* dla, float* dlb,
                            hipStream_t s) {
   const int NG = gg_gate_groups(L), D = dk + dv;
-  const dim3 grid(NG, BH, 2);
+  const dim3 grid(NG, BH, gg_gate_zblocks(dk, dv));
   if (dhT) hipLaunchKernelGGL(k_gg_hsum, dim3(BH), dim3(kThreads), 0, s, hT, dhT, hs, dk, dv);
   if (is_bf16)
     hipLaunchKernelGGL((k_gg_gate_scan<bf16>), grid, dim3(kWave), 0, s, (const bf16*)q,

@@ -251,8 +251,9 @@ gla_status gla_decode(const gla_dims *dims, int dtype,
  * the cumulative products of alpha, beta; log_beta = 0 gives gla_fwd).  It is
  * computed chunkwise (App. C.2) in 16-token chunks; the chunk and subchunk
  * fields of dims are not used.
- *   dims: dk and dv multiples of 16 (GLA_FP32) or 32 (GLA_BF16), each in
- *         [16, 256]; B * H <= 65535; otherwise GLA_ERR_SHAPE.
+ *   dims: dk and dv multiples of 16 (GLA_FP32) or 32 (GLA_BF16), dk in
+ *         [16, 256] and dv in [16, 512] (the GLA-1.3B head shape, dk 256 and
+ *         dv 512, included); B * H <= 65535; otherwise GLA_ERR_SHAPE.
  *   in : q, k [B,H,L,dk], v [B,H,L,dv] in `dtype`; log_alpha [B,H,L,dk] and
  *        log_beta [B,H,L,dv] fp32 (entries <= 0 expected; not checked);
  *        h0 [B,H,dk,dv] fp32 or NULL for zeros.

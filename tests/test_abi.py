@@ -157,7 +157,8 @@ def test_general_gate_errors():
     args = [FAKE] * 5 + [None, FAKE, None]
     assert _abi.ggla_fwd(d, 2, *args, FAKE, n_fwd, None) == 3
     assert _abi.load().ggla_fwd(None, GLA_BF16, *([FAKE] * 8), FAKE, n_fwd, None) == 1
-    assert _abi.ggla_fwd(good_dims(dv=512), GLA_BF16, *args, FAKE, n_fwd, None) == 2
+    assert _abi.ggla_fwd(good_dims(dv=544), GLA_BF16, *args, FAKE, n_fwd, None) == 2
+    assert _abi.ggla_fwd(good_dims(dk=512), GLA_BF16, *args, FAKE, n_fwd, None) == 2
     assert _abi.ggla_fwd(good_dims(dk=48), GLA_BF16, *args, FAKE, n_fwd, None) == 2
     assert _abi.ggla_fwd(good_dims(B=300, H=300), GLA_BF16, *args, FAKE, n_fwd, None) == 2
     assert _abi.ggla_fwd(d, GLA_BF16, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE,

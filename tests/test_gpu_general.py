@@ -3,7 +3,7 @@ through the C ABI) against the fp64 oracle's token recurrence and its BPTT,
 element by element (relative L2 per tensor: <= 1e-5 for fp32 I/O, <= 5e-3 for
 bf16 I/O).  Shapes span several 16-token chunks with ragged tails, both
 gates sharp enough to take the log-space intra-chunk path, a unit column gate
-(where the row-gated path must agree), d_k / d_v up to 256, and empty
+(where the row-gated path must agree), d_k up to 256 and d_v up to 512, and empty
 sequences and batches."""
 import numpy as np
 import pytest
@@ -27,6 +27,9 @@ CASES = [
     ("bf16", 1, 1, 64, 256, 256, "sigmoid16", "sigmoid16", 0.5),
     ("bf16", 2, 1, 90, 32, 224, "extreme", "extreme", 0.5),
     ("bf16", 1, 2, 50, 96, 64, "zero", "const", 0.5),
+    # d_v = 512: the backward's transposed passes hold 512 state rows over four waves
+    ("fp32", 1, 1, 45, 32, 512, "sigmoid16", "sigmoid16", 0.5),
+    ("bf16", 1, 2, 70, 256, 512, "sigmoid16", "sigmoid16", 0.5),
 ]
 
 
@@ -154,10 +157,11 @@ def test_unit_column_gate_matches_row_gated_path():
     assert rel_l2(as_f64(h1), rh) <= TOL["bf16"] and rel_l2(as_f64(h2), rh) <= TOL["bf16"]
 
 
-def test_general_bench_shape_forward_and_backward():
-    # the bench head shape at full length: B8 H4 L2048 dk128 dv256 bf16
-    x, lb = _inputs("bf16", 8, 4, 2048, 128, 256, "sigmoid16", "sigmoid16", 0.0, seed=1001)
-    say("[ggla] bench shape B8 H4 L2048 dk128 dv256 bf16, forward and backward")
+@pytest.mark.parametrize("B,dk,dv", [(8, 128, 256), (4, 256, 512)], ids=["gla340m", "gla1p3b"])
+def test_general_layer_shapes_forward_and_backward(B, dk, dv):
+    # the GLA-340M and GLA-1.3B head shapes at full length (H4 L2048 bf16)
+    x, lb = _inputs("bf16", B, 4, 2048, dk, dv, "sigmoid16", "sigmoid16", 0.0, seed=1001 + dv)
+    say(f"[ggla] layer shape B{B} H4 L2048 dk{dk} dv{dv} bf16, forward and backward")
     d, lbd = _dev(x, lb)
     o, hT = fwd_general(d.q, d.k, d.v, d.log_alpha, lbd)
     g = bwd_general(d.q, d.k, d.v, d.log_alpha, lbd, None, d.do, None, want_dh0=False)
