@@ -73,6 +73,7 @@ KERNEL_SOURCES = [
     "chunkwise_linear_rnn_gla_amd/csrc/gla_bwd.hip",
     "chunkwise_linear_rnn_gla_amd/csrc/gla_bwd_recur.hip",
     "chunkwise_linear_rnn_gla_amd/csrc/gla_dma.h",
+    "chunkwise_linear_rnn_gla_amd/csrc/gla_ggate.hip",
     "chunkwise_linear_rnn_gla_amd/build.py",
 ]
 # rocprofv3 kernel names (mangled or demangled) -> the library's launch names
@@ -81,7 +82,10 @@ KERNEL_NAMES = {"chunk_prep": "chunk_prep", "chunk_recur": "chunk_recur",
                 "chunk_state": "chunk_state", "chunk_attn": "chunk_attn",
                 "chunk_dqdk": "chunk_dqdk", "chunk_dv": "chunk_dv",
                 "rowsum_state": "rowsum_state", "dla_carry": "dla_carry",
-                "bwd_inter": "bwd_inter", "seg_output": "seg_output", "decode": "decode"}
+                "bwd_inter": "bwd_inter", "seg_output": "seg_output", "decode": "decode",
+                "gg_prep": "gg_prep", "gg_recur": "gg_recur", "gg_gate_scan": "gg_gate_scan",
+                "gg_gate_carry": "gg_gate_carry", "gg_gate_add": "gg_gate_add",
+                "gg_hsum": "gg_hsum"}
 
 
 def launch_name(kname):
@@ -89,12 +93,22 @@ def launch_name(kname):
     prep and recurrence kernels' last template argument is the time-reversed
     mode of the backward's dv pass (..., true> / ...Lb1EEEv); the
     recurrence's one before it is 1 for the output pass and 0 for the
-    segments' local-state pass."""
+    segments' local-state pass.  The general gate's fp32 passes (its
+    backward) are named gg_prep_f32 and gg_recur_f32_r<state rows>."""
     import re
     m = re.search(r"k_([a-z_]+[a-z])", kname)
     if not m or m.group(1) not in KERNEL_NAMES:
         return None
     name = KERNEL_NAMES[m.group(1)]
+    if name in ("gg_prep", "gg_recur"):
+        if re.search(r"k_gg_(?:prep|recur)If", kname) or re.search(r"k_gg_(?:prep|recur)<float", kname):
+            name += "_f32"
+            if name == "gg_recur_f32":
+                mt = (re.search(r"k_gg_recurI\w*?Li(\d+)ELi\d+E", kname)
+                      or re.search(r"k_gg_recur<float,\s*[\w:]+,\s*(\d+),", kname))
+                if mt:
+                    name += f"_r{16 * int(mt.group(1))}"
+        return name
     if name in ("chunk_prep", "chunk_recur"):
         tail = re.search(r"L[ib](\d)ELb([01])EEEv", kname)      # mangled
         dtail = re.search(r",\s*(\d+),\s*(true|false)\s*>", kname)  # demangled
@@ -392,6 +406,27 @@ def backward_leg(w, args, torch, gla, _abi, dev, stream):
     kb = max(5, args.steps)
     bwd_ms = timed(bwd, kb, torch)
     fb_ms = timed(fb, kb, torch)
+    # the materialised-state backward on the same inputs, for comparison
+    mat_ms = None
+    mcfg = gla.bwd_config("materialized")
+    try:
+        if args.no_materialized:
+            raise gla.GlaError(0, "skipped")
+        mws = torch.empty(gla.gla_bwd_ex_workspace_size(dims, code, mcfg), dtype=torch.uint8,
+                          device=dev)
+
+        def bwd_mat(i):
+            st = gla.gla_bwd_ex(dims, code, mcfg, xb.q, xb.k, xb.v, xb.log_alpha, xb.h0, xb.do,
+                                None, *outs, mws, mws.numel(), stream)
+            if st:
+                raise gla.GlaError(st, "gla_bwd_ex")
+
+        for i in range(3):
+            bwd_mat(i)
+        mat_ms = timed(bwd_mat, max(5, kb // 5), torch)
+        del mws
+    except gla.GlaError:
+        pass
     _abi.gla_profile_begin(kb * 16)
     timed(bwd, kb, torch)
     _abi.gla_profile_end()
@@ -414,6 +449,7 @@ def backward_leg(w, args, torch, gla, _abi, dev, stream):
             "ms_per_step": round(fb_ms, 5),
             "tokens_per_s": round(tokens / (fb_ms * 1e-3), 1),
             "bwd_ms": round(bwd_ms, 5),
+            "bwd_ms_materialized": round(mat_ms, 5) if mat_ms else None,
             "bwd_tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
             "bwd_tflops": round(fl / (bwd_ms * 1e-3) / 1e12, 2),
             "bwd_flops": fl,
@@ -517,8 +553,10 @@ def general_leg(w, args, torch, gla, _abi, dev, stream):
     gk = {}
     for nm, lst in per.items():
         avg = sum(lst) / len(lst) * 1e-3
+        mt = measured_traffic(nm, "general_" + w.name)
         gk[nm] = {"avg_us": round(avg * 1e6, 2), "algorithmic_bytes": gbytes.get(nm),
-                  "achieved_gbps": round(gbytes[nm] / avg / 1e9, 1) if nm in gbytes else None}
+                  "achieved_gbps": round(gbytes[nm] / avg / 1e9, 1) if nm in gbytes else None,
+                  "traffic": mt["bytes_per_launch"] if mt else None}
     tokens = w.B * w.L
     del gws, og, hg, gouts, dog, lbg
     log(f"[bench] general gate fwd {res['fwd'] * 1e3:.1f} us, fwd+bwd {res['fwd_bwd'] * 1e3:.1f} us")
@@ -705,9 +743,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gla340m_fwd")
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = auto)")
-    ap.add_argument("--only", choices=["fwd", "bwd"], default=None,
-                    help="run only the forward of --workload, or only its backward (for "
-                         "profiler runs)")
+    ap.add_argument("--only", choices=["fwd", "bwd", "general"], default=None,
+                    help="run only the forward of --workload, only its backward, or only the "
+                         "general gate at its head shape (for profiler runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the 1.3B-shape and long-sequence forward legs")
@@ -715,6 +753,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step figure")
     ap.add_argument("--no-layer", action="store_true", help="skip the op-level layer figure")
     ap.add_argument("--no-general", action="store_true", help="skip the general-gate figure")
+    ap.add_argument("--no-materialized", action="store_true",
+                    help="skip timing the materialised-state backward beside the recurrent one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times), the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -760,6 +800,9 @@ def main():
         wb = w if w.backward else WORKLOADS["gla340m_fwdbwd"]
         print(json.dumps({"backward": backward_leg(wb, args, torch, gla, _abi, dev, stream)}))
         return
+    if args.only == "general":
+        print(json.dumps({"general": general_leg(w, args, torch, gla, _abi, dev, stream)}))
+        return
 
     copy_gbps = copy_bandwidth(torch, dev)
     main_leg = forward_leg(w, args, torch, gla, _abi, dev, stream, primary=True)
@@ -799,11 +842,14 @@ def main():
 
     general = None
     if not args.no_general:
-        try:
-            general = general_leg(w, args, torch, gla, _abi, dev, stream)
-        except Exception as e:  # reported, not hidden
-            general = {"error": f"{type(e).__name__}: {e}"}
-            log(f"[bench] general gate failed: {e}")
+        general = {}
+        shapes = [w] if args.no_legs else [w, WORKLOADS["gla1p3b_fwd"]]
+        for wg in shapes:
+            try:
+                general[wg.name] = general_leg(wg, args, torch, gla, _abi, dev, stream)
+            except Exception as e:  # reported, not hidden
+                general[wg.name] = {"error": f"{type(e).__name__}: {e}"}
+                log(f"[bench] general gate failed: {e}")
 
     layer = None
     if not args.no_layer:
