@@ -85,7 +85,7 @@ KERNEL_NAMES = {"chunk_prep": "chunk_prep", "chunk_recur": "chunk_recur",
                 "bwd_inter": "bwd_inter", "seg_output": "seg_output", "decode": "decode",
                 "gg_prep": "gg_prep", "gg_recur": "gg_recur", "gg_gate_scan": "gg_gate_scan",
                 "gg_gate_carry": "gg_gate_carry", "gg_gate_add": "gg_gate_add",
-                "gg_hsum": "gg_hsum"}
+                "gg_hsum": "gg_hsum", "chunk_da_cum": "chunk_da_cum"}
 
 
 def launch_name(kname):

@@ -297,7 +297,8 @@ static gla_status run_two_pass(const Plan& p, const void* q, const void* k, cons
 }
 
 // The backward with the states kept on chip (bf16, C = 64):
-//  * the chunk-local cumsum B of log alpha and dA = (dO V^T) masked, per chunk;
+//  * the chunk-local cumsum B of log alpha and dA = (dO V^T) masked, per chunk
+//    in one launch;
 //  * one launch of two recurrences over the chunks with the transposed state
 //    (k_bwd_inter): the inter-chunk terms of dq (S, chunks in order) and of dk
 //    (dS, chunks backwards), rowsum(hT ⊙ dhT) and dh0;
@@ -319,8 +320,7 @@ static gla_status run_bwd_recurrent(const Plan& p, const void* q, const void* k,
   float* dlt = (float*)(ws + p.off_bdlt);
   float* rs = (float*)(ws + p.off_brs);
   char* vr = ws + p.off_bvrec;
-  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
-  GLA_LAUNCH("chunk_attn", launch_chunk_attn(p, q, k, v, dout, cum, nullptr, dA, s));
+  GLA_LAUNCH("chunk_da_cum", launch_chunk_da_cum(p, v, dout, log_alpha, cum, dA, s));
   const BwdInterJob jq{dout, v, k, h0, dqi, rs, dhT, nullptr, 0};
   const BwdInterJob jk{v, dout, q, dhT, dki, nullptr, nullptr, dh0, 1};
   GLA_LAUNCH("bwd_inter", launch_bwd_inter(p, jq, jk, cum, s));

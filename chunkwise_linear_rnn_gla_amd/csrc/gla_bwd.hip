@@ -106,6 +106,104 @@ __global__ __launch_bounds__(kThreads) void k_chunk_attn(
   pb.finish(pd, [&](int m, int r, float val) { Ab[m * C + r] = val; });
 }
 
+// The recurrent backward's first launch, one workgroup per (chunk,
+// batch-head), 256 threads (bf16, C = 64):
+//  * the chunk-local inclusive cumsum of log alpha into cum (a thread per 4
+//    channels and 16 rows, the 16-row totals combined through LDS);
+//  * dA = (dO V^T) on the lower block triangle, masked to the causal triangle
+//    (zeros above it).  The d_v contraction is split over the four waves (K
+//    steps w, w + 4, ...), each wave holding all the triangle's 16 x 16 tiles,
+//    so every dO and V element of the chunk is read once; the partial tiles
+//    meet in LDS.  Rows past the sequence end read the last row and are
+//    zeroed.
+template <int C>
+__global__ __launch_bounds__(kThreads) void k_chunk_da_cum(
+    const bf16* __restrict__ v, const bf16* __restrict__ dout, const float* __restrict__ a,
+    float* __restrict__ cum, float* __restrict__ dAw, int L, int dk, int dv, int NC) {
+  using M = Mma<bf16>;
+  constexpr int NRT = C / 16, NTRI = NRT * (NRT + 1) / 2;
+  static_assert(NTRI * 4 * kWave >= kThreads, "cumsum totals fit the reduction buffer");
+  __shared__ f32x4 red[4][NTRI][kWave];
+  const int n = blockIdx.x, bh = blockIdx.y, w = wave_id(), l = lane_id(), tid = threadIdx.x;
+  const int r0 = n * C, rv = min(C, L - r0);
+  {
+    f32x4* tot = &red[0][0][0];
+    const int quads = dk / 4, per = quads * (C / 16);  // <= 256 for dk <= 256
+    const int gq = tid % quads, rg = tid / quads;
+    const int rr0 = rg * 16, rr1 = tid < per ? min(rv, rr0 + 16) : rr0;
+    const size_t base = ((size_t)bh * L + r0) * dk + 4 * gq;
+    f32x4 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (rr0 + i < rr1) x[i] = *reinterpret_cast<const f32x4*>(a + base + (size_t)(rr0 + i) * dk);
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (rr0 + i < rr1) {
+        run += x[i];
+        x[i] = run;
+      }
+    if (tid < per) tot[tid] = run;
+    __syncthreads();
+    f32x4 off = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < rg; ++g) off += tot[g * quads + gq];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (rr0 + i < rr1) *reinterpret_cast<f32x4*>(cum + base + (size_t)(rr0 + i) * dk) = x[i] + off;
+    __syncthreads();  // the totals' buffer is reused below
+  }
+  floatx4 acc[NTRI];
+#pragma unroll
+  for (int t = 0; t < NTRI; ++t) acc[t] = zero4();
+  const size_t vo = ((size_t)bh * L + r0) * dv;
+  for (int ks = w; ks < dv / M::K; ks += 4) {
+    const int c = ks * M::K + (l >> 4) * M::KPL;
+    M::frag fa[NRT], fb[NRT];
+#pragma unroll
+    for (int i = 0; i < NRT; ++i) {
+      const int row = i * 16 + (l & 15), rr = row < rv ? row : rv - 1;
+      fa[i] = load_frag<bf16>(dout + vo + (size_t)rr * dv + c);
+      fb[i] = load_frag<bf16>(v + vo + (size_t)rr * dv + c);
+      if (row >= rv) {
+        fa[i] = M::frag{};
+        fb[i] = M::frag{};
+      }
+    }
+    int t = 0;
+#pragma unroll
+    for (int ti = 0; ti < NRT; ++ti)
+#pragma unroll
+      for (int tj = 0; tj <= ti; ++tj, ++t) acc[t] = M::run(fa[ti], fb[tj], acc[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < NTRI; ++t) red[w][t][l] = f32x4{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+  __syncthreads();
+  float* dAb = dAw + ((size_t)bh * NC + n) * C * C;
+  for (int t = w; t < NTRI; t += 4) {
+    int ti = 0, rem = t;
+    while (rem > ti) { rem -= ti + 1; ++ti; }
+    const int tj = rem, col = tj * 16 + (l & 15);
+    const f32x4 sum = red[0][t][l] + red[1][t][l] + red[2][t][l] + red[3][t][l];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = ti * 16 + (l >> 4) * 4 + r;
+      dAb[row * C + col] = (col <= row) ? sum[r] : 0.f;
+    }
+  }
+  for (int it = tid; it < C * C; it += kThreads) {
+    const int row = it / C, col = it % C;
+    if ((col >> 4) > (row >> 4)) dAb[it] = 0.f;
+  }
+}
+
+hipError_t launch_chunk_da_cum(const Plan& p, const void* v, const void* dout, const float* a,
+                               float* cum, float* dA, hipStream_t s) {
+  if (!p.bf16 || p.C != 64 || p.dk % 4 || p.dk > 256 || p.dv % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_chunk_da_cum<64>), dim3(p.NC, p.BH), dim3(kThreads), 0, s,
+                     (const bf16*)v, (const bf16*)dout, a, cum, dA, p.L, p.dk, p.dv, p.NC);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ B3b: dq, dk, dlog b
 // Column layout of the off-diagonal intra operands of k_chunk_dqdk.  For query
 // sub-chunk j >= 1 the dq operand holds K ⊙ e^{z_j - B} over key rows

@@ -166,6 +166,10 @@ hipError_t launch_chunk_recur_rev(const Plan& p, int out, const void* qg, const 
 // ---- backward kernels (gla_bwd.hip) ----
 // A (chunk score matrix) and dA = (dO V^T) ⊙ M per chunk, fp32 C x C blocks
 // (Aw null: dA only).
+// The recurrent backward's chunk-local cumsum of log alpha and masked dA =
+// dO V^T in one launch (bf16, C = 64).
+hipError_t launch_chunk_da_cum(const Plan& p, const void* v, const void* dout, const float* a,
+                               float* cum, float* dA, hipStream_t s);
 hipError_t launch_chunk_attn(const Plan& p, const void* q, const void* k, const void* v,
                              const void* dout, const float* cum, float* Aw, float* dAw,
                              hipStream_t s);
