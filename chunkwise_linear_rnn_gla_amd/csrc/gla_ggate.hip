@@ -766,25 +766,37 @@ __global__ __launch_bounds__(kThreads) void k_gg_hsum(const float* __restrict__ 
 template <typename T> constexpr int gg_row_split(int MT) {
   return MT >= 32 ? 4 : (MT >= (sizeof(T) == 2 ? 4 : 2) ? 2 : 1);
 }
+// SIMDs of the chip (256 CUs x 4).  A launch whose workgroups hold fewer
+// waves than this leaves SIMDs idle; at 128 and 256 state rows it then splits
+// the rows over 4 or 8 waves (32 rows each: ~200-230 VGPRs, two waves per
+// SIMD), trading the per-column work that every wave repeats for the idle
+// SIMDs.  With the chip already full the extra waves only queue.
+constexpr long kChipSimds = 1024;
 
 template <typename T, typename TO, typename TI>
 static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t* r, size_t rb,
                             int L, int NC, hipStream_t s) {
-#define GG_RECUR(MT)                                                                          \
-  hipLaunchKernelGGL((k_gg_recur<T, TO, MT, gg_row_split<T>(MT), TI>), grid,                    \
-                     dim3(kWave * gg_row_split<T>(MT)), 0, s, r, rb, (const TI*)ps.v,          \
-                     ps.lb, ps.init, ps.init_t, (TO*)ps.o, ps.o_off, ps.fin, ps.fin_la,       \
-                     ps.fin_lb, L,                                                            \
-                     ps.dk, ps.dv, NC, ps.rev)
+#define GG_RECUR_W(MT, NWR)                                                                   \
+  hipLaunchKernelGGL((k_gg_recur<T, TO, MT, NWR, TI>), grid, dim3(kWave * (NWR)), 0, s, r, rb,  \
+                     (const TI*)ps.v, ps.lb, ps.init, ps.init_t, (TO*)ps.o, ps.o_off, ps.fin,  \
+                     ps.fin_la, ps.fin_lb, L, ps.dk, ps.dv, NC, ps.rev)
+#define GG_RECUR(MT) GG_RECUR_W(MT, gg_row_split<T>(MT))
+  const bool sparse = (long)grid.x * 2 < kChipSimds;  // two waves per workgroup leave SIMDs idle
   if constexpr (sizeof(T) == 4) {
     if (dkp == 16) { GG_RECUR(1); return; }
     if (dkp == 512) { GG_RECUR(32); return; }
   }
   if (dkp == 32) GG_RECUR(2);
   else if (dkp == 64) GG_RECUR(4);
-  else if (dkp == 128) GG_RECUR(8);
-  else GG_RECUR(16);
+  else if (dkp == 128) {
+    if (sparse) GG_RECUR_W(8, 4);
+    else GG_RECUR(8);
+  } else {
+    if (sparse) GG_RECUR_W(16, 8);
+    else GG_RECUR(16);
+  }
 #undef GG_RECUR
+#undef GG_RECUR_W
 }
 
 // part 0: k_gg_prep, part 1: k_gg_recur (separate so that each launch can be
