@@ -271,25 +271,41 @@ template <int MT> struct GgFrag<float, MT> {
   f4 k[MT];
 };
 
+// Buffer resource over bytes [p, p + bytes): loads outside read 0 and stores
+// outside are dropped.
+__device__ inline __amdgpu_buffer_rsrc_t gg_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+// Fragment loads from a chunk record's resource; off: byte offset of the
+// wave's first tile.
 template <int MT>
-__device__ inline void load_q(GgFrag<bf16, MT>& f, const bf16* qf, int l) {
+__device__ inline void load_q(GgFrag<bf16, MT>& f, __amdgpu_buffer_rsrc_t r, int off, int l) {
 #pragma unroll
-  for (int p = 0; p < MT / 2; ++p) f.q[p] = *reinterpret_cast<const bf16x8*>(qf + ((p * 64 + l) << 3));
+  for (int p = 0; p < MT / 2; ++p)
+    f.q[p] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            r, off + (((p * 64 + l) << 3) << 1), 0, 0));
 }
 template <int MT>
-__device__ inline void load_q(GgFrag<float, MT>& f, const float* qf, int l) {
+__device__ inline void load_q(GgFrag<float, MT>& f, __amdgpu_buffer_rsrc_t r, int off, int l) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) f.q[m] = *reinterpret_cast<const f4*>(qf + ((m * 64 + l) << 2));
+  for (int m = 0; m < MT; ++m)
+    f.q[m] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        r, off + (((m * 64 + l) << 2) << 2), 0, 0));
 }
 template <int MT>
-__device__ inline void load_k(GgFrag<bf16, MT>& f, const bf16* kf, int l) {
+__device__ inline void load_k(GgFrag<bf16, MT>& f, __amdgpu_buffer_rsrc_t r, int off, int l) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) f.k[m] = *reinterpret_cast<const bf16x4*>(kf + ((m * 64 + l) << 2));
+  for (int m = 0; m < MT; ++m)
+    f.k[m] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                                            r, off + (((m * 64 + l) << 2) << 1), 0, 0));
 }
 template <int MT>
-__device__ inline void load_k(GgFrag<float, MT>& f, const float* kf, int l) {
+__device__ inline void load_k(GgFrag<float, MT>& f, __amdgpu_buffer_rsrc_t r, int off, int l) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) f.k[m] = *reinterpret_cast<const f4*>(kf + ((m * 64 + l) << 2));
+  for (int m = 0; m < MT; ++m)
+    f.k[m] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        r, off + (((m * 64 + l) << 2) << 2), 0, 0));
 }
 
 // acc += Q~ S (16 tokens x 16 columns), S in accumulator layout.
@@ -379,54 +395,76 @@ template <typename T, int MT> constexpr int gg_depth() {
   return (sizeof(T) == 2 && MT <= 4) ? 2 : 1;
 }
 
+// The sequence rows of pass chunk n.  Forward: data row d = u = 16 n + t for
+// the chunk's token t, in the window [16 n, min(16 n + 16, L)).  Reversed: d =
+// L - 1 - u, in the window [max(L - 16 (n + 1), 0), L - 16 n).  A lane's row
+// relative to the window's first row is t (forward) or 15 - t + adj with adj =
+// min(L - 16 (n + 1), 0) (reversed); rows off the window (past the sequence)
+// fall outside the buffer resources built on it, so they read 0 and take no
+// stores.  The log beta rows of a reversed pass are the data rows + 1 (the
+// gate of original token L - u), valid up to row L - 1: their window starts a
+// row later and, in chunk 0, holds a row fewer (token 0 has no gate).
+struct GgWin {
+  int base, rows, adj;
+};
+__device__ inline GgWin gg_window(int n, int L, int rev) {
+  if (!rev) {
+    const int b = kGC * n;
+    return {b, min(kGC, L - b), 0};
+  }
+  const int lo = L - kGC * (n + 1), b = max(lo, 0);
+  return {b, L - kGC * n - b, min(lo, 0)};
+}
+// Lane-constant parts of the v / log beta / output offsets (elements, window
+// row 0 at adj = 0): (t or 15 - t) dv + jc for the lane's rows t = 4 g + e.
+struct GgLane {
+  int off[4];
+};
+
 // MT: the wave's tiles; DKP: the record's channels; m0: the wave's first tile
 template <typename T, int MT>
-__device__ inline void gg_load_late(GgIn<T, MT>& in, const uint8_t* __restrict__ rec,
-                                    size_t rec_bytes, int DKP, int m0, int bh, int n, int NC,
+__device__ inline void gg_load_late(GgIn<T, MT>& in, __amdgpu_buffer_rsrc_t rr, int DKP, int m0,
                                     int l, int g) {
-  const T* kf = reinterpret_cast<const T*>(rec + ((size_t)bh * NC + n) * rec_bytes) + kGC * DKP;
-  const float* pf = reinterpret_cast<const float*>(kf + kGC * DKP);
-  load_k(in.f, kf + 256 * m0, l);
+  const int kf = kGC * DKP * (int)sizeof(T), pf = 2 * kf;
+  load_k(in.f, rr, kf + 256 * m0 * (int)sizeof(T), l);
 #pragma unroll
   for (int m = 0; m < MT; ++m)
-    in.ga[m] = *reinterpret_cast<const f4*>(pf + kPfFloats + 16 * (m0 + m) + 4 * g);
+    in.ga[m] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rr, pf + 4 * (kPfFloats + 16 * (m0 + m) + 4 * g), 0, 0));
+}
+template <typename T>
+__device__ inline __amdgpu_buffer_rsrc_t gg_rec_rsrc(const uint8_t* rec, size_t rec_bytes, int bh,
+                                                     int n, int NC) {
+  return gg_rsrc(rec + ((size_t)bh * NC + n) * rec_bytes, (int)rec_bytes);
 }
 
+// vbh, lbh: v and log beta of the (batch, head).  The loads are unconditional
+// and kept raw: a load under a branch, or a select on its value, would wait
+// for it at once.
 template <typename T, int MT, typename TI>
 __device__ inline void gg_load(GgIn<T, MT>& in, const uint8_t* __restrict__ rec, size_t rec_bytes,
-                               int DKP, int m0, const TI* __restrict__ vb,
-                               const float* __restrict__ lbb, int bh, int n, int NC, int L,
-                               int dv, int rev, int l, int g) {
-  const uint8_t* r = rec + ((size_t)bh * NC + n) * rec_bytes;
-  const T* qf = reinterpret_cast<const T*>(r);
-  const float* pf = reinterpret_cast<const float*>(qf + 2 * kGC * DKP);
-  load_q(in.f, qf + 256 * m0, l);  // 256 elements per 16-channel tile in both layouts
-  in.p = *reinterpret_cast<const f4*>(pf + 4 * l);
-  in.pd = *reinterpret_cast<const f4*>(pf + 256 + 4 * g);
-  if constexpr (gg_ahead<T, MT>() == 2) gg_load_late(in, rec, rec_bytes, DKP, m0, bh, n, NC, l, g);
-  // unconditional loads of a clamped row, kept raw: a load under a branch, or
-  // a select on its value here, would wait for it at once; the rows past the
-  // sequence are zeroed where the values are used (gg_valid)
+                               int DKP, int m0, const TI* __restrict__ vbh,
+                               const float* __restrict__ lbh, const GgLane& ln, int bh, int n,
+                               int NC, int L, int dv, int rev, int l, int g) {
+  const __amdgpu_buffer_rsrc_t rr = gg_rec_rsrc<T>(rec, rec_bytes, bh, n, NC);
+  const int pf = 2 * kGC * DKP * (int)sizeof(T);
+  load_q(in.f, rr, 256 * m0 * (int)sizeof(T), l);  // 256 elements per 16-channel tile
+  in.p = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rr, pf + 16 * l, 0, 0));
+  in.pd = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rr, pf + 4 * (256 + 4 * g), 0, 0));
+  if constexpr (gg_ahead<T, MT>() == 2) gg_load_late(in, rr, DKP, m0, l, g);
+  const GgWin w = gg_window(n, L, rev);
+  const __amdgpu_buffer_rsrc_t rv = gg_rsrc(vbh + (size_t)w.base * dv, w.rows * dv * (int)sizeof(TI));
+  const __amdgpu_buffer_rsrc_t rl =
+      gg_rsrc(lbh + (size_t)(w.base + rev) * dv, (w.rows - (rev && n == 0)) * dv * 4);
+  const int adj = w.adj * dv;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int u = n * kGC + 4 * g + e;
-    const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
-    in.v[e] = to_f32(vb[(size_t)(dr > 0 ? dr : 0) * dv]);
-    in.lb[e] = lbb[(size_t)(gr > 0 ? gr : 0) * dv];
-  }
-}
-
-// v and log beta of chunk n as loaded by gg_load, with the rows that have no
-// value (past the sequence) or no gate (the first row of a reversed pass)
-// set to zero.
-template <typename T, int MT>
-__device__ inline void gg_valid(const GgIn<T, MT>& in, int n, int L, int rev, int g, float* v,
-                                float* lb) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int u = n * kGC + 4 * g + e;
-    v[e] = data_row(u, L, rev) >= 0 ? in.v[e] : 0.f;
-    lb[e] = gate_row(u, L, rev) >= 0 ? in.lb[e] : 0.f;
+    const int x = ln.off[e] + adj;
+    if constexpr (sizeof(TI) == 2)
+      in.v[e] = __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(rv, 2 * x, 0, 0) << 16);
+    else
+      in.v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, 4 * x, 0, 0));
+    in.lb[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, 4 * x, 0, 0));
   }
 }
 
@@ -469,8 +507,11 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
         x = init_t ? init[((size_t)bh * dv + jc) * dk + row] : init[((size_t)bh * dk + row) * dv + jc];
       S[m][e] = x;
     }
-  const TI* vb = v + (size_t)bh * L * dv + jc;
-  const float* lbb = lb + (size_t)bh * L * dv + jc;
+  const TI* vbh = v + (size_t)bh * L * dv;
+  const float* lbh = lb + (size_t)bh * L * dv;
+  GgLane ln;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ln.off[e] = (rev ? 15 - (4 * g + e) : 4 * g + e) * dv + jc;
 
   constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW>() : 1;
   // One chunk step: chunk n from `cur`; first the loads of chunk `nl` (if in
@@ -479,19 +520,24 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   // whose load is in flight would wait for that load.
   auto step = [&](int n, GgIn<T, MTW>& cur, GgIn<T, MTW>& ld, int nl) {
     if constexpr (AHEAD == 0)
-      gg_load(cur, rec, rec_bytes, DKP, m0, vb, lbb, bh, n, NC, L, dv, rev, l, g);
-    if constexpr (AHEAD < 2) gg_load_late(cur, rec, rec_bytes, DKP, m0, bh, n, NC, l, g);
+      gg_load(cur, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, n, NC, L, dv, rev, l, g);
+    if constexpr (AHEAD < 2) gg_load_late(cur, gg_rec_rsrc<T>(rec, rec_bytes, bh, n, NC), DKP, m0, l, g);
     // the prefetch is unconditional (past the end it reloads the last chunk,
     // unused): under a branch, the wait counts at its join would force waits
     // on the current set's loads as well
     if constexpr (AHEAD > 0)
-      gg_load(ld, rec, rec_bytes, DKP, m0, vb, lbb, bh, nl < NC ? nl : NC - 1, NC, L, dv, rev, l, g);
+      gg_load(ld, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, nl < NC ? nl : NC - 1, NC, L, dv, rev,
+              l, g);
     const GgFrag<T, MTW>& f = cur.f;
     const f4 p = cur.p, pd = cur.pd;
     const float* pf = reinterpret_cast<const float*>(
         rec + ((size_t)bh * NC + n) * rec_bytes + (size_t)32 * DKP * sizeof(T));
     float vv[4], c[4];
-    gg_valid(cur, n, L, rev, g, vv, c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vv[e] = cur.v[e];
+      c[e] = cur.lb[e];
+    }
     // chunk-local inclusive cumsum of log beta down the 16 rows of column j,
     // as hi (c) + lo (cl) pairs: within the lane's 4 rows, then the totals of
     // the lanes above it (row groups g' < g) added in front
@@ -567,13 +613,28 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
 #pragma unroll
           for (int e = 0; e < 4; ++e) res[e] = gexp<T>(c[e] + cl[e]) * a1[e] + sl[e];
       }
+      // stores through resources on the chunk's window: rows past the
+      // sequence fall outside and are dropped
+      const GgWin wn = gg_window(n, L, rev);
+      const size_t wo = ((size_t)bh * L + wn.base) * dv;
+      const int adj = wn.adj * dv;
+      if (ooff) {
+        const __amdgpu_buffer_rsrc_t ro = gg_rsrc(ooff + wo, wn.rows * dv * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int dr = data_row(n * kGC + 4 * g + e, L, rev);
-        if (dr < 0) continue;
-        const size_t x = ((size_t)bh * L + dr) * dv + jc;
-        if (ooff) ooff[x] = res[e];
-        if (o) o[x] = from_f32<TO>(res[e] + pd[e] * vv[e]);
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res[e]), ro, 4 * (ln.off[e] + adj), 0, 0);
+      }
+      if (o) {
+        const __amdgpu_buffer_rsrc_t ro = gg_rsrc(o + wo, wn.rows * dv * (int)sizeof(TO));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const TO y = from_f32<TO>(res[e] + pd[e] * vv[e]);
+          if constexpr (sizeof(TO) == 2)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, y), ro,
+                                                  2 * (ln.off[e] + adj), 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ro, 4 * (ln.off[e] + adj), 0, 0);
+        }
       }
     }
     // decay and update
@@ -588,14 +649,14 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   if constexpr (AHEAD == 0) {
     for (int n = 0; n < NC; ++n) step(n, ra, ra, NC);
   } else if constexpr (DEPTH == 1) {
-    gg_load(ra, rec, rec_bytes, DKP, m0, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
+    gg_load(ra, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, 0, NC, L, dv, rev, l, g);
     for (int n = 0; n < NC; n += 2) {
       step(n, ra, rb, n + 1);
       if (n + 1 < NC) step(n + 1, rb, ra, n + 2);
     }
   } else {
-    gg_load(ra, rec, rec_bytes, DKP, m0, vb, lbb, bh, 0, NC, L, dv, rev, l, g);
-    gg_load(rb, rec, rec_bytes, DKP, m0, vb, lbb, bh, NC > 1 ? 1 : 0, NC, L, dv, rev, l, g);
+    gg_load(ra, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, 0, NC, L, dv, rev, l, g);
+    gg_load(rb, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, NC > 1 ? 1 : 0, NC, L, dv, rev, l, g);
     for (int n = 0; n < NC; n += 3) {
       step(n, ra, rc, n + 2);
       if (n + 1 < NC) step(n + 1, rb, ra, n + 3);
