@@ -388,11 +388,12 @@ template <typename T, int MT> struct GgIn {
 template <typename T, int MT> constexpr int gg_ahead() {
   return MT <= 4 ? 2 : (MT == 8 ? 1 : 0);
 }
-// Chunks loaded ahead when everything is (gg_ahead == 2): two for bf16 state
+// Chunks loaded ahead when everything is (gg_ahead == 2): two for state
 // slices of up to 64 rows (a chunk step is shorter than the memory latency),
-// else one.
-template <typename T, int MT> constexpr int gg_depth() {
-  return (sizeof(T) == 2 && MT <= 4) ? 2 : 1;
+// except for fp32 slices in workgroups of more than four waves, whose
+// 256-register budget does not hold the third register set; else one.
+template <typename T, int MT, int NWR> constexpr int gg_depth() {
+  return MT <= 4 && (sizeof(T) == 2 || NWR <= 4) ? 2 : 1;
 }
 
 // The sequence rows of pass chunk n.  Forward: data row d = u = 16 n + t for
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
 #pragma unroll
   for (int e = 0; e < 4; ++e) ln.off[e] = (rev ? 15 - (4 * g + e) : 4 * g + e) * dv + jc;
 
-  constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW>() : 1;
+  constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW, NWR>() : 1;
   // One chunk step: chunk n from `cur`; first the loads of chunk `nl` (if in
   // range) go into `ld`.  The loop below is unrolled by the number of register
   // sets so that the sets change roles without copies: a copy of a register
