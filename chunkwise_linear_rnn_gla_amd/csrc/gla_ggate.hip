@@ -515,11 +515,76 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   for (int e = 0; e < 4; ++e) ln.off[e] = (rev ? 15 - (4 * g + e) : 4 * g + e) * dv + jc;
 
   constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW, NWR>() : 1;
+  // fp32 passes with two chunks loaded ahead (PIPE) do chunk n + 1's column
+  // work at the end of chunk n's step (`step`), off the chain that runs from
+  // the state through the inter term, the barrier and the update; their
+  // compensated cumsums make that work long.  The others keep it inside the
+  // step (`step_plain`), which measured faster for them.
+  constexpr bool PIPE = AHEAD == 2 && DEPTH == 2 && sizeof(T) == 4;
+  // The per-column work of a chunk, which does not involve the state: the
+  // chunk-local inclusive cumsum of log beta down the 16 rows of column j as
+  // hi (c) + lo (cl) pairs (within the lane's 4 rows, then the totals of the
+  // lanes above it, row groups g' < g, added in front), the chunk total, V~ =
+  // v e^{b - B}, e^{b}, and for wave 0 the output scales e^{B} and e^{B - b}.
+  struct GgCol {
+    float vv[4], c[4], cl[4], bh, bl, gb;
+    floatx4 vt;
+    float sq[4], sk[4];
+  };
+  auto colwork = [&](const GgIn<T, MTW>& in, GgCol& k) __attribute__((always_inline)) {
+    float err;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k.vv[e] = in.v[e];
+      k.c[e] = in.lb[e];
+    }
+    k.cl[0] = 0.f;
+#pragma unroll
+    for (int e = 1; e < 4; ++e) {
+      k.c[e] = csum<T>(k.c[e - 1], k.c[e], err);
+      k.cl[e] = k.cl[e - 1] + err;
+    }
+    float th[4], tl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      th[r] = __shfl(k.c[3], j + 16 * r);
+      tl[r] = sizeof(T) == 4 ? __shfl(k.cl[3], j + 16 * r) : 0.f;
+    }
+    float eh = 0.f, el = 0.f;  // sum of the totals of row groups before g
+    k.bh = 0.f;
+    k.bl = 0.f;  // chunk total
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r < g) {
+        eh = csum<T>(eh, th[r], err);
+        el += tl[r] + err;
+      }
+      k.bh = csum<T>(k.bh, th[r], err);
+      k.bl += tl[r] + err;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k.c[e] = csum<T>(eh, k.c[e], err);
+      k.cl[e] += el + err;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k.vt[e] = k.vv[e] * gexp<T>((k.bh - k.c[e]) + (k.bl - k.cl[e]));
+    k.gb = gexp<T>(k.bh + k.bl);
+  };
+  // wave 0's output scales
+  auto colscales = [&](GgCol& k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k.sq[e] = gexp<T>(k.c[e] + k.cl[e]);
+      k.sk[e] = gexp<T>((k.c[e] - k.bh) + (k.cl[e] - k.bl));
+    }
+  };
+
   // One chunk step: chunk n from `cur`; first the loads of chunk `nl` (if in
   // range) go into `ld`.  The loop below is unrolled by the number of register
   // sets so that the sets change roles without copies: a copy of a register
   // whose load is in flight would wait for that load.
-  auto step = [&](int n, GgIn<T, MTW>& cur, GgIn<T, MTW>& ld, int nl) {
+  auto step_plain = [&](int n, GgIn<T, MTW>& cur, GgIn<T, MTW>& ld, int nl) {
     if constexpr (AHEAD == 0)
       gg_load(cur, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, n, NC, L, dv, rev, l, g);
     if constexpr (AHEAD < 2) gg_load_late(cur, gg_rec_rsrc<T>(rec, rec_bytes, bh, n, NC), DKP, m0, l, g);
@@ -646,22 +711,120 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
       for (int e = 0; e < 4; ++e) S[m][e] *= cur.ga[m][e] * gb;
     update(S, f, vt);
   };
+  // The PIPE step: as step_plain, with chunk n's column work in `col`; at its
+  // end chunk n + 1's goes into coln from nxt, the set holding that chunk.
+  auto step = [&](int n, GgIn<T, MTW>& cur, GgIn<T, MTW>& ld, int nl, GgCol& col,
+                  const GgIn<T, MTW>& nxt, GgCol& coln) {
+    gg_load(ld, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, nl < NC ? nl : NC - 1, NC, L, dv, rev, l,
+            g);
+    const GgFrag<T, MTW>& f = cur.f;
+    const f4 p = cur.p, pd = cur.pd;
+    const float* pf = reinterpret_cast<const float*>(
+        rec + ((size_t)bh * NC + n) * rec_bytes + (size_t)32 * DKP * sizeof(T));
+    floatx4 a1 = inter(f, S);
+    if constexpr (NWR > 1) {
+      if (w > 0) red[n & 1][w - 1][l] = a1;
+      __syncthreads();  // one per chunk: the buffers alternate, and the next
+                        // write to this one comes after the next barrier
+      if (w == 0)
+#pragma unroll
+        for (int r = 0; r < NWR - 1; ++r) {
+          const f4 x = red[n & 1][r][l];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a1[e] += x[e];
+        }
+    }
+    if (w == 0) {  // wave 0: intra term and output
+      const floatx4 a2 = intra(p, col.vt, T());
+      float res[4];
+      const bool safe = col.bh + col.bl >= -kSafeDecay;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[e] = col.sq[e] * a1[e] + col.sk[e] * a2[e];
+      if (__any(!safe)) {
+        // log-space intra term: sum_{s < t} P[t][s] v_s e^{Bt_t - Bt_s}
+        float sl[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < kGC; ++s) {
+          const int src = j + 16 * (s >> 2);
+          const float cs = __shfl(col.c[s & 3], src);
+          const float ls = sizeof(T) == 4 ? __shfl(col.cl[s & 3], src) : 0.f;
+          const float vs = __shfl(col.vv[s & 3], src);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = 4 * g + e;
+            if (s < t)
+              sl[e] += pf[pf_index(t, s)] * vs * gexp<T>((col.c[e] - cs) + (col.cl[e] - ls));
+          }
+        }
+        if (!safe)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) res[e] = col.sq[e] * a1[e] + sl[e];
+      }
+      // stores through resources on the chunk's window: rows past the
+      // sequence fall outside and are dropped
+      const GgWin wn = gg_window(n, L, rev);
+      const size_t wo = ((size_t)bh * L + wn.base) * dv;
+      const int adj = wn.adj * dv;
+      if (ooff) {
+        const __amdgpu_buffer_rsrc_t ro = gg_rsrc(ooff + wo, wn.rows * dv * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(res[e]), ro, 4 * (ln.off[e] + adj), 0, 0);
+      }
+      if (o) {
+        const __amdgpu_buffer_rsrc_t ro = gg_rsrc(o + wo, wn.rows * dv * (int)sizeof(TO));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const TO y = from_f32<TO>(res[e] + pd[e] * col.vv[e]);
+          if constexpr (sizeof(TO) == 2)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, y), ro,
+                                                  2 * (ln.off[e] + adj), 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), ro, 4 * (ln.off[e] + adj), 0, 0);
+        }
+      }
+    }
+    // decay and update
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[m][e] *= cur.ga[m][e] * col.gb;
+    update(S, f, col.vt);
+    colwork(nxt, coln);
+    if (w == 0) colscales(coln);
+  };
   GgIn<T, MTW> ra, rb, rc;
   if constexpr (AHEAD == 0) {
-    for (int n = 0; n < NC; ++n) step(n, ra, ra, NC);
+    for (int n = 0; n < NC; ++n) step_plain(n, ra, ra, NC);
   } else if constexpr (DEPTH == 1) {
     gg_load(ra, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, 0, NC, L, dv, rev, l, g);
     for (int n = 0; n < NC; n += 2) {
-      step(n, ra, rb, n + 1);
-      if (n + 1 < NC) step(n + 1, rb, ra, n + 2);
+      step_plain(n, ra, rb, n + 1);
+      if (n + 1 < NC) step_plain(n + 1, rb, ra, n + 2);
     }
   } else {
     gg_load(ra, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, 0, NC, L, dv, rev, l, g);
     gg_load(rb, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, NC > 1 ? 1 : 0, NC, L, dv, rev, l, g);
-    for (int n = 0; n < NC; n += 3) {
-      step(n, ra, rc, n + 2);
-      if (n + 1 < NC) step(n + 1, rb, ra, n + 3);
-      if (n + 2 < NC) step(n + 2, rc, rb, n + 4);
+    if constexpr (PIPE) {
+      GgCol ca, cb;
+      colwork(ra, ca);
+      if (w == 0) colscales(ca);
+      // the column sets alternate; the loop covers six chunks per iteration
+      // so that both rotations line up without copies
+      for (int n = 0; n < NC; n += 6) {
+        step(n, ra, rc, n + 2, ca, rb, cb);
+        if (n + 1 < NC) step(n + 1, rb, ra, n + 3, cb, rc, ca);
+        if (n + 2 < NC) step(n + 2, rc, rb, n + 4, ca, ra, cb);
+        if (n + 3 < NC) step(n + 3, ra, rc, n + 5, cb, rb, ca);
+        if (n + 4 < NC) step(n + 4, rb, ra, n + 6, ca, rc, cb);
+        if (n + 5 < NC) step(n + 5, rc, rb, n + 7, cb, ra, ca);
+      }
+    } else {
+      for (int n = 0; n < NC; n += 3) {
+        step_plain(n, ra, rc, n + 2);
+        if (n + 1 < NC) step_plain(n + 1, rb, ra, n + 3);
+        if (n + 2 < NC) step_plain(n + 2, rc, rb, n + 4);
+      }
     }
   }
   if (fin) {
