@@ -515,12 +515,12 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   for (int e = 0; e < 4; ++e) ln.off[e] = (rev ? 15 - (4 * g + e) : 4 * g + e) * dv + jc;
 
   constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW, NWR>() : 1;
-  // fp32 passes with two chunks loaded ahead (PIPE) do chunk n + 1's column
+  // fp32 passes that load whole chunks ahead (PIPE) do chunk n + 1's column
   // work at the end of chunk n's step (`step`), off the chain that runs from
   // the state through the inter term, the barrier and the update; their
   // compensated cumsums make that work long.  The others keep it inside the
   // step (`step_plain`), which measured faster for them.
-  constexpr bool PIPE = AHEAD == 2 && DEPTH == 2 && sizeof(T) == 4;
+  constexpr bool PIPE = AHEAD == 2 && sizeof(T) == 4;
   // The per-column work of a chunk, which does not involve the state: the
   // chunk-local inclusive cumsum of log beta down the 16 rows of column j as
   // hi (c) + lo (cl) pairs (within the lane's 4 rows, then the totals of the
@@ -798,9 +798,19 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
     for (int n = 0; n < NC; ++n) step_plain(n, ra, ra, NC);
   } else if constexpr (DEPTH == 1) {
     gg_load(ra, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, 0, NC, L, dv, rev, l, g);
-    for (int n = 0; n < NC; n += 2) {
-      step_plain(n, ra, rb, n + 1);
-      if (n + 1 < NC) step_plain(n + 1, rb, ra, n + 2);
+    if constexpr (PIPE) {
+      GgCol ca, cb;
+      colwork(ra, ca);
+      if (w == 0) colscales(ca);
+      for (int n = 0; n < NC; n += 2) {
+        step(n, ra, rb, n + 1, ca, rb, cb);
+        if (n + 1 < NC) step(n + 1, rb, ra, n + 2, cb, ra, ca);
+      }
+    } else {
+      for (int n = 0; n < NC; n += 2) {
+        step_plain(n, ra, rb, n + 1);
+        if (n + 1 < NC) step_plain(n + 1, rb, ra, n + 2);
+      }
     }
   } else {
     gg_load(ra, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, 0, NC, L, dv, rev, l, g);
