@@ -515,12 +515,12 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   for (int e = 0; e < 4; ++e) ln.off[e] = (rev ? 15 - (4 * g + e) : 4 * g + e) * dv + jc;
 
   constexpr int AHEAD = gg_ahead<T, MTW>(), DEPTH = AHEAD == 2 ? gg_depth<T, MTW, NWR>() : 1;
-  // fp32 passes that load whole chunks ahead (PIPE) do chunk n + 1's column
+  // fp32 passes that load v and log beta ahead (PIPE) do chunk n + 1's column
   // work at the end of chunk n's step (`step`), off the chain that runs from
   // the state through the inter term, the barrier and the update; their
   // compensated cumsums make that work long.  The others keep it inside the
   // step (`step_plain`), which measured faster for them.
-  constexpr bool PIPE = AHEAD == 2 && sizeof(T) == 4;
+  constexpr bool PIPE = AHEAD >= 1 && sizeof(T) == 4;
   // The per-column work of a chunk, which does not involve the state: the
   // chunk-local inclusive cumsum of log beta down the 16 rows of column j as
   // hi (c) + lo (cl) pairs (within the lane's 4 rows, then the totals of the
@@ -715,6 +715,7 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   // end chunk n + 1's goes into coln from nxt, the set holding that chunk.
   auto step = [&](int n, GgIn<T, MTW>& cur, GgIn<T, MTW>& ld, int nl, GgCol& col,
                   const GgIn<T, MTW>& nxt, GgCol& coln) {
+    if constexpr (AHEAD < 2) gg_load_late(cur, gg_rec_rsrc<T>(rec, rec_bytes, bh, n, NC), DKP, m0, l, g);
     gg_load(ld, rec, rec_bytes, DKP, m0, vbh, lbh, ln, bh, nl < NC ? nl : NC - 1, NC, L, dv, rev, l,
             g);
     const GgFrag<T, MTW>& f = cur.f;
