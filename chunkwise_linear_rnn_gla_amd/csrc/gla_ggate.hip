@@ -187,23 +187,37 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   __syncthreads();
   float* pf = reinterpret_cast<float*>(r + (size_t)2 * kGC * dkp * sizeof(T));
   float* ga = pf + kPfFloats;
+  // a thread per channel: its column of log alpha, q and k read into
+  // registers first (the arrays are written in the same loop, and a load
+  // after a store that may alias it would wait for that store)
   for (int i = tid; i < dkp; i += kThreads) {
+    float at[kGC], al[kGC], qv[kGC], kv[kGC];
+#pragma unroll
+    for (int t = 0; t < kGC; ++t) {
+      at[t] = cs[t * ld + i];
+      qv[t] = qs[t * ld + i];
+      kv[t] = ks[t * ld + i];
+    }
     float c = 0.f, e = 0.f;
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
       float err;
-      c = csum<T>(c, cs[t * ld + i], err);
+      c = csum<T>(c, at[t], err);
       e += err;
-      cs[t * ld + i] = c;
-      cl[t * ld + i] = e;
+      at[t] = c;
+      al[t] = e;
     }
-    ga[i] = gexp<T>(c + e);
-    if (cs[i] - c > kSafeP) atomicOr(&umask[i >> 5], 1u << (i & 31));
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
-      const float at = cs[t * ld + i], al = cl[t * ld + i];
-      stg[qf_index<T>(t, i)] = from_f32<T>(qs[t * ld + i] * gexp<T>(at + al));
-      stg[kGC * dkp + kf_index(t, i)] = from_f32<T>(ks[t * ld + i] * gexp<T>((c - at) + (e - al)));
+      cs[t * ld + i] = at[t];
+      cl[t * ld + i] = al[t];
+    }
+    ga[i] = gexp<T>(c + e);
+    if (at[0] - c > kSafeP) atomicOr(&umask[i >> 5], 1u << (i & 31));
+#pragma unroll
+    for (int t = 0; t < kGC; ++t) {
+      stg[qf_index<T>(t, i)] = from_f32<T>(qv[t] * gexp<T>(at[t] + al[t]));
+      stg[kGC * dkp + kf_index(t, i)] = from_f32<T>(kv[t] * gexp<T>((c - at[t]) + (e - al[t])));
     }
   }
   __syncthreads();
