@@ -486,11 +486,10 @@ __device__ inline void gg_load(GgIn<T, MT>& in, const uint8_t* __restrict__ rec,
 // grid (dv / 16 * BH), NWR waves per workgroup; the dv / 16 column tiles of a
 // (batch, head), which read the same chunk records, take consecutive logical
 // ids placed on one XCD so that its L2 serves their repeated reads.  The NWR
-// waves split the state tile's MT 16-row blocks between them (twice the waves
-// of one per tile, half the per-chunk work each): each forms its share of the
-// inter term Q~ S, the others hand theirs to wave 0 through LDS, and wave 0
-// adds the intra term and writes the output; each wave decays and updates its
-// own rows.  Lane (j, g) = (l % 16, l / 16) owns state column j of the tile
+// waves (1 to 8, chosen by the launcher) split the state tile's MT 16-row
+// blocks between them: each forms its share of the inter term Q~ S, the
+// others hand theirs to wave 0 through LDS, and wave 0 adds the intra term
+// and writes the output; each wave decays and updates its own rows.  Lane (j, g) = (l % 16, l / 16) owns state column j of the tile
 // and, in every 16 x 16 accumulator tile, rows 4 g + e.
 // init: [BH][dk][dv] ([BH][dv][dk] when init_t), or null for zeros.  o (if
 // not null) receives the output, ooff (if not null) the output without the
@@ -539,7 +538,8 @@ __global__ __launch_bounds__(kWave * NWR) void k_gg_recur(
   // chunk-local inclusive cumsum of log beta down the 16 rows of column j as
   // hi (c) + lo (cl) pairs (within the lane's 4 rows, then the totals of the
   // lanes above it, row groups g' < g, added in front), the chunk total, V~ =
-  // v e^{b - B}, e^{b}, and for wave 0 the output scales e^{B} and e^{B - b}.
+  // v e^{b - B} and e^{b}; colscales adds wave 0's output scales e^{B} and
+  // e^{B - b}.
   struct GgCol {
     float vv[4], c[4], cl[4], bh, bl, gb;
     floatx4 vt;
