@@ -142,11 +142,14 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   float* qs = sm;
   float* ks = qs + kGC * ld;
   float* cs = ks + kGC * ld;  // cumsum, hi part
-  float* cl = cs + kGC * ld;  // lo part
-  float* part = cl + kGC * ld;  // the four waves' partial P tiles
+  // lo part of the cumsum: fp32 passes only (for bf16 records the cumsum is
+  // not compensated, its lo part is 0, and the array is left out)
+  constexpr bool LO = sizeof(T) == 4;
+  float* cl = cs + kGC * ld;
+  float* part = (LO ? cl + kGC * ld : cl);  // the four waves' partial P tiles
   uint32_t* umask = reinterpret_cast<uint32_t*>(part + 1024);  // channels left to the log-space sum
   // bf16: Q~ and K~ in record order, written out in 16-byte units (16-byte
-  // aligned: the arrays above are 4 (16 (dkp + 1)) + 1024 + kMaskWords
+  // aligned: the arrays above are 3 (16 (dkp + 1)) + 1024 + kMaskWords
   // floats).  fp32
   // stores its elements directly: staging would take the 256-channel
   // passes' LDS past what lets two workgroups share a CU.
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
       cs[t * ld + i] = at[t];
-      cl[t * ld + i] = al[t];
+      if constexpr (LO) cl[t * ld + i] = al[t];
     }
     ga[i] = gexp<T>(c + e);
     if (at[0] - c > kSafeP) atomicOr(&umask[i >> 5], 1u << (i & 31));
@@ -241,12 +244,12 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
     for (int i0 = w * span; i0 < (w + 1) * span; i0 += 4) {
       const int i = i0 + kk;
       const bool sf = !((umask[i >> 5] >> (i & 31)) & 1u);
-      const float c0 = cs[i], l0 = cl[i];
+      const float c0 = cs[i], l0 = LO ? cl[i] : 0.f;
       const float a = sf ? qs[r16 * ld + i] *
-                               gexp<T>((cs[r16 * ld + i] - c0) + (cl[r16 * ld + i] - l0))
+                               gexp<T>((cs[r16 * ld + i] - c0) + (LO ? cl[r16 * ld + i] - l0 : 0.f))
                          : 0.f;
       const float b = sf ? ks[r16 * ld + i] *
-                               gexp<T>((c0 - cs[r16 * ld + i]) + (l0 - cl[r16 * ld + i]))
+                               gexp<T>((c0 - cs[r16 * ld + i]) + (LO ? l0 - cl[r16 * ld + i] : 0.f))
                          : 0.f;
       acc = mfma4(a, b, acc);
     }
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
     for (int wd = 0; wd < ((dkp + 31) >> 5); ++wd)
       for (uint32_t m = umask[wd]; m; m &= m - 1) {
         const int i = wd * 32 + __builtin_ctz(m);
-        acc += qt[i] * ksr[i] * gexp<T>((ct[i] - csr[i]) + (lt[i] - lsr[i]));
+        acc += qt[i] * ksr[i] * gexp<T>((ct[i] - csr[i]) + (LO ? lt[i] - lsr[i] : 0.f));
       }
   }
   pf[pf_index(t, s)] = s < t ? acc : 0.f;
@@ -1075,9 +1078,10 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
   const size_t rb = gg_rec_bytes(is_bf16, dkp);
   uint8_t* r = static_cast<uint8_t*>(rec);
   if (part == 0) {
-    // 4 arrays of 16 padded rows, 4 partial P tiles, the mask words (69.9 KB
-    // at 256 fp32 channels, 135.5 KB at 512), and for bf16 the staged Q~ and K~
-    const size_t lds = sizeof(float) * (4 * kGC * (dkp + 1) + 1024 + kMaskWords) +
+    // 4 arrays of 16 padded rows (3 for bf16, which has no lo cumsum), 4
+    // partial P tiles, the mask words (69.9 KB at 256 fp32 channels, 135.5 KB
+    // at 512), and for bf16 the staged Q~ and K~
+    const size_t lds = sizeof(float) * ((is_bf16 ? 3 : 4) * kGC * (dkp + 1) + 1024 + kMaskWords) +
                        (is_bf16 ? (size_t)2 * kGC * dkp * 2 : 0);
     const dim3 pg(NC, BH);
     hipError_t e;
