@@ -130,8 +130,9 @@ int gg_padded_dim(int is_bf16, int d) {
 // grid (NC, BH), 256 threads.  dk: channels of the pass's q and k; dkp: the
 // record's (padded) channel count.
 // T: the record and arithmetic type; TI: the element type of q and k (bf16
-// inputs of an fp32 pass are converted as they are read)
-template <typename T, typename TI>
+// inputs of an fp32 pass are converted as they are read); QS: the type q and
+// k are staged in (TI, or fp32)
+template <typename T, typename TI, typename QS>
 __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
                                                       const TI* __restrict__ k,
                                                       const float* __restrict__ la,
@@ -139,9 +140,12 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
                                                       int L, int dk, int dkp, int NC, int rev) {
   extern __shared__ float sm[];
   const int ld = dkp + 1;  // odd row stride: the P loop reads 16 rows at one column
-  float* qs = sm;
-  float* ks = qs + kGC * ld;
-  float* cs = ks + kGC * ld;  // cumsum, hi part
+  // q and k staged in QS: bf16 inputs are exact in bf16, half the LDS of an
+  // fp32 copy, which lets the 256-channel passes fit one more workgroup per
+  // CU (below 256 channels fp32 staging measured faster)
+  QS* qs = reinterpret_cast<QS*>(sm);
+  QS* ks = qs + kGC * ld;
+  float* cs = reinterpret_cast<float*>(ks + kGC * ld);  // cumsum, hi part
   // lo part of the cumsum: fp32 passes only (for bf16 records the cumsum is
   // not compensated, its lo part is 0, and the array is left out)
   constexpr bool LO = sizeof(T) == 4;
@@ -149,8 +153,8 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   float* part = (LO ? cl + kGC * ld : cl);  // the four waves' partial P tiles
   uint32_t* umask = reinterpret_cast<uint32_t*>(part + 1024);  // channels left to the log-space sum
   // bf16: Q~ and K~ in record order, written out in 16-byte units (16-byte
-  // aligned: the arrays above are 3 (16 (dkp + 1)) + 1024 + kMaskWords
-  // floats).  fp32
+  // aligned: the arrays above are 2 (16 (dkp + 1)) QS, 16 (dkp + 1) + 1024
+  // + kMaskWords floats).  fp32
   // stores its elements directly: staging would take the 256-channel
   // passes' LDS past what lets two workgroups share a CU.
   constexpr bool STAGE = sizeof(T) == 2;
@@ -182,8 +186,8 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      qs[t * ld + i + e] = qv[e];
-      ks[t * ld + i + e] = kv[e];
+      qs[t * ld + i + e] = from_f32<QS>(qv[e]);
+      ks[t * ld + i + e] = from_f32<QS>(kv[e]);
       cs[t * ld + i + e] = av[e];
     }
   }
@@ -198,8 +202,8 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
       at[t] = cs[t * ld + i];
-      qv[t] = qs[t * ld + i];
-      kv[t] = ks[t * ld + i];
+      qv[t] = to_f32(qs[t * ld + i]);
+      kv[t] = to_f32(ks[t * ld + i]);
     }
     float c = 0.f, e = 0.f;
 #pragma unroll
@@ -245,10 +249,10 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
       const int i = i0 + kk;
       const bool sf = !((umask[i >> 5] >> (i & 31)) & 1u);
       const float c0 = cs[i], l0 = LO ? cl[i] : 0.f;
-      const float a = sf ? qs[r16 * ld + i] *
+      const float a = sf ? to_f32(qs[r16 * ld + i]) *
                                gexp<T>((cs[r16 * ld + i] - c0) + (LO ? cl[r16 * ld + i] - l0 : 0.f))
                          : 0.f;
-      const float b = sf ? ks[r16 * ld + i] *
+      const float b = sf ? to_f32(ks[r16 * ld + i]) *
                                gexp<T>((c0 - cs[r16 * ld + i]) + (LO ? l0 - cl[r16 * ld + i] : 0.f))
                          : 0.f;
       acc = mfma4(a, b, acc);
@@ -261,8 +265,8 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   float acc = 0.f;
   if (s <= t) {
     acc = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
-    const float* qt = qs + t * ld;
-    const float* ksr = ks + s * ld;
+    const QS* qt = qs + t * ld;
+    const QS* ksr = ks + s * ld;
     const float* ct = cs + t * ld;
     const float* csr = cs + s * ld;
     const float* lt = cl + t * ld;
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
     for (int wd = 0; wd < ((dkp + 31) >> 5); ++wd)
       for (uint32_t m = umask[wd]; m; m &= m - 1) {
         const int i = wd * 32 + __builtin_ctz(m);
-        acc += qt[i] * ksr[i] * gexp<T>((ct[i] - csr[i]) + (LO ? lt[i] - lsr[i] : 0.f));
+        acc += to_f32(qt[i]) * to_f32(ksr[i]) * gexp<T>((ct[i] - csr[i]) + (LO ? lt[i] - lsr[i] : 0.f));
       }
   }
   pf[pf_index(t, s)] = s < t ? acc : 0.f;
@@ -1055,18 +1059,17 @@ static void launch_gg_recur(const GgPass& ps, int dkp, dim3 grid, const uint8_t*
 // part 0: k_gg_prep, part 1: k_gg_recur (separate so that each launch can be
 // timed on its own).  is_bf16: the pass's records and arithmetic; in_bf16: the
 // element type of its q, k and v (bf16 inputs may feed an fp32 pass).
-template <typename T, typename TI>
-static void launch_gg_prep(const GgPass& ps, dim3 pg, size_t lds, uint8_t* r, size_t rb, int L,
-                           int dkp, int NC, hipStream_t s) {
-  hipLaunchKernelGGL((k_gg_prep<T, TI>), pg, dim3(kThreads), lds, s, (const TI*)ps.q,
+template <typename T, typename TI, typename QS>
+static hipError_t launch_gg_prep(const GgPass& ps, dim3 pg, size_t lds, uint8_t* r, size_t rb,
+                                 int L, int dkp, int NC, hipStream_t s) {
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gg_prep<T, TI, QS>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_gg_prep<T, TI, QS>), pg, dim3(kThreads), lds, s, (const TI*)ps.q,
                      (const TI*)ps.k, ps.la, r, rb, L, ps.dk, dkp, NC, ps.rev);
-}
-
-template <typename T, typename TI>
-static hipError_t gg_prep_lds(size_t lds) {
-  if (lds <= 65536) return hipSuccess;
-  return hipFuncSetAttribute((const void*)k_gg_prep<T, TI>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  return hipSuccess;
 }
 
 hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, int BH, int L,
@@ -1078,23 +1081,25 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
   const size_t rb = gg_rec_bytes(is_bf16, dkp);
   uint8_t* r = static_cast<uint8_t*>(rec);
   if (part == 0) {
-    // 4 arrays of 16 padded rows (3 for bf16, which has no lo cumsum), 4
-    // partial P tiles, the mask words (69.9 KB at 256 fp32 channels, 135.5 KB
-    // at 512), and for bf16 the staged Q~ and K~
-    const size_t lds = sizeof(float) * ((is_bf16 ? 3 : 4) * kGC * (dkp + 1) + 1024 + kMaskWords) +
+    // q and k (16 padded rows each; bf16 from 256 bf16 input channels on,
+    // else fp32), the cumsum (and for fp32 its lo part), 4 partial P tiles,
+    // the mask words (53.5 KB at 256 fp32 channels with bf16 inputs, 69.9 KB
+    // with fp32 ones, 135.5 KB at 512 fp32), and for bf16 the staged Q~, K~
+    const bool qsb = in_bf16 && dkp >= 256;
+    const size_t lds = (size_t)2 * kGC * (dkp + 1) * (qsb ? 2 : 4) +
+                       sizeof(float) * ((is_bf16 ? 1 : 2) * kGC * (dkp + 1) + 1024 + kMaskWords) +
                        (is_bf16 ? (size_t)2 * kGC * dkp * 2 : 0);
     const dim3 pg(NC, BH);
     hipError_t e;
-    if (is_bf16) {
-      if ((e = gg_prep_lds<bf16, bf16>(lds)) != hipSuccess) return e;
-      launch_gg_prep<bf16, bf16>(ps, pg, lds, r, rb, L, dkp, NC, s);
-    } else if (in_bf16) {
-      if ((e = gg_prep_lds<float, bf16>(lds)) != hipSuccess) return e;
-      launch_gg_prep<float, bf16>(ps, pg, lds, r, rb, L, dkp, NC, s);
-    } else {
-      if ((e = gg_prep_lds<float, float>(lds)) != hipSuccess) return e;
-      launch_gg_prep<float, float>(ps, pg, lds, r, rb, L, dkp, NC, s);
-    }
+    if (is_bf16)
+      e = qsb ? launch_gg_prep<bf16, bf16, bf16>(ps, pg, lds, r, rb, L, dkp, NC, s)
+              : launch_gg_prep<bf16, bf16, float>(ps, pg, lds, r, rb, L, dkp, NC, s);
+    else if (in_bf16)
+      e = qsb ? launch_gg_prep<float, bf16, bf16>(ps, pg, lds, r, rb, L, dkp, NC, s)
+              : launch_gg_prep<float, bf16, float>(ps, pg, lds, r, rb, L, dkp, NC, s);
+    else
+      e = launch_gg_prep<float, float, float>(ps, pg, lds, r, rb, L, dkp, NC, s);
+    if (e != hipSuccess) return e;
   } else {
     const dim3 rg((ps.dv / 16) * BH);
     // o is written in the element type of the inputs (o_off, when asked
