@@ -983,13 +983,22 @@ __global__ __launch_bounds__(kWave) void k_gg_gate_add(const float* __restrict__
   const f4 cy =
       *reinterpret_cast<const f4*>(tot + ((size_t)bh * NG + cg) * (dk + dv) + (half ? dk : 0) + c);
   const int t0 = cg * kGT, t1 = min(L, t0 + kGT);
-#pragma unroll 8
-  for (int t = t0; t < t1; ++t) {
-    f4* o = reinterpret_cast<f4*>(out + ((size_t)bh * L + t) * d + c);
-    f4 x = *o;
+  // eight rows read before any is written back: the stores go to the array
+  // the loads come from, so the compiler keeps each load after the previous
+  // row's store unless they are batched by hand
+  constexpr int kB = 8;
+  for (int t = t0; t < t1; t += kB) {
+    f4 x[kB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] += cy[e];
-    *o = x;
+    for (int u = 0; u < kB; ++u)
+      if (t + u < t1) x[u] = *reinterpret_cast<const f4*>(out + ((size_t)bh * L + t + u) * d + c);
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (t + u < t1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[u][e] += cy[e];
+        *reinterpret_cast<f4*>(out + ((size_t)bh * L + t + u) * d + c) = x[u];
+      }
   }
 }
 
