@@ -27,6 +27,9 @@ CASES = [
     ("bf16", 1, 1, 64, 256, 256, "sigmoid16", "sigmoid16", 0.5),
     ("bf16", 2, 1, 90, 32, 224, "extreme", "extreme", 0.5),
     ("bf16", 1, 2, 50, 96, 64, "zero", "const", 0.5),
+    # fp32 I/O on a grid that fills the chip (512 workgroups of 128-row tiles):
+    # two waves per tile, the next chunk's column work formed a step early
+    ("fp32", 8, 4, 80, 128, 256, "sigmoid16", "sigmoid16", 0.5),
     # d_v = 512: the backward's transposed passes hold 512 state rows over four waves
     ("fp32", 1, 1, 45, 32, 512, "sigmoid16", "sigmoid16", 0.5),
     ("bf16", 1, 2, 70, 256, 512, "sigmoid16", "sigmoid16", 0.5),
