@@ -27,9 +27,8 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
 ]
-# Per-source extras.  The forward's kernels keep their MFMA accumulators in
-# ordinary VGPRs (no accumulator-register moves around every use of the
-# state); the backward's kernels are faster with the default allocation.
+# Per-source extras.  Most kernels keep their MFMA accumulators in ordinary
+# VGPRs (no accumulator-register moves around every use of an accumulator).
 EXTRA_FLAGS = {
     "gla_prep.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     # the recurrence's chunk body is one long block of LDS reads and MFMAs;
@@ -39,8 +38,13 @@ EXTRA_FLAGS = {
     # the general gate's recurrence rescales and converts its state every
     # chunk: in accumulator registers each such access costs a move
     "gla_ggate.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    # the backward's state recurrences: accumulators read as operands every chunk
-    "gla_bwd_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the backward's state recurrences: accumulators read as operands every
+    # chunk; the ILP scheduler helps its one wave per SIMD as it does the
+    # forward's recurrence
+    "gla_bwd_recur.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    # dq and dk: the intra-chunk products' accumulators are scaled and summed
+    # on the vector ALU right after the MFMAs
+    "gla_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -205,31 +205,21 @@ hipError_t launch_chunk_da_cum(const Plan& p, const void* v, const void* dout, c
 }
 
 // ------------------------------------------------------------------ B3b: dq, dk, dlog b
-// Column layout of the off-diagonal intra operands of k_chunk_dqdk.  For query
-// sub-chunk j >= 1 the dq operand holds K ⊙ e^{z_j - B} over key rows
-// [0, KQ(j)) (z_j = B at row 16 j; rows >= 16 j are 0), at columns
-// [OQ(j), OQ(j) + KQ(j)); for key sub-chunk u < NRT - 1 the dk operand holds
-// Q ⊙ e^{B - z'_u} over query rows [MLO(u), C) (z'_u = B at row 16 u + 15;
-// rows < 16 (u + 1) are 0), at columns [OK(u), OK(u) + C - MLO(u)).  K spans
-// are whole MFMA K steps.
+// K ranges of the sub-chunk products of k_chunk_dqdk, whole MFMA K steps.
+// The dq product of query sub-chunk j runs over key rows [0, KQ(j)) (keys
+// [0, 16 j) are used, or [0, 16 j + 16) when the diagonal block is folded in);
+// the dk product of key sub-chunk u over query rows [MLO(u), C) (queries
+// [16 (u + 1), C), or [16 u, C) folded).
 template <int K, int C>
 struct OffCols {
-  static constexpr int NRT = C / 16;
-  static constexpr int KQ(int j) { return ((16 * j + K - 1) / K) * K; }
-  static constexpr int MLO(int u) { return ((16 * (u + 1)) / K) * K; }
-  static constexpr int OQ(int j) {
-    int o = 0;
-    for (int i = 1; i < j; ++i) o += KQ(i);
-    return o;
-  }
-  static constexpr int OK(int u) {
-    int o = 0;
-    for (int i = 0; i < u; ++i) o += C - MLO(i);
-    return o;
-  }
-  static constexpr int WQ = OQ(NRT) > 0 ? OQ(NRT) : K;       // dq operand columns
-  static constexpr int WK = OK(NRT - 1) > 0 ? OK(NRT - 1) : K;  // dk operand columns
+  static constexpr int KQ(int j, bool fold) { return ((16 * (j + fold) + K - 1) / K) * K; }
+  static constexpr int MLO(int u, bool fold) { return ((16 * (u + !fold)) / K) * K; }
 };
+
+// Largest decay (B at a sub-chunk's first row minus B at its last) of a
+// channel whose diagonal sub-chunk block k_chunk_dqdk folds into its bf16
+// products: e^30 ~ 1e13 leaves fp32 ample range for the gated operands.
+constexpr float kFoldSpan = 30.f;
 
 // One workgroup per (batch-head, chunk, d_k tile of TK channels).
 // IB: the inter-chunk terms (already scaled by Lambda and Gamma) come in fp32
@@ -251,11 +241,14 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   constexpr int WC = NCT < 4 ? NCT : 4, WR = 4 / WC;
   constexpr int NCW = NCT / WC, NRW = (NRT + WR - 1) / WR;
   __shared__ float dad[C][17];                              // diagonal blocks, fp32
+  __shared__ int sharp_w[kThreads / kWave];                 // per wave: a sharp sub-chunk
   __shared__ float qf[C][LDK], kf[C][LDK], bt[C][LDK];
   // One region serves, in turn, dA with its diagonal blocks zeroed (rows for
   // the dq blocks, transposed reads for the dk blocks; with its low part for
   // bf16), the diagonal blocks' terms of dq and dk (dgo), and dlog b.
   using OC = OffCols<M::K, C>;
+  // bf16: the diagonal blocks may join the matrix-core products (see below)
+  constexpr bool FOLD = BF && C % M::K == 0;
   constexpr int DA_BYTES = C * LDA * (int)sizeof(T), DAL_BYTES = BF ? DA_BYTES : 0;
   constexpr int OFF_BYTES = DA_BYTES + DAL_BYTES;
   constexpr int DGO_BYTES = 2 * C * (TK + 4) * 4;
@@ -389,7 +382,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (dgb) dad[m0 + i][(c4 + e) & 15] = xda[i][e];
-        const float xo = dgb ? 0.f : xda[i][e];
+        // a folded diagonal block keeps its causal part (key <= query)
+        const float xo = dgb && (!FOLD || c4 + e > m0 + i) ? 0.f : xda[i][e];
         hi[i][e] = to_f32(from_f32<T>(xo));
         lo[i][e] = xo - hi[i][e];
       }
@@ -413,7 +407,33 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     for (int e = 0; e < 8; ++e) x[e] = raw_get(tb_, e);
     store8(&bt[trow][tc], x);
   }
+  // The diagonal sub-chunk blocks are folded into the products below (their
+  // own keys or queries inside the gated operands, the causal mask from dA)
+  // when no channel of the tile decays by more than kFoldSpan across any
+  // 16-row sub-chunk: the in-block factors e^{z_j - B_s} and e^{B_s - z'_u}
+  // then stay below e^kFoldSpan and the outer ones above e^-kFoldSpan.  A
+  // wave stages whole sub-chunks (16 rows every 16 TK / 8 lanes), so the
+  // lane on a sub-chunk's first row reads the same channels' cumsum on its
+  // last row from the lane 15 rows on.
+  if constexpr (FOLD) {
+    constexpr int LPR = TK / 8;
+    static_assert(16 * LPR <= kWave && (C * LPR) % kWave == 0, "whole sub-chunks per wave");
+    int sharp = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float b0 = has_tile ? raw_get(tb_, e) : 0.f;
+      const float b15 = __shfl_down(b0, 15 * LPR);
+      sharp |= has_tile && (trow & 15) == 0 && b0 - b15 > kFoldSpan;
+    }
+    const bool ws = __ballot(sharp) != 0;
+    if (l == 0) sharp_w[w] = ws;
+  }
   lds_barrier();
+  bool fold = FOLD;
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int i = 0; i < kThreads / kWave; ++i) fold = fold && !sharp_w[i];
+  }
 
   // inter-chunk terms: dO S_{n-1}^T and V dS_n^T, reduction over d_v, in
   // groups of KG K steps whose operands are loaded before their products are
@@ -449,8 +469,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     }
   }
 
-  // intra terms of the off-diagonal sub-chunk blocks, with the reference row
-  // of each block (both factors <= 1):
+  // intra terms of the off-diagonal sub-chunk blocks (and, folded, of the
+  // diagonal ones), with the reference row of each block (off the diagonal
+  // both factors are <= 1):
   //   dq rows of sub-chunk j:  e^{B_m - z_j} ⊙ [dA_off (K ⊙ e^{z_j - B})]
   //   dk rows of sub-chunk u:  e^{z'_u - B_r} ⊙ [dA_off^T (Q ⊙ e^{B - z'_u})]
   // Each lane forms its own B operand (its output channel, the K rows its
@@ -475,20 +496,20 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       fl = 0.f;
     }
   };
-  if constexpr (NRT > 1) {
+  if constexpr (NRT > 1 || FOLD) {
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
       const int j = wr + WR * rt;
-      if (j < 1 || j >= NRT) continue;
+      if (j < !fold || j >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
         const float z = bt[16 * j][c];
         floatx4 t4 = zero4();
-        for (int kk = 0; kk < OC::KQ(j); kk += M::K) {
+        for (int kk = 0; kk < OC::KQ(j, fold); kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
           typename M::frag bh, bl;
-          gated(kf, c, kc, 0, 16 * j, z, false, bh, bl);
+          gated(kf, c, kc, 0, 16 * (j + fold), z, false, bh, bl);
           const auto ah = load_frag<T>(&da[j * 16 + (l & 15)][kc]);
           t4 = M::run(ah, bh, t4);
           if constexpr (BF) {
@@ -506,16 +527,16 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
     for (int rt = 0; rt < NRW; ++rt) {
       const int u = wr + WR * rt;
-      if (u + 1 >= NRT) continue;
+      if (u + !fold >= NRT) continue;
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
         const float z = bt[16 * u + 15][c];
         floatx4 t4 = zero4();
-        for (int kk = OC::MLO(u); kk < C; kk += M::K) {
+        for (int kk = OC::MLO(u, fold); kk < C; kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
           typename M::frag bh, bl, ah, alo;
-          gated(qf, c, kc, 16 * (u + 1), C, z, true, bh, bl);
+          gated(qf, c, kc, 16 * (u + !fold), C, z, true, bh, bl);
           // A[r][m] = dA[m][r] for r in sub-chunk u (the lane's row), m at kc
           if constexpr (BF) {
             ah = col_frag_tr(&da[0][0], LDA, kk, 16 * u, l);
@@ -536,66 +557,68 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         }
       }
     }
-    lds_barrier();  // the diagonal terms below reuse the region
+    lds_barrier();  // the diagonal terms below and dlog b reuse the region
   }
-  // diagonal sub-chunk blocks, fp32 VALU with running gate products.  Thread
-  // (dq or dk, block b, channel c) keeps the block's 16 gates and its 16 k (or
-  // q) values of channel c in registers and forms all 16 rows of the block's
-  // term; the terms go through LDS to the waves that own the rows.
-  static_assert(2 * NRT * TK <= kThreads || (2 * NRT * TK) % kThreads == 0, "diagonal split");
-  for (int it = tid; it < 2 * NRT * TK; it += kThreads) {
-    const int which = it / (NRT * TK), b = (it / TK) % NRT, c = it % TK;
-    float a[16], x[16];
+  if (!fold) {
+    // diagonal sub-chunk blocks, fp32 VALU with running gate products.  Thread
+    // (dq or dk, block b, channel c) keeps the block's 16 gates and its 16 k (or
+    // q) values of channel c in registers and forms all 16 rows of the block's
+    // term; the terms go through LDS to the waves that own the rows.
+    static_assert(2 * NRT * TK <= kThreads || (2 * NRT * TK) % kThreads == 0, "diagonal split");
+    for (int it = tid; it < 2 * NRT * TK; it += kThreads) {
+      const int which = it / (NRT * TK), b = (it / TK) % NRT, c = it % TK;
+      float a[16], x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      // the per-row gate alpha of row i in the block (row 0's is not used)
-      a[i] = i ? gexp<T>(bt[16 * b + i][c] - bt[16 * b + i - 1][c]) : 1.f;
-      x[i] = which ? qf[16 * b + i][c] : kf[16 * b + i][c];
-    }
-    const float* dd = &dad[16 * b][0];  // [16][17]: dA[16 b + m][16 b + s]
-    if (which == 0) {
-      // dq row m: sum over keys s <= m of dA[m][s] k_s e^{B_m - B_s}
+      for (int i = 0; i < 16; ++i) {
+        // the per-row gate alpha of row i in the block (row 0's is not used)
+        a[i] = i ? gexp<T>(bt[16 * b + i][c] - bt[16 * b + i - 1][c]) : 1.f;
+        x[i] = which ? qf[16 * b + i][c] : kf[16 * b + i][c];
+      }
+      const float* dd = &dad[16 * b][0];  // [16][17]: dA[16 b + m][16 b + s]
+      if (which == 0) {
+        // dq row m: sum over keys s <= m of dA[m][s] k_s e^{B_m - B_s}
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        float E = 1.f, sum = 0.f;
+        for (int m = 0; m < 16; ++m) {
+          float E = 1.f, sum = 0.f;
 #pragma unroll
-        for (int s2 = m; s2 >= 0; --s2) {
-          if (s2 < m) E *= a[s2 + 1];
-          sum += dd[m * 17 + s2] * x[s2] * E;
+          for (int s2 = m; s2 >= 0; --s2) {
+            if (s2 < m) E *= a[s2 + 1];
+            sum += dd[m * 17 + s2] * x[s2] * E;
+          }
+          dgo[0][16 * b + m][c] = sum;
         }
-        dgo[0][16 * b + m][c] = sum;
-      }
-    } else {
-      // dk row r: sum over queries s >= r of dA[s][r] q_s e^{B_s - B_r}
+      } else {
+        // dk row r: sum over queries s >= r of dA[s][r] q_s e^{B_s - B_r}
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float F = 1.f, sum = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          float F = 1.f, sum = 0.f;
 #pragma unroll
-        for (int s2 = r; s2 < 16; ++s2) {
-          if (s2 > r) F *= a[s2];
-          sum += dd[s2 * 17 + r] * x[s2] * F;
+          for (int s2 = r; s2 < 16; ++s2) {
+            if (s2 > r) F *= a[s2];
+            sum += dd[s2 * 17 + r] * x[s2] * F;
+          }
+          dgo[1][16 * b + r][c] = sum;
         }
-        dgo[1][16 * b + r][c] = sum;
       }
     }
-  }
-  lds_barrier();
+    lds_barrier();
 #pragma unroll
-  for (int rt = 0; rt < NRW; ++rt) {
-    const int rti = wr + WR * rt;
-    if (rti >= NRT) continue;
+    for (int rt = 0; rt < NRW; ++rt) {
+      const int rti = wr + WR * rt;
+      if (rti >= NRT) continue;
 #pragma unroll
-    for (int ct = 0; ct < NCW; ++ct) {
-      const int c = (wc + WC * ct) * 16 + (l & 15);
+      for (int ct = 0; ct < NCW; ++ct) {
+        const int c = (wc + WC * ct) * 16 + (l & 15);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rti * 16 + (l >> 4) * 4 + r;
-        aq[rt][ct][r] += dgo[0][row][c];
-        ak[rt][ct][r] += dgo[1][row][c];
+        for (int r = 0; r < 4; ++r) {
+          const int row = rti * 16 + (l >> 4) * 4 + r;
+          aq[rt][ct][r] += dgo[0][row][c];
+          ak[rt][ct][r] += dgo[1][row][c];
+        }
       }
     }
+    lds_barrier();  // everyone is done with bt / the operands
   }
-  lds_barrier();  // everyone is done with bt / al / the operands
   float* dlb = reinterpret_cast<float*>(ubuf);  // reuse: dlog b of the tile, [C][LDK]
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {

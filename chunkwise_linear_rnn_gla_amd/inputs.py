@@ -23,7 +23,9 @@ Recipe (the same for every workload):
 Optional gate modes for edge cases: "zero" (alpha == 1), "const" (one
 log-decay value everywhere), "channel_const" (one value per key channel,
 shared over time), "extreme" (log alpha ~ -U(0, 20): gates that underflow
-fp32 products within a few steps).
+fp32 products within a few steps), "spiky" (the sigmoid gate with one entry in
+2,048 replaced by -U(10, 40): rare abrupt forgets, so that some 16-token spans
+of a channel decay far more than the rest).
 """
 from __future__ import annotations
 
@@ -106,6 +108,10 @@ def make_inputs(B, H, L, dk, dv, dtype="bf16", seed=0, gate="sigmoid16", h0_std=
         a = (F.logsigmoid(z[:, :, :1, :]) / 16.0).expand_as(z).contiguous()
     elif gate == "extreme":
         a = -20.0 * torch.rand(B, H, L, dk, generator=g)
+    elif gate == "spiky":
+        spike = torch.rand(B, H, L, dk, generator=g) < 1.0 / 2048
+        depth = 10.0 + 30.0 * torch.rand(B, H, L, dk, generator=g)
+        a = torch.where(spike, -depth, F.logsigmoid(z) / 16.0)
     else:
         raise ValueError(f"unknown gate mode {gate!r}")
     a = a.to(torch.float32).contiguous()

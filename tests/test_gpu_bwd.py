@@ -141,6 +141,21 @@ def test_recurrent_backward_gates(gate, backward_path):
     check_bwd(x, 64, f"recurrent-gate-{gate}", algo="recurrent")
 
 
+@pytest.mark.parametrize("C", [32, 64])
+@pytest.mark.parametrize("gate,value", [("spiky", -0.05), ("const", -1.9), ("const", -2.1)])
+def test_bf16_diagonal_fold_gates(gate, value, C, backward_path):
+    # bf16 dq and dk take a tile's diagonal 16 x 16 blocks into the matrix-core
+    # products when no channel of the tile decays by more than 30 across a
+    # 16-token sub-chunk: constant gates just inside (15 x 1.9 = 28.5) and
+    # just outside (31.5) that span, and rare sharp steps that leave tiles of
+    # both kinds in one launch
+    if C == 32 and backward_path != "auto":
+        pytest.skip("C=32 runs the materialized path under auto already")
+    x = make_inputs(2, 2, 4 * 64 + 37, 64, 128, "bf16", seed=670, gate=gate, h0_std=0.2,
+                    with_do=True, dhT_std=0.2, gate_value=value)
+    check_bwd(x, C, f"fold-{gate}{value}-C{C}")
+
+
 def test_empty_sequence_passes_dhT():
     x = make_inputs(1, 2, 0, 32, 64, "fp32", seed=606, with_do=True, dhT_std=1.0)
     g = run_bwd(x, 64)
