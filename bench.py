@@ -133,6 +133,41 @@ def log(*a):
 
 # ----------------------------------------------------------------- byte and FLOP counts
 
+CSRC = "chunkwise_linear_rnn_gla_amd/csrc"
+
+
+def kernel_sources(launch):
+    """The repository files a kernel's code comes from: the source that
+    defines it, the headers it includes (transitively), the host-side
+    planner and the build flags.  A traffic record stays valid until one of
+    these changes."""
+    import re
+    inv = {v: k for k, v in KERNEL_NAMES.items()}
+    base = launch
+    while base not in inv and "_" in base:
+        base = base.rsplit("_", 1)[0]
+    if launch == "recur_local":
+        base = "chunk_recur"
+    if base not in inv:
+        return list(KERNEL_SOURCES)
+    pat = re.compile(r"void\s+k_" + re.escape(inv[base]) + r"\b")
+    srcs = sorted(glob.glob(os.path.join(ROOT, CSRC, "*.hip")))
+    found = [f for f in srcs if pat.search(open(f).read())]
+    if not found:
+        return list(KERNEL_SOURCES)
+    deps, todo = set(), [found[0]]
+    while todo:
+        f = todo.pop()
+        rel = os.path.relpath(f, ROOT)
+        if rel in deps:
+            continue
+        deps.add(rel)
+        for inc in re.findall(r'#include "([a-z_]+\.h)"', open(f).read()):
+            todo.append(os.path.join(ROOT, CSRC, inc))
+    deps |= {CSRC + "/gla_api.hip", "chunkwise_linear_rnn_gla_amd/build.py"}
+    return sorted(deps)
+
+
 def sources_digest(paths):
     """sha256 over the given repository files (the sources of the kernels)."""
     h = hashlib.sha256()
@@ -714,8 +749,8 @@ def ingest_counters(fetch_dir, write_dir, workload, cal_fetch, cal_write):
                    "copy; bench.py reports them only while the listed sources hash to "
                    "sources_sha256.")
     entries = [e for e in rec.get("entries", []) if e.get("workload") != workload]
-    digest = sources_digest(KERNEL_SOURCES)
     for name in sorted(set(fe) & set(wr)):
+        srcs = kernel_sources(name)
         rb = fe[name][1] * 1024 * fetch_scale
         wb = wr[name][1] * 1024 * write_scale
         entries.append({"kernel": name, "workload": workload, "dispatches": fe[name][0],
@@ -724,7 +759,7 @@ def ingest_counters(fetch_dir, write_dir, workload, cal_fetch, cal_write):
                         "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
                         "read_bytes_per_launch": int(rb), "write_bytes_per_launch": int(wb),
                         "bytes_per_launch": int(rb + wb),
-                        "sources": KERNEL_SOURCES, "sources_sha256": digest})
+                        "sources": srcs, "sources_sha256": sources_digest(srcs)})
     rec["entries"] = entries
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
