@@ -179,7 +179,9 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     P.off_bdA = f; f = align_up(f + BH * P.NC * C * C * 4);
     P.off_bdqi = f; f = align_up(f + LD);
     P.off_bdki = f; f = align_up(f + LD);
-    P.off_bdlt = f; f = align_up(f + BH * P.NC * dk * 4);
+    // running sums of the gate gradient's inter terms (two halves per chunk)
+    P.off_bqpre = f; f = align_up(f + BH * P.NC * 2 * dk * 4);
+    P.off_bksuf = f; f = align_up(f + BH * P.NC * 2 * dk * 4);
     P.off_brs = f; f = align_up(f + BH * dk * 4);
     P.off_bvrec = f; f = align_up(f + P.ws_recur);
     P.ws_bwd = P.bwd_rec ? f : ws_bwd_mat;
@@ -303,8 +305,9 @@ static gla_status run_two_pass(const Plan& p, const void* q, const void* k, cons
 //    (k_bwd_inter): the inter-chunk terms of dq (S, chunks in order) and of dk
 //    (dS, chunks backwards), rowsum(hT ⊙ dhT) and dh0;
 //  * the intra-chunk terms of dq and dk added per chunk, with the closed-form
-//    dlog b = q ⊙ dq - k ⊙ dk and its reverse cumsum inside the chunk, then
-//    the carry over later chunks (zako-mio report ch. 3.4);
+//    dlog b = q ⊙ dq - k ⊙ dk and its reverse cumsum inside the chunk plus
+//    the carry over later chunks (zako-mio report ch. 3.4), whose chunk
+//    totals k_bwd_inter has summed from the inter terms;
 //  * dv: the gradient of v is the forward of the time-reversed sequence with
 //    queries k, keys q, values dout, the gates shifted by one token and dhT
 //    as the initial state, so the two-pass forward's kernels compute it in
@@ -317,16 +320,16 @@ static gla_status run_bwd_recurrent(const Plan& p, const void* q, const void* k,
   float* dA = (float*)(ws + p.off_bdA);
   float* dqi = (float*)(ws + p.off_bdqi);
   float* dki = (float*)(ws + p.off_bdki);
-  float* dlt = (float*)(ws + p.off_bdlt);
+  float* qpre = (float*)(ws + p.off_bqpre);
+  float* ksuf = (float*)(ws + p.off_bksuf);
   float* rs = (float*)(ws + p.off_brs);
   char* vr = ws + p.off_bvrec;
   GLA_LAUNCH("chunk_da_cum", launch_chunk_da_cum(p, v, dout, log_alpha, cum, dA, s));
-  const BwdInterJob jq{dout, v, k, h0, dqi, rs, dhT, nullptr, 0};
-  const BwdInterJob jk{v, dout, q, dhT, dki, nullptr, nullptr, dh0, 1};
+  const BwdInterJob jq{dout, v, k, h0, dqi, rs, dhT, nullptr, 0, q, qpre};
+  const BwdInterJob jk{v, dout, q, dhT, dki, nullptr, nullptr, dh0, 1, k, ksuf};
   GLA_LAUNCH("bwd_inter", launch_bwd_inter(p, jq, jk, cum, s));
   GLA_LAUNCH("chunk_dqdk", launch_chunk_dqdk_inter(p, q, k, cum, dA, dqi, dki, dq, dk,
-                                                   dlog_alpha, dlt, s));
-  GLA_LAUNCH("dla_carry", launch_dla_carry(p, dlt, rs, dlog_alpha, s));
+                                                   dlog_alpha, qpre, ksuf, rs, s));
   // dv: the forward's passes over the reversed sequence (q <- k, k <- q,
   // v <- dout, h0 <- dhT); its final state is not needed (dh0 came above)
   void* qg = vr + p.off_qg;

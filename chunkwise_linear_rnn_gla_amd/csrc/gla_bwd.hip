@@ -223,7 +223,9 @@ constexpr float kFoldSpan = 30.f;
 
 // One workgroup per (batch-head, chunk, d_k tile of TK channels).
 // IB: the inter-chunk terms (already scaled by Lambda and Gamma) come in fp32
-// from dqi / dki (k_bwd_inter) instead of products with materialised states.
+// from dqi / dki (k_bwd_inter) instead of products with materialised states,
+// and dlog alpha is written whole (with the carry over later chunks, from
+// cq, ck and crs); without IB it is chunk-local, its chunk totals go to dlt.
 template <typename T, int C, int TK, bool IB>
 __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -231,6 +233,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     const T* __restrict__ st_lo, const T* __restrict__ dst_n, const T* __restrict__ dst_lo,
     const float* __restrict__ dAw, const float* __restrict__ dqi, const float* __restrict__ dki,
     T* __restrict__ dq, T* __restrict__ dkk, float* __restrict__ dla, float* __restrict__ dlt,
+    const float* __restrict__ cq, const float* __restrict__ ck, const float* __restrict__ crs,
     int L, int dk, int dv, int NC) {
   using M = Mma<T>;
   constexpr bool BF = sizeof(T) == 2;
@@ -369,6 +372,27 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         }
       }
     }
+  }
+  // IB: dlog alpha's carry into this chunk, rowsum(hT ⊙ dhT) plus the later
+  // chunks' totals of q ⊙ dq - k ⊙ dk.  Summed over a chunk, the intra-chunk
+  // parts of q ⊙ dq and of k ⊙ dk are the same double sum over the chunk's
+  // (query, key) pairs, so a chunk's total is that of the inter terms alone,
+  // which k_bwd_inter sums as it walks: an inclusive prefix over chunks of
+  // q ⊙ dq_inter (the later chunks' part is the whole sum minus the prefix)
+  // and an exclusive suffix of k ⊙ dk_inter, each in two halves of the
+  // chunk's rows.  Loaded here, used at the end.
+  float cyq[4], cyk[2], cyr = 0.f;
+  if constexpr (IB) {
+    const int cc = c0 + tid % TK;
+    const float* qp = cq + (size_t)bh * NC * 2 * dk + cc;
+    const float* kp = ck + ((size_t)bh * NC + n) * 2 * dk + cc;
+    cyq[0] = qp[(size_t)(NC - 1) * 2 * dk];
+    cyq[1] = qp[((size_t)(NC - 1) * 2 + 1) * dk];
+    cyq[2] = qp[(size_t)n * 2 * dk];
+    cyq[3] = qp[((size_t)n * 2 + 1) * dk];
+    cyk[0] = kp[0];
+    cyk[1] = kp[dk];
+    cyr = crs[(size_t)bh * dk + cc];
   }
 
   // dA rows of the block as 4-element vectors (hi / lo split, the diagonal
@@ -660,12 +684,14 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     lds_barrier();
     float off = 0.f;
     for (int g2 = g + 1; g2 < NGR; ++g2) off += gtot[g2 * TK + c];
+    if constexpr (IB) off += cyr + ((cyq[0] - cyq[2]) + (cyq[1] - cyq[3])) - (cyk[0] + cyk[1]);
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const int row = g * RPG + i;
       if (row < rv) dla[qo + (size_t)(r0 + row) * dk + c0 + c] = part[i] + off;
     }
-    if (g == 0) dlt[((size_t)bh * NC + n) * dk + c0 + c] = part[0] + off;
+    // without IB, the chunk total for k_dla_carry
+    if (!IB && g == 0) dlt[((size_t)bh * NC + n) * dk + c0 + c] = part[0] + off;
   }
 }
 
@@ -902,18 +928,20 @@ static hipError_t launch_dqdk_t(const Plan& p, const void* q, const void* k, con
   hipLaunchKernelGGL((k_chunk_dqdk<T, C, TK, false>), dim3(p.NC, p.dk / TK, p.BH), dim3(kThreads),
                      0, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, cum,
                      (const T*)st_n, (const T*)st_lo, (const T*)dst_n, (const T*)dst_lo, dAw,
-                     nullptr, nullptr, (T*)dq, (T*)dk, dla, dlt, p.L, p.dk, p.dv, p.NC);
+                     nullptr, nullptr, (T*)dq, (T*)dk, dla, dlt, nullptr, nullptr, nullptr, p.L,
+                     p.dk, p.dv, p.NC);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_dqdk_inter(const Plan& p, const void* q, const void* k, const float* cum,
                                    const float* dAw, const float* dqi, const float* dki, void* dq,
-                                   void* dk, float* dla, float* dlt, hipStream_t s) {
+                                   void* dk, float* dla, const float* qpre, const float* ksuf,
+                                   const float* rs, hipStream_t s) {
   if (!p.bf16 || p.C != 64 || p.dk % 32) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_chunk_dqdk<bf16, 64, 32, true>), dim3(p.NC, p.dk / 32, p.BH),
                      dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k, nullptr, nullptr, cum,
                      nullptr, nullptr, nullptr, nullptr, dAw, dqi, dki, (bf16*)dq, (bf16*)dk, dla,
-                     dlt, p.L, p.dk, p.dv, p.NC);
+                     nullptr, qpre, ksuf, rs, p.L, p.dk, p.dv, p.NC);
   return hipGetLastError();
 }
 

@@ -26,6 +26,15 @@
 // each); dO, V are exact in bf16.  The dq job also leaves rowsum(hT ⊙ dhT)
 // (hT = its final state), the dk job dh0 = dS_{-1}.
 //
+// Gate-gradient sums: summed over the rows of a chunk, the intra-chunk parts
+// of q ⊙ dq and k ⊙ dk cancel, so the chunk totals of the closed form come
+// from the inter terms alone.  Each job multiplies its finished rows by q
+// (dq job) or k (dk job), sums them over the rows and keeps a running sum
+// over the chunks it has walked: an inclusive prefix (dq job) or an
+// exclusive suffix (dk job), written per chunk and per half of its rows, so
+// that the dq/dk kernel adds the carry over later chunks without a pass of
+// its own over dlog alpha.
+//
 // Work split: four waves, each holding a 16-channel column block of U for
 // one half of the d_v rows.  The output product is then a sum over d_v of
 // two halves: each wave forms its half for all 64 rows, passes the rows its
@@ -75,6 +84,33 @@ struct InterLayout {
   static_assert(TB % 1024 == 0 && NCX == 4 * CPW + 1 && SB == 4 * 1024,
                 "1 KB copies, one of Z's input per wave");
 };
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// The sums over the 16 lanes of a DPP row of four values, left in every lane
+// of the row: quad permutations [1,0,3,2] and [2,3,0,1] sum each quad, the
+// half-row mirror adds the neighbouring quad, the row mirror the other half.
+// Written as one asm block rather than with the DPP builtin, which is
+// convergent and so keeps the compiler from unrolling the chunk loop.  The
+// four values interleave, so every DPP add reads a register written at least
+// three instructions earlier; the block opens with the two wait states a
+// DPP read of a just-written register needs.
+__device__ inline void row16_sum4(f32x4& x) {
+  float a = x[0], b = x[1], c = x[2], d = x[3];
+#define GLA_DPP4(CTRL)                                                    \
+  "v_add_f32_dpp %0, %0, %0 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+  "v_add_f32_dpp %1, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+  "v_add_f32_dpp %2, %2, %2 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+  "v_add_f32_dpp %3, %3, %3 " CTRL " row_mask:0xf bank_mask:0xf\n"
+  asm("s_nop 1\n" GLA_DPP4("quad_perm:[1,0,3,2]") GLA_DPP4("quad_perm:[2,3,0,1]")
+          GLA_DPP4("row_half_mirror") GLA_DPP4("row_mirror")
+      : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+#undef GLA_DPP4
+  x[0] = a;
+  x[1] = b;
+  x[2] = c;
+  x[3] = d;
+}
 
 __device__ inline bf16x4 lds_read8(const unsigned char* p) {
   return *reinterpret_cast<const bf16x4*>(p);
@@ -167,6 +203,14 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
   const unsigned char* xu = reinterpret_cast<const unsigned char*>(J.xu) + (size_t)bh * L * DV * 2;
   const unsigned char* zs = reinterpret_cast<const unsigned char*>(J.z) + ((size_t)bh * L * dk + i0) * 2;
   const float* cs = cum + (size_t)bh * L * dk + i0;
+  // the gate-gradient sums' input (q or k) through a resource spanning the
+  // head's L rows (rows past the end of the sequence read 0)
+  const bool sums = J.tsum != nullptr;
+  const __amdgpu_buffer_rsrc_t trsrc = __builtin_amdgcn_make_buffer_rsrc(
+      sums ? const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(J.tin)) +
+                 (size_t)bh * L * dk * 2
+           : reinterpret_cast<unsigned char*>(J.out),
+      0, sums ? L * dk * 2 : 0, 0x00020000);
   int xrow[CPW + 1], xcol[CPW + 1];
 #pragma unroll
   for (int j = 0; j <= CPW; ++j) {
@@ -225,11 +269,14 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
   CumRegs R;
   floatx4 Yk[2];  // the previous chunk's own output rows (this wave's half)
   f32x4 sf[2];    // ... and their scale factors
+  u32x2 tv[2];    // ... and q or k at them (4 bf16 channels each)
+  f32x4 run = zero4();  // running gate-gradient sum of the lane's 4 channels
   int r0prev = 0;
 
   // add the partner's half to the rows this wave finishes, scale and store:
   // lane (g, n) holds rows 16 (2 h + t) + n, channels wc + 4 g + r
   auto finish = [&](int r0, int par) __attribute__((always_inline)) {
+    f32x4 ts = zero4();
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const f32x4 o = *reinterpret_cast<const f32x4*>(lds + pin + par * Lay::PB + t * 1024);
@@ -239,6 +286,20 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
       const int m = 16 * (2 * h + t) + n;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), orsrc,
                                              ((r0 + m) * dk + i0 + wc + 4 * g) * 4, 0, 0);
+      if (sums) {
+        const bf16x4 x = __builtin_bit_cast(bf16x4, tv[t]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ts[r] += static_cast<float>(x[r]) * y[r];
+      }
+    }
+    if (sums) {
+      // over the 16 rows of the lane group, then into the running sum
+      row16_sum4(ts);
+      if (!REV) run += ts;
+      if (n == 0)
+        *reinterpret_cast<f32x4*>(J.tsum + (((size_t)bh * NC + r0 / kBC) * 2 + h) * dk + i0 + wc +
+                                  4 * g) = run;
+      if (REV) run += ts;
     }
   };
 
@@ -260,6 +321,7 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
     // issues its output stores, keeps the compiler's wait for them (it does
     // not see that wait) from also waiting for the stores.
     asm volatile("" ::"v"(R.bcol), "v"(R.blast), "v"(R.bm[0]), "v"(R.bm[1]));
+    if (st > 0 && sums) asm volatile("" ::"v"(tv[0]), "v"(tv[1]));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -294,6 +356,13 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
     // so that they complete during the step
     if (st > 0) finish(r0prev, b ^ 1);
 
+    // this chunk's q or k at the rows this wave finishes (used next step)
+    if (sums) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        tv[t] = __builtin_amdgcn_raw_buffer_load_b64(
+            trsrc, ((r0 + 16 * (2 * h + t) + n) * dk + i0 + wc + 4 * g) * 2, 0, 0);
+    }
     // the next chunk's loads, into the other buffer and the cumsum registers
     if (st + 1 < NC) {
       load_cum(chunk_of(st + 1), R);

@@ -42,7 +42,7 @@ struct Plan {
   // dq and dk (fp32), chunk totals of dlog b, rowsum(hT * dhT), and the
   // two-pass records of the reversed-sequence dv pass (at off_bvrec)
   int bwd_rec;
-  size_t off_bcum, off_bdA, off_bdqi, off_bdki, off_bdlt, off_brs, off_bvrec;
+  size_t off_bcum, off_bdA, off_bdqi, off_bdki, off_bqpre, off_bksuf, off_brs, off_bvrec;
 };
 
 // Forward path and its tuning, as the caller chose them (gla_fwd_config in
@@ -181,10 +181,13 @@ hipError_t launch_chunk_dqdk(const Plan& p, const void* q, const void* k, const 
                              const float* dAw, void* dq, void* dk, float* dla, float* dlt,
                              hipStream_t s);
 // The same with the inter-chunk terms (scaled) from dqi / dki [BH][L][dk]
-// fp32 (bf16 I/O, C = 64, dk % 32 == 0).
+// fp32 (bf16 I/O, C = 64, dk % 32 == 0), writing the whole dlog alpha: the
+// later chunks' totals come from k_bwd_inter's running sums (qpre, ksuf, as
+// BwdInterJob::tsum) and rs = rowsum(hT ⊙ dhT) [BH][dk].
 hipError_t launch_chunk_dqdk_inter(const Plan& p, const void* q, const void* k, const float* cum,
                                    const float* dAw, const float* dqi, const float* dki, void* dq,
-                                   void* dk, float* dla, float* dlt, hipStream_t s);
+                                   void* dk, float* dla, const float* qpre, const float* ksuf,
+                                   const float* rs, hipStream_t s);
 hipError_t launch_chunk_dv(const Plan& p, const void* k, const void* dout, const float* cum,
                            const void* dst_t, const float* Aw, void* dv, hipStream_t s);
 hipError_t launch_rowsum_state(const Plan& p, const float* hT, const float* dhT, float* rs,
@@ -259,6 +262,13 @@ struct BwdInterJob {
   const float* fin_with;
   float* fin_state;
   int rev;
+  // the closed-form gate gradient's chunk sums of the inter term: tin is the
+  // input multiplying it (q for the dq job, k for the dk job), tsum receives,
+  // per chunk and half of the chunk's rows, sum_rows tin ⊙ term as a running
+  // sum: inclusive prefix over chunks (dq job) or exclusive suffix (dk job),
+  // [BH][NC][2][dk] fp32.  Both may be null (no sums).
+  const void* tin;
+  float* tsum;
 };
 bool bwd_inter_supported(int bf16, int C, int dk, int dv, int L);
 hipError_t launch_bwd_inter(const Plan& p, const BwdInterJob& jq, const BwdInterJob& jk,
