@@ -78,7 +78,9 @@ struct InterLayout {
   // exchange of output halves: per parity, wave and tile 64 lanes x 16 B
   static constexpr int PB = 4 * 2 * 1024;
   static constexpr int oP = 2 * RBUF;
-  static constexpr int LDS = 2 * RBUF + 2 * PB;
+  // q or k at the rows each wave finishes (32 rows x 16 channels per wave)
+  static constexpr int oT = 2 * RBUF + 2 * PB;
+  static constexpr int LDS = oT + 4 * 1024;
   static_assert(UPR % 16 == 0, "rows of whole 256-byte bank spans");
   static_assert(LDS <= kLdsLimit, "staged chunk exceeds LDS");
   static_assert(TB % 1024 == 0 && NCX == 4 * CPW + 1 && SB == 4 * 1024,
@@ -203,14 +205,14 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
   const unsigned char* xu = reinterpret_cast<const unsigned char*>(J.xu) + (size_t)bh * L * DV * 2;
   const unsigned char* zs = reinterpret_cast<const unsigned char*>(J.z) + ((size_t)bh * L * dk + i0) * 2;
   const float* cs = cum + (size_t)bh * L * dk + i0;
-  // the gate-gradient sums' input (q or k) through a resource spanning the
-  // head's L rows (rows past the end of the sequence read 0)
+  // the gate-gradient sums' input (q or k): each wave copies the rows it
+  // finishes, 16 bytes per lane (row 32 h + l / 2, 8 channels), rows past the
+  // end of the sequence repeating its last row (masked where they are used)
   const bool sums = J.tsum != nullptr;
-  const __amdgpu_buffer_rsrc_t trsrc = __builtin_amdgcn_make_buffer_rsrc(
-      sums ? const_cast<unsigned char*>(reinterpret_cast<const unsigned char*>(J.tin)) +
-                 (size_t)bh * L * dk * 2
-           : reinterpret_cast<unsigned char*>(J.out),
-      0, sums ? L * dk * 2 : 0, 0x00020000);
+  const unsigned char* ts_in =
+      sums ? reinterpret_cast<const unsigned char*>(J.tin) + ((size_t)bh * L * dk + i0 + wc) * 2
+           : nullptr;
+  const unsigned tlds = lds0 + (unsigned)(Lay::oT + w * 1024);
   int xrow[CPW + 1], xcol[CPW + 1];
 #pragma unroll
   for (int j = 0; j <= CPW; ++j) {
@@ -269,7 +271,6 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
   CumRegs R;
   floatx4 Yk[2];  // the previous chunk's own output rows (this wave's half)
   f32x4 sf[2];    // ... and their scale factors
-  u32x2 tv[2];    // ... and q or k at them (4 bf16 channels each)
   f32x4 run = zero4();  // running gate-gradient sum of the lane's 4 channels
   int r0prev = 0;
 
@@ -286,8 +287,8 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
       const int m = 16 * (2 * h + t) + n;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), orsrc,
                                              ((r0 + m) * dk + i0 + wc + 4 * g) * 4, 0, 0);
-      if (sums) {
-        const bf16x4 x = __builtin_bit_cast(bf16x4, tv[t]);
+      if (sums && r0 + m < L) {
+        const bf16x4 x = lds_read8(lds + Lay::oT + w * 1024 + (16 * t + n) * 32 + 8 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) ts[r] += static_cast<float>(x[r]) * y[r];
       }
@@ -321,7 +322,6 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
     // issues its output stores, keeps the compiler's wait for them (it does
     // not see that wait) from also waiting for the stores.
     asm volatile("" ::"v"(R.bcol), "v"(R.blast), "v"(R.bm[0]), "v"(R.bm[1]));
-    if (st > 0 && sums) asm volatile("" ::"v"(tv[0]), "v"(tv[1]));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -356,12 +356,13 @@ __device__ __attribute__((always_inline)) inline void inter_walk(
     // so that they complete during the step
     if (st > 0) finish(r0prev, b ^ 1);
 
-    // this chunk's q or k at the rows this wave finishes (used next step)
+    // this chunk's q or k at the rows this wave finishes (used next step,
+    // after finish above has read the previous chunk's: its sums are formed,
+    // so those LDS reads have completed)
     if (sums) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        tv[t] = __builtin_amdgcn_raw_buffer_load_b64(
-            trsrc, ((r0 + 16 * (2 * h + t) + n) * dk + i0 + wc + 4 * g) * 2, 0, 0);
+      asm volatile("" ::"v"(run));
+      const int tr = min(r0 + 32 * h + (l >> 1), L - 1);
+      dma16b(make_rsrc(ts_in), (unsigned)((tr * dk + 8 * (l & 1)) * 2), 0u, tlds);
     }
     // the next chunk's loads, into the other buffer and the cumsum registers
     if (st + 1 < NC) {
