@@ -141,6 +141,19 @@ def test_recurrent_backward_gates(gate, backward_path):
     check_bwd(x, 64, f"recurrent-gate-{gate}", algo="recurrent")
 
 
+@pytest.mark.parametrize("gate", ["sigmoid16", "zero"])
+def test_recurrent_backward_long_sequence_carry(gate, backward_path):
+    # dlog alpha's carry over later chunks comes from running sums over 128
+    # chunks: the dq side as the whole sum minus a prefix, the dk side as a
+    # suffix.  With no decay (gate 0) every later chunk contributes in full,
+    # the largest sums the carry has to difference.
+    if backward_path != "auto":
+        pytest.skip("recurrent-path carry (covered once)")
+    x = make_inputs(1, 2, 128 * 64 - 5, 64, 128, "bf16", seed=680, gate=gate, h0_std=0.2,
+                    with_do=True, dhT_std=0.3)
+    check_bwd(x, 64, f"recurrent-long-{gate}", algo="recurrent")
+
+
 @pytest.mark.parametrize("C", [32, 64])
 @pytest.mark.parametrize("gate,value", [("spiky", -0.05), ("const", -1.9), ("const", -2.1)])
 def test_bf16_diagonal_fold_gates(gate, value, C, backward_path):
