@@ -245,7 +245,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   constexpr int NCW = NCT / WC, NRW = (NRT + WR - 1) / WR;
   __shared__ float dad[C][17];                              // diagonal blocks, fp32
   __shared__ int sharp_w[kThreads / kWave];                 // per wave: a sharp sub-chunk
-  __shared__ float qf[C][LDK], kf[C][LDK], bt[C][LDK];
+  // q, k and the cumsum of the tile, channel-major (a channel's tokens are
+  // contiguous, so a lane's run of 8 tokens is two 16-byte reads); a row of
+  // C + 4 floats puts 16 consecutive channels' 16-byte reads on distinct banks
+  constexpr int LDC = C + 4;
+  __shared__ __attribute__((aligned(16))) float qf[TK][LDC], kf[TK][LDC], bt[TK][LDC];
   // One region serves, in turn, dA with its diagonal blocks zeroed (rows for
   // the dq blocks, transposed reads for the dk blocks; with its low part for
   // bf16), the diagonal blocks' terms of dq and dk (dgo), and dlog b.
@@ -420,16 +424,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   stage_da();
   // q, k (0 past the end of the sequence) and the cumsum of the tile
   if (has_tile) {
-    float x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = tvalid ? raw_get(tq_, e) : 0.f;
-    store8(&qf[trow][tc], x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = tvalid ? raw_get(tk_, e) : 0.f;
-    store8(&kf[trow][tc], x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = raw_get(tb_, e);
-    store8(&bt[trow][tc], x);
+    for (int e = 0; e < 8; ++e) {
+      qf[tc + e][trow] = tvalid ? raw_get(tq_, e) : 0.f;
+      kf[tc + e][trow] = tvalid ? raw_get(tk_, e) : 0.f;
+      bt[tc + e][trow] = raw_get(tb_, e);
+    }
   }
   // The diagonal sub-chunk blocks are folded into the products below (their
   // own keys or queries inside the gated operands, the causal mask from dA)
@@ -482,12 +482,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
-        const float blast = bt[C - 1][c];
+        const float blast = bt[c][C - 1];
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[c][rti * 16 + (l >> 4) * 4]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int row = rti * 16 + (l >> 4) * 4 + r;
-          aq[rt][ct][r] *= gexp<T>(bt[row][c]);
-          ak[rt][ct][r] *= gexp<T>(blast - bt[row][c]);
+          aq[rt][ct][r] *= gexp<T>(b4[r]);
+          ak[rt][ct][r] *= gexp<T>(blast - b4[r]);
         }
       }
     }
@@ -503,20 +503,26 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   // for bf16; the A operand is dA's rows (dq) or, read transposed, its
   // columns (dk).  Nothing is written to LDS here.
   // x = src[tok][c] e^{+-(B_tok - z)} for tok in [t0, t1), else 0
-  auto gated = [&](const float (*src)[LDK], int c, int kc, int t0, int t1, float z, bool up,
+  auto gated = [&](const float (*src)[LDC], int c, int kc, int t0, int t1, float z, bool up,
                    typename M::frag& fh, typename M::frag& fl) __attribute__((always_inline)) {
     if constexpr (BF) {
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bt[c][kc]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bt[c][kc + 4]);
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(&src[c][kc]);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(&src[c][kc + 4]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = kc + e;
-        const float g = up ? bt[tok][c] - z : z - bt[tok][c];
-        const float x = (tok >= t0 && tok < t1) ? src[tok][c] * gexp<T>(g) : 0.f;
+        const float bv = e < 4 ? b0[e] : b1[e - 4];
+        const float sv = e < 4 ? s0[e] : s1[e - 4];
+        const float g = up ? bv - z : z - bv;
+        const float x = (tok >= t0 && tok < t1) ? sv * gexp<T>(g) : 0.f;
         fh[e] = static_cast<bf16>(x);
         fl[e] = static_cast<bf16>(x - static_cast<float>(fh[e]));
       }
     } else {
-      const float g = up ? bt[kc][c] - z : z - bt[kc][c];
-      fh = (kc >= t0 && kc < t1) ? src[kc][c] * gexp<T>(g) : 0.f;
+      const float g = up ? bt[c][kc] - z : z - bt[c][kc];
+      fh = (kc >= t0 && kc < t1) ? src[c][kc] * gexp<T>(g) : 0.f;
       fl = 0.f;
     }
   };
@@ -528,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
-        const float z = bt[16 * j][c];
+        const float z = bt[c][16 * j];
         floatx4 t4 = zero4();
         for (int kk = 0; kk < OC::KQ(j, fold); kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
@@ -541,11 +547,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
             t4 = M::run(ah, bl, t4);
           }
         }
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[c][j * 16 + (l >> 4) * 4]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = j * 16 + (l >> 4) * 4 + r;
-          aq[rt][ct][r] += gexp<T>(bt[row][c] - z) * t4[r];
-        }
+        for (int r = 0; r < 4; ++r) aq[rt][ct][r] += gexp<T>(b4[r] - z) * t4[r];
       }
     }
 #pragma unroll
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
-        const float z = bt[16 * u + 15][c];
+        const float z = bt[c][16 * u + 15];
         floatx4 t4 = zero4();
         for (int kk = OC::MLO(u, fold); kk < C; kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
@@ -574,11 +578,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
             t4 = M::run(ah, bl, t4);
           }
         }
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[c][u * 16 + (l >> 4) * 4]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = u * 16 + (l >> 4) * 4 + r;
-          ak[rt][ct][r] += gexp<T>(z - bt[row][c]) * t4[r];
-        }
+        for (int r = 0; r < 4; ++r) ak[rt][ct][r] += gexp<T>(z - b4[r]) * t4[r];
       }
     }
     lds_barrier();  // the diagonal terms below and dlog b reuse the region
@@ -595,8 +597,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         // the per-row gate alpha of row i in the block (row 0's is not used)
-        a[i] = i ? gexp<T>(bt[16 * b + i][c] - bt[16 * b + i - 1][c]) : 1.f;
-        x[i] = which ? qf[16 * b + i][c] : kf[16 * b + i][c];
+        a[i] = i ? gexp<T>(bt[c][16 * b + i] - bt[c][16 * b + i - 1]) : 1.f;
+        x[i] = which ? qf[c][16 * b + i] : kf[c][16 * b + i];
       }
       const float* dd = &dad[16 * b][0];  // [16][17]: dA[16 b + m][16 b + s]
       if (which == 0) {
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = rti * 16 + (l >> 4) * 4 + r;
-        dlb[row * LDK + c] = qf[row][c] * aq[rt][ct][r] - kf[row][c] * ak[rt][ct][r];
+        dlb[row * LDK + c] = qf[c][row] * aq[rt][ct][r] - kf[c][row] * ak[rt][ct][r];
         if (row < rv) {
           const size_t gi = qo + (size_t)(r0 + row) * dk + c0 + c;
           dq[gi] = from_f32<T>(aq[rt][ct][r]);
