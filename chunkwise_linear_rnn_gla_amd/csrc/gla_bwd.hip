@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   constexpr int DA_BYTES = C * LDA * (int)sizeof(T), DAL_BYTES = BF ? DA_BYTES : 0;
   constexpr int OFF_BYTES = DA_BYTES + DAL_BYTES;
   constexpr int DGO_BYTES = 2 * C * (TK + 4) * 4;
-  static_assert(C * LDK * 4 <= DGO_BYTES, "dlog b fits the region");
+  static_assert(TK * (C + 4) * 4 <= DGO_BYTES, "dlog b fits the region");
   __shared__ __attribute__((aligned(16))) unsigned char ubuf[OFF_BYTES > DGO_BYTES ? OFF_BYTES : DGO_BYTES];
   auto da = reinterpret_cast<T(*)[LDA]>(ubuf);
   auto dal = reinterpret_cast<T(*)[LDA]>(ubuf + DA_BYTES);
@@ -645,18 +645,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     }
     lds_barrier();  // everyone is done with bt / the operands
   }
-  float* dlb = reinterpret_cast<float*>(ubuf);  // reuse: dlog b of the tile, [C][LDK]
+  float* dlb = reinterpret_cast<float*>(ubuf);  // reuse: dlog b of the tile, [TK][LDC]
 #pragma unroll
   for (int rt = 0; rt < NRW; ++rt) {
     const int rti = wr + WR * rt;
     if (rti >= NRT) continue;
 #pragma unroll
     for (int ct = 0; ct < NCW; ++ct) {
-      const int c = (wc + WC * ct) * 16 + (l & 15);
+      const int c = (wc + WC * ct) * 16 + (l & 15), row0 = rti * 16 + (l >> 4) * 4;
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(&qf[c][row0]);
+      const f32x4 k4 = *reinterpret_cast<const f32x4*>(&kf[c][row0]);
+      f32x4 d4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d4[r] = q4[r] * aq[rt][ct][r] - k4[r] * ak[rt][ct][r];
+      *reinterpret_cast<f32x4*>(&dlb[c * LDC + row0]) = d4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = rti * 16 + (l >> 4) * 4 + r;
-        dlb[row * LDK + c] = qf[c][row] * aq[rt][ct][r] - kf[c][row] * ak[rt][ct][r];
+        const int row = row0 + r;
         if (row < rv) {
           const size_t gi = qo + (size_t)(r0 + row) * dk + c0 + c;
           dq[gi] = from_f32<T>(aq[rt][ct][r]);
@@ -674,12 +679,22 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   float* gtot = &bt[0][0];  // reuse: [NGR][TK] group totals
   {
     const int c = tid % TK, g = tid / TK;
-    float part[RPG];
+    float part[RPG], xv[RPG];
+    if constexpr (RPG % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < RPG; i += 4) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(&dlb[c * LDC + g * RPG + i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[i + e] = t[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPG; ++i) xv[i] = dlb[c * LDC + g * RPG + i];
+    }
     float s = 0.f;
 #pragma unroll
     for (int i = RPG - 1; i >= 0; --i) {
-      const int row = g * RPG + i;
-      s += row < rv ? dlb[row * LDK + c] : 0.f;
+      s += g * RPG + i < rv ? xv[i] : 0.f;
       part[i] = s;
     }
     gtot[g * TK + c] = s;
