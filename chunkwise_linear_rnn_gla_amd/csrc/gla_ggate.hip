@@ -113,6 +113,33 @@ __device__ inline int pf_index(int t, int s) { return ((t + 16 * (s >> 2)) << 2)
 }  // namespace
 
 constexpr int kPfFloats = 256 + 16;  // P below the diagonal, then its diagonal
+
+// One channel's 16 staged tokens as fp32, in 16-byte LDS units.
+__device__ inline void lds16(const float* p, float* o) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[4 * j + e] = v[e];
+  }
+}
+__device__ inline void lds16(const bf16* p, float* o) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p + 8 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[8 * j + e] = static_cast<float>(v[e]);
+  }
+}
+__device__ inline void sts16(float* p, const float* x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = x[4 * j + e];
+    *reinterpret_cast<f32x4*>(p + 4 * j) = v;
+  }
+}
 // State rows of a pass: up to 256 with bf16 records; the fp32 passes of the
 // backward whose rows are the d_v channels take up to 512.
 constexpr int kMaxRowsF32 = 512, kMaskWords = kMaxRowsF32 / 32;
@@ -139,22 +166,25 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
                                                       uint8_t* __restrict__ rec, size_t rec_bytes,
                                                       int L, int dk, int dkp, int NC, int rev) {
   extern __shared__ float sm[];
-  const int ld = dkp + 1;  // odd row stride: the P loop reads 16 rows at one column
+  // The chunk's q, k and cumsum are staged channel-major, [dkp][16]: a
+  // channel's 16 tokens are contiguous (the per-channel cumsum reads and
+  // writes them in 16-byte units), and the P loop's 64 lanes (16 tokens of 4
+  // channels) read 64 consecutive words.
   // q and k staged in QS: bf16 inputs are exact in bf16, half the LDS of an
   // fp32 copy, which lets the 256-channel passes fit one more workgroup per
   // CU (below 256 channels fp32 staging measured faster)
   QS* qs = reinterpret_cast<QS*>(sm);
-  QS* ks = qs + kGC * ld;
-  float* cs = reinterpret_cast<float*>(ks + kGC * ld);  // cumsum, hi part
+  QS* ks = qs + kGC * dkp;
+  float* cs = reinterpret_cast<float*>(ks + kGC * dkp);  // cumsum, hi part
   // lo part of the cumsum: fp32 passes only (for bf16 records the cumsum is
   // not compensated, its lo part is 0, and the array is left out)
   constexpr bool LO = sizeof(T) == 4;
-  float* cl = cs + kGC * ld;
-  float* part = (LO ? cl + kGC * ld : cl);  // the four waves' partial P tiles
+  float* cl = cs + kGC * dkp;
+  float* part = (LO ? cl + kGC * dkp : cl);  // the four waves' partial P tiles
   uint32_t* umask = reinterpret_cast<uint32_t*>(part + 1024);  // channels left to the log-space sum
   // bf16: Q~ and K~ in record order, written out in 16-byte units (16-byte
-  // aligned: the arrays above are 2 (16 (dkp + 1)) QS, 16 (dkp + 1) + 1024
-  // + kMaskWords floats).  fp32
+  // aligned: the arrays above are 2 (16 dkp) QS, 16 dkp + 1024 + kMaskWords
+  // floats).  fp32
   // stores its elements directly: staging would take the 256-channel
   // passes' LDS past what lets two workgroups share a CU.
   constexpr bool STAGE = sizeof(T) == 2;
@@ -163,9 +193,10 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   if (tid < kMaskWords) umask[tid] = 0u;
   // q, k and log alpha of the chunk, 8 channels per load (dk is a multiple of
-  // 16 and the padded channels are zero)
+  // 16 and the padded channels are zero); consecutive lanes take consecutive
+  // rows, so that a 16-lane group's channel-major stores are consecutive
   for (int x = tid; x < kGC * (dkp / 8); x += kThreads) {
-    const int t = x / (dkp / 8), i = (x - t * (dkp / 8)) * 8, u = n * kGC + t;
+    const int t = x % kGC, i = (x / kGC) * 8, u = n * kGC + t;
     const int dr = data_row(u, L, rev), gr = gate_row(u, L, rev);
     float qv[8], kv[8], av[8];
 #pragma unroll
@@ -186,9 +217,9 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      qs[t * ld + i + e] = from_f32<QS>(qv[e]);
-      ks[t * ld + i + e] = from_f32<QS>(kv[e]);
-      cs[t * ld + i + e] = av[e];
+      qs[(i + e) * kGC + t] = from_f32<QS>(qv[e]);
+      ks[(i + e) * kGC + t] = from_f32<QS>(kv[e]);
+      cs[(i + e) * kGC + t] = av[e];
     }
   }
   __syncthreads();
@@ -199,12 +230,9 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   // after a store that may alias it would wait for that store)
   for (int i = tid; i < dkp; i += kThreads) {
     float at[kGC], al[kGC], qv[kGC], kv[kGC];
-#pragma unroll
-    for (int t = 0; t < kGC; ++t) {
-      at[t] = cs[t * ld + i];
-      qv[t] = to_f32(qs[t * ld + i]);
-      kv[t] = to_f32(ks[t * ld + i]);
-    }
+    lds16(cs + i * kGC, at);
+    lds16(qs + i * kGC, qv);
+    lds16(ks + i * kGC, kv);
     float c = 0.f, e = 0.f;
 #pragma unroll
     for (int t = 0; t < kGC; ++t) {
@@ -214,11 +242,8 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
       at[t] = c;
       al[t] = e;
     }
-#pragma unroll
-    for (int t = 0; t < kGC; ++t) {
-      cs[t * ld + i] = at[t];
-      if constexpr (LO) cl[t * ld + i] = al[t];
-    }
+    sts16(cs + i * kGC, at);
+    if constexpr (LO) sts16(cl + i * kGC, al);
     ga[i] = gexp<T>(c + e);
     if (at[0] - c > kSafeP) atomicOr(&umask[i >> 5], 1u << (i & 31));
 #pragma unroll
@@ -248,12 +273,13 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
     for (int i0 = w * span; i0 < (w + 1) * span; i0 += 4) {
       const int i = i0 + kk;
       const bool sf = !((umask[i >> 5] >> (i & 31)) & 1u);
-      const float c0 = cs[i], l0 = LO ? cl[i] : 0.f;
-      const float a = sf ? to_f32(qs[r16 * ld + i]) *
-                               gexp<T>((cs[r16 * ld + i] - c0) + (LO ? cl[r16 * ld + i] - l0 : 0.f))
+      const int it = i * kGC;
+      const float c0 = cs[it], l0 = LO ? cl[it] : 0.f;
+      const float a = sf ? to_f32(qs[it + r16]) *
+                               gexp<T>((cs[it + r16] - c0) + (LO ? cl[it + r16] - l0 : 0.f))
                          : 0.f;
-      const float b = sf ? to_f32(ks[r16 * ld + i]) *
-                               gexp<T>((c0 - cs[r16 * ld + i]) + (LO ? l0 - cl[r16 * ld + i] : 0.f))
+      const float b = sf ? to_f32(ks[it + r16]) *
+                               gexp<T>((c0 - cs[it + r16]) + (LO ? l0 - cl[it + r16] : 0.f))
                          : 0.f;
       acc = mfma4(a, b, acc);
     }
@@ -265,16 +291,11 @@ __global__ __launch_bounds__(kThreads) void k_gg_prep(const TI* __restrict__ q,
   float acc = 0.f;
   if (s <= t) {
     acc = part[tid] + part[256 + tid] + part[512 + tid] + part[768 + tid];
-    const QS* qt = qs + t * ld;
-    const QS* ksr = ks + s * ld;
-    const float* ct = cs + t * ld;
-    const float* csr = cs + s * ld;
-    const float* lt = cl + t * ld;
-    const float* lsr = cl + s * ld;
     for (int wd = 0; wd < ((dkp + 31) >> 5); ++wd)
       for (uint32_t m = umask[wd]; m; m &= m - 1) {
-        const int i = wd * 32 + __builtin_ctz(m);
-        acc += to_f32(qt[i]) * to_f32(ksr[i]) * gexp<T>((ct[i] - csr[i]) + (LO ? lt[i] - lsr[i] : 0.f));
+        const int i = (wd * 32 + __builtin_ctz(m)) * kGC;
+        acc += to_f32(qs[i + t]) * to_f32(ks[i + s]) *
+               gexp<T>((cs[i + t] - cs[i + s]) + (LO ? cl[i + t] - cl[i + s] : 0.f));
       }
   }
   pf[pf_index(t, s)] = s < t ? acc : 0.f;
@@ -1095,8 +1116,8 @@ hipError_t launch_gg_pass(const GgPass& ps, int part, int is_bf16, int in_bf16, 
     // the mask words (53.5 KB at 256 fp32 channels with bf16 inputs, 69.9 KB
     // with fp32 ones, 135.5 KB at 512 fp32), and for bf16 the staged Q~, K~
     const bool qsb = in_bf16 && dkp >= 256;
-    const size_t lds = (size_t)2 * kGC * (dkp + 1) * (qsb ? 2 : 4) +
-                       sizeof(float) * ((is_bf16 ? 1 : 2) * kGC * (dkp + 1) + 1024 + kMaskWords) +
+    const size_t lds = (size_t)2 * kGC * dkp * (qsb ? 2 : 4) +
+                       sizeof(float) * ((is_bf16 ? 1 : 2) * kGC * dkp + 1024 + kMaskWords) +
                        (is_bf16 ? (size_t)2 * kGC * dkp * 2 : 0);
     const dim3 pg(NC, BH);
     hipError_t e;
