@@ -304,6 +304,24 @@ def timed(fn, steps, torch):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
+def step_percentiles(fn, steps, torch):
+    """Per-step durations (us) of `steps` calls of fn(i), each bracketed by
+    HIP events on the current stream (the stream the library launches on):
+    10th percentile, median and 90th percentile.  A pass of its own, after
+    the timed steps; the events between steps add a little to each."""
+    import statistics
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+    pick = lambda f: us[min(len(us) - 1, int(round(f * (len(us) - 1))))]
+    return {"p10": round(pick(0.1), 2), "median": round(statistics.median(us), 2),
+            "p90": round(pick(0.9), 2), "steps": steps}
+
+
 def copy_bandwidth(torch, dev, copies=60):
     """A plain device copy of 1 GiB, `copies` times: achievable HBM bandwidth
     for context (it also brings the GPU out of its idle clock state)."""
@@ -354,15 +372,20 @@ def forward_leg(w, args, torch, gla, _abi, dev, stream, primary):
     step(0)
     torch.cuda.synchronize()
     assert torch.isfinite(sets[0]["o"].float()).all().item()
-    for i in range(args.warmup):
+    # the metric's own leg runs exactly the requested warm-up and timed steps;
+    # the other legs at least 20 and 50, so that short runs stay steady
+    nwarm = args.warmup if primary else max(20, args.warmup)
+    ksteps = args.steps if primary else max(50, args.steps)
+    for i in range(nwarm):
         step(i)
-    ms = timed(step, args.steps, torch)
-    log(f"[bench] {w.name}: timed {args.steps} steps, {ms * 1e3:.1f} us/step")
-    _abi.gla_profile_begin(args.steps * 8)
-    ms_prof = timed(step, args.steps, torch)
+    ms = timed(step, ksteps, torch)
+    log(f"[bench] {w.name}: timed {ksteps} steps, {ms * 1e3:.1f} us/step")
+    _abi.gla_profile_begin(ksteps * 8)
+    ms_prof = timed(step, ksteps, torch)
     _abi.gla_profile_end()
     per = events_by_kernel(_abi)
-    warm = timed(lambda i: step(i, rotate=False), args.steps, torch) if primary else None
+    warm = timed(lambda i: step(i, rotate=False), ksteps, torch) if primary else None
+    pct = step_percentiles(step, ksteps, torch)
 
     tokens = w.B * w.L
     flops = w.stated_flops_fwd()
@@ -390,7 +413,7 @@ def forward_leg(w, args, torch, gla, _abi, dev, stream, primary):
                 "overhead_bytes_per_launch": over.get(dom),
                 "avg_launch_us": round(dom_s * 1e6, 2)}
     step_gbps = comp / (ms * 1e-3) / 1e9
-    out = {"workload": w.name, "ms_per_step": round(ms, 5),
+    out = {"workload": w.name, "steps": ksteps, "ms_per_step": round(ms, 5),
            "ms_per_step_profiled": round(ms_prof, 5),
            "tokens_per_s": round(tokens / (ms * 1e-3), 1),
            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
@@ -399,7 +422,7 @@ def forward_leg(w, args, torch, gla, _abi, dev, stream, primary):
            "step_roofline": {"bound": "hbm", "compulsory_bytes": comp,
                              "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS,
                              "unit": "GB/s", "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
-           "kernels": kernels, "input_sets": nsets}
+           "kernels": kernels, "input_sets": nsets, "step_us_percentiles": pct}
     if warm is not None:
         out["warm"] = {"ms_per_step": round(warm, 5),
                        "tokens_per_s": round(tokens / (warm * 1e-3), 1)}
@@ -436,11 +459,12 @@ def backward_leg(w, args, torch, gla, _abi, dev, stream):
             raise gla.GlaError(st, "gla_fwd")
         bwd(i)
 
-    for i in range(max(3, args.warmup)):
+    for i in range(max(20, args.warmup)):
         fb(i)
-    kb = max(5, args.steps)
+    kb = max(50, args.steps)
     bwd_ms = timed(bwd, kb, torch)
     fb_ms = timed(fb, kb, torch)
+    bwd_pct = step_percentiles(bwd, kb, torch)
     # the materialised-state backward on the same inputs, for comparison
     mat_ms = None
     mcfg = gla.bwd_config("materialized")
@@ -483,7 +507,7 @@ def backward_leg(w, args, torch, gla, _abi, dev, stream):
     return {"workload": w.name, "steps": kb,
             "ms_per_step": round(fb_ms, 5),
             "tokens_per_s": round(tokens / (fb_ms * 1e-3), 1),
-            "bwd_ms": round(bwd_ms, 5),
+            "bwd_ms": round(bwd_ms, 5), "bwd_step_us_percentiles": bwd_pct,
             "bwd_ms_materialized": round(mat_ms, 5) if mat_ms else None,
             "bwd_tokens_per_s": round(tokens / (bwd_ms * 1e-3), 1),
             "bwd_tflops": round(fl / (bwd_ms * 1e-3) / 1e12, 2),
@@ -910,10 +934,14 @@ def main():
                    "input_sets": main_leg["input_sets"]},
         "tflops": main_leg["tflops"], "frac_bf16_mfma_peak": main_leg["frac_bf16_mfma_peak"],
         "warm": main_leg.get("warm"),
+        "step_us_percentiles": main_leg["step_us_percentiles"],
         "roofline": main_leg["roofline"], "step_roofline": main_leg["step_roofline"],
         "kernels": main_leg["kernels"], "copy_gbps": round(copy_gbps, 1),
         "legs": legs, "fwd_bwd": backward, "decode": decode, "general": general,
         "layer": layer, "cpu_baseline": cpu,
+        # the build, identified by its kernel sources (GPU runs see no git
+        # history)
+        "build": {"sources_sha256": sources_digest(KERNEL_SOURCES)},
     }
     print(json.dumps(out), flush=True)
 
