@@ -125,7 +125,8 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
   }
   const size_t BH = (size_t)P.BH, S = (size_t)dk * dv;
   size_t off = 0;
-  P.off_cum = off; off = align_up(off + BH * L * dk * 4);
+  // the chunk cumsum; fp32: followed by its low part (cum_lo_of)
+  P.off_cum = off; off = align_up(off + BH * L * dk * 4 * (bf16 ? 1 : 2));
   P.off_sg = off; off = align_up(off + BH * (size_t)(P.NSEG > P.NSEGF ? P.NSEG : P.NSEGF) * dk * 4);
   P.off_st = off; off = align_up(off + BH * P.NC * S * P.esize);
   P.off_seg_u = off; off = align_up(off + (P.NSEG > 1 ? BH * P.NSEG * S * 4 : 0));
@@ -461,7 +462,7 @@ gla_status gla_fwd_ex(const gla_dims* dims, int dtype, const gla_fwd_config* cfg
   float* seg_in = (float*)(ws + p.off_seg_in);
 
   if (p.recur) return run_two_pass(p, q, k, v, log_alpha, h0, o, hT, ws, s);
-  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
+  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, cum_lo_of(p, cum), s));
   if (p.fused) {
     // segment entry states from the segments' local states, then one fused
     // pass per segment that keeps the state on chip
@@ -558,7 +559,7 @@ gla_status gla_bwd_ex(const gla_dims* dims, int dtype, const gla_bwd_config* cfg
 
   // recompute the chunk states (not stored by the forward), and the reverse
   // recurrence of the state gradient: independent, so one launch runs both
-  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, s));
+  GLA_LAUNCH("chunk_cumsum", launch_cumsum(p, log_alpha, cum, cum_lo_of(p, cum), s));
   if (p.NSEG > 1) {
     GLA_LAUNCH("chunk_state_local", launch_chunk_state(p, 0, SEG_LOCAL, p.bf16, k, v, cum, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seg_u, sg, s));
     GLA_LAUNCH("segment_scan", launch_segment_scan(p, 0, sg, h0, seg_u, seg_in, hT, s));

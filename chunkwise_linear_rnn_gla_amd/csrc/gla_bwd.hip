@@ -24,16 +24,19 @@ namespace gla {
 // ------------------------------------------------------------------ B3a: A and dA per chunk
 // A (the forward's score matrix, fp32) and dA = (dO V^T) ⊙ M, written to the
 // workspace as C x C fp32 blocks (zeros above the diagonal).
+// fp32 (cum_lo): the decay exponents of A take the cumsum's low part too.
 template <typename T, int C>
 __global__ __launch_bounds__(kThreads) void k_chunk_attn(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ dout, const float* __restrict__ cum, float* __restrict__ Aw,
-    float* __restrict__ dAw, int L, int dk, int dv, int NC) {
+    const T* __restrict__ dout, const float* __restrict__ cum, const float* __restrict__ cum_lo,
+    float* __restrict__ Aw, float* __restrict__ dAw, int L, int dk, int dv, int NC) {
   using M = Mma<T>;
   using PB = PBuilder<T, C>;
   constexpr int LDT = PB::LDT, LDF = PB::LDF, KS = PB::KS;
   constexpr int NRT = C / 16, NTRI = NRT * (NRT + 1) / 2;
+  constexpr bool LO = sizeof(T) == 4;
   __shared__ __attribute__((aligned(16))) unsigned char smem[PB::SLICE_BYTES];
+  __shared__ __attribute__((aligned(16))) float bsl[LO ? C * LDF : 1];
   __shared__ float pd[4][16][17];
   T* qs = reinterpret_cast<T*>(smem);
   T* ks = qs + C * LDT;
@@ -96,9 +99,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_attn(
   for (int s0 = 0; s0 < dk; s0 += KS) {
     lds_barrier();
     PB::stage(q, k, cum, qo, r0, rv, dk, s0, qs, ks, bs, nullptr);
+    if constexpr (LO) PB::stage_lo(cum_lo, qo, r0, rv, dk, s0, bsl);
     lds_barrier();
-    PB::gates(bs, als);
-    pb.offdiag(qs, ks, bs);
+    PB::template gates<LO>(bs, als, bsl);
+    pb.template offdiag<LO>(qs, ks, bs, bsl);
     lds_barrier();
     pb.diag(qs, ks, als);
   }
@@ -226,10 +230,12 @@ constexpr float kFoldSpan = 30.f;
 // from dqi / dki (k_bwd_inter) instead of products with materialised states,
 // and dlog alpha is written whole (with the carry over later chunks, from
 // cq, ck and crs); without IB it is chunk-local, its chunk totals go to dlt.
+// fp32 (cum_lo): every decay exponent takes the cumsum's low part too.
 template <typename T, int C, int TK, bool IB>
 __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ dout, const float* __restrict__ cum, const T* __restrict__ st_n,
+    const T* __restrict__ dout, const float* __restrict__ cum, const float* __restrict__ cum_lo,
+    const T* __restrict__ st_n,
     const T* __restrict__ st_lo, const T* __restrict__ dst_n, const T* __restrict__ dst_lo,
     const float* __restrict__ dAw, const float* __restrict__ dqi, const float* __restrict__ dki,
     T* __restrict__ dq, T* __restrict__ dkk, float* __restrict__ dla, float* __restrict__ dlt,
@@ -237,6 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
     int L, int dk, int dv, int NC) {
   using M = Mma<T>;
   constexpr bool BF = sizeof(T) == 2;
+  constexpr bool LO = !BF;
   constexpr int PT = 16 / (int)sizeof(T);
   constexpr int LDA = C + PT;            // T rows of length C
   constexpr int LDK = TK + 4;            // fp32 rows of length TK
@@ -250,6 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   // C + 4 floats puts 16 consecutive channels' 16-byte reads on distinct banks
   constexpr int LDC = C + 4;
   __shared__ __attribute__((aligned(16))) float qf[TK][LDC], kf[TK][LDC], bt[TK][LDC];
+  __shared__ __attribute__((aligned(16))) float btl[LO ? TK : 1][LDC];  // the cumsum's low part
   // One region serves, in turn, dA with its diagonal blocks zeroed (rows for
   // the dq blocks, transposed reads for the dk blocks; with its low part for
   // bf16), the diagonal blocks' terms of dq and dk (dgo), and dlog b.
@@ -346,11 +354,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   const bool tvalid = trow < rv;
   const size_t tgi = qo + (size_t)(tvalid ? r0 + trow : r0 + rv - 1) * dk + c0 + tc;
   Raw8<T> tq_, tk_;
-  Raw8<float> tb_;
+  Raw8<float> tb_, tbl_;
   if (has_tile) {
     raw_load(tq_, q + tgi);
     raw_load(tk_, k + tgi);
     raw_load(tb_, cum + tgi);
+    if constexpr (LO) raw_load(tbl_, cum_lo + tgi);
   }
   InterFrags f0;
   if constexpr (!IB) {
@@ -429,6 +438,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       qf[tc + e][trow] = tvalid ? raw_get(tq_, e) : 0.f;
       kf[tc + e][trow] = tvalid ? raw_get(tk_, e) : 0.f;
       bt[tc + e][trow] = raw_get(tb_, e);
+      if constexpr (LO) btl[tc + e][trow] = raw_get(tbl_, e);
     }
   }
   // The diagonal sub-chunk blocks are folded into the products below (their
@@ -484,10 +494,16 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         const int c = (wc + WC * ct) * 16 + (l & 15);
         const float blast = bt[c][C - 1];
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[c][rti * 16 + (l >> 4) * 4]);
+        float blastl = 0.f;
+        f32x4 bl4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LO) {
+          blastl = btl[c][C - 1];
+          bl4 = *reinterpret_cast<const f32x4*>(&btl[c][rti * 16 + (l >> 4) * 4]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          aq[rt][ct][r] *= gexp<T>(b4[r]);
-          ak[rt][ct][r] *= gexp<T>(blast - b4[r]);
+          aq[rt][ct][r] *= gexp<T>(b4[r] + bl4[r]);
+          ak[rt][ct][r] *= gexp<T>((blast - b4[r]) + (blastl - bl4[r]));
         }
       }
     }
@@ -503,8 +519,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
   // for bf16; the A operand is dA's rows (dq) or, read transposed, its
   // columns (dk).  Nothing is written to LDS here.
   // x = src[tok][c] e^{+-(B_tok - z)} for tok in [t0, t1), else 0
-  auto gated = [&](const float (*src)[LDC], int c, int kc, int t0, int t1, float z, bool up,
-                   typename M::frag& fh, typename M::frag& fl) __attribute__((always_inline)) {
+  auto gated = [&](const float (*src)[LDC], int c, int kc, int t0, int t1, float z, float zl,
+                   bool up, typename M::frag& fh, typename M::frag& fl)
+                   __attribute__((always_inline)) {
     if constexpr (BF) {
       const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bt[c][kc]);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bt[c][kc + 4]);
@@ -521,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
         fl[e] = static_cast<bf16>(x - static_cast<float>(fh[e]));
       }
     } else {
-      const float g = up ? bt[c][kc] - z : z - bt[c][kc];
+      const float g = up ? (bt[c][kc] - z) + (btl[c][kc] - zl) : (z - bt[c][kc]) + (zl - btl[c][kc]);
       fh = (kc >= t0 && kc < t1) ? src[c][kc] * gexp<T>(g) : 0.f;
       fl = 0.f;
     }
@@ -535,11 +552,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
         const float z = bt[c][16 * j];
+        const float zl = LO ? btl[c][16 * j] : 0.f;
         floatx4 t4 = zero4();
         for (int kk = 0; kk < OC::KQ(j, fold); kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
           typename M::frag bh, bl;
-          gated(kf, c, kc, 0, 16 * (j + fold), z, false, bh, bl);
+          gated(kf, c, kc, 0, 16 * (j + fold), z, zl, false, bh, bl);
           const auto ah = load_frag<T>(&da[j * 16 + (l & 15)][kc]);
           t4 = M::run(ah, bh, t4);
           if constexpr (BF) {
@@ -548,8 +566,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
           }
         }
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[c][j * 16 + (l >> 4) * 4]);
+        f32x4 bl4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LO) bl4 = *reinterpret_cast<const f32x4*>(&btl[c][j * 16 + (l >> 4) * 4]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) aq[rt][ct][r] += gexp<T>(b4[r] - z) * t4[r];
+        for (int r = 0; r < 4; ++r) aq[rt][ct][r] += gexp<T>((b4[r] - z) + (bl4[r] - zl)) * t4[r];
       }
     }
 #pragma unroll
@@ -560,11 +580,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
       for (int ct = 0; ct < NCW; ++ct) {
         const int c = (wc + WC * ct) * 16 + (l & 15);
         const float z = bt[c][16 * u + 15];
+        const float zl = LO ? btl[c][16 * u + 15] : 0.f;
         floatx4 t4 = zero4();
         for (int kk = OC::MLO(u, fold); kk < C; kk += M::K) {
           const int kc = kk + (l >> 4) * M::KPL;
           typename M::frag bh, bl, ah, alo;
-          gated(qf, c, kc, 16 * (u + !fold), C, z, true, bh, bl);
+          gated(qf, c, kc, 16 * (u + !fold), C, z, zl, true, bh, bl);
           // A[r][m] = dA[m][r] for r in sub-chunk u (the lane's row), m at kc
           if constexpr (BF) {
             ah = col_frag_tr(&da[0][0], LDA, kk, 16 * u, l);
@@ -579,8 +600,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
           }
         }
         const f32x4 b4 = *reinterpret_cast<const f32x4*>(&bt[c][u * 16 + (l >> 4) * 4]);
+        f32x4 bl4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LO) bl4 = *reinterpret_cast<const f32x4*>(&btl[c][u * 16 + (l >> 4) * 4]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ak[rt][ct][r] += gexp<T>(z - b4[r]) * t4[r];
+        for (int r = 0; r < 4; ++r) ak[rt][ct][r] += gexp<T>((z - b4[r]) + (zl - bl4[r])) * t4[r];
       }
     }
     lds_barrier();  // the diagonal terms below and dlog b reuse the region
@@ -597,7 +620,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         // the per-row gate alpha of row i in the block (row 0's is not used)
-        a[i] = i ? gexp<T>(bt[c][16 * b + i] - bt[c][16 * b + i - 1]) : 1.f;
+        float d = i ? bt[c][16 * b + i] - bt[c][16 * b + i - 1] : 0.f;
+        if constexpr (LO) d += i ? btl[c][16 * b + i] - btl[c][16 * b + i - 1] : 0.f;
+        a[i] = i ? gexp<T>(d) : 1.f;
         x[i] = which ? qf[c][16 * b + i] : kf[c][16 * b + i];
       }
       const float* dd = &dad[16 * b][0];  // [16][17]: dA[16 b + m][16 b + s]
@@ -714,10 +739,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dqdk(
 
 // ------------------------------------------------------------------ B3c: dv
 // One workgroup per (batch-head, chunk, d_v tile): dV = (K ⊙ Gamma) dS_n + A^T dO.
+// fp32 (cum_lo): Gamma's exponents take the cumsum's low part too.
 template <typename T, int C, int TVD>
 __global__ __launch_bounds__(kThreads) void k_chunk_dv(
     const T* __restrict__ k, const T* __restrict__ dout, const float* __restrict__ cum,
-    const T* __restrict__ dst_t, const float* __restrict__ Aw, T* __restrict__ dvv, int L,
+    const float* __restrict__ cum_lo, const T* __restrict__ dst_t, const float* __restrict__ Aw, T* __restrict__ dvv, int L,
     int dk, int dv, int NC) {
   using M = Mma<T>;
   constexpr bool BF = sizeof(T) == 2;
@@ -791,12 +817,20 @@ __global__ __launch_bounds__(kThreads) void k_chunk_dv(
       const int m = it / (ks / 8), c = (it % (ks / 8)) * 8;
       const int mm = m < rv ? m : rv - 1;
       const size_t gi = qo + (size_t)(r0 + mm) * dk + s0 + c;
-      float kv[8], bv[8], bl[8], x[8];
+      float kv[8], bv[8], bl[8], x[8], d[8];
       load8(k + gi, kv);
       load8(cum + gi, bv);
       load8(blast + s0 + c, bl);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = m < rv ? kv[e] * gexp<T>(bl[e] - bv[e]) : 0.f;
+      for (int e = 0; e < 8; ++e) d[e] = bl[e] - bv[e];
+      if constexpr (!BF) {
+        load8(cum_lo + gi, bv);
+        load8(cum_lo + (blast - cum) + s0 + c, bl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[e] += bl[e] - bv[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = m < rv ? kv[e] * gexp<T>(d[e]) : 0.f;
       store8(&kt[m][c], x);
     }
     lds_barrier();
@@ -919,8 +953,8 @@ static hipError_t launch_attn_t(const Plan& p, const void* q, const void* k, con
                                 const void* dout, const float* cum, float* Aw, float* dAw,
                                 hipStream_t s) {
   hipLaunchKernelGGL((k_chunk_attn<T, C>), dim3(p.NC, p.BH), dim3(kThreads), 0, s, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)dout, cum, Aw, dAw, p.L, p.dk, p.dv,
-                     p.NC);
+                     (const T*)k, (const T*)v, (const T*)dout, cum, cum_lo_of(p, cum), Aw, dAw,
+                     p.L, p.dk, p.dv, p.NC);
   return hipGetLastError();
 }
 
@@ -944,7 +978,7 @@ static hipError_t launch_dqdk_t(const Plan& p, const void* q, const void* k, con
                                 hipStream_t s) {
   hipLaunchKernelGGL((k_chunk_dqdk<T, C, TK, false>), dim3(p.NC, p.dk / TK, p.BH), dim3(kThreads),
                      0, s, (const T*)q, (const T*)k, (const T*)v, (const T*)dout, cum,
-                     (const T*)st_n, (const T*)st_lo, (const T*)dst_n, (const T*)dst_lo, dAw,
+                     cum_lo_of(p, cum), (const T*)st_n, (const T*)st_lo, (const T*)dst_n, (const T*)dst_lo, dAw,
                      nullptr, nullptr, (T*)dq, (T*)dk, dla, dlt, nullptr, nullptr, nullptr, p.L,
                      p.dk, p.dv, p.NC);
   return hipGetLastError();
@@ -957,7 +991,7 @@ hipError_t launch_chunk_dqdk_inter(const Plan& p, const void* q, const void* k, 
   if (!p.bf16 || p.C != 64 || p.dk % 32) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_chunk_dqdk<bf16, 64, 32, true>), dim3(p.NC, p.dk / 32, p.BH),
                      dim3(kThreads), 0, s, (const bf16*)q, (const bf16*)k, nullptr, nullptr, cum,
-                     nullptr, nullptr, nullptr, nullptr, dAw, dqi, dki, (bf16*)dq, (bf16*)dk, dla,
+                     nullptr, nullptr, nullptr, nullptr, nullptr, dAw, dqi, dki, (bf16*)dq, (bf16*)dk, dla,
                      nullptr, qpre, ksuf, rs, p.L, p.dk, p.dv, p.NC);
   return hipGetLastError();
 }
@@ -994,7 +1028,7 @@ template <typename T, int C, int TVD>
 static hipError_t launch_dv_t(const Plan& p, const void* k, const void* dout, const float* cum,
                               const void* dst_t, const float* Aw, void* dv, hipStream_t s) {
   hipLaunchKernelGGL((k_chunk_dv<T, C, TVD>), dim3(p.NC, p.dv / TVD, p.BH), dim3(kThreads), 0, s,
-                     (const T*)k, (const T*)dout, cum, (const T*)dst_t, Aw, (T*)dv, p.L, p.dk,
+                     (const T*)k, (const T*)dout, cum, cum_lo_of(p, cum), (const T*)dst_t, Aw, (T*)dv, p.L, p.dk,
                      p.dv, p.NC);
   return hipGetLastError();
 }

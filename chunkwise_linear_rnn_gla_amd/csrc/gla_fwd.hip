@@ -23,12 +23,29 @@ namespace gla {
 // 16 consecutive rows (16 independent 16-byte loads in flight); the 16-row
 // group totals are combined through LDS.  Within a row group the sum runs in
 // row order, and group offsets are added in group order.
+//
+// With cum_lo (the fp32 backward), every sum is compensated (two-sum): cum
+// holds the rounded cumsum and cum_lo the rounding error it leaves, so that a
+// decay exponent B_m - B_r = (cum_m - cum_r) + (lo_m - lo_r) keeps its
+// accuracy relative to its own size however large |B| grows in the chunk.
 constexpr int kCumRows = 16;
 
+__device__ inline f32x4 two_sum4(const f32x4& a, const f32x4& b, f32x4& err) {
+  f32x4 s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s[e] = a[e] + b[e];
+    const float bp = s[e] - a[e];
+    err[e] = (a[e] - (s[e] - bp)) + (b[e] - bp);
+  }
+  return s;
+}
+
 __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ a,
-                                                     float* __restrict__ cum, int L, int dk,
+                                                     float* __restrict__ cum,
+                                                     float* __restrict__ cum_lo, int L, int dk,
                                                      int C, int NC, int BH) {
-  __shared__ f32x4 tot[kThreads];
+  __shared__ f32x4 tot[kThreads], totl[kThreads];
   const int quads = dk / 4, groups = C / kCumRows;      // per chunk
   const int per_chunk = quads * groups;                 // threads per chunk (<= 256)
   const int cpb = kThreads / per_chunk;                 // chunks per block
@@ -45,28 +62,63 @@ __global__ __launch_bounds__(kThreads) void k_cumsum(const float* __restrict__ a
   for (int i = 0; i < kCumRows; ++i)
     if (r0 + i < r1) v[i] = *reinterpret_cast<const f32x4*>(a + base + (size_t)(r0 + i) * dk);
   f32x4 run = {0.f, 0.f, 0.f, 0.f};
+  if (!cum_lo) {
+#pragma unroll
+    for (int i = 0; i < kCumRows; ++i) {
+      if (r0 + i < r1) {
+        run += v[i];
+        v[i] = run;
+      }
+    }
+    tot[t] = run;
+    __syncthreads();
+    f32x4 off = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < rg; ++g) off += tot[sub * per_chunk + g * quads + gq];
+#pragma unroll
+    for (int i = 0; i < kCumRows; ++i)
+      if (r0 + i < r1) *reinterpret_cast<f32x4*>(cum + base + (size_t)(r0 + i) * dk) = v[i] + off;
+    return;
+  }
+  // compensated: (v[i], vl[i]) is the group's running sum as hi + lo
+  f32x4 vl[kCumRows], runl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kCumRows; ++i) {
+    vl[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (r0 + i < r1) {
-      run += v[i];
+      f32x4 e;
+      run = two_sum4(run, v[i], e);
+      runl += e;
       v[i] = run;
+      vl[i] = runl;
     }
   }
   tot[t] = run;
+  totl[t] = runl;
   __syncthreads();
-  f32x4 off = {0.f, 0.f, 0.f, 0.f};
-  for (int g = 0; g < rg; ++g) off += tot[sub * per_chunk + g * quads + gq];
+  f32x4 off = {0.f, 0.f, 0.f, 0.f}, offl = {0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < rg; ++g) {
+    f32x4 e;
+    off = two_sum4(off, tot[sub * per_chunk + g * quads + gq], e);
+    offl += e + totl[sub * per_chunk + g * quads + gq];
+  }
 #pragma unroll
   for (int i = 0; i < kCumRows; ++i)
-    if (r0 + i < r1) *reinterpret_cast<f32x4*>(cum + base + (size_t)(r0 + i) * dk) = v[i] + off;
+    if (r0 + i < r1) {
+      f32x4 e;
+      const f32x4 h = two_sum4(v[i], off, e);
+      *reinterpret_cast<f32x4*>(cum + base + (size_t)(r0 + i) * dk) = h;
+      *reinterpret_cast<f32x4*>(cum_lo + base + (size_t)(r0 + i) * dk) = vl[i] + offl + e;
+    }
 }
 
-hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t s) {
+hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, float* cum_lo,
+                         hipStream_t s) {
   const int per_chunk = (p.dk / 4) * (p.C / kCumRows);
   const int cpb = kThreads / per_chunk;
   const long chunks = (long)p.BH * p.NC;
   dim3 grid((unsigned)((chunks + cpb - 1) / cpb));
-  hipLaunchKernelGGL(k_cumsum, grid, dim3(kThreads), 0, s, a, cum, p.L, p.dk, p.C, p.NC, p.BH);
+  hipLaunchKernelGGL(k_cumsum, grid, dim3(kThreads), 0, s, a, cum, cum_lo, p.L, p.dk, p.C, p.NC,
+                     p.BH);
   return hipGetLastError();
 }
 
@@ -89,10 +141,16 @@ hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t 
 // One launch can run two jobs (the forward recurrence of S and the reverse one
 // of dS): workgroups below nblk0 take job0, the rest job1, so that the two
 // chains, each mostly waiting on its own latencies, share the compute units.
+//
+// fp32: the decay exponents also take the cumsum's low part (cum_lo, the
+// two-sum compensation of k_cumsum), so that they stay accurate however large
+// the chunk-local cumsum grows.
 template <typename T, int TS, int SPLIT>
 __global__ __launch_bounds__(kThreads) void k_chunk_state(
-    StateJob job0, StateJob job1, int nblk0, const float* __restrict__ cum, int L, int dk, int dv,
-    int C, int NC, int NSEG, int seg_chunks) {
+    StateJob job0, StateJob job1, int nblk0, const float* __restrict__ cum,
+    const float* __restrict__ cum_lo, int L, int dk, int dv, int C, int NC, int NSEG,
+    int seg_chunks) {
+  constexpr bool LO = sizeof(T) == 4;
   const bool second = blockIdx.x >= (unsigned)nblk0;
   const StateJob& J = second ? job1 : job0;
   const int bid = second ? (int)blockIdx.x - nblk0 : (int)blockIdx.x;
@@ -157,13 +215,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
   const int nb = seg * seg_chunks, ne = min(NC, nb + seg_chunks), nsteps = max(0, ne - nb);
   // prefetch registers: this thread's rows of X, Y, cumsum and the chunk total
   Raw8<T> rx[RPT], ry[RPT];
-  f32x4 rb[RPT][2], rg[2];
+  f32x4 rb[RPT][2], rg[2], rbl[RPT][2], rgl[2];
 #define GLA_STATE_FETCH(NCH)                                                              \
   do {                                                                                     \
     const int fr0 = (NCH) * C, frv = min(C, L - fr0);                                      \
     const float* glast = cum + xo + (size_t)(fr0 + frv - 1) * dk + i0 + c0;                \
     rg[0] = *reinterpret_cast<const f32x4*>(glast);                                        \
     rg[1] = *reinterpret_cast<const f32x4*>(glast + 4);                                    \
+    if constexpr (LO) {                                                                    \
+      const float* gll = cum_lo + (glast - cum);                                           \
+      rgl[0] = *reinterpret_cast<const f32x4*>(gll);                                       \
+      rgl[1] = *reinterpret_cast<const f32x4*>(gll + 4);                                   \
+    }                                                                                      \
     _Pragma("unroll") for (int u = 0; u < RPT; ++u) {                                      \
       const int row = rbase + u * RS;                                                      \
       if (row < frv) {                                                                     \
@@ -172,10 +235,16 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
         const float* bp = cum + xo + (size_t)(fr0 + row) * dk + i0 + c0;                   \
         rb[u][0] = *reinterpret_cast<const f32x4*>(bp);                                    \
         rb[u][1] = *reinterpret_cast<const f32x4*>(bp + 4);                                \
+        if constexpr (LO) {                                                                \
+          const float* bpl = cum_lo + (bp - cum);                                          \
+          rbl[u][0] = *reinterpret_cast<const f32x4*>(bpl);                                \
+          rbl[u][1] = *reinterpret_cast<const f32x4*>(bpl + 4);                            \
+        }                                                                                  \
       } else {                                                                             \
         raw_zero(rx[u]);                                                                   \
         raw_zero(ry[u]);                                                                   \
         rb[u][0] = rb[u][1] = f32x4{};                                                     \
+        rbl[u][0] = rbl[u][1] = f32x4{};                                                   \
       }                                                                                    \
     }                                                                                      \
   } while (0)
@@ -195,7 +264,12 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float b = rb[u][e >> 2][e & 3], g = rg[e >> 2][e & 3];
-        xv[e] = raw_get(rx[u], e) * gexp<T>(REV ? b : g - b);
+        if constexpr (LO) {
+          const float bl = rbl[u][e >> 2][e & 3], gl = rgl[e >> 2][e & 3];
+          xv[e] = raw_get(rx[u], e) * (REV ? gexp<T>(b) * gexp<T>(bl) : gexp<T>((g - b) + (gl - bl)));
+        } else {
+          xv[e] = raw_get(rx[u], e) * gexp<T>(REV ? b : g - b);
+        }
         xlo[e] = xv[e] - to_f32(from_f32<T>(xv[e]));
         yv[e] = raw_get(ry[u], e);
       }
@@ -208,6 +282,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(
       for (int e = 0; e < 8; ++e) {
         gam[c0 + e] = gexp<T>(rg[e >> 2][e & 3]);
         gsum[e] += rg[e >> 2][e & 3];
+        if constexpr (LO) {
+          gam[c0 + e] *= gexp<T>(rgl[e >> 2][e & 3]);
+          gsum[e] += rgl[e >> 2][e & 3];
+        }
       }
     }
     // prefetch the next chunk while this one is consumed
@@ -333,8 +411,8 @@ template <typename T, int TS, int SPLIT>
 static hipError_t launch_cs(const Plan& p, const StateJob& a, const StateJob* b, hipStream_t s) {
   const int per = (p.dv / TS) * (p.dk / TS) * p.BH * p.NSEG;
   hipLaunchKernelGGL((k_chunk_state<T, TS, SPLIT>), dim3(b ? 2 * per : per), dim3(kThreads), 0, s,
-                     a, b ? *b : a, per, cum_of(a), p.L, p.dk, p.dv, p.C, p.NC, p.NSEG,
-                     p.seg_chunks);
+                     a, b ? *b : a, per, cum_of(a), cum_lo_of(p, cum_of(a)), p.L, p.dk, p.dv,
+                     p.C, p.NC, p.NSEG, p.seg_chunks);
   return hipGetLastError();
 }
 

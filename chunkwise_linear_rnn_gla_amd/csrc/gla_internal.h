@@ -62,7 +62,17 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
                const FwdOptions& opt = FwdOptions());
 
 // ---- forward kernels (gla_fwd.hip) ----
-hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, hipStream_t s);
+// cum_lo (nullable): the low part of a compensated cumsum.
+hipError_t launch_cumsum(const Plan& p, const float* a, float* cum, float* cum_lo, hipStream_t s);
+// The materialised and fused paths' fp32 chunk cumsum is followed in the
+// workspace by its low part (the two-sum compensation written by
+// k_cumsum); bf16 keeps no low part.
+inline float* cum_lo_of(const Plan& p, float* cum) {
+  return p.bf16 ? nullptr : cum + (size_t)p.BH * p.L * p.dk;
+}
+inline const float* cum_lo_of(const Plan& p, const float* cum) {
+  return p.bf16 ? nullptr : cum + (size_t)p.BH * p.L * p.dk;
+}
 
 // Chunk-state recurrence.  Forward (rev = 0): S_n = diag(g_n) S_{n-1} +
 // (X ⊙ e^{b_n - B})^T Y with X = k, Y = v; writes S_{n-1} per chunk.

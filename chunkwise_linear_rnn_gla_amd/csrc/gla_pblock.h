@@ -204,18 +204,39 @@ struct PBuilder {
     }
   }
 
-  // Per-row gates within each sub-chunk: als[row] = e^{B_row - B_{row-1}}
-  // (1 at a sub-chunk's first row, where it is never used).
-  __device__ static void gates(const float* bs, float* als) {
-    for (int it = threadIdx.x; it < C * KS; it += NTH) {
-      const int row = it / KS, c = it % KS;
-      als[row * LDF + c] =
-          (row & 15) ? gexp<T>(bs[row * LDF + c] - bs[(row - 1) * LDF + c]) : 1.f;
+  // The low part of a compensated cumsum (cum_lo) for the staged slice, in
+  // the layout of bs (rows past rv repeat the last valid row).
+  __device__ static void stage_lo(const float* cum_lo, size_t qo, int r0, int rv, int dk, int s0,
+                                  float* bsl) {
+    for (int it = threadIdx.x; it < C * (KS / 8); it += NTH) {
+      const int row = it / (KS / 8), c8 = (it % (KS / 8)) * 8;
+      const int crow = row < rv ? r0 + row : r0 + rv - 1;
+      float bv[8];
+      load8(cum_lo + qo + (size_t)crow * dk + s0 + c8, bv);
+      store8(bsl + row * LDF + c8, bv);
     }
   }
 
-  // Off-diagonal blocks, MFMA, accumulated over slices.  Needs qs, ks, bs.
-  __device__ void offdiag(const S* qs, const S* ks, const float* bs) {
+  // Per-row gates within each sub-chunk: als[row] = e^{B_row - B_{row-1}}
+  // (1 at a sub-chunk's first row, where it is never used); with bsl, the
+  // difference of the cumsum's hi + lo pairs.
+  template <bool LO = false>
+  __device__ static void gates(const float* bs, float* als, const float* bsl = nullptr) {
+    for (int it = threadIdx.x; it < C * KS; it += NTH) {
+      const int row = it / KS, c = it % KS;
+      float d = 0.f;
+      if (row & 15) {
+        d = bs[row * LDF + c] - bs[(row - 1) * LDF + c];
+        if constexpr (LO) d += bsl[row * LDF + c] - bsl[(row - 1) * LDF + c];
+      }
+      als[row * LDF + c] = (row & 15) ? gexp<T>(d) : 1.f;
+    }
+  }
+
+  // Off-diagonal blocks, MFMA, accumulated over slices.  Needs qs, ks, bs
+  // (and, LO, the cumsum's low part bsl).
+  template <bool LO = false>
+  __device__ void offdiag(const S* qs, const S* ks, const float* bs, const float* bsl = nullptr) {
 #pragma unroll
     for (int t = 0; t < NPW; ++t) {
       const int pi = w + NWV * t;
@@ -229,8 +250,14 @@ struct PBuilder {
 #pragma unroll
         for (int e = 0; e < M::KPL; ++e) {
           const float z = bs[(jq * 16) * LDF + cq + e];
-          sa[e] = gexp<T>(bs[(jq * 16 + m) * LDF + cq + e] - z);
-          sb[e] = gexp<T>(z - bs[(ju * 16 + m) * LDF + cq + e]);
+          float da = bs[(jq * 16 + m) * LDF + cq + e] - z, db = z - bs[(ju * 16 + m) * LDF + cq + e];
+          if constexpr (LO) {
+            const float zl = bsl[(jq * 16) * LDF + cq + e];
+            da += bsl[(jq * 16 + m) * LDF + cq + e] - zl;
+            db += zl - bsl[(ju * 16 + m) * LDF + cq + e];
+          }
+          sa[e] = gexp<T>(da);
+          sb[e] = gexp<T>(db);
         }
         typename M::frag a, b;
         if constexpr (BF && sizeof(S) == 4) {
