@@ -26,7 +26,8 @@ bool make_plan(int B, int H, int L, int dk, int dv, int C, int c, int bf16, Plan
     if (dk % 16 || dv % 16) return false;
   }
   if (dk < 16 || dk > 256 || dv < 16 || dv > 512) return false;
-  if ((int64_t)B * H > (1 << 20) || L > (1 << 24)) return false;
+  // B * H is a grid dimension (y or z) of most launches, which HIP caps at 65535
+  if ((int64_t)B * H > 65535 || L > (1 << 24)) return false;
   if (opt.algo < FWD_AUTO || opt.algo > FWD_MATERIALIZED) return false;
   if (opt.bwd_algo < BWD_AUTO || opt.bwd_algo > BWD_RECURRENT) return false;
   if (opt.recur_waves < 0 || opt.recur_segments < 0) return false;

@@ -40,7 +40,8 @@
  *               reach memory).  chunk in {16, 32, 64} for GLA_FP32 and
  *               {32, 64} for GLA_BF16; subchunk == 16.  dk and dv multiples
  *               of 16 (GLA_FP32) or 32 (GLA_BF16), 16 <= dk <= 256,
- *               16 <= dv <= 512.  Otherwise GLA_ERR_SHAPE.
+ *               16 <= dv <= 512; B * H <= 65535 and L <= 2^24.  Otherwise
+ *               GLA_ERR_SHAPE.
  */
 #ifndef GLA_H_
 #define GLA_H_

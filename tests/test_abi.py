@@ -71,6 +71,7 @@ def test_workspace_size_valid_and_monotone():
     (dict(dk=512), GLA_FP32),
     (dict(L=-1), GLA_FP32),
     (dict(B=-2), GLA_FP32),
+    (dict(B=256, H=257), GLA_FP32),  # B * H is a grid dimension: at most 65535
 ])
 def test_shape_errors(kw, dtype):
     st, _ = ws_status(good_dims(**kw), dtype)
